@@ -1,0 +1,120 @@
+"""Pins of the oracle's forward pass (CPU only).
+
+Integer mode is checked against torch's scaled_dot_product_attention (fp64) under a mask
+built by the brute-force membership predicate; W >= N is checked against SDPA's own causal
+path; interpolated mode against the dense augmented-key formulation and against the integer
+gather where the weights are 0 (and near 1); softmax invariants hold exactly.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from dense_reference import dense_augmented, dense_int_forward, rope_complex
+from fibonacci_offset_dilated_amd.workloads import FIB_BASE, POW2_BASE
+
+SMALL_FIB = FIB_BASE[:10]  # up to 55, so that offsets bite at tiny N
+
+
+def _inputs(seed, B, H, N, D=64):
+    rng = np.random.default_rng(seed)
+    return [rng.standard_normal((B, H, N, D)) for _ in range(4)]
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 13, 64, 200])
+@pytest.mark.parametrize("W", [1, 6, 12])
+@pytest.mark.parametrize("alpha", [np.float32(1.0), np.float32(0.5), np.float32(0.7), np.float32(1.5)])
+def test_int_matches_masked_sdpa(N, W, alpha):
+    q, k, v, _ = _inputs(N * 100 + W, 2, 2, N)
+    o, lse = O.forward(q, k, v, W, alpha, SMALL_FIB, 10000.0, O.INT)
+    o2, lse2 = dense_int_forward(q, k, v, W, alpha, SMALL_FIB)
+    np.testing.assert_allclose(o, o2.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lse2.numpy(), rtol=0, atol=1e-12)
+
+
+def test_int_pow2_base_matches_masked_sdpa():
+    q, k, v, _ = _inputs(5, 1, 2, 300)
+    a = O.schedule_linear(16)[7]
+    o, _ = O.forward(q, k, v, 12, a, POW2_BASE, 10000.0, O.INT)
+    o2, _ = dense_int_forward(q, k, v, 12, a, POW2_BASE)
+    np.testing.assert_allclose(o, o2.numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("N,W", [(1, 1), (7, 7), (64, 64), (50, 200)])
+def test_window_covering_sequence_is_causal_attention(N, W):
+    q, k, v, _ = _inputs(N + W, 1, 2, N)
+    o, _ = O.forward(q, k, v, W, np.float32(1.0), FIB_BASE, 10000.0, O.INT)
+    qr = rope_complex(torch.as_tensor(q), 10000.0)
+    kr = rope_complex(torch.as_tensor(k), 10000.0)
+    ref = torch.nn.functional.scaled_dot_product_attention(qr, kr, torch.as_tensor(v), is_causal=True)
+    np.testing.assert_allclose(o, ref.numpy(), rtol=0, atol=1e-12)
+    o_i, _ = O.forward(q, k, v, W, np.float32(1.3), FIB_BASE, 10000.0, O.INTERP)
+    np.testing.assert_allclose(o_i, ref.numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("alpha", [np.float32(0.97), np.float32(1.04), np.float32(0.6), np.float32(1.5)])
+@pytest.mark.parametrize("W", [4, 12])
+def test_interp_matches_dense_augmented(alpha, W):
+    q, k, v, _ = _inputs(int(alpha * 100) + W, 1, 2, 90)
+    o, lse = O.forward(q, k, v, W, alpha, SMALL_FIB, 10000.0, O.INTERP)
+    at = torch.tensor(float(alpha), dtype=torch.float64)
+    o2, lse2 = dense_augmented(q, k, v, W, at, SMALL_FIB)
+    np.testing.assert_allclose(o, o2.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lse2.numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("W", [1, 6, 12])
+def test_interp_with_integer_offsets_equals_int(W):
+    # alpha = 1: every d_k is an integer, so w = 0 and the interpolated gather is the integer one
+    q, k, v, _ = _inputs(W, 2, 1, 1100)
+    oi, li = O.forward(q, k, v, W, np.float32(1.0), FIB_BASE, 10000.0, O.INT)
+    op, lp = O.forward(q, k, v, W, np.float32(1.0), FIB_BASE, 10000.0, O.INTERP)
+    np.testing.assert_array_equal(oi, op)
+    np.testing.assert_array_equal(li, lp)
+
+
+def test_interp_weight_to_one_converges_to_int():
+    # alpha = 1 + eps: d = f (1 + eps), c = f + 1, w = 1 - f eps -> 1; the virtual key tends
+    # to row i - f, i.e. the integer gather at alpha = 1. W = 12 keeps the same entries.
+    # Query i = f is excluded: there the integer key (distance f) is valid but the
+    # interpolated pair needs c = f + 1 <= i and is not.
+    q, k, v, _ = _inputs(9, 1, 1, 1100)
+    oi, _ = O.forward(q, k, v, 12, np.float32(1.0), FIB_BASE, 10000.0, O.INT)
+    keep = np.array([i not in FIB_BASE for i in range(1100)])
+    prev = None
+    for e in (2.0 ** -12, 2.0 ** -16, 2.0 ** -20):
+        a = np.float32(1.0 + e)
+        op, _ = O.forward(q, k, v, 12, a, FIB_BASE, 10000.0, O.INTERP)
+        err = np.abs(op - oi)[..., keep, :].max()
+        assert err < 1e4 * e
+        if prev is not None:
+            assert err < prev
+        prev = err
+
+
+def test_softmax_invariants():
+    q, k, _, _ = _inputs(4, 1, 2, 1200)
+    ones = np.ones_like(q)
+    for mode in (O.INT, O.INTERP):
+        o, _ = O.forward(q, k, ones, 12, np.float32(1.2), FIB_BASE, 10000.0, mode)
+        np.testing.assert_allclose(o, 1.0, rtol=0, atol=1e-13)
+    zeros = np.zeros_like(q)
+    a = np.float32(1.2)
+    _, lse = O.forward(zeros, k, ones, 12, a, FIB_BASE, 10000.0, O.INT)
+    R = O.int_offsets(a, FIB_BASE, 12)
+    n = np.array([min(12, i + 1) + sum(1 for r in R if r <= i) for i in range(1200)])
+    np.testing.assert_allclose(lse[0, 0], np.log(n), rtol=0, atol=1e-13)
+
+
+def test_forward_rows_and_workers_agree():
+    q, k, v, _ = _inputs(6, 1, 3, 400)
+    a = np.float32(1.37)
+    o, lse = O.forward(q, k, v, 12, a, FIB_BASE, 10000.0, O.INTERP)
+    o2, lse2 = O.forward(q, k, v, 12, a, FIB_BASE, 10000.0, O.INTERP, workers=2)
+    np.testing.assert_array_equal(o, o2)
+    rows = np.array([0, 5, 399, 123])
+    orow, lrow = O.forward_rows(q[0, 1], k[0, 1], v[0, 1], rows, 12, a, FIB_BASE, 10000.0, O.INTERP)
+    np.testing.assert_allclose(orow, o[0, 1][rows], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lrow, lse[0, 1][rows], rtol=0, atol=1e-14)
