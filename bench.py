@@ -1,0 +1,231 @@
+"""Benchmark of the Fibonacci-offset sparse attention forward on one MI355X.
+
+Workload (timed step): the long-context shape B=1, H=32, N=131072, D=64, bf16, W=12,
+Fibonacci base up to 987, alpha = 1.5 (layer 15 of the staggered-linear schedule), integer
+offsets, forward. One step = one call of fib_sparse_attn_fwd over the whole batch (offset
+table, RoPE, window + offset gather, softmax, output and LSE). Inputs are seeded N(0, 1)
+draws already resident in HBM. The other rows of the path (interpolated forward, integer and
+interpolated backward) are timed on the same inputs and reported under "components".
+
+Printed: one JSON line with metric, value (tokens/s = B*H*N / step time), a roofline object
+for the forward kernel (algorithmic bytes / HIP-event time vs 8 TB/s) and the fp64 CPU
+oracle's throughput on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+D = 64
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sources_sha() -> str:
+    csrc = os.path.join(ROOT, "fibonacci_offset_dilated_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(f"{kernel}|{workload}")
+    except Exception:
+        return None
+    if not rec or rec.get("sources_sha") != kernel_sources_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def make_inputs(B, H, N, seed, with_dout, dev):
+    import torch
+
+    from fibonacci_offset_dilated_amd.synthetic import normal_inputs
+
+    arrs = normal_inputs(seed, (B, H, N, D), with_dout=with_dout)
+    outs = []
+    for a in arrs:
+        # fp32 -> bf16 round-to-nearest-even (torch's cast); the draws are finite
+        outs.append(torch.from_numpy(a).to(dev).to(torch.bfloat16))
+        del a
+    return outs, arrs
+
+
+def time_calls(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps  # ms
+
+
+def cpu_baseline(arrs, B, H, N, W, alpha, base, mode, budget_s):
+    """fp64 oracle on a bounded sample: as many whole heads as fit the time budget, run in a
+    process pool over all host cores of this process's affinity mask."""
+    import oracle as O
+    from fibonacci_offset_dilated_amd.synthetic import bf16_bits_to_f32, f32_to_bf16_bits
+
+    cores = len(os.sched_getaffinity(0))
+    # probe: one head-chunk of rows to estimate the per-query cost
+    q = bf16_bits_to_f32(f32_to_bf16_bits(arrs[0][0, 0])).astype(np.float64)
+    k = bf16_bits_to_f32(f32_to_bf16_bits(arrs[1][0, 0])).astype(np.float64)
+    v = bf16_bits_to_f32(f32_to_bf16_bits(arrs[2][0, 0])).astype(np.float64)
+    rows = np.arange(0, min(N, 8192))
+    t = time.perf_counter()
+    O.forward_rows(q, k, v, rows, W, alpha, base, 10000.0, mode)
+    per_q = (time.perf_counter() - t) / len(rows)
+    heads = int(max(1, min(B * H, (budget_s * cores) / max(per_q * N, 1e-9))))
+    heads = max(min(heads, B * H), 1)
+    heads = min(B * H, max(heads - heads % max(1, min(cores, heads)), 1))
+    sel = [(i // H, i % H) for i in range(heads)]
+
+    def conv(x):
+        return np.stack([bf16_bits_to_f32(f32_to_bf16_bits(x[b, h])).astype(np.float64) for b, h in sel])[None]
+
+    qs, ks, vs = conv(arrs[0]), conv(arrs[1]), conv(arrs[2])
+    workers = min(cores, heads)
+    t = time.perf_counter()
+    O.forward(qs, ks, vs, W, alpha, base, 10000.0, mode, workers=workers)
+    dt = time.perf_counter() - t
+    return {"value": heads * N / dt, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"{heads} of {B * H} heads x N={N} (fp64 NumPy forward, integer mode, process pool)",
+            "seconds": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-components", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (the op shards over "
+              "B*H with no communication; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import fibonacci_offset_dilated_amd as F
+    from fibonacci_offset_dilated_amd.synthetic import seed_for
+    from fibonacci_offset_dilated_amd.workloads import BY_CONFIG, FIB_BASE, INT, INTERP
+
+    w = BY_CONFIG[5]
+    B, H, N, W = w.B, w.H, w.N, 12
+    alpha = F.schedule_alpha(F.SCHED_LINEAR, 15, 16)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    F.lib()
+    log(f"inputs B={B} H={H} N={N} D={D} bf16 (seeded)")
+    (q, k, v, do), arrs = make_inputs(B, H, N, seed_for(5, 0, 12, 15), True, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def fwd_int():
+        F.fwd(q, k, v, W, alpha, FIB_BASE, 10000.0, INT, out=o, lse=lse)
+
+    log("timing integer forward")
+    ms = time_calls(fwd_int, args.steps, args.warmup, stream)
+    rows = B * H * N
+    bytes_per_launch = rows * (4 * D * 2 + 4)  # read Q, K, V; write O (bf16) and LSE (fp32)
+    achieved = bytes_per_launch / (ms * 1e-3) / 1e9
+    workload = "long_context_b1h32_n131072_bf16_w12_fib987_alpha1.5"
+    traffic = measured_traffic("fwd_int", workload)
+
+    components = None
+    if not args.no_components:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        dal = torch.empty(1, dtype=torch.float32, device=dev)
+        ws = torch.empty(F.bwd_workspace_size(B, H, N, D, F.BF16, INTERP), dtype=torch.uint8, device=dev)
+        o2 = torch.empty_like(q)
+        lse2 = torch.empty_like(lse)
+
+        def fwd_interp():
+            F.fwd(q, k, v, W, alpha, FIB_BASE, 10000.0, INTERP, out=o2, lse=lse2)
+
+        def bwd(mode, oo, ll):
+            return lambda: F.bwd(q, k, v, oo, ll, do, W, alpha, FIB_BASE, 10000.0, mode, dq=dq, dk=dk, dv=dv,
+                                 dalpha=dal, workspace=ws)
+
+        log("timing interpolated forward and both backwards")
+        fwd_interp()
+        ms_interp = time_calls(fwd_interp, max(3, args.steps // 2), 1, stream)
+        ms_bwd_int = time_calls(bwd(INT, o, lse), 3, 1, stream)
+        ms_bwd_interp = time_calls(bwd(INTERP, o2, lse2), 3, 1, stream)
+        bwd_bytes = rows * (8 * D * 2 + 4)
+        components = {
+            "fwd_int_ms": round(ms, 4),
+            "fwd_interp_ms": round(ms_interp, 4),
+            "interp_over_int": round(ms_interp / ms, 3),
+            "bwd_int_ms": round(ms_bwd_int, 4),
+            "bwd_interp_ms": round(ms_bwd_interp, 4),
+            "fwd_interp_hbm_frac": round(bytes_per_launch / (ms_interp * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bwd_int_hbm_frac": round(bwd_bytes / (ms_bwd_int * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bwd_interp_hbm_frac": round(bwd_bytes / (ms_bwd_interp * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(arrs, B, H, N, W, alpha, FIB_BASE, INT, args.cpu_budget)
+
+    out = {
+        "metric": "sparse-attn fwd tokens/s per layer (B*H*N)",
+        "value": rows / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": workload, "B": B, "H": H, "N": N, "D": D, "W": W, "alpha": float(alpha),
+                   "base": "fibonacci 1..987", "mode": "integer", "rope_theta": 10000.0},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "bytes_per_launch": bytes_per_launch},
+        "cpu_baseline": cpu,
+        "components": components,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

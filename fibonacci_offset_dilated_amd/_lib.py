@@ -1,0 +1,205 @@
+"""ctypes binding of libfibattn.so (the C ABI declared in include/fibattn.h).
+
+Argument marshalling only: every step of the attention runs in the library's HIP kernels.
+torch supplies device memory and the current HIP stream. The library must have been built
+(``python -m fibonacci_offset_dilated_amd.build``); loading fails loudly otherwise, and there
+is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfibattn.so")
+
+FIB_OK = 0
+F32, BF16 = 0, 1
+INT, INTERP = 0, 1
+SCHED_FIXED, SCHED_LINEAR, SCHED_COPRIME = 0, 1, 2
+MAX_BASE = 32
+
+_lib = None
+
+# exported symbols and their ctypes signatures (mirrors include/fibattn.h)
+_c = ctypes
+_SIGS = {
+    "fib_sparse_attn_fwd": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                       _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int,
+                                       _c.c_int, _c.c_float, _c.c_void_p, _c.c_int, _c.c_float, _c.c_int,
+                                       _c.c_void_p]),
+    "fib_sparse_attn_bwd": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                       _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                       _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int,
+                                       _c.c_int, _c.c_float, _c.c_void_p, _c.c_int, _c.c_float, _c.c_int,
+                                       _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "fib_sparse_attn_bwd_workspace_size": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64,
+                                                         _c.c_int, _c.c_int]),
+    "fib_status_string": (_c.c_char_p, [_c.c_int]),
+    "fib_sparse_attn_offset_table": (_c.c_int, [_c.c_float, _c.c_void_p, _c.c_int, _c.c_int, _c.c_int,
+                                                _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p]),
+    "fib_sparse_attn_index_set": (_c.c_int, [_c.c_int64, _c.c_int, _c.c_float, _c.c_void_p, _c.c_int,
+                                             _c.c_int, _c.c_void_p, _c.c_int64, _c.c_void_p]),
+    "fib_schedule_alpha": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_void_p]),
+}
+SYMBOLS = tuple(_SIGS)
+
+
+class FibError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfibattn.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m fibonacci_offset_dilated_amd.build` (there is no fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().fib_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != FIB_OK:
+        raise FibError(status, where)
+
+
+def _base_array(base: Sequence[int]):
+    arr = (ctypes.c_int32 * max(1, len(base)))(*[int(b) for b in base])
+    return arr, len(base)
+
+
+def schedule_alpha(kind: int, layer: int, n_layers: int) -> np.float32:
+    out = ctypes.c_float()
+    _check(lib().fib_schedule_alpha(int(kind), int(layer), int(n_layers), ctypes.byref(out)), "fib_schedule_alpha")
+    return np.float32(out.value)
+
+
+def offset_table(alpha, base: Sequence[int], W: int, mode: int):
+    """The library's offset table: (dist, w, f) lists (see fib_sparse_attn_offset_table)."""
+    b, n = _base_array(base)
+    cap = max(1, n)
+    dist = (ctypes.c_int32 * cap)()
+    w = (ctypes.c_float * cap)()
+    f = (ctypes.c_int32 * cap)()
+    cnt = ctypes.c_int()
+    _check(lib().fib_sparse_attn_offset_table(ctypes.c_float(float(np.float32(alpha))), b, n, int(W), int(mode),
+                                              dist, w, f, ctypes.byref(cnt)), "fib_sparse_attn_offset_table")
+    m = cnt.value
+    return list(dist[:m]), [np.float32(x) for x in w[:m]], list(f[:m])
+
+
+# ---- torch-facing wrappers ---------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_qkv(*ts):
+    torch = _torch()
+    ref = ts[0]
+    for t in ts:
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError("tensors must be CUDA (HIP) tensors")
+        if t.dim() != 4 or t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError("q, k, v (and o, dout, grads) must share shape [B, H, N, D], dtype and device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def fwd(q, k, v, W: int, alpha, base: Sequence[int], theta: float = 10000.0, mode: int = INT,
+        out=None, lse=None, with_lse: bool = True, stream=None):
+    """Sparse attention forward on the current stream; returns (O, LSE or None)."""
+    torch = _torch()
+    _check_qkv(q, k, v)
+    B, H, N, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_qkv(q, out)
+    if lse is None and with_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    b, n = _base_array(base)
+    st = lib().fib_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, D, _dtype_code(q),
+                                   int(W), ctypes.c_float(float(np.float32(alpha))), b, n,
+                                   ctypes.c_float(float(theta)), int(mode), _stream(stream))
+    _check(st, "fib_sparse_attn_fwd")
+    return out, lse
+
+
+def bwd_workspace_size(B, H, N, D, dtype_code: int, mode: int) -> int:
+    return int(lib().fib_sparse_attn_bwd_workspace_size(B, H, N, D, int(dtype_code), int(mode)))
+
+
+def bwd(q, k, v, o, lse, dout, W: int, alpha, base: Sequence[int], theta: float = 10000.0, mode: int = INT,
+        dq=None, dk=None, dv=None, dalpha=None, workspace=None, want_dalpha: bool = True, stream=None):
+    """Sparse attention backward; returns (dQ, dK, dV, dalpha tensor [1] or None)."""
+    torch = _torch()
+    _check_qkv(q, k, v, o, dout)
+    B, H, N, D = q.shape
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    _check_qkv(q, dq, dk, dv)
+    if dalpha is None and want_dalpha:
+        dalpha = torch.empty(1, dtype=torch.float32, device=q.device)
+    need = bwd_workspace_size(B, H, N, D, _dtype_code(q), mode)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    b, n = _base_array(base)
+    st = lib().fib_sparse_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dalpha), B, H, N, D, _dtype_code(q),
+                                   int(W), ctypes.c_float(float(np.float32(alpha))), b, n,
+                                   ctypes.c_float(float(theta)), int(mode), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "fib_sparse_attn_bwd")
+    return dq, dk, dv, dalpha
+
+
+def index_set(N: int, W: int, alpha, base: Sequence[int], mode: int, device="cuda", stream=None):
+    """Device export of the attended rows, int32 [N, W + n_entries] (-1 where absent)."""
+    torch = _torch()
+    dist, _, _ = offset_table(alpha, base, W, mode)
+    cols = W + len(dist)
+    out = torch.empty((N, cols), dtype=torch.int32, device=device)
+    b, n = _base_array(base)
+    st = lib().fib_sparse_attn_index_set(int(N), int(W), ctypes.c_float(float(np.float32(alpha))), b, n, int(mode),
+                                         _ptr(out), cols, _stream(stream))
+    _check(st, "fib_sparse_attn_index_set")
+    return out

@@ -1,0 +1,52 @@
+// Internal launch interface between the C ABI (fibattn_api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fib_common.h"
+
+namespace fib {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t BH, N;
+  int dtype, mode, W;
+  Table tab;
+  Rope rope;
+  hipStream_t stream;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dalpha;
+  int64_t BH, N;
+  int dtype, mode, W;
+  Table tab;
+  Rope rope;
+  void* workspace;
+  hipStream_t stream;
+};
+
+hipError_t launch_fwd_generic(const FwdArgs& a);
+bool fwd_ring_supported(const FwdArgs& a);
+hipError_t launch_fwd_ring(const FwdArgs& a);
+hipError_t launch_index_set(int32_t* out, int64_t N, int W, const Table& tab, int64_t cols, hipStream_t s);
+
+size_t bwd_workspace_bytes(int64_t BH, int64_t N, int dtype, int mode);
+hipError_t launch_bwd(const BwdArgs& a);
+
+}  // namespace fib

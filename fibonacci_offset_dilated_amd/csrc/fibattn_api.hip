@@ -1,0 +1,254 @@
+// C ABI of the Fibonacci-offset dilated sparse attention library: argument validation,
+// the exact offset-table builder, the per-layer schedules and kernel dispatch.
+//
+// Rules implemented here ("Depth-Staggered Fibonacci Spacing for Sparse Attention",
+// gist.science summaries of arXiv 2606.28560):
+//   Method > Architecture and attention mechanism: d_k = alpha * f_k per base offset f_k;
+//   Results 2 (efficiency): static schedules take integer offsets, learned ones interpolate;
+//   Method > Experimental variables: Fixed (alpha = 1), Staggered-linear (0.5 at layer 0 to
+//   1.5 at the last layer) and Staggered-coprime (the linear values reassigned by
+//   l -> 7l mod L) schedules.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/fibattn.h"
+#include "fib_launch.h"
+
+using namespace fib;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_shape(int64_t B, int64_t H, int64_t N, int64_t D, int dtype) {
+  if (B < 1 || H < 1 || N < 1) return FIB_ERR_SHAPE;
+  if (D != kD) return FIB_ERR_HEAD_DIM;
+  if (dtype != FIB_F32 && dtype != FIB_BF16) return FIB_ERR_DTYPE;
+  if (N > 0x7fffffffLL) return FIB_ERR_SHAPE;
+  if (B > (1LL << 31) || H > (1LL << 31) || B * H > (1LL << 31)) return FIB_ERR_SHAPE;
+  const int64_t BH = B * H;
+  if ((double)BH * (double)N * (double)D > 9.0e18) return FIB_ERR_SHAPE;
+  // one block per 64 queries per head in the general kernels
+  if ((double)BH * (double)((N + 63) / 64) > 2147483647.0) return FIB_ERR_SHAPE;
+  return FIB_OK;
+}
+
+int check_base(const int32_t* base, int n_base) {
+  if (base == nullptr) return FIB_ERR_NULL;
+  if (n_base < 1 || n_base > FIB_MAX_BASE) return FIB_ERR_BASE;
+  for (int e = 0; e < n_base; ++e) {
+    if (base[e] < 1 || base[e] > (1 << 24)) return FIB_ERR_BASE;
+    if (e > 0 && base[e] <= base[e - 1]) return FIB_ERR_BASE;
+  }
+  return FIB_OK;
+}
+
+int check_scalars(int W, float alpha, float theta, int mode) {
+  if (W < 1) return FIB_ERR_WINDOW;
+  if (!isfinite(alpha) || alpha <= 0.f) return FIB_ERR_ALPHA;
+  if (!isfinite(theta) || theta <= 0.f) return FIB_ERR_THETA;
+  if (mode != FIB_INT && mode != FIB_INTERP) return FIB_ERR_MODE;
+  return FIB_OK;
+}
+
+// Offset table. alpha * f is exact in fp64 (a 24-bit significand times f <= 2^24), so the
+// rounding (ties to even, the default rounding mode of nearbyint) and the ceiling act on the
+// true product.
+void build_table(float alpha, const int32_t* base, int n_base, int W, int mode, Table* t) {
+  memset(t, 0, sizeof(*t));
+  for (int e = 0; e < n_base; ++e) {
+    const double d = (double)alpha * (double)base[e];
+    if (mode == FIB_INT) {
+      const double r = nearbyint(d);
+      if (r < (double)W || r > 2147483647.0) continue;
+      if (t->n > 0 && t->dist[t->n - 1] == (int)r) continue;  // r is non-decreasing in f
+      t->dist[t->n] = (int)r;
+      t->w[t->n] = 0.f;
+      t->f[t->n] = 0.f;
+      t->n++;
+    } else {
+      if (d < (double)W) continue;
+      const double c = ceil(d);
+      if (c > 2147483647.0) continue;
+      t->dist[t->n] = (int)c;
+      t->w[t->n] = (float)(c - d);
+      t->f[t->n] = (float)base[e];
+      t->n++;
+    }
+  }
+}
+
+Rope make_rope(float theta) {
+  Rope r;
+  for (int j = 0; j < kHalf; ++j)
+    r.rev[j] = pow((double)theta, -2.0 * (double)j / (double)kD) / (2.0 * M_PI);
+  return r;
+}
+
+// fp32 nearest to p / q (q > 0), ties to an even significand.
+float f32_nearest_ratio(int64_t p, int64_t q) {
+  const float g = (float)((double)p / (double)q);
+  float best = g;
+  double best_err = -1.0;
+  const float cand[3] = {nextafterf(g, -INFINITY), g, nextafterf(g, INFINITY)};
+  for (float c : cand) {
+    const double err = fabs((double)c * (double)q - (double)p);  // exact: 24 + 31 bits
+    bool better = best_err < 0.0 || err < best_err;
+    if (!better && err == best_err) {
+      uint32_t u;
+      memcpy(&u, &c, 4);
+      better = (u & 1u) == 0;
+    }
+    if (better) {
+      best = c;
+      best_err = err;
+    }
+  }
+  return best;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fib_status_string(int status) {
+  switch (status) {
+    case FIB_OK: return "ok";
+    case FIB_ERR_NULL: return "a required pointer is NULL";
+    case FIB_ERR_SHAPE: return "bad shape (B, H, N must be >= 1 and within index range)";
+    case FIB_ERR_HEAD_DIM: return "unsupported head size (D must be 64)";
+    case FIB_ERR_DTYPE: return "bad dtype (FIB_F32 or FIB_BF16)";
+    case FIB_ERR_WINDOW: return "window W must be >= 1";
+    case FIB_ERR_ALPHA: return "alpha must be finite and > 0";
+    case FIB_ERR_BASE: return "base must hold 1..32 strictly increasing offsets in [1, 2^24]";
+    case FIB_ERR_THETA: return "rope_theta must be finite and > 0";
+    case FIB_ERR_MODE: return "mode must be FIB_INT or FIB_INTERP";
+    case FIB_ERR_ALIGN: return "device pointers must be 16-byte aligned";
+    case FIB_ERR_WORKSPACE: return "backward workspace missing or too small";
+    case FIB_ERR_LAUNCH: return "kernel launch failed";
+    case FIB_ERR_SCHEDULE: return "bad schedule kind, layer or layer count";
+    case FIB_ERR_CAPACITY: return "output array too small";
+    default: return "unknown status";
+  }
+}
+
+int fib_schedule_alpha(int schedule, int layer, int n_layers, float* out_alpha) {
+  if (out_alpha == nullptr) return FIB_ERR_NULL;
+  if (n_layers < 1 || layer < 0 || layer >= n_layers) return FIB_ERR_SCHEDULE;
+  switch (schedule) {
+    case FIB_SCHED_FIXED:
+      *out_alpha = 1.0f;
+      return FIB_OK;
+    case FIB_SCHED_LINEAR:
+      if (n_layers < 2) return FIB_ERR_SCHEDULE;
+      // 0.5 + l / (L - 1) = (L - 1 + 2 l) / (2 (L - 1))
+      *out_alpha = f32_nearest_ratio((int64_t)(n_layers - 1) + 2 * (int64_t)layer, 2 * (int64_t)(n_layers - 1));
+      return FIB_OK;
+    case FIB_SCHED_COPRIME: {
+      if (n_layers < 2 || n_layers % 7 == 0) return FIB_ERR_SCHEDULE;
+      const int src = (int)((7LL * layer) % n_layers);
+      *out_alpha = f32_nearest_ratio((int64_t)(n_layers - 1) + 2 * (int64_t)src, 2 * (int64_t)(n_layers - 1));
+      return FIB_OK;
+    }
+    default:
+      return FIB_ERR_SCHEDULE;
+  }
+}
+
+int fib_sparse_attn_offset_table(float alpha, const int32_t* base, int n_base, int W, int mode,
+                                 int32_t* out_dist, float* out_w, int32_t* out_f, int* out_n) {
+  if (out_dist == nullptr || out_w == nullptr || out_f == nullptr || out_n == nullptr) return FIB_ERR_NULL;
+  int st = check_base(base, n_base);
+  if (st) return st;
+  st = check_scalars(W, alpha, 1.f, mode);
+  if (st) return st;
+  Table t;
+  build_table(alpha, base, n_base, W, mode, &t);
+  for (int e = 0; e < t.n; ++e) {
+    out_dist[e] = t.dist[e];
+    out_w[e] = t.w[e];
+    out_f[e] = (int32_t)t.f[e];
+  }
+  *out_n = t.n;
+  return FIB_OK;
+}
+
+int fib_sparse_attn_index_set(int64_t N, int W, float alpha, const int32_t* base, int n_base, int mode,
+                              int32_t* out, int64_t out_cols, void* stream) {
+  if (out == nullptr) return FIB_ERR_NULL;
+  if (N < 1 || N > 0x7fffffffLL) return FIB_ERR_SHAPE;
+  int st = check_base(base, n_base);
+  if (st) return st;
+  st = check_scalars(W, alpha, 1.f, mode);
+  if (st) return st;
+  Table t;
+  build_table(alpha, base, n_base, W, mode, &t);
+  if (out_cols != (int64_t)W + t.n) return FIB_ERR_CAPACITY;
+  if ((double)N * (double)out_cols > 4.0e18) return FIB_ERR_SHAPE;
+  if (launch_index_set(out, N, W, t, out_cols, (hipStream_t)stream) != hipSuccess) return FIB_ERR_LAUNCH;
+  return FIB_OK;
+}
+
+int fib_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                        int W, float alpha, const int32_t* base, int n_base,
+                        float rope_theta, int mode, void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return FIB_ERR_NULL;
+  int st = check_shape(B, H, N, D, dtype);
+  if (st) return st;
+  st = check_base(base, n_base);
+  if (st) return st;
+  st = check_scalars(W, alpha, rope_theta, mode);
+  if (st) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u))
+    return FIB_ERR_ALIGN;
+  FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.BH = B * H; a.N = N; a.dtype = dtype; a.mode = mode; a.W = W;
+  build_table(alpha, base, n_base, W, mode, &a.tab);
+  a.rope = make_rope(rope_theta);
+  a.stream = (hipStream_t)stream;
+  hipError_t e = fwd_ring_supported(a) ? launch_fwd_ring(a) : launch_fwd_generic(a);
+  return e == hipSuccess ? FIB_OK : FIB_ERR_LAUNCH;
+}
+
+size_t fib_sparse_attn_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, int mode) {
+  if (check_shape(B, H, N, D, dtype) != FIB_OK) return 0;
+  if (mode != FIB_INT && mode != FIB_INTERP) return 0;
+  return bwd_workspace_bytes(B * H, N, dtype, mode);
+}
+
+int fib_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse,
+                        void* dq, void* dk, void* dv, float* dalpha,
+                        int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                        int W, float alpha, const int32_t* base, int n_base,
+                        float rope_theta, int mode,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || dout == nullptr || lse == nullptr ||
+      dq == nullptr || dk == nullptr || dv == nullptr)
+    return FIB_ERR_NULL;
+  int st = check_shape(B, H, N, D, dtype);
+  if (st) return st;
+  st = check_base(base, n_base);
+  if (st) return st;
+  st = check_scalars(W, alpha, rope_theta, mode);
+  if (st) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 3u) || ((uintptr_t)dalpha & 3u))
+    return FIB_ERR_ALIGN;
+  const size_t need = bwd_workspace_bytes(B * H, N, dtype, mode);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FIB_ERR_WORKSPACE;
+  if (workspace != nullptr && !aligned16(workspace)) return FIB_ERR_ALIGN;
+  BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dalpha = dalpha;
+  a.BH = B * H; a.N = N; a.dtype = dtype; a.mode = mode; a.W = W;
+  build_table(alpha, base, n_base, W, mode, &a.tab);
+  a.rope = make_rope(rope_theta);
+  a.workspace = workspace;
+  a.stream = (hipStream_t)stream;
+  return launch_bwd(a) == hipSuccess ? FIB_OK : FIB_ERR_LAUNCH;
+}
+
+}  // extern "C"

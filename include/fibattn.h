@@ -1,0 +1,160 @@
+/*
+ * fibattn.h - C ABI of the Fibonacci-offset dilated sparse attention library (gfx950).
+ *
+ * The operation is the attention layer of "Depth-Staggered Fibonacci Spacing for Sparse
+ * Attention: Static Schedules Beat Learned Dilation and Extrapolate Where Dense Attention
+ * Fails" (arXiv 2606.28560; gist.science technical summaries, Korean and Spanish pages),
+ * cited below as [FIB]:
+ *   - Method > Architecture and attention mechanism: query i attends a dense local window
+ *     of W keys plus one key per base offset f_k (fib = 1, 2, 3, 5, ..., 987) placed at
+ *     distance d_k = alpha * f_k, alpha a per-layer scalar in [0.5, 1.5]; non-integer
+ *     offsets linearly interpolate the key/value rows so that a gradient reaches alpha;
+ *     RoPE is applied before the gather.
+ *   - Results 2 (efficiency): static schedules use integer offsets (a fused boolean-mask
+ *     path), learned ones the interpolated gather.
+ *   - Method > Experimental variables: the Fixed, Staggered-linear and Staggered-coprime
+ *     (l -> 7l mod L) per-layer schedules.
+ *
+ * Conventions fixed by this library where the pages are silent:
+ *   - causal; window = distances 0..W-1 (the query itself included);
+ *   - integer mode (FIB_INT): r_k = round-half-to-even(alpha * f_k) computed exactly
+ *     (fp32 alpha times an integer, in fp64); offsets r_k < W are dropped; equal offsets
+ *     collapse; offset r is used by query i when r <= i;
+ *   - interpolated mode (FIB_INTERP): entries with d_k >= W are kept, c_k = ceil(d_k),
+ *     w_k = c_k - d_k; query i (when c_k <= i) attends the virtual key
+ *     (1 - w_k) * K^[i - c_k] + w_k * K^[i - c_k + 1] with the same blend of V rows;
+ *   - RoPE: rotate-half pairs (j, j + D/2), omega_j = theta^(-2j/D), positions 0..N-1,
+ *     applied to Q and K inside the call (inputs are un-rotated); V is not rotated;
+ *   - softmax scale 1/sqrt(D); fp32 accumulation; O, dQ, dK, dV in the input dtype
+ *     (round to nearest even for bf16); LSE natural log, fp32.
+ *
+ * Memory layout: every tensor is [B, H, N, D] row-major and contiguous (D fastest); LSE is
+ * [B, H, N]. Device pointers must be 16-byte aligned. D = 64 is the supported head size.
+ *
+ * Ownership: the caller allocates and owns all device buffers (outputs and backward
+ * workspace included); the library never allocates or frees device memory. Host arrays
+ * (base, out_* of the table helper) are read or written during the call only. The library
+ * keeps no state between calls and is reentrant. Device work is enqueued on `stream`
+ * (a hipStream_t; NULL = the null stream) and the call returns without synchronizing.
+ *
+ * Errors: every call returns FIB_OK (0) or a negative FIB_ERR_* status. On an argument
+ * error nothing is launched and no output is touched. Device faults surface at the
+ * caller's next synchronization (HIP semantics). No C++ exception crosses this ABI.
+ */
+#ifndef FIBATTN_H
+#define FIBATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define FIB_OK 0
+#define FIB_ERR_NULL (-1)        /* a required pointer is NULL */
+#define FIB_ERR_SHAPE (-2)       /* B, H or N < 1, or B*H*N*D does not fit the index range */
+#define FIB_ERR_HEAD_DIM (-3)    /* D is not 64 */
+#define FIB_ERR_DTYPE (-4)       /* dtype is not FIB_F32 or FIB_BF16 */
+#define FIB_ERR_WINDOW (-5)      /* W < 1 */
+#define FIB_ERR_ALPHA (-6)       /* alpha not finite or <= 0 */
+#define FIB_ERR_BASE (-7)        /* n_base outside [1, 32], or base not strictly increasing in [1, 2^24] */
+#define FIB_ERR_THETA (-8)       /* rope_theta not finite or <= 0 */
+#define FIB_ERR_MODE (-9)        /* mode is not FIB_INT or FIB_INTERP */
+#define FIB_ERR_ALIGN (-10)      /* a device pointer is not 16-byte aligned */
+#define FIB_ERR_WORKSPACE (-11)  /* backward workspace NULL or smaller than required */
+#define FIB_ERR_LAUNCH (-12)     /* the HIP runtime reported an error at launch */
+#define FIB_ERR_SCHEDULE (-13)   /* bad schedule kind, layer or layer count */
+#define FIB_ERR_CAPACITY (-14)   /* an output array is too small */
+
+/* element types of Q, K, V, O, dO, dQ, dK, dV */
+#define FIB_F32 0
+#define FIB_BF16 1
+
+/* offset modes */
+#define FIB_INT 0     /* rounded integer offsets ([FIB] Results 2, static schedules) */
+#define FIB_INTERP 1  /* interpolated K/V rows at non-integer offsets ([FIB] Method) */
+
+/* per-layer schedules of alpha ([FIB] Method > Experimental variables) */
+#define FIB_SCHED_FIXED 0    /* alpha = 1 for every layer */
+#define FIB_SCHED_LINEAR 1   /* fp32 nearest to 0.5 + l / (L - 1) */
+#define FIB_SCHED_COPRIME 2  /* linear value at index (7 l) mod L; needs gcd(7, L) = 1 */
+
+#define FIB_MAX_BASE 32
+
+/*
+ * Forward ([FIB] Method > Architecture and attention mechanism).
+ *   q, k, v  device, [B, H, N, D] of `dtype`, un-rotated (RoPE is applied inside).
+ *   o        device, [B, H, N, D] of `dtype`, written.
+ *   lse      device, [B, H, N] fp32 log-sum-exp of the scaled logits, written; may be NULL.
+ *   W        window size >= 1.
+ *   alpha    per-layer dilation (> 0, finite; the pages use [0.5, 1.5]).
+ *   base     host, n_base strictly increasing offsets in [1, 2^24] (e.g. 1, 2, 3, 5, ..., 987).
+ *   rope_theta  RoPE base (e.g. 10000).
+ *   mode     FIB_INT or FIB_INTERP.
+ *   stream   hipStream_t (NULL = null stream).
+ * Returns FIB_OK or FIB_ERR_*.
+ */
+int fib_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                        int W, float alpha, const int32_t* base, int n_base,
+                        float rope_theta, int mode, void* stream);
+
+/*
+ * Backward of the forward above with respect to q, k, v and alpha, given dO
+ * ([FIB] Method: interpolation lets the gradient reach alpha; Learned schedule).
+ *   o, lse   device, the forward's outputs for the same arguments (lse must not be NULL).
+ *   dout     device, [B, H, N, D] of `dtype`, gradient of the loss w.r.t. O.
+ *   dq, dk, dv  device, [B, H, N, D] of `dtype`, overwritten with the gradients w.r.t.
+ *            the un-rotated inputs.
+ *   dalpha   device, 1 fp32, overwritten with dL/dalpha (0 in FIB_INT mode, where the
+ *            offsets are piecewise constant in alpha); may be NULL to skip it.
+ *   workspace  device scratch of at least fib_sparse_attn_bwd_workspace_size(...) bytes,
+ *            16-byte aligned; its contents on entry are ignored.
+ * The result is deterministic (no floating-point atomics).
+ */
+int fib_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse,
+                        void* dq, void* dk, void* dv, float* dalpha,
+                        int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                        int W, float alpha, const int32_t* base, int n_base,
+                        float rope_theta, int mode,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace fib_sparse_attn_bwd needs for these sizes (0 on bad sizes). */
+size_t fib_sparse_attn_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D,
+                                          int dtype, int mode);
+
+/* Static, human-readable text of a status code. */
+const char* fib_status_string(int status);
+
+/*
+ * Host-only: the per-layer offset table the kernels use ([FIB] Method: d_k = alpha * f_k).
+ *   FIB_INT:    out_dist[e] = kept offsets r (ascending), out_w[e] = 0, out_f[e] = 0.
+ *   FIB_INTERP: out_dist[e] = c_k = ceil(alpha f_k), out_w[e] = fp32(c_k - alpha f_k),
+ *               out_f[e] = f_k, for kept entries in base order.
+ * Entries whose distance does not fit in int32 are dropped (no query can use them).
+ * out_* are host arrays of capacity >= n_base; *out_n receives the entry count.
+ */
+int fib_sparse_attn_offset_table(float alpha, const int32_t* base, int n_base, int W, int mode,
+                                 int32_t* out_dist, float* out_w, int32_t* out_f, int* out_n);
+
+/*
+ * Device debug export of the attended rows, computed by the same device table and
+ * validity code as the attention kernels. out: device int32 [N, out_cols], out_cols must
+ * equal W + (entry count of fib_sparse_attn_offset_table); column s < W holds the window
+ * key i - s, column W + e the row i - dist[e] (interpolated: the lower row i - c_e), and
+ * -1 where the key does not exist (before position 0).
+ */
+int fib_sparse_attn_index_set(int64_t N, int W, float alpha, const int32_t* base, int n_base,
+                              int mode, int32_t* out, int64_t out_cols, void* stream);
+
+/* Host-only: alpha of layer `layer` of an n_layers schedule (FIB_SCHED_*), as fp32. */
+int fib_schedule_alpha(int schedule, int layer, int n_layers, float* out_alpha);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FIBATTN_H */

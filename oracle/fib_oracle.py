@@ -351,10 +351,16 @@ def _head_backward(qh, kh, vh, doh, W, alpha, base, theta, mode, rows=None):
         dqr[ri] += np.einsum("ns,nsd->nd", ds, key) * scale
         dkey = ds[..., None] * q[:, None, :] * scale
         dval = p[..., None] * do[:, None, :]
-        vmask = valid[..., None]
-        for tgt, src in ((dkr, dkey), (dv, dval)):
-            np.add.at(tgt, lo.ravel(), (np.where(vmask, (1.0 - w)[..., None] * src, 0.0)).reshape(-1, D))
-            np.add.at(tgt, hi.ravel(), (np.where(vmask, w[..., None] * src, 0.0)).reshape(-1, D))
+        # scatter per key slot: within one slot the rows lo (and hi) of distinct queries are
+        # distinct, so a plain indexed add is exact
+        for col in range(S):
+            mcol = valid[:, col]
+            if not mcol.any():
+                continue
+            lo_c, hi_c, w_c = lo[mcol, col], hi[mcol, col], w[mcol, col][:, None]
+            for tgt, src in ((dkr, dkey), (dv, dval)):
+                tgt[lo_c] += (1.0 - w_c) * src[mcol, col]
+                tgt[hi_c] += w_c * src[mcol, col]
         if mode == INTERP:
             dk_diff = np.einsum("nd,nsd->ns", q, kr[hi] - kr[lo]) * scale
             dv_diff = np.einsum("nd,nsd->ns", do, vh[hi] - vh[lo])

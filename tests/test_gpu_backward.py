@@ -1,0 +1,129 @@
+"""GPU parity of the backward pass (dQ, dK, dV, dalpha) against the CPU oracle, via the C ABI.
+
+Bounds: max-abs error on dQ, dK, dV within 1e-4 (fp32) / 2e-2 (bf16); relative error on
+dalpha within 1e-4 (fp32) / 1e-2 (bf16). The GPU uses its own bf16 O (for Delta) and fp32 LSE
+from the forward, as a training step would; the oracle computes exact gradients.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import fibonacci_offset_dilated_amd as F
+import oracle as O
+from fibonacci_offset_dilated_amd.synthetic import seed_for, uniform_alphas
+from fibonacci_offset_dilated_amd.workloads import (BF16, BY_CONFIG, F32, FIB_BASE, INT, INTERP, POW2_BASE,
+                                                    UNIFORM_ALPHA_RANGE, UNIFORM_ALPHA_SEED)
+from gpu_util import TOL, TOL_DALPHA, host, inputs, maxabs, say
+
+pytestmark = pytest.mark.gpu
+WORKERS = min(16, len(os.sched_getaffinity(0)))
+
+
+def gpu_grads(qkvd, W, alpha, base, mode):
+    (q, _), (k, _), (v, _), (do, _) = qkvd
+    o, lse = F.fwd(q, k, v, W, alpha, base, 10000.0, mode)
+    dq, dk, dv, da = F.bwd(q, k, v, o, lse, do, W, alpha, base, 10000.0, mode)
+    torch.cuda.synchronize()
+    return dq, dk, dv, da
+
+
+def check(qkvd, W, alpha, base, mode, dtype):
+    (_, q64), (_, k64), (_, v64), (_, d64) = qkvd
+    dq, dk, dv, da = gpu_grads(qkvd, W, alpha, base, mode)
+    rq, rk, rv, ra = O.backward(q64, k64, v64, d64, W, alpha, base, 10000.0, mode, workers=WORKERS)
+    eq, ek, ev = maxabs(host(dq), rq), maxabs(host(dk), rk), maxabs(host(dv), rv)
+    got_a = float(da.item())
+    if mode == INT:
+        assert got_a == 0.0
+        ea = 0.0
+    else:
+        ea = abs(got_a - ra) / max(abs(ra), 1e-30)
+    say(f"  dQ {eq:.2e} dK {ek:.2e} dV {ev:.2e} dalpha {got_a:.6g} vs {ra:.6g} rel {ea:.2e}")
+    assert max(eq, ek, ev) <= TOL[dtype], (eq, ek, ev)
+    assert ea <= TOL_DALPHA[dtype]
+
+
+@pytest.mark.parametrize("layer", range(16))
+def test_learned_dilation_layers_backward(layer):
+    w = BY_CONFIG[3]
+    a = uniform_alphas(UNIFORM_ALPHA_SEED, 16, *UNIFORM_ALPHA_RANGE)[layer]
+    say(f"learned dilation bwd B8H8N1024 bf16 W=12 layer={layer} alpha={a}")
+    qkvd = inputs(seed_for(3, 0, 12, layer), (w.B, w.H, w.N, w.D), BF16, with_dout=True)
+    check(qkvd, 12, a, FIB_BASE, INTERP, BF16)
+
+
+EDGE = [
+    (1, 1, 1, 1, 1.0, FIB_BASE),
+    (1, 2, 2, 12, 1.0, FIB_BASE),
+    (2, 1, 65, 6, 0.7, FIB_BASE),
+    (1, 2, 200, 16, 1.3, FIB_BASE),
+    (1, 1, 300, 17, 1.07, FIB_BASE),
+    (1, 1, 257, 40, 0.93, POW2_BASE),
+    (1, 2, 130, 130, 1.0, FIB_BASE),
+    (1, 1, 100, 12, 40.0, FIB_BASE),
+    (1, 1, 1100, 12, 1.5, FIB_BASE),
+]
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("mode", [INT, INTERP], ids=["int", "interp"])
+@pytest.mark.parametrize("case", EDGE, ids=[f"B{c[0]}H{c[1]}N{c[2]}W{c[3]}a{c[4]}" for c in EDGE])
+def test_backward_edge_shapes(case, mode, dtype):
+    B, H, N, W, alpha, base = case
+    say("bwd edge", case, mode, dtype)
+    qkvd = inputs(2000 + N + W, (B, H, N, 64), dtype, with_dout=True)
+    check(qkvd, W, np.float32(alpha), base, mode, dtype)
+
+
+@pytest.fixture(scope="module")
+def long_inputs():
+    w = BY_CONFIG[5]
+    say("long context inputs B1H32N131072 bf16 (+dO)")
+    return inputs(seed_for(5, 0, 12, 15), (w.B, w.H, w.N, w.D), BF16, with_dout=True)
+
+
+@pytest.mark.parametrize("mode", [INT, INTERP], ids=["int", "interp"])
+def test_long_context_backward_sampled(long_inputs, mode):
+    """dQ on sampled query rows; dK/dV on key ranges, from the oracle restricted to the queries
+    that read those keys; dalpha over the whole call."""
+    w = BY_CONFIG[5]
+    a = F.schedule_alpha(F.SCHED_LINEAR, 15, 16)
+    say(f"long context bwd N=131072 H=32 alpha={a} mode={mode}")
+    dq, dk, dv, da = gpu_grads(long_inputs, 12, a, FIB_BASE, mode)
+    (_, q64), (_, k64), (_, v64), (_, d64) = long_inputs
+    reach = 1481 + 12 + 2
+    for h in (0, 21):
+        for j0 in (0, 60000, w.N - 300):
+            j1 = min(w.N, j0 + 300)
+            rows = np.arange(j0, min(w.N, j1 + reach))
+            rq, rk, rv, _ = O.backward(q64[:, h:h + 1], k64[:, h:h + 1], v64[:, h:h + 1], d64[:, h:h + 1], 12, a,
+                                       FIB_BASE, 10000.0, mode, rows=rows)
+            eq = maxabs(host(dq[0, h, j0:j1]), rq[0, 0, j0:j1])
+            ek = maxabs(host(dk[0, h, j0:j1]), rk[0, 0, j0:j1])
+            ev = maxabs(host(dv[0, h, j0:j1]), rv[0, 0, j0:j1])
+            say(f"  head {h} rows {j0}:{j1} dQ {eq:.2e} dK {ek:.2e} dV {ev:.2e}")
+            assert max(eq, ek, ev) <= TOL[BF16]
+    if mode == INT:
+        assert float(da.item()) == 0.0
+    else:
+        # dalpha over 4 of the heads at full length: the same kernels on a 4-head call
+        hs = [0, 9, 18, 27]
+        sub = [t[:, hs].contiguous() for t, _ in long_inputs]
+        o4, l4 = F.fwd(sub[0], sub[1], sub[2], 12, a, FIB_BASE, 10000.0, mode)
+        _, _, _, da4 = F.bwd(sub[0], sub[1], sub[2], o4, l4, sub[3], 12, a, FIB_BASE, 10000.0, mode)
+        _, _, _, ra = O.backward(q64[:, hs], k64[:, hs], v64[:, hs], d64[:, hs], 12, a, FIB_BASE, 10000.0, mode,
+                                 workers=WORKERS)
+        rel = abs(float(da4.item()) - ra) / abs(ra)
+        say(f"  dalpha(4 heads) {float(da4.item()):.6g} vs {ra:.6g} rel {rel:.2e}")
+        assert rel <= TOL_DALPHA[BF16]
+
+
+def test_backward_deterministic():
+    say("bwd determinism")
+    qkvd = inputs(9, (1, 4, 2500, 64), BF16, with_dout=True)
+    r1 = gpu_grads(qkvd, 12, np.float32(1.21), FIB_BASE, INTERP)
+    r2 = gpu_grads(qkvd, 12, np.float32(1.21), FIB_BASE, INTERP)
+    for x, y in zip(r1, r2):
+        assert torch.equal(x, y)

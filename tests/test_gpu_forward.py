@@ -1,0 +1,211 @@
+"""GPU parity of the forward pass against the CPU oracle, through the C ABI.
+
+Values: max-abs error on O and LSE within 1e-4 (fp32 inputs) / 2e-2 (bf16 inputs).
+Index sets: the library's device export equals the oracle's, bit for bit.
+Workloads: the five measured configurations (full comparison where the oracle is quick,
+sampled heads or rows at the large ones), plus ragged and degenerate shapes.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import fibonacci_offset_dilated_amd as F
+import oracle as O
+from fibonacci_offset_dilated_amd.synthetic import seed_for, uniform_alphas
+from fibonacci_offset_dilated_amd.workloads import (BF16, BY_CONFIG, F32, FIB_BASE, INT, INTERP, POW2_BASE,
+                                                    UNIFORM_ALPHA_RANGE, UNIFORM_ALPHA_SEED)
+from gpu_util import TOL, host, inputs, maxabs, say
+
+pytestmark = pytest.mark.gpu
+WORKERS = min(16, len(os.sched_getaffinity(0)))
+
+
+def alpha_of(w, layer):
+    if w.schedule == "fixed1":
+        return F.schedule_alpha(F.SCHED_FIXED, layer, 16)
+    if w.schedule == "linear":
+        return F.schedule_alpha(F.SCHED_LINEAR, layer, 16)
+    if w.schedule == "coprime":
+        return F.schedule_alpha(F.SCHED_COPRIME, layer, 16)
+    if w.schedule == "layer15_linear":
+        return F.schedule_alpha(F.SCHED_LINEAR, 15, 16)
+    return uniform_alphas(UNIFORM_ALPHA_SEED, 16, *UNIFORM_ALPHA_RANGE)[layer]
+
+
+def run_fwd(qkv, W, alpha, base, mode):
+    (q, _), (k, _), (v, _) = qkv[:3]
+    o, lse = F.fwd(q, k, v, W, alpha, base, 10000.0, mode)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check_full(qkv, W, alpha, base, mode, dtype, heads=None):
+    (_, q64), (_, k64), (_, v64) = qkv[:3]
+    o, lse = run_fwd(qkv, W, alpha, base, mode)
+    oh, lh = host(o), host(lse)
+    if heads is None:
+        ro, rl = O.forward(q64, k64, v64, W, alpha, base, 10000.0, mode, workers=WORKERS)
+        eo, el = maxabs(oh, ro), maxabs(lh, rl)
+    else:
+        eo = el = 0.0
+        for b, h in heads:
+            ro, rl = O.forward(q64[b:b + 1, h:h + 1], k64[b:b + 1, h:h + 1], v64[b:b + 1, h:h + 1], W, alpha, base,
+                               10000.0, mode)
+            eo = max(eo, maxabs(oh[b, h], ro[0, 0]))
+            el = max(el, maxabs(lh[b, h], rl[0, 0]))
+    assert np.isfinite(oh).all()
+    assert eo <= TOL[dtype] and el <= TOL[dtype], (eo, el)
+    return eo, el
+
+
+def check_index_set(N, W, alpha, base, mode):
+    got = F.index_set(N, W, alpha, base, mode).cpu().numpy()
+    want = O.index_sets(N, W, alpha, base, mode)
+    assert got.shape == want.shape
+    assert np.array_equal(got, want)
+
+
+# ---- the five workloads ----------------------------------------------------------------
+
+def test_single_head_fp32():
+    w = BY_CONFIG[1]
+    say("single head fp32 N=1024 W=12 alpha=1 INT")
+    qkv = inputs(seed_for(1, 0, 12, 0), (w.B, w.H, w.N, w.D), F32)
+    a = alpha_of(w, 0)
+    eo, el = check_full(qkv, 12, a, FIB_BASE, INT, F32)
+    check_index_set(w.N, 12, a, FIB_BASE, INT)
+    say("  max err O", eo, "LSE", el)
+
+
+@pytest.mark.parametrize("W", [6, 8, 10, 12])
+@pytest.mark.parametrize("layer", range(16))
+def test_staggered_linear_layers(W, layer):
+    w = BY_CONFIG[2]
+    a = alpha_of(w, layer)
+    say(f"staggered linear B8H8N1024 bf16 W={W} layer={layer} alpha={a}")
+    qkv = inputs(seed_for(2, 0, W, layer), (w.B, w.H, w.N, w.D), BF16)
+    check_full(qkv, W, a, FIB_BASE, INT, BF16)
+    check_index_set(w.N, W, a, FIB_BASE, INT)
+
+
+@pytest.mark.parametrize("layer", range(16))
+def test_learned_dilation_layers_forward(layer):
+    w = BY_CONFIG[3]
+    a = alpha_of(w, layer)
+    say(f"learned dilation B8H8N1024 bf16 INTERP W=12 layer={layer} alpha={a}")
+    qkv = inputs(seed_for(3, 0, 12, layer), (w.B, w.H, w.N, w.D), BF16)
+    check_full(qkv, 12, a, FIB_BASE, INTERP, BF16)
+    check_index_set(w.N, 12, a, FIB_BASE, INTERP)
+
+
+@pytest.mark.parametrize("base_id,base", [(0, FIB_BASE), (1, POW2_BASE)], ids=["fib", "pow2"])
+@pytest.mark.parametrize("layer", range(16))
+def test_coprime_extrapolation_layers(base_id, base, layer):
+    w = BY_CONFIG[4]
+    a = alpha_of(w, layer)
+    say(f"coprime B4H8N4096 bf16 W=12 base={base_id} layer={layer} alpha={a}")
+    qkv = inputs(seed_for(4, base_id, 12, layer), (w.B, w.H, w.N, w.D), BF16)
+    heads = [((layer + 3 * base_id) % 4, (layer * 5) % 8), ((layer + 1) % 4, (layer * 3 + 1) % 8)]
+    check_full(qkv, 12, a, base, INT, BF16, heads=heads)
+    check_index_set(w.N, 12, a, base, INT)
+
+
+@pytest.fixture(scope="module")
+def long_inputs():
+    w = BY_CONFIG[5]
+    say("long context inputs B1H32N131072 bf16")
+    return inputs(seed_for(5, 0, 12, 15), (w.B, w.H, w.N, w.D), BF16)
+
+
+@pytest.mark.parametrize("mode", [INT, INTERP], ids=["int", "interp"])
+def test_long_context_sampled_rows(long_inputs, mode):
+    w = BY_CONFIG[5]
+    a = alpha_of(w, 15)
+    say(f"long context N=131072 H=32 alpha={a} mode={mode}")
+    o, lse = run_fwd(long_inputs, 12, a, FIB_BASE, mode)
+    rng = np.random.default_rng(mode)
+    rows = np.unique(np.concatenate([np.arange(0, 40), np.arange(980, 1500), rng.integers(0, w.N, 600),
+                                     np.arange(w.N - 70, w.N)]))
+    (_, q64), (_, k64), (_, v64) = long_inputs[:3]
+    eo = el = 0.0
+    for h in (0, 7, 19, 31):
+        ro, rl = O.forward_rows(q64[0, h], k64[0, h], v64[0, h], rows, 12, a, FIB_BASE, 10000.0, mode)
+        eo = max(eo, maxabs(host(o[0, h])[rows], ro))
+        el = max(el, maxabs(host(lse[0, h])[rows], rl))
+    say("  max err O", eo, "LSE", el)
+    assert eo <= TOL[BF16] and el <= TOL[BF16]
+    assert torch.isfinite(o.float()).all().item()
+    check_index_set(w.N, 12, a, FIB_BASE, mode)
+
+
+# ---- edge cases ------------------------------------------------------------------------
+
+EDGE = [
+    # (B, H, N, W, alpha, base)
+    (1, 1, 1, 1, 1.0, FIB_BASE),
+    (1, 2, 2, 12, 1.0, FIB_BASE),
+    (2, 3, 3, 1, 0.5, FIB_BASE),
+    (1, 2, 63, 12, 1.5, FIB_BASE),
+    (1, 2, 65, 6, 0.7, FIB_BASE),
+    (2, 1, 200, 16, 1.3, FIB_BASE),
+    (1, 1, 300, 17, 1.1, FIB_BASE),
+    (1, 1, 257, 40, 0.9, POW2_BASE),
+    (1, 2, 130, 130, 1.0, FIB_BASE),      # window covers the sequence: causal attention
+    (1, 1, 100, 12, 40.0, FIB_BASE),      # every offset beyond the sequence
+    (1, 1, 1000, 1, 1.0, (1,)),            # one offset of 1 next to a window of 1
+    (1, 1, 777, 12, 0.5, tuple(range(1, 33))),
+]
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("mode", [INT, INTERP], ids=["int", "interp"])
+@pytest.mark.parametrize("case", EDGE, ids=[f"B{c[0]}H{c[1]}N{c[2]}W{c[3]}a{c[4]}" for c in EDGE])
+def test_edge_shapes(case, mode, dtype):
+    B, H, N, W, alpha, base = case
+    say("edge", case, mode, dtype)
+    qkv = inputs(1000 + N + W, (B, H, N, 64), dtype)
+    check_full(qkv, W, np.float32(alpha), base, mode, dtype)
+    check_index_set(N, W, np.float32(alpha), base, mode)
+
+
+@pytest.mark.parametrize("mode", [INT, INTERP], ids=["int", "interp"])
+def test_probes_ones_and_zero_query(mode):
+    N, W, a = 1500, 12, np.float32(1.37)
+    say("probes", mode)
+    (q, _), (k, k64), (v, _) = inputs(77, (1, 2, N, 64), BF16)
+    ones = torch.ones_like(v)
+    o, _ = F.fwd(q, k, ones, W, a, FIB_BASE, 10000.0, mode)
+    assert maxabs(host(o), 1.0) <= 1e-6
+    _, lse = F.fwd(torch.zeros_like(q), k, v, W, a, FIB_BASE, 10000.0, mode)
+    ids = O.index_sets(N, W, a, FIB_BASE, mode)
+    n = (ids >= 0).sum(axis=1)
+    assert maxabs(host(lse)[0, 0], np.log(n)) <= 1e-5
+
+
+@pytest.mark.parametrize("mode", [INT, INTERP], ids=["int", "interp"])
+def test_nan_locality(mode):
+    N, W, a = 1700, 12, np.float32(1.37) if mode == INTERP else np.float32(1.3)
+    say("nan locality", mode)
+    (q, _), (k, _), (v, _) = inputs(78, (1, 1, N, 64), BF16)
+    ids = O.index_sets(N, W, a, FIB_BASE, mode)
+    for tensor_name, j0 in (("k", 333), ("v", 1000)):
+        kk, vv = k.clone(), v.clone()
+        (kk if tensor_name == "k" else vv)[0, 0, j0, 5] = float("nan")
+        o, _ = F.fwd(q, kk, vv, W, a, FIB_BASE, 10000.0, mode)
+        bad = torch.isnan(o[0, 0]).any(dim=1).cpu().numpy()
+        reads = (ids == j0).any(axis=1)
+        if mode == INTERP:
+            hi = np.where(ids[:, W:] >= 0, ids[:, W:] + 1, -1)
+            reads |= (hi == j0).any(axis=1)
+        assert np.array_equal(bad, reads), tensor_name
+
+
+def test_deterministic_repeat():
+    say("determinism")
+    qkv = inputs(5, (2, 4, 3000, 64), BF16)
+    for mode in (INT, INTERP):
+        o1, l1 = run_fwd(qkv, 12, np.float32(1.5), FIB_BASE, mode)
+        o2, l2 = run_fwd(qkv, 12, np.float32(1.5), FIB_BASE, mode)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
