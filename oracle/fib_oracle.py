@@ -329,6 +329,7 @@ def _head_backward(qh, kh, vh, doh, W, alpha, base, theta, mode, rows=None):
     dkr = np.zeros((N, D))
     dv = np.zeros((N, D))
     dalpha = 0.0
+    dalpha_abs = 0.0  # sum over queries of |query's contribution to dalpha|
     S = W + len(dist)
     fk = np.concatenate([np.zeros(W), fs])
     step = _chunk(S, D)
@@ -365,10 +366,12 @@ def _head_backward(qh, kh, vh, doh, W, alpha, base, theta, mode, rows=None):
             dk_diff = np.einsum("nd,nsd->ns", q, kr[hi] - kr[lo]) * scale
             dv_diff = np.einsum("nd,nsd->ns", do, vh[hi] - vh[lo])
             g = ds * dk_diff + p * dv_diff
-            dalpha += float(np.sum(np.where(valid, -fk[None, :] * g, 0.0)))
+            per_query = np.sum(np.where(valid, -fk[None, :] * g, 0.0), axis=1)
+            dalpha += float(np.sum(per_query))
+            dalpha_abs += float(np.sum(np.abs(per_query)))
     dq = rope_inverse(dqr, theta)
     dk = rope_inverse(dkr, theta)
-    return dq, dk, dv, dalpha
+    return dq, dk, dv, dalpha, dalpha_abs
 
 
 def _bh_iter(x):
@@ -424,14 +427,20 @@ def forward_rows(qh, kh, vh, rows, W, alpha, base, theta=10000.0, mode=INT):
     return _head_forward(qh, kh, vh, W, alpha, base, theta, mode, rows=rows)
 
 
-def backward(q, k, v, dout, W, alpha, base, theta=10000.0, mode=INT, workers=1, rows=None):
-    """dQ, dK, dV [B,H,N,D] (fp64, w.r.t. the un-rotated inputs) and dalpha (float)."""
+def backward(q, k, v, dout, W, alpha, base, theta=10000.0, mode=INT, workers=1, rows=None, return_abs=False):
+    """dQ, dK, dV [B,H,N,D] (fp64, w.r.t. the un-rotated inputs) and dalpha (float).
+
+    With ``return_abs`` a fifth value is returned: the sum over queries of the absolute value
+    of each query's contribution to dalpha (the scale against which the summed dalpha can be
+    compared when the contributions cancel).
+    """
     q, k, v, dout = (np.asarray(t, dtype=np.float64) for t in (q, k, v, dout))
     B, H, N, D = q.shape
     dq = np.zeros_like(q)
     dk = np.zeros_like(q)
     dv = np.zeros_like(q)
     dalpha = 0.0
+    dalpha_abs = 0.0
     jobs = [(q[b, h], k[b, h], v[b, h], dout[b, h], W, alpha, base, theta, mode, rows)
             for b, h in _bh_iter(q)]
     nw = _workers(workers)
@@ -440,9 +449,12 @@ def backward(q, k, v, dout, W, alpha, base, theta=10000.0, mode=INT, workers=1, 
             res = list(ex.map(_bwd_task, jobs))
     else:
         res = [_bwd_task(j) for j in jobs]
-    for (b, h), (a, bb, c, da) in zip(_bh_iter(q), res):
+    for (b, h), (a, bb, c, da, dabs) in zip(_bh_iter(q), res):
         dq[b, h] = a
         dk[b, h] = bb
         dv[b, h] = c
         dalpha += da
+        dalpha_abs += dabs
+    if return_abs:
+        return dq, dk, dv, dalpha, dalpha_abs
     return dq, dk, dv, dalpha

@@ -44,6 +44,8 @@ def test_interp_backward_vs_autograd(alpha, W):
     np.testing.assert_allclose(dk, kt.grad.numpy(), rtol=0, atol=1e-11)
     np.testing.assert_allclose(dv, vt.grad.numpy(), rtol=0, atol=1e-11)
     np.testing.assert_allclose(da, at.grad.item(), rtol=1e-10, atol=1e-10)
+    *_, da2, dabs = O.backward(q, k, v, do, W, alpha, SMALL_FIB, 10000.0, O.INTERP, return_abs=True)
+    assert da2 == da and dabs >= abs(da) and dabs > 0
 
 
 def _loss(q, k, v, do, W, alpha, mode):
