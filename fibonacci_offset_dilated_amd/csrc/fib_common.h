@@ -46,14 +46,14 @@ __device__ __forceinline__ float2 rope_cs(int64_t p, double rev) {
 __device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
-// fp32 -> bf16 bits, round to nearest even; NaN stays a (quiet) NaN.
-__device__ __forceinline__ uint32_t f2bf(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// fp32 -> bf16, round to nearest even (NaN stays NaN): the hardware conversion
+// v_cvt_pk_bf16_f32, two values per instruction.
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
-__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+__device__ __forceinline__ uint32_t f2bf(float x) { return pack_bf2(x, 0.f) & 0xffffu; }
 
 // 8 consecutive elements <-> 8 floats
 template <typename T> struct Vec8;

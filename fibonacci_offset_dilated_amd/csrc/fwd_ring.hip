@@ -3,9 +3,9 @@
 //
 // Operation ("Depth-Staggered Fibonacci Spacing for Sparse Attention", gist.science summaries
 // of arXiv 2606.28560, Method > Architecture and attention mechanism): query i attends the
-// window rows i-W+1..i and one (integer mode) or one interpolated pair of (interpolated mode)
-// rows per table entry, after RoPE; Results 2 notes that static offsets allow a fused path,
-// which this kernel is for both modes.
+// window rows i-W+1..i and one row (integer mode) or one interpolated pair of rows
+// (interpolated mode) per table entry, after RoPE. Results 2 notes that static offsets allow
+// a fused path; here both modes run fused in this kernel.
 //
 // Design (gfx950):
 //  * One 256-thread workgroup (4 waves) per CU sweeps a contiguous segment of one head in
@@ -17,13 +17,17 @@
 //    B = the wave's 16 rotated queries). The window band is a 32-key by 16-query block; a
 //    table entry is a 16-row slab whose diagonal holds the 16 logits (query n reads slab
 //    row n), picked out of the lanes that own it.
-//  * Table entries beyond the ring read raw K rows from global memory and use relative RoPE:
-//    <R_i q, R_(i-d) k> = <R_d q, k>, with cos/sin of R_d computed once per workgroup.
+//  * Table entries beyond the ring read raw K and V rows from global memory, prefetched one
+//    step ahead into registers, and use relative RoPE <R_i q, R_(i-d) k> = <R_d q, k> with
+//    cos/sin of R_d computed once per workgroup; their P V runs on VALU.
 //  * Softmax over all logits of a query at once (they fit in registers), fp32, base 2.
 //  * P V on MFMA as O^T = V^T P^T: V^T operands come from the ring through the LDS transpose
 //    read (ds_read_b64_tr_b16); table entries use a diagonal P^T block, two slabs per MFMA
 //    (interpolated mode: the lower and upper slab of one entry, weights 1-w and w).
-//  * Ring rows use a 16-byte-chunk XOR swizzle (chunk ^ (slot & 7)) against bank conflicts.
+//  * Ring rows are padded to 144 bytes: with 64 LDS banks, 16 consecutive rows then start on 16
+//    distinct 4-bank groups, so the A-operand reads (16 rows, one 16-byte chunk each) and the
+//    transpose reads (4 rows x 32 bytes per 16 lanes) are conflict-free, and every read of a
+//    row is one base address plus immediate offsets.
 #include "fib_common.h"
 #include "fib_launch.h"
 
@@ -31,18 +35,18 @@ namespace fib {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) float f4;
 typedef __attribute__((ext_vector_type(4))) short s4;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kT = 16 * kWaves;       // queries (and ring rows) per step
-constexpr int kP = 576;               // ring rows
+constexpr int kP = 512;               // ring rows (a power of two: slot = row & (kP - 1))
+constexpr int kRow = 144;             // ring row stride in bytes (128 + 16 padding)
 constexpr int kMaxCov = kP - kT;      // largest distance served from the ring
 constexpr int kMaxBand = 16;          // window band rows before a 16-query block
-constexpr int kMaxUnc = 8;            // distances served from global memory
-constexpr int kStageRows = 17;        // per-wave staging rows for V of far entries
+constexpr int kMaxFar = 4;            // table entries served from global memory
+constexpr int kMaxUnc = 2 * kMaxFar;  // their distances (interpolated: c and c - 1)
 
 struct RingArgs {
   const bf16_t* q;
@@ -50,34 +54,31 @@ struct RingArgs {
   const bf16_t* v;
   bf16_t* o;
   float* lse;
-  int64_t N;
+  int N;
   int W;
-  int n_ent;        // table entries
   int n_cov;        // entries served from the ring (a prefix of the table)
-  int n_unc;        // far distances (integer: one per far entry; interpolated: c and c-1)
+  int n_far;        // entries served from global memory (after the covered ones)
   int seg_len;      // rows per workgroup (multiple of kT)
   int segs;         // segments per head
   int warm;         // rows inserted before the segment start (multiple of kT)
   float scale_log2;
-  int dist[kMaxEnt];
+  int dist[kMaxEnt];  // covered distances; slots past n_cov hold a harmless in-ring distance
   float w[kMaxEnt];
+  int far_dist[kMaxFar];
+  float far_w[kMaxFar];
   int unc_dist[kMaxUnc];
   Rope rope;
 };
 
 struct __align__(16) Smem {
-  uint8_t ringK[kP * 128];
-  uint8_t ringV[kP * 128];
-  uint8_t stage[kWaves][kStageRows * 128];
+  uint8_t ringK[kP * kRow];
+  uint8_t ringV[kP * kRow];
   float2 unc_cs[kMaxUnc][kHalf];
   float2 base_cs[2][kHalf];
 };
 
-__device__ __forceinline__ int slot_of(int64_t row) {
-  // rows may be negative by up to kP (zero-filled ring slots stand for them)
-  return (int)((row + (int64_t)kP * 4) % kP);
-}
-__device__ __forceinline__ int chunk_off(int slot, int chunk) { return slot * 128 + ((chunk ^ (slot & 7)) << 4); }
+// byte offset of ring row `row` (any integer, negative rows included: slots are row mod kP)
+__device__ __forceinline__ int row_off(int row) { return (row & (kP - 1)) * kRow; }
 
 __device__ __forceinline__ uint4 lds_read16(const uint8_t* base, int off) {
   return *reinterpret_cast<const uint4*>(base + off);
@@ -89,8 +90,7 @@ __device__ __forceinline__ void lds_write16(uint8_t* base, int off, uint4 x) {
 // LDS transpose read of 4 bf16: lane j (of 16) supplies the address of 4 consecutive
 // elements of row (k0 + j/4); lane i receives rows k0..k0+3 of column i.
 __device__ __forceinline__ s4 tr16(const uint8_t* base, int off) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s4*)(base + off));
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(base + off));
 }
 
 __device__ __forceinline__ bf16x8 as_bf8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -99,13 +99,9 @@ __device__ __forceinline__ bf16x8 cat_bf8(s4 a, s4 b) {
   s8 c = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   return __builtin_bit_cast(bf16x8, c);
 }
-__device__ __forceinline__ bf16x4 as_bf4(s4 a) { return __builtin_bit_cast(bf16x4, a); }
 
 __device__ __forceinline__ f4 mfma32(bf16x8 a, bf16x8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f4 mfma16(bf16x4 a, bf16x4 b, f4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ void unpack8(uint4 x, float* f) {
@@ -133,34 +129,95 @@ __device__ __forceinline__ void rotate_pack(uint4 lo, uint4 hi, const float2* cs
   *out_hi = pack8(rb);
 }
 
+// 2^x on the hardware unit (v_exp_f32); arguments here are <= 0 and results below the
+// normal range are negligible softmax weights
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+__device__ __forceinline__ bf16x2 as_bf2(uint32_t x) { return __builtin_bit_cast(bf16x2, x); }
+// c + x.lo * w.lo + x.hi * w.hi on bf16 pairs, fp32 accumulation (v_dot2_f32_bf16)
+__device__ __forceinline__ float dot2(uint32_t x, uint32_t w, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(as_bf2(x), as_bf2(w), c, false);
+}
+
 // value of x rounded to bf16 (nearest even), as fp32
-__device__ __forceinline__ float round_bf(float x) { return __uint_as_float(f2bf(x) << 16); }
+__device__ __forceinline__ float round_bf(float x) { return __uint_as_float(pack_bf2(0.f, x) & 0xffff0000u); }
 
 // select x[l & 3]
 __device__ __forceinline__ float sel4(f4 x, int l) {
-  float a = (l & 1) ? x[1] : x[0];
-  float b = (l & 1) ? x[3] : x[2];
+  const float a = (l & 1) ? x[1] : x[0];
+  const float b = (l & 1) ? x[3] : x[2];
   return (l & 2) ? b : a;
 }
 
-// 4 bf16 slots with value p at slot (l & 3), zeros elsewhere (as 2 packed dwords)
-__device__ __forceinline__ void diag_slots(float p, int l, bool diag, uint32_t* d0, uint32_t* d1) {
-  const uint32_t b = diag ? f2bf(p) : 0u;
+// 4 bf16 slots holding p (already bf16-exact, or 0) at slot (l & 3), zeros elsewhere
+__device__ __forceinline__ void diag_slots(float p, int l, uint32_t* d0, uint32_t* d1) {
+  const uint32_t b = __float_as_uint(p) >> 16;
   const int s = l & 3;
   *d0 = s == 0 ? b : (s == 1 ? (b << 16) : 0u);
   *d1 = s == 2 ? b : (s == 3 ? (b << 16) : 0u);
 }
 
-__device__ __forceinline__ float wave_xor_max(float x) {
+__device__ __forceinline__ float xor_max(float x) {
   x = fmaxf(x, __shfl_xor(x, 16));
   return fmaxf(x, __shfl_xor(x, 32));
 }
-__device__ __forceinline__ float wave_xor_sum(float x) {
+__device__ __forceinline__ float xor_sum(float x) {
   x += __shfl_xor(x, 16);
   return x + __shfl_xor(x, 32);
 }
 
+// Rows of the far table entries for one step, held in registers and loaded one step ahead:
+// lane (n, g) holds, per far entry, K row i0w - d + n (dims 8g.., 32+8g..; the A operand of
+// the logit MFMA) and V row i0w - d + n (dims 16mb + 4g .. +3 for mb < 4; the lane's slice of
+// O^T), and in interpolated mode the same for the upper row (+1).
+struct FarRows {
+  uint4 k[kMaxFar][2];
+  uint4 kh[kMaxFar][2];
+  uint2 v[kMaxFar][4];
+  uint2 vh[kMaxFar][4];
+};
+
+__device__ __forceinline__ int far_row(const RingArgs& a, int f, int i0w, int n, int up) {
+  const int r = i0w - a.far_dist[f] + n + up;
+  return r < 0 ? 0 : (r >= a.N ? a.N - 1 : r);
+}
+
 template <int MODE>
+__device__ __forceinline__ void load_far_k(FarRows& fr, const RingArgs& a, const bf16_t* Kh, int i0w, int n, int g) {
+#pragma unroll
+  for (int f = 0; f < kMaxFar; ++f) {
+    if (f < a.n_far) {
+      const bf16_t* kp = Kh + (int64_t)far_row(a, f, i0w, n, 0) * kD;
+      fr.k[f][0] = *reinterpret_cast<const uint4*>(kp + 8 * g);
+      fr.k[f][1] = *reinterpret_cast<const uint4*>(kp + kHalf + 8 * g);
+      if (MODE == 1) {
+        const bf16_t* kq = Kh + (int64_t)far_row(a, f, i0w, n, 1) * kD;
+        fr.kh[f][0] = *reinterpret_cast<const uint4*>(kq + 8 * g);
+        fr.kh[f][1] = *reinterpret_cast<const uint4*>(kq + kHalf + 8 * g);
+      }
+    }
+  }
+}
+
+template <int MODE>
+__device__ __forceinline__ void load_far_v(FarRows& fr, const RingArgs& a, const bf16_t* Vh, int i0w, int n, int g) {
+#pragma unroll
+  for (int f = 0; f < kMaxFar; ++f) {
+    if (f < a.n_far) {
+      const bf16_t* vp = Vh + (int64_t)far_row(a, f, i0w, n, 0) * kD;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) fr.v[f][mb] = *reinterpret_cast<const uint2*>(vp + 16 * mb + 4 * g);
+      if (MODE == 1) {
+        const bf16_t* vq = Vh + (int64_t)far_row(a, f, i0w, n, 1) * kD;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) fr.vh[f][mb] = *reinterpret_cast<const uint2*>(vq + 16 * mb + 4 * g);
+      }
+    }
+  }
+}
+
+template <int MODE, int NC>
 __global__ __launch_bounds__(kThreads, 1) void fwd_ring_kernel(RingArgs a) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
@@ -170,12 +227,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_ring_kernel(RingArgs a) {
   const int n = l & 15;   // query (and row) within the wave's 16
   const int g = l >> 4;   // lane group: dims 8g..8g+7 and 32+8g..32+8g+7
   const bool diag_lane = g == (n >> 2);
+  const int jr = n >> 2;  // transpose-read row within a 4-row group
+  const int jc = n & 3;   // transpose-read 4-column group
 
   const int64_t head = blockIdx.x / a.segs;
   const int seg = blockIdx.x % a.segs;
-  const int64_t N = a.N;
-  const int64_t s0 = (int64_t)seg * a.seg_len;
-  const int64_t s1 = s0 + a.seg_len < N ? s0 + a.seg_len : N;
+  const int N = a.N;
+  const int s0 = seg * a.seg_len;
+  const int s1 = s0 + a.seg_len < N ? s0 + a.seg_len : N;
   const size_t hoff = (size_t)head * (size_t)N * kD;
   const bf16_t* Qh = a.q + hoff;
   const bf16_t* Kh = a.k + hoff;
@@ -184,15 +243,15 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_ring_kernel(RingArgs a) {
   // ---- set-up: zero the ring, cos/sin of the far distances and of the first step base
   {
     uint4* z = reinterpret_cast<uint4*>(sm.ringK);
-    const int n16 = (2 * kP * 128) / 16;
+    const int n16 = (2 * kP * kRow) / 16;
     for (int x = tid; x < n16; x += kThreads) z[x] = make_uint4(0, 0, 0, 0);
-    for (int x = tid; x < a.n_unc * kHalf; x += kThreads) {
+    const int n_unc = MODE == 1 ? 2 * a.n_far : a.n_far;
+    for (int x = tid; x < n_unc * kHalf; x += kThreads) {
       const int u = x / kHalf, j = x % kHalf;
       sm.unc_cs[u][j] = rope_cs(a.unc_dist[u], a.rope.rev[j]);
     }
   }
-  int64_t p0 = s0 - a.warm;
-  if (p0 < 0) p0 = 0;
+  int p0 = s0 - a.warm > 0 ? s0 - a.warm : 0;
   if (tid < kHalf) sm.base_cs[0][tid] = rope_cs(p0, a.rope.rev[tid]);
   // per-lane rotation by t = 16 wave + n (the row's offset from the step base)
   float2 cs_t[8];
@@ -200,13 +259,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_ring_kernel(RingArgs a) {
   for (int t = 0; t < 8; ++t) cs_t[t] = rope_cs(16 * wave + n, a.rope.rev[8 * g + t]);
   __syncthreads();
 
-  // prefetch of the rows this lane inserts: q/k/v dims 8g.. and 32+8g.. of row p0 + 16w + n
-  auto load_rows = [&](int64_t pb, uint4* q2, uint4* k2, uint4* v2) {
-    const int64_t r = pb + 16 * wave + n;
+  // rows this lane inserts: q/k/v dims 8g.. and 32+8g.. of row pb + 16w + n
+  auto load_rows = [&](int pb, uint4* q2, uint4* k2, uint4* v2) {
+    const int r = pb + 16 * wave + n;
     if (r < N) {
-      const bf16_t* qp = Qh + r * kD;
-      const bf16_t* kp = Kh + r * kD;
-      const bf16_t* vp = Vh + r * kD;
+      const bf16_t* qp = Qh + (int64_t)r * kD;
+      const bf16_t* kp = Kh + (int64_t)r * kD;
+      const bf16_t* vp = Vh + (int64_t)r * kD;
       q2[0] = *reinterpret_cast<const uint4*>(qp + 8 * g);
       q2[1] = *reinterpret_cast<const uint4*>(qp + kHalf + 8 * g);
       k2[0] = *reinterpret_cast<const uint4*>(kp + 8 * g);
@@ -219,6 +278,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_ring_kernel(RingArgs a) {
   };
   uint4 pq[2], pk[2], pv[2];
   load_rows(p0, pq, pk, pv);
+  // far rows of the first computed step (p0 reaches s0 exactly: both are multiples of kT)
+  FarRows fr;
+  if (a.n_far > 0) {
+    load_far_k<MODE>(fr, a, Kh, s0 + 16 * wave, n, g);
+    load_far_v<MODE>(fr, a, Vh, s0 + 16 * wave, n, g);
+  }
 
   const float sl2 = a.scale_log2;
   int buf = 0;
@@ -234,83 +299,80 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_ring_kernel(RingArgs a) {
     rotate_pack(pk[0], pk[1], cs, &kr0, &kr1);
     rotate_pack(pq[0], pq[1], cs, &qh0, &qh1);
     const uint4 qraw0 = pq[0], qraw1 = pq[1];
+    const int bw = p0 + 16 * wave;  // row i0w of this wave's queries
     {
-      const int sl = slot_of(p0 + 16 * wave + n);
-      lds_write16(sm.ringK, chunk_off(sl, g), kr0);
-      lds_write16(sm.ringK, chunk_off(sl, 4 + g), kr1);
-      lds_write16(sm.ringV, chunk_off(sl, g), pv[0]);
-      lds_write16(sm.ringV, chunk_off(sl, 4 + g), pv[1]);
+      const int ro = row_off(bw + n) + 16 * g;
+      lds_write16(sm.ringK, ro, kr0);
+      lds_write16(sm.ringK, ro + 64, kr1);
+      lds_write16(sm.ringV, ro, pv[0]);
+      lds_write16(sm.ringV, ro + 64, pv[1]);
     }
     __syncthreads();
     // next step's rows and base rotation
-    const int64_t pn = p0 + kT;
+    const int pn = p0 + kT;
     if (pn < s1) load_rows(pn, pq, pk, pv);
     if (wave == 0 && l < kHalf) sm.base_cs[buf ^ 1][l] = rope_cs(pn, a.rope.rev[l]);
 
     if (p0 >= s0) {
-      const int64_t i0w = p0 + 16 * wave;
-      const int64_t iq = i0w + n;  // this lane's query
+      const int i0w = p0 + 16 * wave;
+      const int iq = i0w + n;  // this lane's query
       const bf16x8 bq0 = as_bf8(qh0), bq1 = as_bf8(qh1);
 
-      // ---- logits: window band (keys i0w-16+kappa, kappa < 32) and table entries
-      f4 S0 = {0, 0, 0, 0}, S1 = {0, 0, 0, 0};
-      {
-        const int sa = slot_of(i0w - 16 + n), sb = slot_of(i0w + n);
-        S0 = mfma32(as_bf8(lds_read16(sm.ringK, chunk_off(sa, g))), bq0, S0);
-        S0 = mfma32(as_bf8(lds_read16(sm.ringK, chunk_off(sa, 4 + g))), bq1, S0);
-        S1 = mfma32(as_bf8(lds_read16(sm.ringK, chunk_off(sb, g))), bq0, S1);
-        S1 = mfma32(as_bf8(lds_read16(sm.ringK, chunk_off(sb, 4 + g))), bq1, S1);
-      }
-      float s_ent[kMaxEnt];
-      // covered entries: slabs from the ring
-      for (int e = 0; e < a.n_cov; ++e) {
-        const int d = a.dist[e];
-        const int sl = slot_of(i0w - d + n);
-        f4 S = {0, 0, 0, 0};
-        S = mfma32(as_bf8(lds_read16(sm.ringK, chunk_off(sl, g))), bq0, S);
-        S = mfma32(as_bf8(lds_read16(sm.ringK, chunk_off(sl, 4 + g))), bq1, S);
-        float s = sel4(S, l);
-        if (MODE == 1) {
-          const int sh = slot_of(i0w - d + 1 + n);
-          f4 H = {0, 0, 0, 0};
-          H = mfma32(as_bf8(lds_read16(sm.ringK, chunk_off(sh, g))), bq0, H);
-          H = mfma32(as_bf8(lds_read16(sm.ringK, chunk_off(sh, 4 + g))), bq1, H);
-          s = fmaf(a.w[e], sel4(H, l) - s, s);
-        }
-        s_ent[e] = (diag_lane && (int64_t)d <= iq) ? s * sl2 : -INFINITY;
-      }
-      // far entries: raw K rows from global memory, relatively rotated queries
-      for (int e = a.n_cov; e < a.n_ent; ++e) {
-        const int d = a.dist[e];
-        const int u = MODE == 1 ? 2 * (e - a.n_cov) : e - a.n_cov;
-        float s;
-        {
-          int64_t r = i0w - d + n;
-          r = r < 0 ? 0 : r;
-          const bf16_t* kp = Kh + r * kD;
-          const uint4 k0 = *reinterpret_cast<const uint4*>(kp + 8 * g);
-          const uint4 k1 = *reinterpret_cast<const uint4*>(kp + kHalf + 8 * g);
+      // ---- logits of the far entries first, so their next rows can be requested early
+      float s_far[kMaxFar];
+#pragma unroll
+      for (int f = 0; f < kMaxFar; ++f) {
+        s_far[f] = -INFINITY;
+        if (f < a.n_far) {
+          const int u = MODE == 1 ? 2 * f : f;
           uint4 r0, r1;
           rotate_pack(qraw0, qraw1, &sm.unc_cs[u][8 * g], &r0, &r1);
           f4 S = {0, 0, 0, 0};
-          S = mfma32(as_bf8(k0), as_bf8(r0), S);
-          S = mfma32(as_bf8(k1), as_bf8(r1), S);
-          s = sel4(S, l);
+          S = mfma32(as_bf8(fr.k[f][0]), as_bf8(r0), S);
+          S = mfma32(as_bf8(fr.k[f][1]), as_bf8(r1), S);
+          float s = sel4(S, l);
+          if (MODE == 1) {
+            rotate_pack(qraw0, qraw1, &sm.unc_cs[u + 1][8 * g], &r0, &r1);
+            f4 H = {0, 0, 0, 0};
+            H = mfma32(as_bf8(fr.kh[f][0]), as_bf8(r0), H);
+            H = mfma32(as_bf8(fr.kh[f][1]), as_bf8(r1), H);
+            s = fmaf(a.far_w[f], sel4(H, l) - s, s);
+          }
+          s_far[f] = (diag_lane && a.far_dist[f] <= iq) ? s * sl2 : -INFINITY;
         }
-        if (MODE == 1) {
-          int64_t r = i0w - d + 1 + n;
-          r = r < 0 ? 0 : r;
-          const bf16_t* kp = Kh + r * kD;
-          const uint4 k0 = *reinterpret_cast<const uint4*>(kp + 8 * g);
-          const uint4 k1 = *reinterpret_cast<const uint4*>(kp + kHalf + 8 * g);
-          uint4 r0, r1;
-          rotate_pack(qraw0, qraw1, &sm.unc_cs[u + 1][8 * g], &r0, &r1);
-          f4 H = {0, 0, 0, 0};
-          H = mfma32(as_bf8(k0), as_bf8(r0), H);
-          H = mfma32(as_bf8(k1), as_bf8(r1), H);
-          s = fmaf(a.w[e], sel4(H, l) - s, s);
+      }
+      if (a.n_far > 0 && pn < s1) load_far_k<MODE>(fr, a, Kh, i0w + kT, n, g);
+
+      // ---- window band: keys i0w - 16 + kappa, kappa < 32
+      f4 S0 = {0, 0, 0, 0}, S1 = {0, 0, 0, 0};
+      {
+        const int sa = row_off(bw - 16 + n) + 16 * g, sb = row_off(bw + n) + 16 * g;
+        S0 = mfma32(as_bf8(lds_read16(sm.ringK, sa)), bq0, S0);
+        S0 = mfma32(as_bf8(lds_read16(sm.ringK, sa + 64)), bq1, S0);
+        S1 = mfma32(as_bf8(lds_read16(sm.ringK, sb)), bq0, S1);
+        S1 = mfma32(as_bf8(lds_read16(sm.ringK, sb + 64)), bq1, S1);
+      }
+      // ---- covered entries: 16-row slabs from the ring
+      float s_ent[NC];
+#pragma unroll
+      for (int e = 0; e < NC; ++e) {
+        s_ent[e] = -INFINITY;
+        if (e < a.n_cov) {
+          const int d = a.dist[e];
+          const int sl = row_off(bw - d + n) + 16 * g;
+          f4 S = {0, 0, 0, 0};
+          S = mfma32(as_bf8(lds_read16(sm.ringK, sl)), bq0, S);
+          S = mfma32(as_bf8(lds_read16(sm.ringK, sl + 64)), bq1, S);
+          float s = sel4(S, l);
+          if (MODE == 1) {
+            const int sh = row_off(bw - d + 1 + n) + 16 * g;
+            f4 H = {0, 0, 0, 0};
+            H = mfma32(as_bf8(lds_read16(sm.ringK, sh)), bq0, H);
+            H = mfma32(as_bf8(lds_read16(sm.ringK, sh + 64)), bq1, H);
+            s = fmaf(a.w[e], sel4(H, l) - s, s);
+          }
+          s_ent[e] = (diag_lane && d <= iq) ? s * sl2 : -INFINITY;
         }
-        s_ent[e] = (diag_lane && (int64_t)d <= iq) ? s * sl2 : -INFINITY;
       }
 
       // ---- softmax over the window band and the entries
@@ -319,151 +381,138 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_ring_kernel(RingArgs a) {
       for (int v = 0; v < 4; ++v) {
         const int d0 = n + 16 - 4 * g - v;  // >= 1
         const int d1 = n - 4 * g - v;
-        sw0[v] = (d0 < a.W && (int64_t)d0 <= iq) ? S0[v] * sl2 : -INFINITY;
+        sw0[v] = (d0 < a.W && d0 <= iq) ? S0[v] * sl2 : -INFINITY;
         sw1[v] = (d1 >= 0 && d1 < a.W) ? S1[v] * sl2 : -INFINITY;
       }
       float m = -INFINITY;
 #pragma unroll
       for (int v = 0; v < 4; ++v) m = fmaxf(m, fmaxf(sw0[v], sw1[v]));
-      for (int e = 0; e < a.n_ent; ++e) m = fmaxf(m, s_ent[e]);
-      m = wave_xor_max(m);  // every query has its own key (distance 0), so m is finite
-      // lsum (fp32 weights) gives LSE; lnorm sums the bf16 weights the P V products use, so
-      // that O is normalised by exactly the weights applied (rows of P sum to 1)
+#pragma unroll
+      for (int e = 0; e < NC; ++e) m = fmaxf(m, s_ent[e]);
+#pragma unroll
+      for (int f = 0; f < kMaxFar; ++f) m = fmaxf(m, s_far[f]);
+      m = xor_max(m);  // every query has its own key (distance 0), so m is finite
+      // lsum (fp32 weights) gives LSE; lnorm sums the bf16 weights the P V products apply,
+      // so that O is normalised by exactly those weights (rows of P sum to 1)
       float lsum = 0.f, lnorm = 0.f;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        sw0[v] = exp2f(sw0[v] - m);
-        sw1[v] = exp2f(sw1[v] - m);
-        lsum += sw0[v] + sw1[v];
-        lnorm += round_bf(sw0[v]) + round_bf(sw1[v]);
+        const float p0v = ex2(sw0[v] - m), p1v = ex2(sw1[v] - m);
+        lsum += p0v + p1v;
+        sw0[v] = round_bf(p0v);
+        sw1[v] = round_bf(p1v);
+        lnorm += sw0[v] + sw1[v];
       }
-      for (int e = 0; e < a.n_ent; ++e) {
-        s_ent[e] = exp2f(s_ent[e] - m);
-        lsum += s_ent[e];
-        if (MODE == 0)
-          lnorm += round_bf(s_ent[e]);
-        else
-          lnorm += round_bf(s_ent[e] * (1.f - a.w[e])) + round_bf(s_ent[e] * a.w[e]);
+      // entry weights: integer mode keeps the bf16 weight in s_ent; interpolated mode keeps
+      // the fp32 weight (its two bf16 parts are formed at use)
+#pragma unroll
+      for (int e = 0; e < NC; ++e) {
+        const float p = ex2(s_ent[e] - m);
+        lsum += p;
+        if (MODE == 0) {
+          s_ent[e] = round_bf(p);
+          lnorm += s_ent[e];
+        } else {
+          s_ent[e] = p;
+          lnorm += round_bf(p * (1.f - a.w[e])) + round_bf(p * a.w[e]);
+        }
       }
-      lsum = wave_xor_sum(lsum);
-      lnorm = wave_xor_sum(lnorm);
+#pragma unroll
+      for (int f = 0; f < kMaxFar; ++f) {
+        const float p = ex2(s_far[f] - m);
+        lsum += p;
+        s_far[f] = p;
+        lnorm += MODE == 0 ? round_bf(p) : round_bf(p * (1.f - a.far_w[f])) + round_bf(p * a.far_w[f]);
+      }
+      lsum = xor_sum(lsum);
+      lnorm = xor_sum(lnorm);
 
       // ---- P V: O^T[dim 16 mb + 4 g + v][query n]
       f4 acc[4];
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) acc[mb] = f4{0, 0, 0, 0};
-      const int jr = n >> 2;              // transpose-read row within a 4-row group
-      const int jc = n & 3;               // transpose-read 4-column group
-      auto tr_off = [&](int64_t row, int mb) {
-        const int sl = slot_of(row);
-        const int chunk = 2 * mb + (jc >> 1);
-        return sl * 128 + ((chunk ^ (sl & 7)) << 4) + ((jc & 1) << 3);
-      };
+      // transpose reads: lane (jr, jc) of a 16-lane group reads row k0 + jr, dims
+      // 16 mb + 4 jc .. +3, i.e. bytes 32 mb + 8 jc of the row
+      auto tr_base = [&](int row) { return row_off(row) + 8 * jc; };
       {
-        uint32_t pw[4];
-        pw[0] = pack_bf2(sw0[0], sw0[1]);
-        pw[1] = pack_bf2(sw0[2], sw0[3]);
-        pw[2] = pack_bf2(sw1[0], sw1[1]);
-        pw[3] = pack_bf2(sw1[2], sw1[3]);
-        const bf16x8 bp = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
-        const int64_t r0 = i0w - 16 + 4 * g + jr, r1 = i0w + 4 * g + jr;
+        const bf16x8 bp = __builtin_bit_cast(
+            bf16x8, make_uint4(pack_bf2(sw0[0], sw0[1]), pack_bf2(sw0[2], sw0[3]), pack_bf2(sw1[0], sw1[1]),
+                               pack_bf2(sw1[2], sw1[3])));
+        const int r0 = tr_base(bw - 16 + 4 * g + jr), r1 = tr_base(bw + 4 * g + jr);
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
-          acc[mb] = mfma32(cat_bf8(tr16(sm.ringV, tr_off(r0, mb)), tr16(sm.ringV, tr_off(r1, mb))), bp, acc[mb]);
+          acc[mb] = mfma32(cat_bf8(tr16(sm.ringV, r0 + 32 * mb), tr16(sm.ringV, r1 + 32 * mb)), bp, acc[mb]);
       }
-      // stage far V rows (this wave's region), rows i0w - d + r for r < 16 (+1 upper row)
-      auto stage_rows = [&](int d) {
-        uint8_t* st = sm.stage[wave];
-        for (int r = n; r < kStageRows; r += 16) {
-          int64_t row = i0w - d + r;
-          row = row < 0 ? 0 : (row >= N ? N - 1 : row);
-          const bf16_t* vp = Vh + row * kD;
-          lds_write16(st, r * 128 + ((g ^ (r & 7)) << 4), *reinterpret_cast<const uint4*>(vp + 8 * g));
-          lds_write16(st, r * 128 + (((4 + g) ^ (r & 7)) << 4), *reinterpret_cast<const uint4*>(vp + kHalf + 8 * g));
+      // far entries on VALU: the lane's O^T slice += p * V[row][16 mb + 4 g + v]; p lives in the
+      // query's diagonal lane and is broadcast to its other three lanes. A separate register
+      // accumulator keeps this off the MFMA accumulators.
+      float accf[4][4];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) accf[mb][0] = accf[mb][1] = accf[mb][2] = accf[mb][3] = 0.f;
+#pragma unroll
+      for (int f = 0; f < kMaxFar; ++f) {
+        if (f < a.n_far) {
+          const float p = __shfl(s_far[f], 16 * (n >> 2) + n);
+          const float plo = MODE == 1 ? round_bf(p * (1.f - a.far_w[f])) : round_bf(p);
+          const float phi = MODE == 1 ? round_bf(p * a.far_w[f]) : 0.f;
+          const uint32_t blo = __float_as_uint(plo), bhi = __float_as_uint(phi);
+          if (MODE == 0) {
+            // weights (p, 0) and (0, p) pick one bf16 of a pair: one dot2 per element
+            const uint32_t w0 = blo >> 16, w1 = blo & 0xffff0000u;
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+              const uint2 x = fr.v[f][mb];
+              accf[mb][0] = dot2(x.x, w0, accf[mb][0]);
+              accf[mb][1] = dot2(x.x, w1, accf[mb][1]);
+              accf[mb][2] = dot2(x.y, w0, accf[mb][2]);
+              accf[mb][3] = dot2(x.y, w1, accf[mb][3]);
+            }
+          } else {
+            // pair the lower-row and upper-row element of a dim, weights (1-w) p and w p
+            const uint32_t wp = (blo >> 16) | (bhi & 0xffff0000u);
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+              const uint2 x = fr.v[f][mb], y = fr.vh[f][mb];
+              accf[mb][0] = dot2(__builtin_amdgcn_perm(y.x, x.x, 0x05040100u), wp, accf[mb][0]);
+              accf[mb][1] = dot2(__builtin_amdgcn_perm(y.x, x.x, 0x07060302u), wp, accf[mb][1]);
+              accf[mb][2] = dot2(__builtin_amdgcn_perm(y.y, x.y, 0x05040100u), wp, accf[mb][2]);
+              accf[mb][3] = dot2(__builtin_amdgcn_perm(y.y, x.y, 0x07060302u), wp, accf[mb][3]);
+            }
+          }
         }
-      };
-      auto st_off = [&](int r, int mb) {
-        const int chunk = 2 * mb + (jc >> 1);
-        return r * 128 + ((chunk ^ (r & 7)) << 4) + ((jc & 1) << 3);
-      };
+      }
+      if (a.n_far > 0 && pn < s1) load_far_v<MODE>(fr, a, Vh, i0w + kT, n, g);
+
+      // covered entries on MFMA with a diagonal P^T block (integer mode: two entries per
+      // MFMA, a missing second entry has weight 0 and an in-ring dummy distance; interpolated
+      // mode: the lower and upper slab of one entry)
       if (MODE == 0) {
-        int e = 0;
-        for (; e + 1 < a.n_ent; e += 2) {
-          uint32_t d0, d1, d2, d3;
-          diag_slots(s_ent[e], l, diag_lane, &d0, &d1);
-          diag_slots(s_ent[e + 1], l, diag_lane, &d2, &d3);
-          const bf16x8 bp = __builtin_bit_cast(bf16x8, make_uint4(d0, d1, d2, d3));
-          const bool far0 = e >= a.n_cov, far1 = e + 1 >= a.n_cov;
-          s4 lo[4], hi[4];
-          if (far0) {
-            stage_rows(a.dist[e]);
-            __builtin_amdgcn_s_waitcnt(0);
-            __builtin_amdgcn_wave_barrier();
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) lo[mb] = tr16(sm.stage[wave], st_off(4 * g + jr, mb));
-          } else {
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) lo[mb] = tr16(sm.ringV, tr_off(i0w - a.dist[e] + 4 * g + jr, mb));
-          }
-          if (far1) {
-            __builtin_amdgcn_s_waitcnt(0);
-            __builtin_amdgcn_wave_barrier();
-            stage_rows(a.dist[e + 1]);
-            __builtin_amdgcn_s_waitcnt(0);
-            __builtin_amdgcn_wave_barrier();
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) hi[mb] = tr16(sm.stage[wave], st_off(4 * g + jr, mb));
-          } else {
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) hi[mb] = tr16(sm.ringV, tr_off(i0w - a.dist[e + 1] + 4 * g + jr, mb));
-          }
-#pragma unroll
-          for (int mb = 0; mb < 4; ++mb) acc[mb] = mfma32(cat_bf8(lo[mb], hi[mb]), bp, acc[mb]);
-          __builtin_amdgcn_s_waitcnt(0);
-          __builtin_amdgcn_wave_barrier();
-        }
-        if (e < a.n_ent) {
-          uint32_t d0, d1;
-          diag_slots(s_ent[e], l, diag_lane, &d0, &d1);
-          const bf16x4 bp = __builtin_bit_cast(bf16x4, make_uint2(d0, d1));
-          if (e >= a.n_cov) {
-            stage_rows(a.dist[e]);
-            __builtin_amdgcn_s_waitcnt(0);
-            __builtin_amdgcn_wave_barrier();
+        for (int e = 0; e < NC; e += 2) {
+          if (e < a.n_cov) {
+            uint32_t d0, d1, d2, d3;
+            diag_slots(diag_lane ? s_ent[e] : 0.f, l, &d0, &d1);
+            diag_slots(diag_lane ? s_ent[e + 1] : 0.f, l, &d2, &d3);
+            const bf16x8 bp = __builtin_bit_cast(bf16x8, make_uint4(d0, d1, d2, d3));
+            const int ra = tr_base(bw - a.dist[e] + 4 * g + jr), rb = tr_base(bw - a.dist[e + 1] + 4 * g + jr);
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb)
-              acc[mb] = mfma16(as_bf4(tr16(sm.stage[wave], st_off(4 * g + jr, mb))), bp, acc[mb]);
-            __builtin_amdgcn_s_waitcnt(0);
-            __builtin_amdgcn_wave_barrier();
-          } else {
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-              acc[mb] = mfma16(as_bf4(tr16(sm.ringV, tr_off(i0w - a.dist[e] + 4 * g + jr, mb))), bp, acc[mb]);
+              acc[mb] = mfma32(cat_bf8(tr16(sm.ringV, ra + 32 * mb), tr16(sm.ringV, rb + 32 * mb)), bp, acc[mb]);
           }
         }
       } else {
-        for (int e = 0; e < a.n_ent; ++e) {
-          const float w = a.w[e];
-          uint32_t d0, d1, d2, d3;
-          diag_slots(s_ent[e] * (1.f - w), l, diag_lane, &d0, &d1);
-          diag_slots(s_ent[e] * w, l, diag_lane, &d2, &d3);
-          const bf16x8 bp = __builtin_bit_cast(bf16x8, make_uint4(d0, d1, d2, d3));
-          const int d = a.dist[e];
-          if (e >= a.n_cov) {
-            stage_rows(d);
-            __builtin_amdgcn_s_waitcnt(0);
-            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int e = 0; e < NC; ++e) {
+          if (e < a.n_cov) {
+            const float p = diag_lane ? s_ent[e] : 0.f;
+            uint32_t d0, d1, d2, d3;
+            diag_slots(round_bf(p * (1.f - a.w[e])), l, &d0, &d1);
+            diag_slots(round_bf(p * a.w[e]), l, &d2, &d3);
+            const bf16x8 bp = __builtin_bit_cast(bf16x8, make_uint4(d0, d1, d2, d3));
+            const int ra = tr_base(bw - a.dist[e] + 4 * g + jr), rb = tr_base(bw - a.dist[e] + 1 + 4 * g + jr);
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb)
-              acc[mb] = mfma32(cat_bf8(tr16(sm.stage[wave], st_off(4 * g + jr, mb)),
-                                       tr16(sm.stage[wave], st_off(4 * g + jr + 1, mb))), bp, acc[mb]);
-            __builtin_amdgcn_s_waitcnt(0);
-            __builtin_amdgcn_wave_barrier();
-          } else {
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-              acc[mb] = mfma32(cat_bf8(tr16(sm.ringV, tr_off(i0w - d + 4 * g + jr, mb)),
-                                       tr16(sm.ringV, tr_off(i0w - d + 1 + 4 * g + jr, mb))), bp, acc[mb]);
+              acc[mb] = mfma32(cat_bf8(tr16(sm.ringV, ra + 32 * mb), tr16(sm.ringV, rb + 32 * mb)), bp, acc[mb]);
           }
         }
       }
@@ -471,12 +520,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_ring_kernel(RingArgs a) {
       // ---- epilogue
       if (iq < s1) {
         const float inv = 1.f / lnorm;
-        bf16_t* op = a.o + hoff + iq * kD + 4 * g;
+        bf16_t* op = a.o + hoff + (int64_t)iq * kD + 4 * g;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
           uint2 x;
-          x.x = pack_bf2(acc[mb][0] * inv, acc[mb][1] * inv);
-          x.y = pack_bf2(acc[mb][2] * inv, acc[mb][3] * inv);
+          x.x = pack_bf2((acc[mb][0] + accf[mb][0]) * inv, (acc[mb][1] + accf[mb][1]) * inv);
+          x.y = pack_bf2((acc[mb][2] + accf[mb][2]) * inv, (acc[mb][3] + accf[mb][3]) * inv);
           *reinterpret_cast<uint2*>(op + 16 * mb) = x;
         }
         if (g == 0 && a.lse != nullptr) a.lse[(size_t)head * N + iq] = (m + log2f(lsum)) * 0.69314718055994530942f;
@@ -486,21 +535,34 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_ring_kernel(RingArgs a) {
   }
 }
 
-// far distances of a table: integer d, or c and c - 1 per interpolated entry
-int count_far(const FwdArgs& f, int* n_cov) {
+// Entries usable by some query (distance < N), split into the ring-covered prefix and the far
+// rest (the table is sorted by distance in both modes).
+void split_table(const FwdArgs& f, int* n_cov, int* n_far) {
+  int n = 0;
+  while (n < f.tab.n && f.tab.dist[n] < f.N) ++n;
   int cov = 0;
-  while (cov < f.tab.n && f.tab.dist[cov] <= kMaxCov) ++cov;
+  while (cov < n && f.tab.dist[cov] <= kMaxCov) ++cov;
   *n_cov = cov;
-  const int far = f.tab.n - cov;
-  return f.mode == 1 ? 2 * far : far;
+  *n_far = n - cov;
+}
+
+template <int MODE, int NC>
+hipError_t launch(const RingArgs& a, unsigned blocks, hipStream_t s) {
+  const size_t smem = sizeof(Smem);
+  hipError_t e = hipFuncSetAttribute((const void*)fwd_ring_kernel<MODE, NC>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
+  fwd_ring_kernel<MODE, NC><<<blocks, kThreads, smem, s>>>(a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 bool fwd_ring_supported(const FwdArgs& f) {
-  if (f.dtype != 1 || f.W > kMaxBand) return false;
-  int cov;
-  return count_far(f, &cov) <= kMaxUnc;
+  if (f.dtype != 1 || f.W > kMaxBand || f.N > (1LL << 30)) return false;
+  int cov, far;
+  split_table(f, &cov, &far);
+  return far <= kMaxFar && cov <= 16;
 }
 
 hipError_t launch_fwd_ring(const FwdArgs& f) {
@@ -510,18 +572,22 @@ hipError_t launch_fwd_ring(const FwdArgs& f) {
   a.v = (const bf16_t*)f.v;
   a.o = (bf16_t*)f.o;
   a.lse = f.lse;
-  a.N = f.N;
+  a.N = (int)f.N;
   a.W = f.W;
-  a.n_ent = f.tab.n;
-  a.n_unc = count_far(f, &a.n_cov);
+  split_table(f, &a.n_cov, &a.n_far);
   for (int e = 0; e < kMaxEnt; ++e) {
-    a.dist[e] = f.tab.dist[e];
-    a.w[e] = f.tab.w[e];
+    // slots past the covered prefix get a harmless in-ring distance and weight 0
+    a.dist[e] = e < a.n_cov ? f.tab.dist[e] : kMaxBand;
+    a.w[e] = e < a.n_cov ? f.tab.w[e] : 0.f;
+  }
+  for (int x = 0; x < kMaxFar; ++x) {
+    a.far_dist[x] = x < a.n_far ? f.tab.dist[a.n_cov + x] : 0;
+    a.far_w[x] = x < a.n_far ? f.tab.w[a.n_cov + x] : 0.f;
   }
   int u = 0;
-  for (int e = a.n_cov; e < f.tab.n; ++e) {
-    a.unc_dist[u++] = f.tab.dist[e];
-    if (f.mode == 1) a.unc_dist[u++] = f.tab.dist[e] - 1;
+  for (int x = 0; x < a.n_far; ++x) {
+    a.unc_dist[u++] = a.far_dist[x];
+    if (f.mode == 1) a.unc_dist[u++] = a.far_dist[x] - 1;
   }
   for (; u < kMaxUnc; ++u) a.unc_dist[u] = 0;
   // rows before a segment start that the ring must hold: the band and the covered distances
@@ -539,16 +605,9 @@ hipError_t launch_fwd_ring(const FwdArgs& f) {
   a.segs = (int)segs;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)kD));
   a.rope = f.rope;
-  const size_t smem = sizeof(Smem);
-  const void* fn = f.mode == 0 ? (const void*)fwd_ring_kernel<0> : (const void*)fwd_ring_kernel<1>;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  if (e != hipSuccess) return e;
-  dim3 grid((unsigned)(segs * f.BH)), block(kThreads);
-  if (f.mode == 0)
-    fwd_ring_kernel<0><<<grid, block, smem, f.stream>>>(a);
-  else
-    fwd_ring_kernel<1><<<grid, block, smem, f.stream>>>(a);
-  return hipGetLastError();
+  const unsigned blocks = (unsigned)(segs * f.BH);
+  if (f.mode == 0) return a.n_cov <= 8 ? launch<0, 8>(a, blocks, f.stream) : launch<0, 16>(a, blocks, f.stream);
+  return a.n_cov <= 8 ? launch<1, 8>(a, blocks, f.stream) : launch<1, 16>(a, blocks, f.stream);
 }
 
 }  // namespace fib
