@@ -8,11 +8,12 @@
 // a fused path; here both modes run fused in this kernel.
 //
 // Design (gfx950):
-//  * One 256-thread workgroup (4 waves) per CU sweeps a contiguous segment of one head in
-//    steps of 64 queries; wave w owns queries p0 + 16w .. p0 + 16w + 15 of each step.
+//  * One workgroup per CU (4 or 8 waves; 8 gives two waves per SIMD to cover latencies)
+//    sweeps a contiguous segment of one head in steps of 16 queries per wave; wave w owns
+//    queries p0 + 16w .. p0 + 16w + 15 of each step.
 //  * LDS ring of the last kP rows: K rotated by RoPE (bf16) and raw V (bf16). Each row is
 //    loaded from HBM and rotated once, when it enters the ring; the window band and every
-//    table entry whose distance is <= kP - 64 read it from LDS afterwards.
+//    table entry whose distance is <= kP - (rows per step) read it from LDS afterwards.
 //  * Logits on MFMA as S^T = K^ Q^T (v_mfma_f32_16x16x32_bf16; A = 16 key rows from the ring,
 //    B = the wave's 16 rotated queries). The window band is a 32-key by 16-query block; a
 //    table entry is a 16-row slab whose diagonal holds the 16 logits (query n reads slab
@@ -38,12 +39,11 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f4;
 typedef __attribute__((ext_vector_type(4))) short s4;
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kT = 16 * kWaves;       // queries (and ring rows) per step
 constexpr int kP = 512;               // ring rows (a power of two: slot = row & (kP - 1))
 constexpr int kRow = 144;             // ring row stride in bytes (128 + 16 padding)
-constexpr int kMaxCov = kP - kT;      // largest distance served from the ring
+// queries (and ring rows) per step: 16 per wave; the largest distance served from the ring
+constexpr int step_rows(int waves) { return 16 * waves; }
+constexpr int max_cov(int waves) { return kP - step_rows(waves); }
 constexpr int kMaxBand = 16;          // window band rows before a 16-query block
 constexpr int kMaxFar = 4;            // table entries served from global memory
 constexpr int kMaxUnc = 2 * kMaxFar;  // their distances (interpolated: c and c - 1)
@@ -58,6 +58,7 @@ struct RingArgs {
   int W;
   int n_cov;        // entries served from the ring (a prefix of the table)
   int n_far;        // entries served from global memory (after the covered ones)
+  int early_rows;   // steps whose rows start below this need the position checks
   int seg_len;      // rows per workgroup (multiple of kT)
   int segs;         // segments per head
   int warm;         // rows inserted before the segment start (multiple of kT)
@@ -150,9 +151,22 @@ __device__ __forceinline__ float sel4(f4 x, int l) {
   return (l & 2) ? b : a;
 }
 
-// 4 bf16 slots holding p (already bf16-exact, or 0) at slot (l & 3), zeros elsewhere
+// rotate the pairs (x[t], x[8 + t]) of 16 unpacked values by cos/sin cs[t]; packed bf16 halves
+__device__ __forceinline__ void rotate_pack_f(const float* x, const float2* cs, uint4* out_lo, uint4* out_hi) {
+  float ra[8], rb[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    ra[t] = x[t] * cs[t].x - x[8 + t] * cs[t].y;
+    rb[t] = x[8 + t] * cs[t].x + x[t] * cs[t].y;
+  }
+  *out_lo = pack8(ra);
+  *out_hi = pack8(rb);
+}
+
+// 4 bf16 slots holding bf16(p) at slot (l & 3), zeros elsewhere (p is 0 outside the diagonal
+// lanes: their logits are masked)
 __device__ __forceinline__ void diag_slots(float p, int l, uint32_t* d0, uint32_t* d1) {
-  const uint32_t b = __float_as_uint(p) >> 16;
+  const uint32_t b = pack_bf2(p, 0.f) & 0xffffu;
   const int s = l & 3;
   *d0 = s == 0 ? b : (s == 1 ? (b << 16) : 0u);
   *d1 = s == 2 ? b : (s == 3 ? (b << 16) : 0u);
@@ -161,10 +175,6 @@ __device__ __forceinline__ void diag_slots(float p, int l, uint32_t* d0, uint32_
 __device__ __forceinline__ float xor_max(float x) {
   x = fmaxf(x, __shfl_xor(x, 16));
   return fmaxf(x, __shfl_xor(x, 32));
-}
-__device__ __forceinline__ float xor_sum(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
 }
 
 // Rows of the far table entries for one step, held in registers and loaded one step ahead:
@@ -178,9 +188,10 @@ struct FarRows {
   uint2 vh[kMaxFar][4];
 };
 
+// far rows are > kP - 128 rows behind their queries, so only the lower clamp can apply
 __device__ __forceinline__ int far_row(const RingArgs& a, int f, int i0w, int n, int up) {
   const int r = i0w - a.far_dist[f] + n + up;
-  return r < 0 ? 0 : (r >= a.N ? a.N - 1 : r);
+  return r < 0 ? 0 : r;
 }
 
 template <int MODE>
@@ -217,8 +228,10 @@ __device__ __forceinline__ void load_far_v(FarRows& fr, const RingArgs& a, const
   }
 }
 
-template <int MODE, int NC>
-__global__ __launch_bounds__(kThreads, 1) void fwd_ring_kernel(RingArgs a) {
+template <int MODE, int NC, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
+  constexpr int kThreads = 64 * WAVES;
+  constexpr int kT = step_rows(WAVES);
   extern __shared__ __align__(16) uint8_t smem_raw[];
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
   const int tid = threadIdx.x;
@@ -286,6 +299,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_ring_kernel(RingArgs a) {
   }
 
   const float sl2 = a.scale_log2;
+  // additive masks: window keys by distance (band key kappa of the lane at distance
+  // n + 16 - 4g - v in block 0 and n - 4g - v in block 1), table entries outside the
+  // diagonal lanes
+  float bias0[4], bias1[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int d0 = n + 16 - 4 * g - v, d1 = n - 4 * g - v;
+    bias0[v] = d0 < a.W ? 0.f : -INFINITY;
+    bias1[v] = (d1 >= 0 && d1 < a.W) ? 0.f : -INFINITY;
+  }
+  const float bias_diag = diag_lane ? 0.f : -INFINITY;
   int buf = 0;
   for (; p0 < s1; p0 += kT, buf ^= 1) {
     // ---- insert rows p0 + 16w + n: rotate K (and Q for this step's queries) by R_(p0 + t)
@@ -317,8 +341,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_ring_kernel(RingArgs a) {
       const int i0w = p0 + 16 * wave;
       const int iq = i0w + n;  // this lane's query
       const bf16x8 bq0 = as_bf8(qh0), bq1 = as_bf8(qh1);
+      // keys before position 0 (and table distances longer than the query position) occur
+      // only in the first steps of a sequence; afterwards the masks are the fixed biases
+      const bool early = i0w < a.early_rows;
 
       // ---- logits of the far entries first, so their next rows can be requested early
+      float qf[16];
+      unpack8(qraw0, qf);
+      unpack8(qraw1, qf + 8);
       float s_far[kMaxFar];
 #pragma unroll
       for (int f = 0; f < kMaxFar; ++f) {
@@ -326,19 +356,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_ring_kernel(RingArgs a) {
         if (f < a.n_far) {
           const int u = MODE == 1 ? 2 * f : f;
           uint4 r0, r1;
-          rotate_pack(qraw0, qraw1, &sm.unc_cs[u][8 * g], &r0, &r1);
+          rotate_pack_f(qf, &sm.unc_cs[u][8 * g], &r0, &r1);
           f4 S = {0, 0, 0, 0};
           S = mfma32(as_bf8(fr.k[f][0]), as_bf8(r0), S);
           S = mfma32(as_bf8(fr.k[f][1]), as_bf8(r1), S);
           float s = sel4(S, l);
           if (MODE == 1) {
-            rotate_pack(qraw0, qraw1, &sm.unc_cs[u + 1][8 * g], &r0, &r1);
+            rotate_pack_f(qf, &sm.unc_cs[u + 1][8 * g], &r0, &r1);
             f4 H = {0, 0, 0, 0};
             H = mfma32(as_bf8(fr.kh[f][0]), as_bf8(r0), H);
             H = mfma32(as_bf8(fr.kh[f][1]), as_bf8(r1), H);
             s = fmaf(a.far_w[f], sel4(H, l) - s, s);
           }
-          s_far[f] = (diag_lane && a.far_dist[f] <= iq) ? s * sl2 : -INFINITY;
+          s = fmaf(s, sl2, bias_diag);
+          if (early && a.far_dist[f] > iq) s = -INFINITY;
+          s_far[f] = s;
         }
       }
       if (a.n_far > 0 && pn < s1) load_far_k<MODE>(fr, a, Kh, i0w + kT, n, g);
@@ -371,18 +403,23 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_ring_kernel(RingArgs a) {
             H = mfma32(as_bf8(lds_read16(sm.ringK, sh + 64)), bq1, H);
             s = fmaf(a.w[e], sel4(H, l) - s, s);
           }
-          s_ent[e] = (diag_lane && d <= iq) ? s * sl2 : -INFINITY;
+          s = fmaf(s, sl2, bias_diag);
+          if (early && d > iq) s = -INFINITY;
+          s_ent[e] = s;
         }
       }
 
-      // ---- softmax over the window band and the entries
+      // ---- softmax over the window band and the entries (base-2 logits)
       float sw0[4], sw1[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int d0 = n + 16 - 4 * g - v;  // >= 1
-        const int d1 = n - 4 * g - v;
-        sw0[v] = (d0 < a.W && d0 <= iq) ? S0[v] * sl2 : -INFINITY;
-        sw1[v] = (d1 >= 0 && d1 < a.W) ? S1[v] * sl2 : -INFINITY;
+        sw0[v] = fmaf(S0[v], sl2, bias0[v]);
+        sw1[v] = fmaf(S1[v], sl2, bias1[v]);
+      }
+      if (early) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (n + 16 - 4 * g - v > iq) sw0[v] = -INFINITY;
       }
       float m = -INFINITY;
 #pragma unroll
@@ -392,45 +429,74 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_ring_kernel(RingArgs a) {
 #pragma unroll
       for (int f = 0; f < kMaxFar; ++f) m = fmaxf(m, s_far[f]);
       m = xor_max(m);  // every query has its own key (distance 0), so m is finite
-      // lsum (fp32 weights) gives LSE; lnorm sums the bf16 weights the P V products apply,
-      // so that O is normalised by exactly those weights (rows of P sum to 1)
-      float lsum = 0.f, lnorm = 0.f;
+      // lsum: the fp32 sum of the weights, for LSE (each query's weights are spread over its
+      // four lanes: window keys in all four, table entries in its diagonal lane)
+      float lsum = 0.f;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float p0v = ex2(sw0[v] - m), p1v = ex2(sw1[v] - m);
-        lsum += p0v + p1v;
-        sw0[v] = round_bf(p0v);
-        sw1[v] = round_bf(p1v);
-        lnorm += sw0[v] + sw1[v];
+        sw0[v] = ex2(sw0[v] - m);
+        sw1[v] = ex2(sw1[v] - m);
+        lsum += sw0[v] + sw1[v];
       }
-      // entry weights: integer mode keeps the bf16 weight in s_ent; interpolated mode keeps
-      // the fp32 weight (its two bf16 parts are formed at use)
 #pragma unroll
       for (int e = 0; e < NC; ++e) {
-        const float p = ex2(s_ent[e] - m);
-        lsum += p;
-        if (MODE == 0) {
-          s_ent[e] = round_bf(p);
-          lnorm += s_ent[e];
-        } else {
-          s_ent[e] = p;
-          lnorm += round_bf(p * (1.f - a.w[e])) + round_bf(p * a.w[e]);
-        }
+        s_ent[e] = ex2(s_ent[e] - m);
+        lsum += s_ent[e];
       }
 #pragma unroll
       for (int f = 0; f < kMaxFar; ++f) {
-        const float p = ex2(s_far[f] - m);
-        lsum += p;
-        s_far[f] = p;
-        lnorm += MODE == 0 ? round_bf(p) : round_bf(p * (1.f - a.far_w[f])) + round_bf(p * a.far_w[f]);
+        s_far[f] = ex2(s_far[f] - m);
+        lsum += s_far[f];
       }
-      lsum = xor_sum(lsum);
-      lnorm = xor_sum(lnorm);
+      lsum += __shfl_xor(lsum, 16);
+      lsum += __shfl_xor(lsum, 32);
 
-      // ---- P V: O^T[dim 16 mb + 4 g + v][query n]
+      // ---- P V: O^T[dim 16 mb + 4 g + v][query n], weights in bf16. The normaliser is the
+      // sum of exactly the bf16 weights applied (rows of P sum to 1): an all-ones A block adds
+      // a fifth output block whose every entry is the column sum of P^T.
       f4 acc[4];
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) acc[mb] = f4{0, 0, 0, 0};
+      f4 accn = {0, 0, 0, 0};
+      const bf16x8 ones = as_bf8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+      float lnorm_far = 0.f;
+      // far entries on VALU first: the lane's O^T slice += p * V[row][16 mb + 4 g + v]; p lives
+      // in the query's diagonal lane and is broadcast to its other three lanes
+#pragma unroll
+      for (int f = 0; f < kMaxFar; ++f) {
+        if (f < a.n_far) {
+          const float p = __shfl(s_far[f], 16 * (n >> 2) + n);
+          const float plo = MODE == 1 ? round_bf(p * (1.f - a.far_w[f])) : round_bf(p);
+          const float phi = MODE == 1 ? round_bf(p * a.far_w[f]) : 0.f;
+          lnorm_far += plo + phi;
+          const uint32_t blo = __float_as_uint(plo), bhi = __float_as_uint(phi);
+          if (MODE == 0) {
+            // weights (p, 0) and (0, p) pick one bf16 of a pair: one dot2 per element
+            const uint32_t w0 = blo >> 16, w1 = blo & 0xffff0000u;
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+              const uint2 x = fr.v[f][mb];
+              acc[mb][0] = dot2(x.x, w0, acc[mb][0]);
+              acc[mb][1] = dot2(x.x, w1, acc[mb][1]);
+              acc[mb][2] = dot2(x.y, w0, acc[mb][2]);
+              acc[mb][3] = dot2(x.y, w1, acc[mb][3]);
+            }
+          } else {
+            // pair the lower-row and upper-row element of a dim, weights (1-w) p and w p
+            const uint32_t wp = (blo >> 16) | (bhi & 0xffff0000u);
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+              const uint2 x = fr.v[f][mb], y = fr.vh[f][mb];
+              acc[mb][0] = dot2(__builtin_amdgcn_perm(y.x, x.x, 0x05040100u), wp, acc[mb][0]);
+              acc[mb][1] = dot2(__builtin_amdgcn_perm(y.x, x.x, 0x07060302u), wp, acc[mb][1]);
+              acc[mb][2] = dot2(__builtin_amdgcn_perm(y.y, x.y, 0x05040100u), wp, acc[mb][2]);
+              acc[mb][3] = dot2(__builtin_amdgcn_perm(y.y, x.y, 0x07060302u), wp, acc[mb][3]);
+            }
+          }
+        }
+      }
+      if (a.n_far > 0 && pn < s1) load_far_v<MODE>(fr, a, Vh, i0w + kT, n, g);
+
       // transpose reads: lane (jr, jc) of a 16-lane group reads row k0 + jr, dims
       // 16 mb + 4 jc .. +3, i.e. bytes 32 mb + 8 jc of the row
       auto tr_base = [&](int row) { return row_off(row) + 8 * jc; };
@@ -442,47 +508,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_ring_kernel(RingArgs a) {
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
           acc[mb] = mfma32(cat_bf8(tr16(sm.ringV, r0 + 32 * mb), tr16(sm.ringV, r1 + 32 * mb)), bp, acc[mb]);
+        accn = mfma32(ones, bp, accn);
       }
-      // far entries on VALU: the lane's O^T slice += p * V[row][16 mb + 4 g + v]; p lives in the
-      // query's diagonal lane and is broadcast to its other three lanes. A separate register
-      // accumulator keeps this off the MFMA accumulators.
-      float accf[4][4];
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) accf[mb][0] = accf[mb][1] = accf[mb][2] = accf[mb][3] = 0.f;
-#pragma unroll
-      for (int f = 0; f < kMaxFar; ++f) {
-        if (f < a.n_far) {
-          const float p = __shfl(s_far[f], 16 * (n >> 2) + n);
-          const float plo = MODE == 1 ? round_bf(p * (1.f - a.far_w[f])) : round_bf(p);
-          const float phi = MODE == 1 ? round_bf(p * a.far_w[f]) : 0.f;
-          const uint32_t blo = __float_as_uint(plo), bhi = __float_as_uint(phi);
-          if (MODE == 0) {
-            // weights (p, 0) and (0, p) pick one bf16 of a pair: one dot2 per element
-            const uint32_t w0 = blo >> 16, w1 = blo & 0xffff0000u;
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-              const uint2 x = fr.v[f][mb];
-              accf[mb][0] = dot2(x.x, w0, accf[mb][0]);
-              accf[mb][1] = dot2(x.x, w1, accf[mb][1]);
-              accf[mb][2] = dot2(x.y, w0, accf[mb][2]);
-              accf[mb][3] = dot2(x.y, w1, accf[mb][3]);
-            }
-          } else {
-            // pair the lower-row and upper-row element of a dim, weights (1-w) p and w p
-            const uint32_t wp = (blo >> 16) | (bhi & 0xffff0000u);
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-              const uint2 x = fr.v[f][mb], y = fr.vh[f][mb];
-              accf[mb][0] = dot2(__builtin_amdgcn_perm(y.x, x.x, 0x05040100u), wp, accf[mb][0]);
-              accf[mb][1] = dot2(__builtin_amdgcn_perm(y.x, x.x, 0x07060302u), wp, accf[mb][1]);
-              accf[mb][2] = dot2(__builtin_amdgcn_perm(y.y, x.y, 0x05040100u), wp, accf[mb][2]);
-              accf[mb][3] = dot2(__builtin_amdgcn_perm(y.y, x.y, 0x07060302u), wp, accf[mb][3]);
-            }
-          }
-        }
-      }
-      if (a.n_far > 0 && pn < s1) load_far_v<MODE>(fr, a, Vh, i0w + kT, n, g);
-
       // covered entries on MFMA with a diagonal P^T block (integer mode: two entries per
       // MFMA, a missing second entry has weight 0 and an in-ring dummy distance; interpolated
       // mode: the lower and upper slab of one entry)
@@ -491,41 +518,44 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_ring_kernel(RingArgs a) {
         for (int e = 0; e < NC; e += 2) {
           if (e < a.n_cov) {
             uint32_t d0, d1, d2, d3;
-            diag_slots(diag_lane ? s_ent[e] : 0.f, l, &d0, &d1);
-            diag_slots(diag_lane ? s_ent[e + 1] : 0.f, l, &d2, &d3);
+            diag_slots(s_ent[e], l, &d0, &d1);
+            diag_slots(s_ent[e + 1], l, &d2, &d3);
             const bf16x8 bp = __builtin_bit_cast(bf16x8, make_uint4(d0, d1, d2, d3));
             const int ra = tr_base(bw - a.dist[e] + 4 * g + jr), rb = tr_base(bw - a.dist[e + 1] + 4 * g + jr);
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb)
               acc[mb] = mfma32(cat_bf8(tr16(sm.ringV, ra + 32 * mb), tr16(sm.ringV, rb + 32 * mb)), bp, acc[mb]);
+            accn = mfma32(ones, bp, accn);
           }
         }
       } else {
 #pragma unroll
         for (int e = 0; e < NC; ++e) {
           if (e < a.n_cov) {
-            const float p = diag_lane ? s_ent[e] : 0.f;
+            const float p = s_ent[e];
             uint32_t d0, d1, d2, d3;
-            diag_slots(round_bf(p * (1.f - a.w[e])), l, &d0, &d1);
-            diag_slots(round_bf(p * a.w[e]), l, &d2, &d3);
+            diag_slots(p * (1.f - a.w[e]), l, &d0, &d1);
+            diag_slots(p * a.w[e], l, &d2, &d3);
             const bf16x8 bp = __builtin_bit_cast(bf16x8, make_uint4(d0, d1, d2, d3));
             const int ra = tr_base(bw - a.dist[e] + 4 * g + jr), rb = tr_base(bw - a.dist[e] + 1 + 4 * g + jr);
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb)
               acc[mb] = mfma32(cat_bf8(tr16(sm.ringV, ra + 32 * mb), tr16(sm.ringV, rb + 32 * mb)), bp, acc[mb]);
+            accn = mfma32(ones, bp, accn);
           }
         }
       }
 
       // ---- epilogue
       if (iq < s1) {
+        const float lnorm = accn[0] + lnorm_far;
         const float inv = 1.f / lnorm;
         bf16_t* op = a.o + hoff + (int64_t)iq * kD + 4 * g;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
           uint2 x;
-          x.x = pack_bf2((acc[mb][0] + accf[mb][0]) * inv, (acc[mb][1] + accf[mb][1]) * inv);
-          x.y = pack_bf2((acc[mb][2] + accf[mb][2]) * inv, (acc[mb][3] + accf[mb][3]) * inv);
+          x.x = pack_bf2(acc[mb][0] * inv, acc[mb][1] * inv);
+          x.y = pack_bf2(acc[mb][2] * inv, acc[mb][3] * inv);
           *reinterpret_cast<uint2*>(op + 16 * mb) = x;
         }
         if (g == 0 && a.lse != nullptr) a.lse[(size_t)head * N + iq] = (m + log2f(lsum)) * 0.69314718055994530942f;
@@ -535,24 +565,28 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_ring_kernel(RingArgs a) {
   }
 }
 
+// waves per workgroup: 8 (two per SIMD) where the registers fit, else 4
+int waves_for(int mode) { return mode == 0 ? 8 : 4; }
+
 // Entries usable by some query (distance < N), split into the ring-covered prefix and the far
 // rest (the table is sorted by distance in both modes).
 void split_table(const FwdArgs& f, int* n_cov, int* n_far) {
   int n = 0;
   while (n < f.tab.n && f.tab.dist[n] < f.N) ++n;
+  const int cov_max = max_cov(waves_for(f.mode));
   int cov = 0;
-  while (cov < n && f.tab.dist[cov] <= kMaxCov) ++cov;
+  while (cov < n && f.tab.dist[cov] <= cov_max) ++cov;
   *n_cov = cov;
   *n_far = n - cov;
 }
 
-template <int MODE, int NC>
+template <int MODE, int NC, int WAVES>
 hipError_t launch(const RingArgs& a, unsigned blocks, hipStream_t s) {
   const size_t smem = sizeof(Smem);
-  hipError_t e = hipFuncSetAttribute((const void*)fwd_ring_kernel<MODE, NC>,
+  hipError_t e = hipFuncSetAttribute((const void*)fwd_ring_kernel<MODE, NC, WAVES>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
-  fwd_ring_kernel<MODE, NC><<<blocks, kThreads, smem, s>>>(a);
+  fwd_ring_kernel<MODE, NC, WAVES><<<blocks, 64 * WAVES, smem, s>>>(a);
   return hipGetLastError();
 }
 
@@ -590,10 +624,14 @@ hipError_t launch_fwd_ring(const FwdArgs& f) {
     if (f.mode == 1) a.unc_dist[u++] = a.far_dist[x] - 1;
   }
   for (; u < kMaxUnc; ++u) a.unc_dist[u] = 0;
+  const int kT = step_rows(waves_for(f.mode));
   // rows before a segment start that the ring must hold: the band and the covered distances
   int need = kMaxBand;
   for (int e = 0; e < a.n_cov; ++e) need = f.tab.dist[e] > need ? f.tab.dist[e] : need;
   a.warm = ((need + kT - 1) / kT) * kT;
+  int early = kMaxBand;
+  for (int e = 0; e < a.n_cov + a.n_far; ++e) early = f.tab.dist[e] > early ? f.tab.dist[e] : early;
+  a.early_rows = early;
   // segments: about one workgroup per CU in total
   const int64_t tiles = (f.N + kT - 1) / kT;
   int64_t segs = (256 + f.BH - 1) / f.BH;
@@ -606,8 +644,9 @@ hipError_t launch_fwd_ring(const FwdArgs& f) {
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)kD));
   a.rope = f.rope;
   const unsigned blocks = (unsigned)(segs * f.BH);
-  if (f.mode == 0) return a.n_cov <= 8 ? launch<0, 8>(a, blocks, f.stream) : launch<0, 16>(a, blocks, f.stream);
-  return a.n_cov <= 8 ? launch<1, 8>(a, blocks, f.stream) : launch<1, 16>(a, blocks, f.stream);
+  if (f.mode == 0)
+    return a.n_cov <= 8 ? launch<0, 8, 8>(a, blocks, f.stream) : launch<0, 16, 8>(a, blocks, f.stream);
+  return a.n_cov <= 8 ? launch<1, 8, 4>(a, blocks, f.stream) : launch<1, 16, 4>(a, blocks, f.stream);
 }
 
 }  // namespace fib
