@@ -8,9 +8,9 @@
 // a fused path; here both modes run fused in this kernel.
 //
 // Design (gfx950):
-//  * One workgroup per CU (4 or 8 waves; 8 gives two waves per SIMD to cover latencies)
-//    sweeps a contiguous segment of one head in steps of 16 queries per wave; wave w owns
-//    queries p0 + 16w .. p0 + 16w + 15 of each step.
+//  * One workgroup per CU (8 waves in integer mode, two per SIMD to cover latencies; 4 in
+//    interpolated mode, whose far rows need twice the registers) sweeps a contiguous segment
+//    of one head in steps of 16 queries per wave; wave w owns queries p0 + 16w .. + 15.
 //  * LDS ring of the last kP rows: K rotated by RoPE (bf16) and raw V (bf16). Each row is
 //    loaded from HBM and rotated once, when it enters the ring; the window band and every
 //    table entry whose distance is <= kP - (rows per step) read it from LDS afterwards.
@@ -20,11 +20,16 @@
 //    row n), picked out of the lanes that own it.
 //  * Table entries beyond the ring read raw K and V rows from global memory, prefetched one
 //    step ahead into registers, and use relative RoPE <R_i q, R_(i-d) k> = <R_d q, k> with
-//    cos/sin of R_d computed once per workgroup; their P V runs on VALU.
-//  * Softmax over all logits of a query at once (they fit in registers), fp32, base 2.
+//    cos/sin of R_d computed once per workgroup; their P V runs on VALU (v_dot2_f32_bf16).
+//  * Softmax over all logits of a query at once (they fit in registers), fp32, base 2; the
+//    four lanes of a query combine through v_permlane16/32_swap.
 //  * P V on MFMA as O^T = V^T P^T: V^T operands come from the ring through the LDS transpose
 //    read (ds_read_b64_tr_b16); table entries use a diagonal P^T block, two slabs per MFMA
-//    (interpolated mode: the lower and upper slab of one entry, weights 1-w and w).
+//    (integer mode: two entries; interpolated mode: the lower and upper slab of one entry,
+//    weights 1-w and w), built with v_perm_b32 from one packed pair of bf16 weights.
+//  * Output dimensions are permuted so that a lane's 16 accumulators are the dims 8g..8g+7
+//    and 32+8g..32+8g+7 of its query: V is stored in the ring in that order, far V rows load
+//    as two 16-byte pieces and each lane stores two 16-byte pieces of O.
 //  * Ring rows are padded to 144 bytes: with 64 LDS banks, 16 consecutive rows then start on 16
 //    distinct 4-bank groups, so the A-operand reads (16 rows, one 16-byte chunk each) and the
 //    transpose reads (4 rows x 32 bytes per 16 lanes) are conflict-free, and every read of a
@@ -45,6 +50,7 @@ constexpr int kRow = 144;             // ring row stride in bytes (128 + 16 padd
 constexpr int step_rows(int waves) { return 16 * waves; }
 constexpr int max_cov(int waves) { return kP - step_rows(waves); }
 constexpr int kMaxBand = 16;          // window band rows before a 16-query block
+constexpr int kMaxCov = 16;           // table entries served from the ring
 constexpr int kMaxFar = 4;            // table entries served from global memory
 constexpr int kMaxUnc = 2 * kMaxFar;  // their distances (interpolated: c and c - 1)
 
@@ -57,14 +63,13 @@ struct RingArgs {
   int N;
   int W;
   int n_cov;        // entries served from the ring (a prefix of the table)
-  int n_far;        // entries served from global memory (after the covered ones)
   int early_rows;   // steps whose rows start below this need the position checks
-  int seg_len;      // rows per workgroup (multiple of kT)
+  int seg_len;      // rows per workgroup (multiple of the step)
   int segs;         // segments per head
-  int warm;         // rows inserted before the segment start (multiple of kT)
+  int warm;         // rows inserted before the segment start (multiple of the step)
   float scale_log2;
-  int dist[kMaxEnt];  // covered distances; slots past n_cov hold a harmless in-ring distance
-  float w[kMaxEnt];
+  int dist[kMaxCov];  // covered distances; slots past n_cov hold a harmless in-ring distance
+  float w[kMaxCov];
   int far_dist[kMaxFar];
   float far_w[kMaxFar];
   int unc_dist[kMaxUnc];
@@ -86,6 +91,9 @@ __device__ __forceinline__ uint4 lds_read16(const uint8_t* base, int off) {
 }
 __device__ __forceinline__ void lds_write16(uint8_t* base, int off, uint4 x) {
   *reinterpret_cast<uint4*>(base + off) = x;
+}
+__device__ __forceinline__ void lds_write8(uint8_t* base, int off, uint32_t x, uint32_t y) {
+  *reinterpret_cast<uint2*>(base + off) = make_uint2(x, y);
 }
 
 // LDS transpose read of 4 bf16: lane j (of 16) supplies the address of 4 consecutive
@@ -116,15 +124,13 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
   return x;
 }
 
-// rotate pairs (lo[t], hi[t]) by angles with cos/sin cs[t]; returns packed bf16 halves
-__device__ __forceinline__ void rotate_pack(uint4 lo, uint4 hi, const float2* cs, uint4* out_lo, uint4* out_hi) {
-  float a[8], b[8], ra[8], rb[8];
-  unpack8(lo, a);
-  unpack8(hi, b);
+// rotate the pairs (x[t], x[8 + t]) of 16 unpacked values by cos/sin cs[t]; packed bf16 halves
+__device__ __forceinline__ void rotate_pack_f(const float* x, const float2* cs, uint4* out_lo, uint4* out_hi) {
+  float ra[8], rb[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    ra[t] = a[t] * cs[t].x - b[t] * cs[t].y;
-    rb[t] = b[t] * cs[t].x + a[t] * cs[t].y;
+    ra[t] = x[t] * cs[t].x - x[8 + t] * cs[t].y;
+    rb[t] = x[8 + t] * cs[t].x + x[t] * cs[t].y;
   }
   *out_lo = pack8(ra);
   *out_hi = pack8(rb);
@@ -141,9 +147,6 @@ __device__ __forceinline__ float dot2(uint32_t x, uint32_t w, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(as_bf2(x), as_bf2(w), c, false);
 }
 
-// value of x rounded to bf16 (nearest even), as fp32
-__device__ __forceinline__ float round_bf(float x) { return __uint_as_float(pack_bf2(0.f, x) & 0xffff0000u); }
-
 // select x[l & 3]
 __device__ __forceinline__ float sel4(f4 x, int l) {
   const float a = (l & 1) ? x[1] : x[0];
@@ -151,87 +154,115 @@ __device__ __forceinline__ float sel4(f4 x, int l) {
   return (l & 2) ? b : a;
 }
 
-// rotate the pairs (x[t], x[8 + t]) of 16 unpacked values by cos/sin cs[t]; packed bf16 halves
-__device__ __forceinline__ void rotate_pack_f(const float* x, const float2* cs, uint4* out_lo, uint4* out_hi) {
-  float ra[8], rb[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    ra[t] = x[t] * cs[t].x - x[8 + t] * cs[t].y;
-    rb[t] = x[8 + t] * cs[t].x + x[t] * cs[t].y;
-  }
-  *out_lo = pack8(ra);
-  *out_hi = pack8(rb);
+// Reductions over the four lanes of a query (l, l ^ 16, l ^ 32, l ^ 48): each swap exchanges
+// half of two copies of x, after which the pair holds x of both partner lanes.
+__device__ __forceinline__ float quad_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const uint32_t w = __float_as_uint(x);
+  auto s = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float quad_add(float x) {
+  const uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const uint32_t w = __float_as_uint(x);
+  auto s = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-// 4 bf16 slots holding bf16(p) at slot (l & 3), zeros elsewhere (p is 0 outside the diagonal
-// lanes: their logits are masked)
-__device__ __forceinline__ void diag_slots(float p, int l, uint32_t* d0, uint32_t* d1) {
-  const uint32_t b = pack_bf2(p, 0.f) & 0xffffu;
-  const int s = l & 3;
-  *d0 = s == 0 ? b : (s == 1 ? (b << 16) : 0u);
-  *d1 = s == 2 ? b : (s == 3 ? (b << 16) : 0u);
-}
-
-__device__ __forceinline__ float xor_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+// Diagonal P^T block of two slabs for the PV MFMA. The B operand of lane (n, g) holds slab-A
+// rows 4g..4g+3 (slots 0-3) and slab-B rows 4g..4g+3 (slots 4-7) for query n; the diagonal
+// weight of query n sits in lane g = n / 4, slot n % 4 (slab A) and 4 + n % 4 (slab B).
+// x packs (weight A, weight B) as bf16 in the query's diagonal lane and zero elsewhere;
+// sel[] are the lane's byte selectors (v_perm_b32) that place x's halves in those slots.
+__device__ __forceinline__ bf16x8 diag_block(uint32_t x, const uint32_t* sel) {
+  return __builtin_bit_cast(bf16x8, make_uint4(__builtin_amdgcn_perm(x, x, sel[0]), __builtin_amdgcn_perm(x, x, sel[1]),
+                                               __builtin_amdgcn_perm(x, x, sel[2]), __builtin_amdgcn_perm(x, x, sel[3])));
 }
 
 // Rows of the far table entries for one step, held in registers and loaded one step ahead:
-// lane (n, g) holds, per far entry, K row i0w - d + n (dims 8g.., 32+8g..; the A operand of
-// the logit MFMA) and V row i0w - d + n (dims 16mb + 4g .. +3 for mb < 4; the lane's slice of
-// O^T), and in interpolated mode the same for the upper row (+1).
+// lane (n, g) holds, per far entry, K and V row i0w - d + n, dims 8g..8g+7 and 32+8g..32+8g+7
+// (K: the A operand of the logit MFMA; V: the lane's slice of O), and in interpolated mode
+// the same for the upper row (+1).
+template <int NF>
 struct FarRows {
-  uint4 k[kMaxFar][2];
-  uint4 kh[kMaxFar][2];
-  uint2 v[kMaxFar][4];
-  uint2 vh[kMaxFar][4];
+  uint4 k[NF > 0 ? NF : 1][2];
+  uint4 kh[NF > 0 ? NF : 1][2];
+  uint4 v[NF > 0 ? NF : 1][2];
+  uint4 vh[NF > 0 ? NF : 1][2];
 };
 
 // far rows are > kP - 128 rows behind their queries, so only the lower clamp can apply
-__device__ __forceinline__ int far_row(const RingArgs& a, int f, int i0w, int n, int up) {
-  const int r = i0w - a.far_dist[f] + n + up;
-  return r < 0 ? 0 : r;
+__device__ __forceinline__ const bf16_t* far_ptr(const bf16_t* base, int d, int i0w, int n, int up, int g) {
+  const int r = i0w - d + n + up;
+  return base + (int64_t)(r < 0 ? 0 : r) * kD + 8 * g;
 }
 
-template <int MODE>
-__device__ __forceinline__ void load_far_k(FarRows& fr, const RingArgs& a, const bf16_t* Kh, int i0w, int n, int g) {
+template <int MODE, int NF>
+__device__ __forceinline__ void load_far_k(FarRows<NF>& fr, const RingArgs& a, const bf16_t* Kh, int i0w, int n, int g) {
 #pragma unroll
-  for (int f = 0; f < kMaxFar; ++f) {
-    if (f < a.n_far) {
-      const bf16_t* kp = Kh + (int64_t)far_row(a, f, i0w, n, 0) * kD;
-      fr.k[f][0] = *reinterpret_cast<const uint4*>(kp + 8 * g);
-      fr.k[f][1] = *reinterpret_cast<const uint4*>(kp + kHalf + 8 * g);
-      if (MODE == 1) {
-        const bf16_t* kq = Kh + (int64_t)far_row(a, f, i0w, n, 1) * kD;
-        fr.kh[f][0] = *reinterpret_cast<const uint4*>(kq + 8 * g);
-        fr.kh[f][1] = *reinterpret_cast<const uint4*>(kq + kHalf + 8 * g);
-      }
+  for (int f = 0; f < NF; ++f) {
+    const bf16_t* kp = far_ptr(Kh, a.far_dist[f], i0w, n, 0, g);
+    fr.k[f][0] = *reinterpret_cast<const uint4*>(kp);
+    fr.k[f][1] = *reinterpret_cast<const uint4*>(kp + kHalf);
+    if (MODE == 1) {
+      const bf16_t* kq = far_ptr(Kh, a.far_dist[f], i0w, n, 1, g);
+      fr.kh[f][0] = *reinterpret_cast<const uint4*>(kq);
+      fr.kh[f][1] = *reinterpret_cast<const uint4*>(kq + kHalf);
     }
   }
 }
 
-template <int MODE>
-__device__ __forceinline__ void load_far_v(FarRows& fr, const RingArgs& a, const bf16_t* Vh, int i0w, int n, int g) {
+template <int MODE, int NF>
+__device__ __forceinline__ void load_far_v(FarRows<NF>& fr, const RingArgs& a, const bf16_t* Vh, int i0w, int n, int g) {
 #pragma unroll
-  for (int f = 0; f < kMaxFar; ++f) {
-    if (f < a.n_far) {
-      const bf16_t* vp = Vh + (int64_t)far_row(a, f, i0w, n, 0) * kD;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) fr.v[f][mb] = *reinterpret_cast<const uint2*>(vp + 16 * mb + 4 * g);
-      if (MODE == 1) {
-        const bf16_t* vq = Vh + (int64_t)far_row(a, f, i0w, n, 1) * kD;
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) fr.vh[f][mb] = *reinterpret_cast<const uint2*>(vq + 16 * mb + 4 * g);
-      }
+  for (int f = 0; f < NF; ++f) {
+    const bf16_t* vp = far_ptr(Vh, a.far_dist[f], i0w, n, 0, g);
+    fr.v[f][0] = *reinterpret_cast<const uint4*>(vp);
+    fr.v[f][1] = *reinterpret_cast<const uint4*>(vp + kHalf);
+    if (MODE == 1) {
+      const bf16_t* vq = far_ptr(Vh, a.far_dist[f], i0w, n, 1, g);
+      fr.vh[f][0] = *reinterpret_cast<const uint4*>(vq);
+      fr.vh[f][1] = *reinterpret_cast<const uint4*>(vq + kHalf);
     }
   }
 }
 
-template <int MODE, int NC, int WAVES>
+// acc[mb][v] += weights x V, one far row (or row pair) of the lane's 16 output dims: acc[0]
+// and acc[1] are dims 8g..8g+3 and 8g+4..8g+7 (x0 = first 16 bytes), acc[2] and acc[3] the
+// dims 32 + the same (x1). Integer mode: w0 = (p, 0) and w1 = (0, p) pick one element of a
+// bf16 pair. Interpolated mode: the lower and upper row's element of a dim are paired and
+// dotted with (p (1-w), p w).
+__device__ __forceinline__ void far_pv_int(f4* acc, uint4 x0, uint4 x1, uint32_t w0, uint32_t w1) {
+  const uint32_t e[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    acc[mb][0] = dot2(e[2 * mb], w0, acc[mb][0]);
+    acc[mb][1] = dot2(e[2 * mb], w1, acc[mb][1]);
+    acc[mb][2] = dot2(e[2 * mb + 1], w0, acc[mb][2]);
+    acc[mb][3] = dot2(e[2 * mb + 1], w1, acc[mb][3]);
+  }
+}
+__device__ __forceinline__ void far_pv_interp(f4* acc, uint4 x0, uint4 x1, uint4 y0, uint4 y1, uint32_t wp) {
+  const uint32_t e[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+  const uint32_t h[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    acc[mb][0] = dot2(__builtin_amdgcn_perm(h[2 * mb], e[2 * mb], 0x05040100u), wp, acc[mb][0]);
+    acc[mb][1] = dot2(__builtin_amdgcn_perm(h[2 * mb], e[2 * mb], 0x07060302u), wp, acc[mb][1]);
+    acc[mb][2] = dot2(__builtin_amdgcn_perm(h[2 * mb + 1], e[2 * mb + 1], 0x05040100u), wp, acc[mb][2]);
+    acc[mb][3] = dot2(__builtin_amdgcn_perm(h[2 * mb + 1], e[2 * mb + 1], 0x07060302u), wp, acc[mb][3]);
+  }
+}
+
+template <int MODE, int NC, int NF, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
   constexpr int kThreads = 64 * WAVES;
   constexpr int kT = step_rows(WAVES);
+  constexpr uint32_t kOnes = 0x3f803f80u;  // bf16 pair (1, 1)
   extern __shared__ __align__(16) uint8_t smem_raw[];
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
   const int tid = threadIdx.x;
@@ -258,7 +289,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
     uint4* z = reinterpret_cast<uint4*>(sm.ringK);
     const int n16 = (2 * kP * kRow) / 16;
     for (int x = tid; x < n16; x += kThreads) z[x] = make_uint4(0, 0, 0, 0);
-    const int n_unc = MODE == 1 ? 2 * a.n_far : a.n_far;
+    constexpr int n_unc = MODE == 1 ? 2 * NF : NF;
     for (int x = tid; x < n_unc * kHalf; x += kThreads) {
       const int u = x / kHalf, j = x % kHalf;
       sm.unc_cs[u][j] = rope_cs(a.unc_dist[u], a.rope.rev[j]);
@@ -276,15 +307,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
   auto load_rows = [&](int pb, uint4* q2, uint4* k2, uint4* v2) {
     const int r = pb + 16 * wave + n;
     if (r < N) {
-      const bf16_t* qp = Qh + (int64_t)r * kD;
-      const bf16_t* kp = Kh + (int64_t)r * kD;
-      const bf16_t* vp = Vh + (int64_t)r * kD;
-      q2[0] = *reinterpret_cast<const uint4*>(qp + 8 * g);
-      q2[1] = *reinterpret_cast<const uint4*>(qp + kHalf + 8 * g);
-      k2[0] = *reinterpret_cast<const uint4*>(kp + 8 * g);
-      k2[1] = *reinterpret_cast<const uint4*>(kp + kHalf + 8 * g);
-      v2[0] = *reinterpret_cast<const uint4*>(vp + 8 * g);
-      v2[1] = *reinterpret_cast<const uint4*>(vp + kHalf + 8 * g);
+      const bf16_t* qp = Qh + (int64_t)r * kD + 8 * g;
+      const bf16_t* kp = Kh + (int64_t)r * kD + 8 * g;
+      const bf16_t* vp = Vh + (int64_t)r * kD + 8 * g;
+      q2[0] = *reinterpret_cast<const uint4*>(qp);
+      q2[1] = *reinterpret_cast<const uint4*>(qp + kHalf);
+      k2[0] = *reinterpret_cast<const uint4*>(kp);
+      k2[1] = *reinterpret_cast<const uint4*>(kp + kHalf);
+      v2[0] = *reinterpret_cast<const uint4*>(vp);
+      v2[1] = *reinterpret_cast<const uint4*>(vp + kHalf);
     } else {
       q2[0] = q2[1] = k2[0] = k2[1] = v2[0] = v2[1] = make_uint4(0, 0, 0, 0);
     }
@@ -292,11 +323,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
   uint4 pq[2], pk[2], pv[2];
   load_rows(p0, pq, pk, pv);
   // far rows of the first computed step (p0 reaches s0 exactly: both are multiples of kT)
-  FarRows fr;
-  if (a.n_far > 0) {
-    load_far_k<MODE>(fr, a, Kh, s0 + 16 * wave, n, g);
-    load_far_v<MODE>(fr, a, Vh, s0 + 16 * wave, n, g);
-  }
+  FarRows<NF> fr;
+  load_far_k<MODE, NF>(fr, a, Kh, s0 + 16 * wave, n, g);
+  load_far_v<MODE, NF>(fr, a, Vh, s0 + 16 * wave, n, g);
 
   const float sl2 = a.scale_log2;
   // additive masks: window keys by distance (band key kappa of the lane at distance
@@ -310,6 +339,21 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
     bias1[v] = (d1 >= 0 && d1 < a.W) ? 0.f : -INFINITY;
   }
   const float bias_diag = diag_lane ? 0.f : -INFINITY;
+  // byte selectors of diag_block: slot s = l & 3 of slab A (lo half of x) and slab B (hi half)
+  uint32_t sel[4];
+  {
+    const uint32_t zero = 0x0c0c0c0cu;
+    const uint32_t a_half = (l & 1) ? 0x01000c0cu : 0x0c0c0100u;
+    const uint32_t b_half = (l & 1) ? 0x03020c0cu : 0x0c0c0302u;
+    const bool low = (l & 2) == 0;
+    sel[0] = low ? a_half : zero;
+    sel[1] = low ? zero : a_half;
+    sel[2] = low ? b_half : zero;
+    sel[3] = low ? zero : b_half;
+  }
+  // ds_bpermute address of the query's diagonal lane
+  const int diag_addr = 4 * (16 * (n >> 2) + n);
+
   int buf = 0;
   for (; p0 < s1; p0 += kT, buf ^= 1) {
     // ---- insert rows p0 + 16w + n: rotate K (and Q for this step's queries) by R_(p0 + t)
@@ -319,17 +363,25 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
       const float2 b = sm.base_cs[buf][8 * g + t];
       cs[t] = make_float2(b.x * cs_t[t].x - b.y * cs_t[t].y, b.y * cs_t[t].x + b.x * cs_t[t].y);
     }
+    float qf[16], kf[16];
+    unpack8(pq[0], qf);
+    unpack8(pq[1], qf + 8);
+    unpack8(pk[0], kf);
+    unpack8(pk[1], kf + 8);
     uint4 kr0, kr1, qh0, qh1;
-    rotate_pack(pk[0], pk[1], cs, &kr0, &kr1);
-    rotate_pack(pq[0], pq[1], cs, &qh0, &qh1);
-    const uint4 qraw0 = pq[0], qraw1 = pq[1];
+    rotate_pack_f(kf, cs, &kr0, &kr1);
+    rotate_pack_f(qf, cs, &qh0, &qh1);
     const int bw = p0 + 16 * wave;  // row i0w of this wave's queries
     {
-      const int ro = row_off(bw + n) + 16 * g;
-      lds_write16(sm.ringK, ro, kr0);
-      lds_write16(sm.ringK, ro + 64, kr1);
-      lds_write16(sm.ringV, ro, pv[0]);
-      lds_write16(sm.ringV, ro + 64, pv[1]);
+      // K^ as loaded; V in output order: dims 8g..8g+3 | 8g+4.. | 32+8g.. | 36+8g.. go to
+      // ring positions 4g, 16+4g, 32+4g, 48+4g
+      const int ro = row_off(bw + n);
+      lds_write16(sm.ringK, ro + 16 * g, kr0);
+      lds_write16(sm.ringK, ro + 64 + 16 * g, kr1);
+      lds_write8(sm.ringV, ro + 8 * g, pv[0].x, pv[0].y);
+      lds_write8(sm.ringV, ro + 32 + 8 * g, pv[0].z, pv[0].w);
+      lds_write8(sm.ringV, ro + 64 + 8 * g, pv[1].x, pv[1].y);
+      lds_write8(sm.ringV, ro + 96 + 8 * g, pv[1].z, pv[1].w);
     }
     __syncthreads();
     // next step's rows and base rotation
@@ -346,34 +398,26 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
       const bool early = i0w < a.early_rows;
 
       // ---- logits of the far entries first, so their next rows can be requested early
-      float qf[16];
-      unpack8(qraw0, qf);
-      unpack8(qraw1, qf + 8);
-      float s_far[kMaxFar];
+      float s_far[NF > 0 ? NF : 1];
 #pragma unroll
-      for (int f = 0; f < kMaxFar; ++f) {
-        s_far[f] = -INFINITY;
-        if (f < a.n_far) {
-          const int u = MODE == 1 ? 2 * f : f;
-          uint4 r0, r1;
-          rotate_pack_f(qf, &sm.unc_cs[u][8 * g], &r0, &r1);
-          f4 S = {0, 0, 0, 0};
-          S = mfma32(as_bf8(fr.k[f][0]), as_bf8(r0), S);
-          S = mfma32(as_bf8(fr.k[f][1]), as_bf8(r1), S);
-          float s = sel4(S, l);
-          if (MODE == 1) {
-            rotate_pack_f(qf, &sm.unc_cs[u + 1][8 * g], &r0, &r1);
-            f4 H = {0, 0, 0, 0};
-            H = mfma32(as_bf8(fr.kh[f][0]), as_bf8(r0), H);
-            H = mfma32(as_bf8(fr.kh[f][1]), as_bf8(r1), H);
-            s = fmaf(a.far_w[f], sel4(H, l) - s, s);
-          }
-          s = fmaf(s, sl2, bias_diag);
-          if (early && a.far_dist[f] > iq) s = -INFINITY;
-          s_far[f] = s;
+      for (int f = 0; f < NF; ++f) {
+        const int u = MODE == 1 ? 2 * f : f;
+        uint4 r0, r1;
+        rotate_pack_f(qf, &sm.unc_cs[u][8 * g], &r0, &r1);
+        f4 S = {0, 0, 0, 0};
+        S = mfma32(as_bf8(fr.k[f][0]), as_bf8(r0), S);
+        S = mfma32(as_bf8(fr.k[f][1]), as_bf8(r1), S);
+        float s = sel4(S, l);
+        if (MODE == 1) {
+          rotate_pack_f(qf, &sm.unc_cs[u + 1][8 * g], &r0, &r1);
+          f4 H = {0, 0, 0, 0};
+          H = mfma32(as_bf8(fr.kh[f][0]), as_bf8(r0), H);
+          H = mfma32(as_bf8(fr.kh[f][1]), as_bf8(r1), H);
+          s = fmaf(a.far_w[f], sel4(H, l) - s, s);
         }
+        s_far[f] = fmaf(s, sl2, bias_diag);
       }
-      if (a.n_far > 0 && pn < s1) load_far_k<MODE>(fr, a, Kh, i0w + kT, n, g);
+      if (pn < s1) load_far_k<MODE, NF>(fr, a, Kh, i0w + kT, n, g);
 
       // ---- window band: keys i0w - 16 + kappa, kappa < 32
       f4 S0 = {0, 0, 0, 0}, S1 = {0, 0, 0, 0};
@@ -384,29 +428,25 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
         S1 = mfma32(as_bf8(lds_read16(sm.ringK, sb)), bq0, S1);
         S1 = mfma32(as_bf8(lds_read16(sm.ringK, sb + 64)), bq1, S1);
       }
-      // ---- covered entries: 16-row slabs from the ring
+      // ---- covered entries: 16-row slabs from the ring (entries past n_cov are masked)
       float s_ent[NC];
 #pragma unroll
       for (int e = 0; e < NC; ++e) {
-        s_ent[e] = -INFINITY;
-        if (e < a.n_cov) {
-          const int d = a.dist[e];
-          const int sl = row_off(bw - d + n) + 16 * g;
-          f4 S = {0, 0, 0, 0};
-          S = mfma32(as_bf8(lds_read16(sm.ringK, sl)), bq0, S);
-          S = mfma32(as_bf8(lds_read16(sm.ringK, sl + 64)), bq1, S);
-          float s = sel4(S, l);
-          if (MODE == 1) {
-            const int sh = row_off(bw - d + 1 + n) + 16 * g;
-            f4 H = {0, 0, 0, 0};
-            H = mfma32(as_bf8(lds_read16(sm.ringK, sh)), bq0, H);
-            H = mfma32(as_bf8(lds_read16(sm.ringK, sh + 64)), bq1, H);
-            s = fmaf(a.w[e], sel4(H, l) - s, s);
-          }
-          s = fmaf(s, sl2, bias_diag);
-          if (early && d > iq) s = -INFINITY;
-          s_ent[e] = s;
+        const int d = a.dist[e];
+        const int sl = row_off(bw - d + n) + 16 * g;
+        f4 S = {0, 0, 0, 0};
+        S = mfma32(as_bf8(lds_read16(sm.ringK, sl)), bq0, S);
+        S = mfma32(as_bf8(lds_read16(sm.ringK, sl + 64)), bq1, S);
+        float s = sel4(S, l);
+        if (MODE == 1) {
+          const int sh = row_off(bw - d + 1 + n) + 16 * g;
+          f4 H = {0, 0, 0, 0};
+          H = mfma32(as_bf8(lds_read16(sm.ringK, sh)), bq0, H);
+          H = mfma32(as_bf8(lds_read16(sm.ringK, sh + 64)), bq1, H);
+          s = fmaf(a.w[e], sel4(H, l) - s, s);
         }
+        s = fmaf(s, sl2, bias_diag);
+        s_ent[e] = e < a.n_cov ? s : -INFINITY;
       }
 
       // ---- softmax over the window band and the entries (base-2 logits)
@@ -420,15 +460,21 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
 #pragma unroll
         for (int v = 0; v < 4; ++v)
           if (n + 16 - 4 * g - v > iq) sw0[v] = -INFINITY;
-      }
-      float m = -INFINITY;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) m = fmaxf(m, fmaxf(sw0[v], sw1[v]));
+        for (int e = 0; e < NC; ++e)
+          if (a.dist[e] > iq) s_ent[e] = -INFINITY;
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+          if (a.far_dist[f] > iq) s_far[f] = -INFINITY;
+      }
+      float m = fmaxf(fmaxf(sw0[0], sw0[1]), fmaxf(sw0[2], sw0[3]));
+#pragma unroll
+      for (int v = 0; v < 4; ++v) m = fmaxf(m, sw1[v]);
 #pragma unroll
       for (int e = 0; e < NC; ++e) m = fmaxf(m, s_ent[e]);
 #pragma unroll
-      for (int f = 0; f < kMaxFar; ++f) m = fmaxf(m, s_far[f]);
-      m = xor_max(m);  // every query has its own key (distance 0), so m is finite
+      for (int f = 0; f < NF; ++f) m = fmaxf(m, s_far[f]);
+      m = quad_max(m);  // every query has its own key (distance 0), so m is finite
       // lsum: the fp32 sum of the weights, for LSE (each query's weights are spread over its
       // four lanes: window keys in all four, table entries in its diagonal lane)
       float lsum = 0.f;
@@ -444,60 +490,45 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
         lsum += s_ent[e];
       }
 #pragma unroll
-      for (int f = 0; f < kMaxFar; ++f) {
+      for (int f = 0; f < NF; ++f) {
         s_far[f] = ex2(s_far[f] - m);
         lsum += s_far[f];
       }
-      lsum += __shfl_xor(lsum, 16);
-      lsum += __shfl_xor(lsum, 32);
+      lsum = quad_add(lsum);
 
-      // ---- P V: O^T[dim 16 mb + 4 g + v][query n], weights in bf16. The normaliser is the
-      // sum of exactly the bf16 weights applied (rows of P sum to 1): an all-ones A block adds
-      // a fifth output block whose every entry is the column sum of P^T.
+      // ---- P V: O^T[dim][query n], weights in bf16. The normaliser is the sum of exactly the
+      // bf16 weights applied (rows of P sum to 1): an all-ones A block adds a fifth output
+      // block whose every entry is the column sum of P^T; far weights add through dot2.
       f4 acc[4];
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) acc[mb] = f4{0, 0, 0, 0};
       f4 accn = {0, 0, 0, 0};
-      const bf16x8 ones = as_bf8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+      const bf16x8 ones = as_bf8(make_uint4(kOnes, kOnes, kOnes, kOnes));
       float lnorm_far = 0.f;
-      // far entries on VALU first: the lane's O^T slice += p * V[row][16 mb + 4 g + v]; p lives
-      // in the query's diagonal lane and is broadcast to its other three lanes
+      // far entries on VALU first; the weights live in the query's diagonal lane and reach
+      // its other three lanes by ds_bpermute, packed two per dword
+      if (MODE == 0) {
 #pragma unroll
-      for (int f = 0; f < kMaxFar; ++f) {
-        if (f < a.n_far) {
-          const float p = __shfl(s_far[f], 16 * (n >> 2) + n);
-          const float plo = MODE == 1 ? round_bf(p * (1.f - a.far_w[f])) : round_bf(p);
-          const float phi = MODE == 1 ? round_bf(p * a.far_w[f]) : 0.f;
-          lnorm_far += plo + phi;
-          const uint32_t blo = __float_as_uint(plo), bhi = __float_as_uint(phi);
-          if (MODE == 0) {
-            // weights (p, 0) and (0, p) pick one bf16 of a pair: one dot2 per element
-            const uint32_t w0 = blo >> 16, w1 = blo & 0xffff0000u;
+        for (int f = 0; f < NF; f += 2) {
+          const uint32_t x = pack_bf2(s_far[f], f + 1 < NF ? s_far[f + 1] : 0.f);
+          const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute(diag_addr, (int)x);
+          lnorm_far = dot2(y, kOnes, lnorm_far);
+          far_pv_int(acc, fr.v[f][0], fr.v[f][1], y & 0xffffu, y << 16);
+          if (f + 1 < NF) far_pv_int(acc, fr.v[f + 1][0], fr.v[f + 1][1], y >> 16, y & 0xffff0000u);
+        }
+      } else {
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-              const uint2 x = fr.v[f][mb];
-              acc[mb][0] = dot2(x.x, w0, acc[mb][0]);
-              acc[mb][1] = dot2(x.x, w1, acc[mb][1]);
-              acc[mb][2] = dot2(x.y, w0, acc[mb][2]);
-              acc[mb][3] = dot2(x.y, w1, acc[mb][3]);
-            }
-          } else {
-            // pair the lower-row and upper-row element of a dim, weights (1-w) p and w p
-            const uint32_t wp = (blo >> 16) | (bhi & 0xffff0000u);
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-              const uint2 x = fr.v[f][mb], y = fr.vh[f][mb];
-              acc[mb][0] = dot2(__builtin_amdgcn_perm(y.x, x.x, 0x05040100u), wp, acc[mb][0]);
-              acc[mb][1] = dot2(__builtin_amdgcn_perm(y.x, x.x, 0x07060302u), wp, acc[mb][1]);
-              acc[mb][2] = dot2(__builtin_amdgcn_perm(y.y, x.y, 0x05040100u), wp, acc[mb][2]);
-              acc[mb][3] = dot2(__builtin_amdgcn_perm(y.y, x.y, 0x07060302u), wp, acc[mb][3]);
-            }
-          }
+        for (int f = 0; f < NF; ++f) {
+          const float p = s_far[f];
+          const uint32_t x = pack_bf2(p * (1.f - a.far_w[f]), p * a.far_w[f]);
+          const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute(diag_addr, (int)x);
+          lnorm_far = dot2(y, kOnes, lnorm_far);
+          far_pv_interp(acc, fr.v[f][0], fr.v[f][1], fr.vh[f][0], fr.vh[f][1], y);
         }
       }
-      if (a.n_far > 0 && pn < s1) load_far_v<MODE>(fr, a, Vh, i0w + kT, n, g);
+      if (pn < s1) load_far_v<MODE, NF>(fr, a, Vh, i0w + kT, n, g);
 
-      // transpose reads: lane (jr, jc) of a 16-lane group reads row k0 + jr, dims
+      // transpose reads: lane (jr, jc) of a 16-lane group reads row k0 + jr, ring positions
       // 16 mb + 4 jc .. +3, i.e. bytes 32 mb + 8 jc of the row
       auto tr_base = [&](int row) { return row_off(row) + 8 * jc; };
       {
@@ -516,48 +547,42 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
       if (MODE == 0) {
 #pragma unroll
         for (int e = 0; e < NC; e += 2) {
-          if (e < a.n_cov) {
-            uint32_t d0, d1, d2, d3;
-            diag_slots(s_ent[e], l, &d0, &d1);
-            diag_slots(s_ent[e + 1], l, &d2, &d3);
-            const bf16x8 bp = __builtin_bit_cast(bf16x8, make_uint4(d0, d1, d2, d3));
-            const int ra = tr_base(bw - a.dist[e] + 4 * g + jr), rb = tr_base(bw - a.dist[e + 1] + 4 * g + jr);
+          const bf16x8 bp = diag_block(pack_bf2(s_ent[e], s_ent[e + 1]), sel);
+          const int ra = tr_base(bw - a.dist[e] + 4 * g + jr), rb = tr_base(bw - a.dist[e + 1] + 4 * g + jr);
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-              acc[mb] = mfma32(cat_bf8(tr16(sm.ringV, ra + 32 * mb), tr16(sm.ringV, rb + 32 * mb)), bp, acc[mb]);
-            accn = mfma32(ones, bp, accn);
-          }
+          for (int mb = 0; mb < 4; ++mb)
+            acc[mb] = mfma32(cat_bf8(tr16(sm.ringV, ra + 32 * mb), tr16(sm.ringV, rb + 32 * mb)), bp, acc[mb]);
+          accn = mfma32(ones, bp, accn);
         }
       } else {
 #pragma unroll
         for (int e = 0; e < NC; ++e) {
-          if (e < a.n_cov) {
-            const float p = s_ent[e];
-            uint32_t d0, d1, d2, d3;
-            diag_slots(p * (1.f - a.w[e]), l, &d0, &d1);
-            diag_slots(p * a.w[e], l, &d2, &d3);
-            const bf16x8 bp = __builtin_bit_cast(bf16x8, make_uint4(d0, d1, d2, d3));
-            const int ra = tr_base(bw - a.dist[e] + 4 * g + jr), rb = tr_base(bw - a.dist[e] + 1 + 4 * g + jr);
+          const float p = s_ent[e];
+          const bf16x8 bp = diag_block(pack_bf2(p * (1.f - a.w[e]), p * a.w[e]), sel);
+          const int ra = tr_base(bw - a.dist[e] + 4 * g + jr), rb = tr_base(bw - a.dist[e] + 1 + 4 * g + jr);
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-              acc[mb] = mfma32(cat_bf8(tr16(sm.ringV, ra + 32 * mb), tr16(sm.ringV, rb + 32 * mb)), bp, acc[mb]);
-            accn = mfma32(ones, bp, accn);
-          }
+          for (int mb = 0; mb < 4; ++mb)
+            acc[mb] = mfma32(cat_bf8(tr16(sm.ringV, ra + 32 * mb), tr16(sm.ringV, rb + 32 * mb)), bp, acc[mb]);
+          accn = mfma32(ones, bp, accn);
         }
       }
 
-      // ---- epilogue
+      // ---- epilogue: the lane's dims 8g..8g+7 (acc[0], acc[1]) and 32+8g.. (acc[2], acc[3])
       if (iq < s1) {
         const float lnorm = accn[0] + lnorm_far;
         const float inv = 1.f / lnorm;
-        bf16_t* op = a.o + hoff + (int64_t)iq * kD + 4 * g;
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          uint2 x;
-          x.x = pack_bf2(acc[mb][0] * inv, acc[mb][1] * inv);
-          x.y = pack_bf2(acc[mb][2] * inv, acc[mb][3] * inv);
-          *reinterpret_cast<uint2*>(op + 16 * mb) = x;
-        }
+        bf16_t* op = a.o + hoff + (int64_t)iq * kD + 8 * g;
+        uint4 x0, x1;
+        x0.x = pack_bf2(acc[0][0] * inv, acc[0][1] * inv);
+        x0.y = pack_bf2(acc[0][2] * inv, acc[0][3] * inv);
+        x0.z = pack_bf2(acc[1][0] * inv, acc[1][1] * inv);
+        x0.w = pack_bf2(acc[1][2] * inv, acc[1][3] * inv);
+        x1.x = pack_bf2(acc[2][0] * inv, acc[2][1] * inv);
+        x1.y = pack_bf2(acc[2][2] * inv, acc[2][3] * inv);
+        x1.z = pack_bf2(acc[3][0] * inv, acc[3][1] * inv);
+        x1.w = pack_bf2(acc[3][2] * inv, acc[3][3] * inv);
+        *reinterpret_cast<uint4*>(op) = x0;
+        *reinterpret_cast<uint4*>(op + kHalf) = x1;
         if (g == 0 && a.lse != nullptr) a.lse[(size_t)head * N + iq] = (m + log2f(lsum)) * 0.69314718055994530942f;
       }
     }
@@ -580,14 +605,35 @@ void split_table(const FwdArgs& f, int* n_cov, int* n_far) {
   *n_far = n - cov;
 }
 
-template <int MODE, int NC, int WAVES>
+template <int MODE, int NC, int NF, int WAVES>
 hipError_t launch(const RingArgs& a, unsigned blocks, hipStream_t s) {
   const size_t smem = sizeof(Smem);
-  hipError_t e = hipFuncSetAttribute((const void*)fwd_ring_kernel<MODE, NC, WAVES>,
+  hipError_t e = hipFuncSetAttribute((const void*)fwd_ring_kernel<MODE, NC, NF, WAVES>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
-  fwd_ring_kernel<MODE, NC, WAVES><<<blocks, 64 * WAVES, smem, s>>>(a);
+  fwd_ring_kernel<MODE, NC, NF, WAVES><<<blocks, 64 * WAVES, smem, s>>>(a);
   return hipGetLastError();
+}
+
+// kernel instance by (covered entries rounded up to 8 or 16, far entries)
+template <int MODE, int WAVES>
+hipError_t launch_mode(const RingArgs& a, int n_far, unsigned blocks, hipStream_t s) {
+  if (a.n_cov <= 8) {
+    switch (n_far) {
+      case 0: return launch<MODE, 8, 0, WAVES>(a, blocks, s);
+      case 1: return launch<MODE, 8, 1, WAVES>(a, blocks, s);
+      case 2: return launch<MODE, 8, 2, WAVES>(a, blocks, s);
+      case 3: return launch<MODE, 8, 3, WAVES>(a, blocks, s);
+      default: return launch<MODE, 8, 4, WAVES>(a, blocks, s);
+    }
+  }
+  switch (n_far) {
+    case 0: return launch<MODE, 16, 0, WAVES>(a, blocks, s);
+    case 1: return launch<MODE, 16, 1, WAVES>(a, blocks, s);
+    case 2: return launch<MODE, 16, 2, WAVES>(a, blocks, s);
+    case 3: return launch<MODE, 16, 3, WAVES>(a, blocks, s);
+    default: return launch<MODE, 16, 4, WAVES>(a, blocks, s);
+  }
 }
 
 }  // namespace
@@ -596,7 +642,7 @@ bool fwd_ring_supported(const FwdArgs& f) {
   if (f.dtype != 1 || f.W > kMaxBand || f.N > (1LL << 30)) return false;
   int cov, far;
   split_table(f, &cov, &far);
-  return far <= kMaxFar && cov <= 16;
+  return far <= kMaxFar && cov <= kMaxCov;
 }
 
 hipError_t launch_fwd_ring(const FwdArgs& f) {
@@ -608,18 +654,19 @@ hipError_t launch_fwd_ring(const FwdArgs& f) {
   a.lse = f.lse;
   a.N = (int)f.N;
   a.W = f.W;
-  split_table(f, &a.n_cov, &a.n_far);
-  for (int e = 0; e < kMaxEnt; ++e) {
+  int n_far;
+  split_table(f, &a.n_cov, &n_far);
+  for (int e = 0; e < kMaxCov; ++e) {
     // slots past the covered prefix get a harmless in-ring distance and weight 0
     a.dist[e] = e < a.n_cov ? f.tab.dist[e] : kMaxBand;
     a.w[e] = e < a.n_cov ? f.tab.w[e] : 0.f;
   }
   for (int x = 0; x < kMaxFar; ++x) {
-    a.far_dist[x] = x < a.n_far ? f.tab.dist[a.n_cov + x] : 0;
-    a.far_w[x] = x < a.n_far ? f.tab.w[a.n_cov + x] : 0.f;
+    a.far_dist[x] = x < n_far ? f.tab.dist[a.n_cov + x] : 0;
+    a.far_w[x] = x < n_far ? f.tab.w[a.n_cov + x] : 0.f;
   }
   int u = 0;
-  for (int x = 0; x < a.n_far; ++x) {
+  for (int x = 0; x < n_far; ++x) {
     a.unc_dist[u++] = a.far_dist[x];
     if (f.mode == 1) a.unc_dist[u++] = a.far_dist[x] - 1;
   }
@@ -630,7 +677,7 @@ hipError_t launch_fwd_ring(const FwdArgs& f) {
   for (int e = 0; e < a.n_cov; ++e) need = f.tab.dist[e] > need ? f.tab.dist[e] : need;
   a.warm = ((need + kT - 1) / kT) * kT;
   int early = kMaxBand;
-  for (int e = 0; e < a.n_cov + a.n_far; ++e) early = f.tab.dist[e] > early ? f.tab.dist[e] : early;
+  for (int e = 0; e < a.n_cov + n_far; ++e) early = f.tab.dist[e] > early ? f.tab.dist[e] : early;
   a.early_rows = early;
   // segments: about one workgroup per CU in total
   const int64_t tiles = (f.N + kT - 1) / kT;
@@ -644,9 +691,8 @@ hipError_t launch_fwd_ring(const FwdArgs& f) {
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)kD));
   a.rope = f.rope;
   const unsigned blocks = (unsigned)(segs * f.BH);
-  if (f.mode == 0)
-    return a.n_cov <= 8 ? launch<0, 8, 8>(a, blocks, f.stream) : launch<0, 16, 8>(a, blocks, f.stream);
-  return a.n_cov <= 8 ? launch<1, 8, 4>(a, blocks, f.stream) : launch<1, 16, 4>(a, blocks, f.stream);
+  if (f.mode == 0) return launch_mode<0, 8>(a, n_far, blocks, f.stream);
+  return launch_mode<1, 4>(a, n_far, blocks, f.stream);
 }
 
 }  // namespace fib

@@ -244,3 +244,22 @@ def test_ring_cases(case, mode):
     say("ring", case, mode)
     qkv = inputs(3000 + N + W, (B, H, N, 64), BF16)
     check_full(qkv, W, np.float32(alpha), base, mode, BF16)
+
+
+# ---- the persistent schedule that groups a head's consecutive segments on one XCD ----------
+# (taken when far entries exist and there are at least two segments per CU: long sequences)
+
+GROUPED = [
+    # (B, H, N, W, alpha, base, heads checked in full)
+    (2, 8, 16000, 12, 1.5, FIB_BASE, [(0, 0), (0, 7), (1, 7)]),   # ragged last segment
+    (1, 13, 20000, 12, 1.0, FIB_BASE, [(0, 0), (0, 5), (0, 12)]),  # heads not a multiple of 8
+]
+
+
+@pytest.mark.parametrize("mode", [INT, INTERP], ids=["int", "interp"])
+@pytest.mark.parametrize("case", GROUPED, ids=[f"B{c[0]}H{c[1]}N{c[2]}a{c[4]}" for c in GROUPED])
+def test_grouped_schedule(case, mode):
+    B, H, N, W, alpha, base, heads = case
+    say("grouped", case[:5], mode)
+    qkv = inputs(4000 + N + H, (B, H, N, 64), BF16)
+    check_full(qkv, W, np.float32(alpha), base, mode, BF16, heads=heads)
