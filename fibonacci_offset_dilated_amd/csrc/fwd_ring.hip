@@ -8,9 +8,9 @@
 // a fused path; here both modes run fused in this kernel.
 //
 // Design (gfx950):
-//  * One workgroup per CU (8 waves in integer mode, two per SIMD to cover latencies; 4 in
-//    interpolated mode, whose far rows need twice the registers) sweeps a contiguous segment
-//    of one head in steps of 16 queries per wave; wave w owns queries p0 + 16w .. + 15.
+//  * One workgroup per CU (8 waves, two per SIMD to cover latencies; 4 when four interpolated
+//    far entries need registers for eight far rows) sweeps a contiguous segment of one head
+//    in steps of 16 queries per wave; wave w owns queries p0 + 16w .. + 15.
 //  * LDS ring of the last kP rows: K rotated by RoPE (bf16) and raw V (bf16). Each row is
 //    loaded from HBM and rotated once, when it enters the ring; the window band and every
 //    table entry whose distance is <= kP - (rows per step) read it from LDS afterwards.
@@ -76,14 +76,19 @@ struct RingArgs {
   Rope rope;
 };
 
+// Rows 0..kMirror-1 of the ring are also stored after its end, so that any 32 consecutive
+// ring rows (slots s..s+31, s < kP) are one base address plus constant offsets.
+constexpr int kMirror = 32;
+
 struct __align__(16) Smem {
-  uint8_t ringK[kP * kRow];
-  uint8_t ringV[kP * kRow];
+  uint8_t ringK[(kP + kMirror) * kRow];
+  uint8_t ringV[(kP + kMirror) * kRow];
   float2 unc_cs[kMaxUnc][kHalf];
   float2 base_cs[2][kHalf];
 };
 
-// byte offset of ring row `row` (any integer, negative rows included: slots are row mod kP)
+// byte offset of ring row `row` (any integer, negative rows included: slots are row mod kP);
+// wave-uniform arguments keep it on the scalar unit
 __device__ __forceinline__ int row_off(int row) { return (row & (kP - 1)) * kRow; }
 
 __device__ __forceinline__ uint4 lds_read16(const uint8_t* base, int off) {
@@ -195,21 +200,26 @@ struct FarRows {
   uint4 vh[NF > 0 ? NF : 1][2];
 };
 
-// far rows are > kP - 128 rows behind their queries, so only the lower clamp can apply
-__device__ __forceinline__ const bf16_t* far_ptr(const bf16_t* base, int d, int i0w, int n, int up, int g) {
-  const int r = i0w - d + n + up;
-  return base + (int64_t)(r < 0 ? 0 : r) * kD + 8 * g;
+// Element offset of the lane's row of a far entry's 16-row slab for the wave's queries
+// i0w.. (row i0w - d + n; far distances exceed the ring reach, so the slab never passes row
+// N - 1). lane_off = n * D + 8 g. A slab that starts before row 0 clamps each lane's row to
+// row 0 (the queries that read rows before it are masked).
+__device__ __forceinline__ int64_t far_off(int d, int i0w, int n, int g, int lane_off) {
+  const int r0 = i0w - d;
+  if (r0 >= 0) return (int64_t)r0 * kD + lane_off;
+  return (int64_t)(r0 + n > 0 ? r0 + n : 0) * kD + 8 * g;
 }
 
 template <int MODE, int NF>
-__device__ __forceinline__ void load_far_k(FarRows<NF>& fr, const RingArgs& a, const bf16_t* Kh, int i0w, int n, int g) {
+__device__ __forceinline__ void load_far_k(FarRows<NF>& fr, const RingArgs& a, const bf16_t* Kh, int i0w, int n, int g,
+                                           int lane_off) {
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    const bf16_t* kp = far_ptr(Kh, a.far_dist[f], i0w, n, 0, g);
+    const bf16_t* kp = Kh + far_off(a.far_dist[f], i0w, n, g, lane_off);
     fr.k[f][0] = *reinterpret_cast<const uint4*>(kp);
     fr.k[f][1] = *reinterpret_cast<const uint4*>(kp + kHalf);
     if (MODE == 1) {
-      const bf16_t* kq = far_ptr(Kh, a.far_dist[f], i0w, n, 1, g);
+      const bf16_t* kq = Kh + far_off(a.far_dist[f] - 1, i0w, n, g, lane_off);
       fr.kh[f][0] = *reinterpret_cast<const uint4*>(kq);
       fr.kh[f][1] = *reinterpret_cast<const uint4*>(kq + kHalf);
     }
@@ -217,14 +227,15 @@ __device__ __forceinline__ void load_far_k(FarRows<NF>& fr, const RingArgs& a, c
 }
 
 template <int MODE, int NF>
-__device__ __forceinline__ void load_far_v(FarRows<NF>& fr, const RingArgs& a, const bf16_t* Vh, int i0w, int n, int g) {
+__device__ __forceinline__ void load_far_v(FarRows<NF>& fr, const RingArgs& a, const bf16_t* Vh, int i0w, int n, int g,
+                                           int lane_off) {
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    const bf16_t* vp = far_ptr(Vh, a.far_dist[f], i0w, n, 0, g);
+    const bf16_t* vp = Vh + far_off(a.far_dist[f], i0w, n, g, lane_off);
     fr.v[f][0] = *reinterpret_cast<const uint4*>(vp);
     fr.v[f][1] = *reinterpret_cast<const uint4*>(vp + kHalf);
     if (MODE == 1) {
-      const bf16_t* vq = far_ptr(Vh, a.far_dist[f], i0w, n, 1, g);
+      const bf16_t* vq = Vh + far_off(a.far_dist[f] - 1, i0w, n, g, lane_off);
       fr.vh[f][0] = *reinterpret_cast<const uint4*>(vq);
       fr.vh[f][1] = *reinterpret_cast<const uint4*>(vq + kHalf);
     }
@@ -266,7 +277,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63;
   const int n = l & 15;   // query (and row) within the wave's 16
   const int g = l >> 4;   // lane group: dims 8g..8g+7 and 32+8g..32+8g+7
@@ -287,7 +298,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
   // ---- set-up: zero the ring, cos/sin of the far distances and of the first step base
   {
     uint4* z = reinterpret_cast<uint4*>(sm.ringK);
-    const int n16 = (2 * kP * kRow) / 16;
+    const int n16 = (2 * (kP + kMirror) * kRow) / 16;
     for (int x = tid; x < n16; x += kThreads) z[x] = make_uint4(0, 0, 0, 0);
     constexpr int n_unc = MODE == 1 ? 2 * NF : NF;
     for (int x = tid; x < n_unc * kHalf; x += kThreads) {
@@ -303,29 +314,35 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
   for (int t = 0; t < 8; ++t) cs_t[t] = rope_cs(16 * wave + n, a.rope.rev[8 * g + t]);
   __syncthreads();
 
-  // rows this lane inserts: q/k/v dims 8g.. and 32+8g.. of row pb + 16w + n
+  // element offset of the lane's part of a 16-row slab: row n, dims 8g.. (and 32+8g..)
+  const int lane_off = n * kD + 8 * g;
+  // rows this lane inserts: q/k/v dims 8g.. and 32+8g.. of row pb + 16w + n. Rows past the
+  // end repeat row N - 1: only queries past the end read them.
   auto load_rows = [&](int pb, uint4* q2, uint4* k2, uint4* v2) {
-    const int r = pb + 16 * wave + n;
-    if (r < N) {
-      const bf16_t* qp = Qh + (int64_t)r * kD + 8 * g;
-      const bf16_t* kp = Kh + (int64_t)r * kD + 8 * g;
-      const bf16_t* vp = Vh + (int64_t)r * kD + 8 * g;
-      q2[0] = *reinterpret_cast<const uint4*>(qp);
-      q2[1] = *reinterpret_cast<const uint4*>(qp + kHalf);
-      k2[0] = *reinterpret_cast<const uint4*>(kp);
-      k2[1] = *reinterpret_cast<const uint4*>(kp + kHalf);
-      v2[0] = *reinterpret_cast<const uint4*>(vp);
-      v2[1] = *reinterpret_cast<const uint4*>(vp + kHalf);
+    const int rb = pb + 16 * wave;
+    int64_t off;
+    if (rb + 15 < N) {
+      off = (int64_t)rb * kD + lane_off;
     } else {
-      q2[0] = q2[1] = k2[0] = k2[1] = v2[0] = v2[1] = make_uint4(0, 0, 0, 0);
+      const int r = rb + n < N ? rb + n : N - 1;
+      off = (int64_t)r * kD + 8 * g;
     }
+    const bf16_t* qp = Qh + off;
+    const bf16_t* kp = Kh + off;
+    const bf16_t* vp = Vh + off;
+    q2[0] = *reinterpret_cast<const uint4*>(qp);
+    q2[1] = *reinterpret_cast<const uint4*>(qp + kHalf);
+    k2[0] = *reinterpret_cast<const uint4*>(kp);
+    k2[1] = *reinterpret_cast<const uint4*>(kp + kHalf);
+    v2[0] = *reinterpret_cast<const uint4*>(vp);
+    v2[1] = *reinterpret_cast<const uint4*>(vp + kHalf);
   };
   uint4 pq[2], pk[2], pv[2];
   load_rows(p0, pq, pk, pv);
   // far rows of the first computed step (p0 reaches s0 exactly: both are multiples of kT)
   FarRows<NF> fr;
-  load_far_k<MODE, NF>(fr, a, Kh, s0 + 16 * wave, n, g);
-  load_far_v<MODE, NF>(fr, a, Vh, s0 + 16 * wave, n, g);
+  load_far_k<MODE, NF>(fr, a, Kh, s0 + 16 * wave, n, g, lane_off);
+  load_far_v<MODE, NF>(fr, a, Vh, s0 + 16 * wave, n, g, lane_off);
 
   const float sl2 = a.scale_log2;
   // additive masks: window keys by distance (band key kappa of the lane at distance
@@ -353,6 +370,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
   }
   // ds_bpermute address of the query's diagonal lane
   const int diag_addr = 4 * (16 * (n >> 2) + n);
+  // lane parts of the LDS addresses: slab reads (row n, chunk g) and transpose reads (row
+  // 4g + jr, ring positions 4 jc..)
+  const int lane_k = n * kRow + 16 * g;
+  const int lane_v = (4 * g + jr) * kRow + 8 * jc;
 
   int buf = 0;
   for (; p0 < s1; p0 += kT, buf ^= 1) {
@@ -375,18 +396,24 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
     {
       // K^ as loaded; V in output order: dims 8g..8g+3 | 8g+4.. | 32+8g.. | 36+8g.. go to
       // ring positions 4g, 16+4g, 32+4g, 48+4g
-      const int ro = row_off(bw + n);
-      lds_write16(sm.ringK, ro + 16 * g, kr0);
-      lds_write16(sm.ringK, ro + 64 + 16 * g, kr1);
-      lds_write8(sm.ringV, ro + 8 * g, pv[0].x, pv[0].y);
-      lds_write8(sm.ringV, ro + 32 + 8 * g, pv[0].z, pv[0].w);
-      lds_write8(sm.ringV, ro + 64 + 8 * g, pv[1].x, pv[1].y);
-      lds_write8(sm.ringV, ro + 96 + 8 * g, pv[1].z, pv[1].w);
+      const int slot = bw & (kP - 1);
+      auto put = [&](int ro) {
+        uint8_t* kp = sm.ringK + ro + 16 * g;
+        uint8_t* vp = sm.ringV + ro + 8 * g;
+        lds_write16(kp, 0, kr0);
+        lds_write16(kp, 64, kr1);
+        lds_write8(vp, 0, pv[0].x, pv[0].y);
+        lds_write8(vp, 32, pv[0].z, pv[0].w);
+        lds_write8(vp, 64, pv[1].x, pv[1].y);
+        lds_write8(vp, 96, pv[1].z, pv[1].w);
+      };
+      put((slot + n) * kRow);
+      if (slot < kMirror) put((slot + kP + n) * kRow);  // mirrored rows are stored twice
     }
     __syncthreads();
-    // next step's rows and base rotation
+    // next step's rows (the last step loads harmless repeats) and base rotation
     const int pn = p0 + kT;
-    if (pn < s1) load_rows(pn, pq, pk, pv);
+    load_rows(pn < s1 ? pn : p0, pq, pk, pv);
     if (wave == 0 && l < kHalf) sm.base_cs[buf ^ 1][l] = rope_cs(pn, a.rope.rev[l]);
 
     if (p0 >= s0) {
@@ -417,36 +444,40 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
         }
         s_far[f] = fmaf(s, sl2, bias_diag);
       }
-      if (pn < s1) load_far_k<MODE, NF>(fr, a, Kh, i0w + kT, n, g);
+      load_far_k<MODE, NF>(fr, a, Kh, i0w + kT, n, g, lane_off);
 
       // ---- window band: keys i0w - 16 + kappa, kappa < 32
       f4 S0 = {0, 0, 0, 0}, S1 = {0, 0, 0, 0};
+      const int band = row_off(bw - 16);  // slab 0 at +0, slab 1 at +16 rows
       {
-        const int sa = row_off(bw - 16 + n) + 16 * g, sb = row_off(bw + n) + 16 * g;
+        const int sa = band + lane_k;
         S0 = mfma32(as_bf8(lds_read16(sm.ringK, sa)), bq0, S0);
         S0 = mfma32(as_bf8(lds_read16(sm.ringK, sa + 64)), bq1, S0);
-        S1 = mfma32(as_bf8(lds_read16(sm.ringK, sb)), bq0, S1);
-        S1 = mfma32(as_bf8(lds_read16(sm.ringK, sb + 64)), bq1, S1);
+        S1 = mfma32(as_bf8(lds_read16(sm.ringK, sa + 16 * kRow)), bq0, S1);
+        S1 = mfma32(as_bf8(lds_read16(sm.ringK, sa + 16 * kRow + 64)), bq1, S1);
       }
       // ---- covered entries: 16-row slabs from the ring (entries past n_cov are masked)
       float s_ent[NC];
 #pragma unroll
       for (int e = 0; e < NC; ++e) {
-        const int d = a.dist[e];
-        const int sl = row_off(bw - d + n) + 16 * g;
+        const int sl = row_off(bw - a.dist[e]) + lane_k;
         f4 S = {0, 0, 0, 0};
         S = mfma32(as_bf8(lds_read16(sm.ringK, sl)), bq0, S);
         S = mfma32(as_bf8(lds_read16(sm.ringK, sl + 64)), bq1, S);
         float s = sel4(S, l);
         if (MODE == 1) {
-          const int sh = row_off(bw - d + 1 + n) + 16 * g;
+          // the upper slab is the next row
           f4 H = {0, 0, 0, 0};
-          H = mfma32(as_bf8(lds_read16(sm.ringK, sh)), bq0, H);
-          H = mfma32(as_bf8(lds_read16(sm.ringK, sh + 64)), bq1, H);
+          H = mfma32(as_bf8(lds_read16(sm.ringK, sl + kRow)), bq0, H);
+          H = mfma32(as_bf8(lds_read16(sm.ringK, sl + kRow + 64)), bq1, H);
           s = fmaf(a.w[e], sel4(H, l) - s, s);
         }
-        s = fmaf(s, sl2, bias_diag);
-        s_ent[e] = e < a.n_cov ? s : -INFINITY;
+        s_ent[e] = fmaf(s, sl2, bias_diag);
+      }
+      if (a.n_cov < NC) {
+#pragma unroll
+        for (int e = 0; e < NC; ++e)
+          if (e >= a.n_cov) s_ent[e] = -INFINITY;
       }
 
       // ---- softmax over the window band and the entries (base-2 logits)
@@ -526,16 +557,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
           far_pv_interp(acc, fr.v[f][0], fr.v[f][1], fr.vh[f][0], fr.vh[f][1], y);
         }
       }
-      if (pn < s1) load_far_v<MODE, NF>(fr, a, Vh, i0w + kT, n, g);
+      load_far_v<MODE, NF>(fr, a, Vh, i0w + kT, n, g, lane_off);
 
       // transpose reads: lane (jr, jc) of a 16-lane group reads row k0 + jr, ring positions
-      // 16 mb + 4 jc .. +3, i.e. bytes 32 mb + 8 jc of the row
-      auto tr_base = [&](int row) { return row_off(row) + 8 * jc; };
+      // 16 mb + 4 jc .. +3, i.e. bytes 32 mb + 8 jc of the row (k0 = 4g of the slab)
       {
         const bf16x8 bp = __builtin_bit_cast(
             bf16x8, make_uint4(pack_bf2(sw0[0], sw0[1]), pack_bf2(sw0[2], sw0[3]), pack_bf2(sw1[0], sw1[1]),
                                pack_bf2(sw1[2], sw1[3])));
-        const int r0 = tr_base(bw - 16 + 4 * g + jr), r1 = tr_base(bw + 4 * g + jr);
+        const int r0 = band + lane_v, r1 = r0 + 16 * kRow;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
           acc[mb] = mfma32(cat_bf8(tr16(sm.ringV, r0 + 32 * mb), tr16(sm.ringV, r1 + 32 * mb)), bp, acc[mb]);
@@ -548,7 +578,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
 #pragma unroll
         for (int e = 0; e < NC; e += 2) {
           const bf16x8 bp = diag_block(pack_bf2(s_ent[e], s_ent[e + 1]), sel);
-          const int ra = tr_base(bw - a.dist[e] + 4 * g + jr), rb = tr_base(bw - a.dist[e + 1] + 4 * g + jr);
+          const int ra = row_off(bw - a.dist[e]) + lane_v, rb = row_off(bw - a.dist[e + 1]) + lane_v;
 #pragma unroll
           for (int mb = 0; mb < 4; ++mb)
             acc[mb] = mfma32(cat_bf8(tr16(sm.ringV, ra + 32 * mb), tr16(sm.ringV, rb + 32 * mb)), bp, acc[mb]);
@@ -559,7 +589,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
         for (int e = 0; e < NC; ++e) {
           const float p = s_ent[e];
           const bf16x8 bp = diag_block(pack_bf2(p * (1.f - a.w[e]), p * a.w[e]), sel);
-          const int ra = tr_base(bw - a.dist[e] + 4 * g + jr), rb = tr_base(bw - a.dist[e] + 1 + 4 * g + jr);
+          const int ra = row_off(bw - a.dist[e]) + lane_v, rb = ra + kRow;
 #pragma unroll
           for (int mb = 0; mb < 4; ++mb)
             acc[mb] = mfma32(cat_bf8(tr16(sm.ringV, ra + 32 * mb), tr16(sm.ringV, rb + 32 * mb)), bp, acc[mb]);
@@ -571,7 +601,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
       if (iq < s1) {
         const float lnorm = accn[0] + lnorm_far;
         const float inv = 1.f / lnorm;
-        bf16_t* op = a.o + hoff + (int64_t)iq * kD + 8 * g;
+        bf16_t* op = a.o + hoff + (int64_t)i0w * kD + lane_off;
         uint4 x0, x1;
         x0.x = pack_bf2(acc[0][0] * inv, acc[0][1] * inv);
         x0.y = pack_bf2(acc[0][2] * inv, acc[0][3] * inv);
@@ -583,39 +613,59 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
         x1.w = pack_bf2(acc[3][2] * inv, acc[3][3] * inv);
         *reinterpret_cast<uint4*>(op) = x0;
         *reinterpret_cast<uint4*>(op + kHalf) = x1;
-        if (g == 0 && a.lse != nullptr) a.lse[(size_t)head * N + iq] = (m + log2f(lsum)) * 0.69314718055994530942f;
+        if (g == 0 && a.lse != nullptr) (a.lse + (size_t)head * N + i0w)[n] = (m + log2f(lsum)) * 0.69314718055994530942f;
       }
     }
     __syncthreads();
   }
 }
 
-// waves per workgroup: 8 (two per SIMD) where the registers fit, else 4
-int waves_for(int mode) { return mode == 0 ? 8 : 4; }
-
-// Entries usable by some query (distance < N), split into the ring-covered prefix and the far
-// rest (the table is sorted by distance in both modes).
-void split_table(const FwdArgs& f, int* n_cov, int* n_far) {
+// Entries usable by some query (distance < N), split into the ring-covered prefix (distance
+// <= the ring reach of a workgroup of `waves` waves) and the far rest (the table is sorted by
+// distance in both modes).
+void split_table(const FwdArgs& f, int waves, int* n_cov, int* n_far) {
   int n = 0;
   while (n < f.tab.n && f.tab.dist[n] < f.N) ++n;
-  const int cov_max = max_cov(waves_for(f.mode));
+  const int cov_max = max_cov(waves);
   int cov = 0;
   while (cov < n && f.tab.dist[cov] <= cov_max) ++cov;
   *n_cov = cov;
   *n_far = n - cov;
 }
 
+// Waves per workgroup and the table split: 8 waves (two per SIMD) where the registers fit
+// 256 per lane, else 4 (interpolated mode with many far entries: their row pairs need twice
+// the registers).
+int plan(const FwdArgs& f, int* n_cov, int* n_far) {
+  split_table(f, 8, n_cov, n_far);
+  if (f.mode == 1 && (*n_far > 3 || (*n_far == 3 && *n_cov > 8))) {
+    split_table(f, 4, n_cov, n_far);
+    return 4;
+  }
+  return 8;
+}
+
+// instances that plan() never picks (they would not fit 256 registers at 8 waves)
+template <int MODE, int NC, int NF, int WAVES>
+constexpr bool unused_instance() {
+  return MODE == 1 && WAVES == 8 && (NF > 3 || (NF == 3 && NC > 8));
+}
+
 template <int MODE, int NC, int NF, int WAVES>
 hipError_t launch(const RingArgs& a, unsigned blocks, hipStream_t s) {
+  if constexpr (unused_instance<MODE, NC, NF, WAVES>()) {
+    return hipErrorInvalidValue;
+  } else {
   const size_t smem = sizeof(Smem);
   hipError_t e = hipFuncSetAttribute((const void*)fwd_ring_kernel<MODE, NC, NF, WAVES>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
   fwd_ring_kernel<MODE, NC, NF, WAVES><<<blocks, 64 * WAVES, smem, s>>>(a);
   return hipGetLastError();
+  }
 }
 
-// kernel instance by (covered entries rounded up to 8 or 16, far entries)
+// kernel instance by (covered entries rounded up to 8 or 16, far entries, waves)
 template <int MODE, int WAVES>
 hipError_t launch_mode(const RingArgs& a, int n_far, unsigned blocks, hipStream_t s) {
   if (a.n_cov <= 8) {
@@ -641,7 +691,7 @@ hipError_t launch_mode(const RingArgs& a, int n_far, unsigned blocks, hipStream_
 bool fwd_ring_supported(const FwdArgs& f) {
   if (f.dtype != 1 || f.W > kMaxBand || f.N > (1LL << 30)) return false;
   int cov, far;
-  split_table(f, &cov, &far);
+  plan(f, &cov, &far);
   return far <= kMaxFar && cov <= kMaxCov;
 }
 
@@ -655,7 +705,7 @@ hipError_t launch_fwd_ring(const FwdArgs& f) {
   a.N = (int)f.N;
   a.W = f.W;
   int n_far;
-  split_table(f, &a.n_cov, &n_far);
+  const int waves = plan(f, &a.n_cov, &n_far);
   for (int e = 0; e < kMaxCov; ++e) {
     // slots past the covered prefix get a harmless in-ring distance and weight 0
     a.dist[e] = e < a.n_cov ? f.tab.dist[e] : kMaxBand;
@@ -671,7 +721,7 @@ hipError_t launch_fwd_ring(const FwdArgs& f) {
     if (f.mode == 1) a.unc_dist[u++] = a.far_dist[x] - 1;
   }
   for (; u < kMaxUnc; ++u) a.unc_dist[u] = 0;
-  const int kT = step_rows(waves_for(f.mode));
+  const int kT = step_rows(waves);
   // rows before a segment start that the ring must hold: the band and the covered distances
   int need = kMaxBand;
   for (int e = 0; e < a.n_cov; ++e) need = f.tab.dist[e] > need ? f.tab.dist[e] : need;
@@ -692,6 +742,7 @@ hipError_t launch_fwd_ring(const FwdArgs& f) {
   a.rope = f.rope;
   const unsigned blocks = (unsigned)(segs * f.BH);
   if (f.mode == 0) return launch_mode<0, 8>(a, n_far, blocks, f.stream);
+  if (waves == 8) return launch_mode<1, 8>(a, n_far, blocks, f.stream);
   return launch_mode<1, 4>(a, n_far, blocks, f.stream);
 }
 
