@@ -53,6 +53,7 @@ constexpr int kMaxBand = 16;          // window band rows before a 16-query bloc
 constexpr int kMaxCov = 16;           // table entries served from the ring
 constexpr int kMaxFar = 4;            // table entries served from global memory
 constexpr int kMaxUnc = 2 * kMaxFar;  // their distances (interpolated: c and c - 1)
+constexpr int kBlocksTarget = 512;    // workgroups per launch to aim for (256 CUs)
 
 struct RingArgs {
   const bf16_t* q;
@@ -64,7 +65,7 @@ struct RingArgs {
   int W;
   int n_cov;        // entries served from the ring (a prefix of the table)
   int early_rows;   // steps whose rows start below this need the position checks
-  int seg_len;      // rows per workgroup (multiple of the step)
+  int seg_len;      // rows per segment (multiple of the step)
   int segs;         // segments per head
   int warm;         // rows inserted before the segment start (multiple of the step)
   float scale_log2;
@@ -85,6 +86,7 @@ struct __align__(16) Smem {
   uint8_t ringV[(kP + kMirror) * kRow];
   float2 unc_cs[kMaxUnc][kHalf];
   float2 base_cs[2][kHalf];
+  float2 warm_cs[8][kHalf];  // step bases of the warm-up rows
 };
 
 // byte offset of ring row `row` (any integer, negative rows included: slots are row mod kP);
@@ -285,64 +287,19 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
   const int jr = n >> 2;  // transpose-read row within a 4-row group
   const int jc = n & 3;   // transpose-read 4-column group
 
-  const int64_t head = blockIdx.x / a.segs;
-  const int seg = blockIdx.x % a.segs;
   const int N = a.N;
-  const int s0 = seg * a.seg_len;
-  const int s1 = s0 + a.seg_len < N ? s0 + a.seg_len : N;
-  const size_t hoff = (size_t)head * (size_t)N * kD;
-  const bf16_t* Qh = a.q + hoff;
-  const bf16_t* Kh = a.k + hoff;
-  const bf16_t* Vh = a.v + hoff;
-
-  // ---- set-up: zero the ring, cos/sin of the far distances and of the first step base
+  // ---- per-launch set-up: cos/sin of the far distances; per-lane rotation by t = 16 wave + n
+  // (the row's offset from a step base)
   {
-    uint4* z = reinterpret_cast<uint4*>(sm.ringK);
-    const int n16 = (2 * (kP + kMirror) * kRow) / 16;
-    for (int x = tid; x < n16; x += kThreads) z[x] = make_uint4(0, 0, 0, 0);
     constexpr int n_unc = MODE == 1 ? 2 * NF : NF;
     for (int x = tid; x < n_unc * kHalf; x += kThreads) {
       const int u = x / kHalf, j = x % kHalf;
       sm.unc_cs[u][j] = rope_cs(a.unc_dist[u], a.rope.rev[j]);
     }
   }
-  int p0 = s0 - a.warm > 0 ? s0 - a.warm : 0;
-  if (tid < kHalf) sm.base_cs[0][tid] = rope_cs(p0, a.rope.rev[tid]);
-  // per-lane rotation by t = 16 wave + n (the row's offset from the step base)
   float2 cs_t[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) cs_t[t] = rope_cs(16 * wave + n, a.rope.rev[8 * g + t]);
-  __syncthreads();
-
-  // element offset of the lane's part of a 16-row slab: row n, dims 8g.. (and 32+8g..)
-  const int lane_off = n * kD + 8 * g;
-  // rows this lane inserts: q/k/v dims 8g.. and 32+8g.. of row pb + 16w + n. Rows past the
-  // end repeat row N - 1: only queries past the end read them.
-  auto load_rows = [&](int pb, uint4* q2, uint4* k2, uint4* v2) {
-    const int rb = pb + 16 * wave;
-    int64_t off;
-    if (rb + 15 < N) {
-      off = (int64_t)rb * kD + lane_off;
-    } else {
-      const int r = rb + n < N ? rb + n : N - 1;
-      off = (int64_t)r * kD + 8 * g;
-    }
-    const bf16_t* qp = Qh + off;
-    const bf16_t* kp = Kh + off;
-    const bf16_t* vp = Vh + off;
-    q2[0] = *reinterpret_cast<const uint4*>(qp);
-    q2[1] = *reinterpret_cast<const uint4*>(qp + kHalf);
-    k2[0] = *reinterpret_cast<const uint4*>(kp);
-    k2[1] = *reinterpret_cast<const uint4*>(kp + kHalf);
-    v2[0] = *reinterpret_cast<const uint4*>(vp);
-    v2[1] = *reinterpret_cast<const uint4*>(vp + kHalf);
-  };
-  uint4 pq[2], pk[2], pv[2];
-  load_rows(p0, pq, pk, pv);
-  // far rows of the first computed step (p0 reaches s0 exactly: both are multiples of kT)
-  FarRows<NF> fr;
-  load_far_k<MODE, NF>(fr, a, Kh, s0 + 16 * wave, n, g, lane_off);
-  load_far_v<MODE, NF>(fr, a, Vh, s0 + 16 * wave, n, g, lane_off);
 
   const float sl2 = a.scale_log2;
   // additive masks: window keys by distance (band key kappa of the lane at distance
@@ -374,9 +331,116 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
   // 4g + jr, ring positions 4 jc..)
   const int lane_k = n * kRow + 16 * g;
   const int lane_v = (4 * g + jr) * kRow + 8 * jc;
+  // element offset of the lane's part of a 16-row slab: row n, dims 8g.. (and 32+8g..)
+  const int lane_off = n * kD + 8 * g;
+
+  // stores row rb + n of the lane (rb wave-uniform): K^ as given; V in output order, dims
+  // 8g..8g+3 | 8g+4.. | 32+8g.. | 36+8g.. at ring positions 4g, 16+4g, 32+4g, 48+4g
+  auto put_row = [&](int rb, uint4 kr0, uint4 kr1, uint4 v0, uint4 v1) {
+    const int slot = rb & (kP - 1);
+    auto put = [&](int ro) {
+      uint8_t* kp = sm.ringK + ro + 16 * g;
+      uint8_t* vp = sm.ringV + ro + 8 * g;
+      lds_write16(kp, 0, kr0);
+      lds_write16(kp, 64, kr1);
+      lds_write8(vp, 0, v0.x, v0.y);
+      lds_write8(vp, 32, v0.z, v0.w);
+      lds_write8(vp, 64, v1.x, v1.y);
+      lds_write8(vp, 96, v1.z, v1.w);
+    };
+    put((slot + n) * kRow);
+    if (slot < kMirror) put((slot + kP + n) * kRow);  // mirrored rows are stored twice
+  };
+
+  const int64_t head = blockIdx.x / a.segs;
+  const int seg = blockIdx.x % a.segs;
+  const int s0 = seg * a.seg_len;
+  const int s1 = s0 + a.seg_len < N ? s0 + a.seg_len : N;
+  const size_t hoff = (size_t)head * (size_t)N * kD;
+  const bf16_t* Qh = a.q + hoff;
+  const bf16_t* Kh = a.k + hoff;
+  const bf16_t* Vh = a.v + hoff;
+
+  // rows this lane inserts: q/k/v dims 8g.. and 32+8g.. of row pb + 16w + n. Rows past the
+  // end repeat row N - 1: only queries past the end read them.
+  auto load_rows = [&](int pb, uint4* q2, uint4* k2, uint4* v2) {
+    const int rb = pb + 16 * wave;
+    int64_t off;
+    if (rb + 15 < N) {
+      off = (int64_t)rb * kD + lane_off;
+    } else {
+      const int r = rb + n < N ? rb + n : N - 1;
+      off = (int64_t)r * kD + 8 * g;
+    }
+    const bf16_t* qp = Qh + off;
+    const bf16_t* kp = Kh + off;
+    const bf16_t* vp = Vh + off;
+    q2[0] = *reinterpret_cast<const uint4*>(qp);
+    q2[1] = *reinterpret_cast<const uint4*>(qp + kHalf);
+    k2[0] = *reinterpret_cast<const uint4*>(kp);
+    k2[1] = *reinterpret_cast<const uint4*>(kp + kHalf);
+    v2[0] = *reinterpret_cast<const uint4*>(vp);
+    v2[1] = *reinterpret_cast<const uint4*>(vp + kHalf);
+  };
+
+  // ---- warm-up: ring rows [ws, s0), the band and covered rows of the first steps. Rows
+  // before 0 are never stored: their slots must read as zero (finite, and masked).
+  const int ws = s0 - a.warm > 0 ? s0 - a.warm : 0;
+  const int n_warm = (s0 - ws) / kT;  // whole steps (s0 and the warm-up are step multiples)
+  if (s0 < a.warm) {
+    uint4* z = reinterpret_cast<uint4*>(sm.ringK);
+    const int n16 = (2 * (kP + kMirror) * kRow) / 16;
+    for (int x = tid; x < n16; x += kThreads) z[x] = make_uint4(0, 0, 0, 0);
+  }
+  if (tid < kHalf * (n_warm + 1)) {
+    const int j = tid / kHalf, t = tid % kHalf;
+    if (j < n_warm) sm.warm_cs[j][t] = rope_cs(ws + j * kT, a.rope.rev[t]);
+    else sm.base_cs[0][t] = rope_cs(s0, a.rope.rev[t]);
+  }
+  uint4 pq[2], pk[2], pv[2];
+  load_rows(s0, pq, pk, pv);
+  __syncthreads();
+  {
+    // kWB steps of warm rows in flight at once: K rotated by R_(base + t), V as loaded
+    constexpr int kWB = WAVES == 8 ? 3 : 4;
+    for (int j0 = 0; j0 < n_warm; j0 += kWB) {
+      uint4 wk[kWB][2], wv[kWB][2];
+#pragma unroll
+      for (int jj = 0; jj < kWB; ++jj) {
+        if (j0 + jj < n_warm) {
+          const int64_t off = (int64_t)(ws + (j0 + jj) * kT + 16 * wave) * kD + lane_off;
+          wk[jj][0] = *reinterpret_cast<const uint4*>(Kh + off);
+          wk[jj][1] = *reinterpret_cast<const uint4*>(Kh + off + kHalf);
+          wv[jj][0] = *reinterpret_cast<const uint4*>(Vh + off);
+          wv[jj][1] = *reinterpret_cast<const uint4*>(Vh + off + kHalf);
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < kWB; ++jj) {
+        if (j0 + jj < n_warm) {
+          float2 cs[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const float2 b = sm.warm_cs[j0 + jj][8 * g + t];
+            cs[t] = make_float2(b.x * cs_t[t].x - b.y * cs_t[t].y, b.y * cs_t[t].x + b.x * cs_t[t].y);
+          }
+          float kf[16];
+          unpack8(wk[jj][0], kf);
+          unpack8(wk[jj][1], kf + 8);
+          uint4 kr0, kr1;
+          rotate_pack_f(kf, cs, &kr0, &kr1);
+          put_row(ws + (j0 + jj) * kT + 16 * wave, kr0, kr1, wv[jj][0], wv[jj][1]);
+        }
+      }
+    }
+  }
+  // (the first step's barrier orders these stores before any read of them)
+  // far K rows of the first step (requested after the warm-up rows, whose registers they reuse)
+  FarRows<NF> fr;
+  load_far_k<MODE, NF>(fr, a, Kh, s0 + 16 * wave, n, g, lane_off);
 
   int buf = 0;
-  for (; p0 < s1; p0 += kT, buf ^= 1) {
+  for (int p0 = s0; p0 < s1; p0 += kT, buf ^= 1) {
     // ---- insert rows p0 + 16w + n: rotate K (and Q for this step's queries) by R_(p0 + t)
     float2 cs[8];
 #pragma unroll
@@ -393,58 +457,20 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
     rotate_pack_f(kf, cs, &kr0, &kr1);
     rotate_pack_f(qf, cs, &qh0, &qh1);
     const int bw = p0 + 16 * wave;  // row i0w of this wave's queries
-    {
-      // K^ as loaded; V in output order: dims 8g..8g+3 | 8g+4.. | 32+8g.. | 36+8g.. go to
-      // ring positions 4g, 16+4g, 32+4g, 48+4g
-      const int slot = bw & (kP - 1);
-      auto put = [&](int ro) {
-        uint8_t* kp = sm.ringK + ro + 16 * g;
-        uint8_t* vp = sm.ringV + ro + 8 * g;
-        lds_write16(kp, 0, kr0);
-        lds_write16(kp, 64, kr1);
-        lds_write8(vp, 0, pv[0].x, pv[0].y);
-        lds_write8(vp, 32, pv[0].z, pv[0].w);
-        lds_write8(vp, 64, pv[1].x, pv[1].y);
-        lds_write8(vp, 96, pv[1].z, pv[1].w);
-      };
-      put((slot + n) * kRow);
-      if (slot < kMirror) put((slot + kP + n) * kRow);  // mirrored rows are stored twice
-    }
+    put_row(bw, kr0, kr1, pv[0], pv[1]);
     __syncthreads();
     // next step's rows (the last step loads harmless repeats) and base rotation
     const int pn = p0 + kT;
     load_rows(pn < s1 ? pn : p0, pq, pk, pv);
     if (wave == 0 && l < kHalf) sm.base_cs[buf ^ 1][l] = rope_cs(pn, a.rope.rev[l]);
 
-    if (p0 >= s0) {
+    {
       const int i0w = p0 + 16 * wave;
       const int iq = i0w + n;  // this lane's query
       const bf16x8 bq0 = as_bf8(qh0), bq1 = as_bf8(qh1);
       // keys before position 0 (and table distances longer than the query position) occur
       // only in the first steps of a sequence; afterwards the masks are the fixed biases
       const bool early = i0w < a.early_rows;
-
-      // ---- logits of the far entries first, so their next rows can be requested early
-      float s_far[NF > 0 ? NF : 1];
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const int u = MODE == 1 ? 2 * f : f;
-        uint4 r0, r1;
-        rotate_pack_f(qf, &sm.unc_cs[u][8 * g], &r0, &r1);
-        f4 S = {0, 0, 0, 0};
-        S = mfma32(as_bf8(fr.k[f][0]), as_bf8(r0), S);
-        S = mfma32(as_bf8(fr.k[f][1]), as_bf8(r1), S);
-        float s = sel4(S, l);
-        if (MODE == 1) {
-          rotate_pack_f(qf, &sm.unc_cs[u + 1][8 * g], &r0, &r1);
-          f4 H = {0, 0, 0, 0};
-          H = mfma32(as_bf8(fr.kh[f][0]), as_bf8(r0), H);
-          H = mfma32(as_bf8(fr.kh[f][1]), as_bf8(r1), H);
-          s = fmaf(a.far_w[f], sel4(H, l) - s, s);
-        }
-        s_far[f] = fmaf(s, sl2, bias_diag);
-      }
-      load_far_k<MODE, NF>(fr, a, Kh, i0w + kT, n, g, lane_off);
 
       // ---- window band: keys i0w - 16 + kappa, kappa < 32
       f4 S0 = {0, 0, 0, 0}, S1 = {0, 0, 0, 0};
@@ -479,6 +505,30 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
         for (int e = 0; e < NC; ++e)
           if (e >= a.n_cov) s_ent[e] = -INFINITY;
       }
+
+      // ---- far entries: their K rows were requested at the end of the previous step
+      float s_far[NF > 0 ? NF : 1];
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int u = MODE == 1 ? 2 * f : f;
+        uint4 r0, r1;
+        rotate_pack_f(qf, &sm.unc_cs[u][8 * g], &r0, &r1);
+        f4 S = {0, 0, 0, 0};
+        S = mfma32(as_bf8(fr.k[f][0]), as_bf8(r0), S);
+        S = mfma32(as_bf8(fr.k[f][1]), as_bf8(r1), S);
+        float s = sel4(S, l);
+        if (MODE == 1) {
+          rotate_pack_f(qf, &sm.unc_cs[u + 1][8 * g], &r0, &r1);
+          f4 H = {0, 0, 0, 0};
+          H = mfma32(as_bf8(fr.kh[f][0]), as_bf8(r0), H);
+          H = mfma32(as_bf8(fr.kh[f][1]), as_bf8(r1), H);
+          s = fmaf(a.far_w[f], sel4(H, l) - s, s);
+        }
+        s_far[f] = fmaf(s, sl2, bias_diag);
+      }
+      // their V rows, for the end of this step (K and V rows are never held together)
+      load_far_v<MODE, NF>(fr, a, Vh, i0w, n, g, lane_off);
+
 
       // ---- softmax over the window band and the entries (base-2 logits)
       float sw0[4], sw1[4];
@@ -536,29 +586,6 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
       f4 accn = {0, 0, 0, 0};
       const bf16x8 ones = as_bf8(make_uint4(kOnes, kOnes, kOnes, kOnes));
       float lnorm_far = 0.f;
-      // far entries on VALU first; the weights live in the query's diagonal lane and reach
-      // its other three lanes by ds_bpermute, packed two per dword
-      if (MODE == 0) {
-#pragma unroll
-        for (int f = 0; f < NF; f += 2) {
-          const uint32_t x = pack_bf2(s_far[f], f + 1 < NF ? s_far[f + 1] : 0.f);
-          const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute(diag_addr, (int)x);
-          lnorm_far = dot2(y, kOnes, lnorm_far);
-          far_pv_int(acc, fr.v[f][0], fr.v[f][1], y & 0xffffu, y << 16);
-          if (f + 1 < NF) far_pv_int(acc, fr.v[f + 1][0], fr.v[f + 1][1], y >> 16, y & 0xffff0000u);
-        }
-      } else {
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          const float p = s_far[f];
-          const uint32_t x = pack_bf2(p * (1.f - a.far_w[f]), p * a.far_w[f]);
-          const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute(diag_addr, (int)x);
-          lnorm_far = dot2(y, kOnes, lnorm_far);
-          far_pv_interp(acc, fr.v[f][0], fr.v[f][1], fr.vh[f][0], fr.vh[f][1], y);
-        }
-      }
-      load_far_v<MODE, NF>(fr, a, Vh, i0w + kT, n, g, lane_off);
-
       // transpose reads: lane (jr, jc) of a 16-lane group reads row k0 + jr, ring positions
       // 16 mb + 4 jc .. +3, i.e. bytes 32 mb + 8 jc of the row (k0 = 4g of the slab)
       {
@@ -597,6 +624,28 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
         }
       }
 
+      // far entries on VALU; the weights live in the query's diagonal lane and reach
+      // its other three lanes by ds_bpermute, packed two per dword
+      if (MODE == 0) {
+#pragma unroll
+        for (int f = 0; f < NF; f += 2) {
+          const uint32_t x = pack_bf2(s_far[f], f + 1 < NF ? s_far[f + 1] : 0.f);
+          const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute(diag_addr, (int)x);
+          lnorm_far = dot2(y, kOnes, lnorm_far);
+          far_pv_int(acc, fr.v[f][0], fr.v[f][1], y & 0xffffu, y << 16);
+          if (f + 1 < NF) far_pv_int(acc, fr.v[f + 1][0], fr.v[f + 1][1], y >> 16, y & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const float p = s_far[f];
+          const uint32_t x = pack_bf2(p * (1.f - a.far_w[f]), p * a.far_w[f]);
+          const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute(diag_addr, (int)x);
+          lnorm_far = dot2(y, kOnes, lnorm_far);
+          far_pv_interp(acc, fr.v[f][0], fr.v[f][1], fr.vh[f][0], fr.vh[f][1], y);
+        }
+      }
+
       // ---- epilogue: the lane's dims 8g..8g+7 (acc[0], acc[1]) and 32+8g.. (acc[2], acc[3])
       if (iq < s1) {
         const float lnorm = accn[0] + lnorm_far;
@@ -615,6 +664,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
         *reinterpret_cast<uint4*>(op + kHalf) = x1;
         if (g == 0 && a.lse != nullptr) (a.lse + (size_t)head * N + i0w)[n] = (m + log2f(lsum)) * 0.69314718055994530942f;
       }
+      // far K rows of the next step (the last step loads rows that are never used)
+      load_far_k<MODE, NF>(fr, a, Kh, i0w + kT, n, g, lane_off);
     }
     __syncthreads();
   }
@@ -729,18 +780,19 @@ hipError_t launch_fwd_ring(const FwdArgs& f) {
   int early = kMaxBand;
   for (int e = 0; e < a.n_cov + n_far; ++e) early = f.tab.dist[e] > early ? f.tab.dist[e] : early;
   a.early_rows = early;
-  // segments: about one workgroup per CU in total
+  // Segments: about two workgroups per CU in total (one runs per CU at a time; the second
+  // round evens out the finishing times of the CUs)
   const int64_t tiles = (f.N + kT - 1) / kT;
-  int64_t segs = (256 + f.BH - 1) / f.BH;
+  int64_t segs = (kBlocksTarget + f.BH - 1) / f.BH;
   if (segs > tiles) segs = tiles;
   if (segs < 1) segs = 1;
   const int64_t per = (tiles + segs - 1) / segs;
   segs = (tiles + per - 1) / per;
   a.seg_len = (int)(per * kT);
   a.segs = (int)segs;
+  const unsigned blocks = (unsigned)(segs * f.BH);
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)kD));
   a.rope = f.rope;
-  const unsigned blocks = (unsigned)(segs * f.BH);
   if (f.mode == 0) return launch_mode<0, 8>(a, n_far, blocks, f.stream);
   if (waves == 8) return launch_mode<1, 8>(a, n_far, blocks, f.stream);
   return launch_mode<1, 4>(a, n_far, blocks, f.stream);
