@@ -126,8 +126,8 @@ def cpu_baseline(arrs, B, H, N, W, alpha, base, mode, budget_s):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20, help="untimed steps first (the GPU clocks ramp up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-components", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
@@ -191,9 +191,9 @@ def main():
 
         log("timing interpolated forward and both backwards")
         fwd_interp()
-        ms_interp = time_calls(fwd_interp, max(3, args.steps // 2), 1, stream)
-        ms_bwd_int = time_calls(bwd(INT, o, lse), 3, 1, stream)
-        ms_bwd_interp = time_calls(bwd(INTERP, o2, lse2), 3, 1, stream)
+        ms_interp = time_calls(fwd_interp, args.steps, args.warmup, stream)
+        ms_bwd_int = time_calls(bwd(INT, o, lse), 5, 2, stream)
+        ms_bwd_interp = time_calls(bwd(INTERP, o2, lse2), 5, 2, stream)
         bwd_bytes = rows * (8 * D * 2 + 4)
         components = {
             "fwd_int_ms": round(ms, 4),
