@@ -118,9 +118,85 @@ def cpu_baseline(arrs, B, H, N, W, alpha, base, mode, budget_s):
     t = time.perf_counter()
     O.forward(qs, ks, vs, W, alpha, base, 10000.0, mode, workers=workers)
     dt = time.perf_counter() - t
-    return {"value": heads * N / dt, "unit": "tokens/s", "cores": workers, "kind": "oracle",
-            "sample": f"{heads} of {B * H} heads x N={N} (fp64 NumPy forward, integer mode, process pool)",
-            "seconds": round(dt, 3)}
+    out = {"value": heads * N / dt, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+           "sample": f"{heads} of {B * H} heads x N={N} (fp64 NumPy forward, integer mode, process pool)",
+           "seconds": round(dt, 3), "cpu_model": cpu_model(), "numpy": np.__version__}
+    # backward of the oracle on a bounded sample: one head's sampled rows, timed the same way
+    do = bf16_bits_to_f32(f32_to_bf16_bits(arrs[3][0, 0])).astype(np.float64)
+    rows_b = np.arange(0, min(N, 2048))
+    t = time.perf_counter()
+    O.backward(q[None, None], k[None, None], v[None, None], do[None, None], W, alpha, base, 10000.0, mode, rows=rows_b)
+    dtb = time.perf_counter() - t
+    out["backward"] = {"value": len(rows_b) / dtb, "unit": "tokens/s", "cores": 1,
+                       "sample": f"{len(rows_b)} query rows of one head (fp64 NumPy backward, one process)"}
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def small_configs(dev, stream, args):
+    """The smaller measured workloads, timed the same way (launch- and tail-bound at these sizes):
+    the 4x-extrapolation shape B4 H8 N4096 (integer forward, 16 coprime-schedule layers), and
+    the training shape B8 H8 N1024 (integer forward at the linear schedule's layers,
+    interpolated forward and backward at the learned-dilation alphas)."""
+    import torch
+
+    import fibonacci_offset_dilated_amd as F
+    from fibonacci_offset_dilated_amd.synthetic import seed_for, uniform_alphas
+    from fibonacci_offset_dilated_amd.workloads import (BY_CONFIG, FIB_BASE, INT, INTERP, UNIFORM_ALPHA_RANGE,
+                                                        UNIFORM_ALPHA_SEED)
+
+    def per_layer_us(make, layers):
+        calls = [make(l) for l in layers]
+        for c in calls:
+            c()
+        reps = max(5, args.steps // 5)
+        ms = time_calls(lambda: [c() for c in calls], reps, 2, stream)
+        return ms * 1e3 / len(calls)
+
+    out = {}
+    w4 = BY_CONFIG[4]
+    (q, k, v), _ = make_inputs(w4.B, w4.H, w4.N, seed_for(4, 0, 12, 0), False, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w4.B, w4.H, w4.N), dtype=torch.float32, device=dev)
+    al4 = [F.schedule_alpha(F.SCHED_COPRIME, l, 16) for l in range(16)]
+    us = per_layer_us(lambda l: (lambda: F.fwd(q, k, v, 12, al4[l], FIB_BASE, 10000.0, INT, out=o, lse=lse)), range(16))
+    rows4 = w4.B * w4.H * w4.N
+    out["c4_fwd_int_us_per_layer"] = round(us, 2)
+    out["c4_fwd_int_hbm_frac"] = round(rows4 * (4 * D * 2 + 4) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    del q, k, v, o, lse
+
+    w2 = BY_CONFIG[3]
+    (q, k, v, do), _ = make_inputs(w2.B, w2.H, w2.N, seed_for(3, 0, 12, 0), True, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w2.B, w2.H, w2.N), dtype=torch.float32, device=dev)
+    al2 = [F.schedule_alpha(F.SCHED_LINEAR, l, 16) for l in range(16)]
+    al3 = uniform_alphas(UNIFORM_ALPHA_SEED, 16, *UNIFORM_ALPHA_RANGE)
+    us_int = per_layer_us(lambda l: (lambda: F.fwd(q, k, v, 12, al2[l], FIB_BASE, 10000.0, INT, out=o, lse=lse)),
+                          range(16))
+    us_interp = per_layer_us(lambda l: (lambda: F.fwd(q, k, v, 12, al3[l], FIB_BASE, 10000.0, INTERP, out=o,
+                                                      lse=lse)), range(16))
+    outs = [F.fwd(q, k, v, 12, al3[l], FIB_BASE, 10000.0, INTERP) for l in range(16)]
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dal = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(F.bwd_workspace_size(w2.B, w2.H, w2.N, D, F.BF16, INTERP), dtype=torch.uint8, device=dev)
+    us_bwd = per_layer_us(lambda l: (lambda: F.bwd(q, k, v, outs[l][0], outs[l][1], do, 12, al3[l], FIB_BASE, 10000.0,
+                                                   INTERP, dq=dq, dk=dk, dv=dv, dalpha=dal, workspace=ws)), range(16))
+    rows2 = w2.B * w2.H * w2.N
+    out["b8h8n1024_fwd_int_us_per_layer"] = round(us_int, 2)
+    out["b8h8n1024_fwd_interp_us_per_layer"] = round(us_interp, 2)
+    out["b8h8n1024_interp_over_int"] = round(us_interp / us_int, 3)
+    out["b8h8n1024_bwd_interp_us_per_layer"] = round(us_bwd, 2)
+    out["b8h8n1024_fwd_int_hbm_frac"] = round(rows2 * (4 * D * 2 + 4) / (us_int * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    return out
 
 
 def main():
@@ -205,6 +281,9 @@ def main():
             "bwd_int_hbm_frac": round(bwd_bytes / (ms_bwd_int * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "bwd_interp_hbm_frac": round(bwd_bytes / (ms_bwd_interp * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         }
+
+    if not args.no_components:
+        components["small_configs"] = small_configs(dev, stream, args)
 
     cpu = None
     if not args.no_cpu_baseline:
