@@ -293,13 +293,20 @@ hipError_t run(const BwdArgs& a) {
   float* delta = (float*)a.workspace;
   float* part = delta + ((a.BH * a.N + 63) / 64) * 64;
   dim3 grid((unsigned)blocks), block(256);
-  bwd_query_kernel<T, MODE><<<grid, block, 0, a.stream>>>((const T*)a.q, (const T*)a.k, (const T*)a.v,
-      (const T*)a.o, (const T*)a.dout, a.lse, (T*)a.dq, delta, part, a.N, a.W, a.tab, a.rope, scale, tiles);
+  int64_t n_part = blocks;
+  if (bwdq_ring_supported(a)) {
+    const hipError_t e = launch_bwdq_ring(a, delta, part);
+    if (e != hipSuccess) return e;
+    n_part = bwdq_ring_blocks(a);
+  } else {
+    bwd_query_kernel<T, MODE><<<grid, block, 0, a.stream>>>((const T*)a.q, (const T*)a.k, (const T*)a.v,
+        (const T*)a.o, (const T*)a.dout, a.lse, (T*)a.dq, delta, part, a.N, a.W, a.tab, a.rope, scale, tiles);
+  }
   bwd_key_kernel<T, MODE><<<grid, block, 0, a.stream>>>((const T*)a.q, (const T*)a.k, (const T*)a.v,
       (const T*)a.dout, a.lse, delta, (T*)a.dk, (T*)a.dv, a.N, a.W, a.tab, a.rope, scale, tiles);
   if (a.dalpha != nullptr) {
     if (MODE == 1)
-      dalpha_reduce_kernel<<<1, 256, 0, a.stream>>>(part, blocks, a.dalpha);
+      dalpha_reduce_kernel<<<1, 256, 0, a.stream>>>(part, n_part, a.dalpha);
     else
       store_zero_kernel<<<1, 1, 0, a.stream>>>(a.dalpha);
   }

@@ -1,0 +1,636 @@
+// Query side of the backward pass on the LDS ring (bf16, D = 64, W <= 16, integer and
+// interpolated offsets): dQ, Delta and the per-workgroup partials of d(alpha).
+//
+// Operation ("Depth-Staggered Fibonacci Spacing for Sparse Attention", gist.science summaries
+// of arXiv 2606.28560, Method > Architecture and attention mechanism; the interpolated rows
+// exist so that the Learned schedule of Method > Experimental variables can train alpha):
+// with s = <R_i q_i, key>/sqrt(D), P = exp(s - LSE_i), Delta_i = <dO_i, O_i>,
+// dP = <dO_i, value>, dS = P (dP - Delta_i),
+//   dQ_i = R_i^T sum dS key^ / sqrt(D)           (key^ the rotated key; R_i^T undoes RoPE)
+//   dalpha += -f [dS (s_hi - s_lo) + P <dO_i, v_hi - v_lo>]   (interpolated entries)
+//
+// Design: the forward's ring (fwd_ring.hip) with a second operand set. Per step each wave
+// takes 16 queries; the ring holds K^ and V (both in natural dim order). Logits S^T = K^ Q^T
+// and dP^T = V dO^T on MFMA (window band: 32 keys x 16 queries; a table entry: a 16-row slab
+// whose diagonal is used), P from the stored LSE (no max), dS on VALU, then
+// dQ^T = K^T dS^T on MFMA, K^T read from the ring through the transpose read with addresses
+// chosen so that lane (n, g) accumulates dims 8g..8g+7 and 32+8g..32+8g+7 of query n: the
+// same dims whose RoPE angles it computed for the insert, so it undoes R_i in registers. Far
+// entries (beyond the ring) read raw K and V rows from global memory; their logits use the
+// relative rotation <R_d q, k>, their dP a VALU dot, and their dQ contribution
+// dS R_(-d) k is added in the un-rotated frame.
+#include "ring_common.h"
+
+namespace fib {
+namespace {
+
+using namespace ring;
+
+struct BqArgs {
+  const bf16_t* q;
+  const bf16_t* k;
+  const bf16_t* v;
+  const bf16_t* o;
+  const bf16_t* dout;
+  const float* lse;
+  bf16_t* dq;
+  float* delta;
+  float* dalpha_part;  // one per workgroup (interpolated mode)
+  int N;
+  int W;
+  int n_cov;
+  int early_rows;
+  int seg_len;
+  int segs;
+  int warm;
+  float scale;       // 1 / sqrt(D)
+  float scale_log2;  // scale * log2(e)
+  int dist[kMaxCov];
+  float w[kMaxCov];
+  float f[kMaxCov];
+  int far_dist[kMaxFar];
+  float far_w[kMaxFar];
+  float far_f[kMaxFar];
+  int unc_dist[kMaxUnc];
+  Rope rope;
+};
+
+struct __align__(16) BqSmem {
+  uint8_t ringK[(kP + kMirror) * kRow];
+  uint8_t ringV[(kP + kMirror) * kRow];
+  float2 unc_cs[kMaxUnc][kHalf];
+  float2 base_cs[2][kHalf];
+  float2 warm_cs[8][kHalf];
+  float red[16];
+};
+
+template <int NF>
+struct FarK {
+  uint4 k[NF > 0 ? NF : 1][2];
+  uint4 kh[NF > 0 ? NF : 1][2];
+};
+
+template <int MODE, int NF>
+__device__ __forceinline__ void load_far(FarK<NF>& fr, const BqArgs& a, const bf16_t* X, int i0w, int n, int g,
+                                         int lane_off) {
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const bf16_t* p = X + far_off(a.far_dist[f], i0w, n, g, lane_off);
+    fr.k[f][0] = *reinterpret_cast<const uint4*>(p);
+    fr.k[f][1] = *reinterpret_cast<const uint4*>(p + kHalf);
+    if (MODE == 1) {
+      const bf16_t* r = X + far_off(a.far_dist[f] - 1, i0w, n, g, lane_off);
+      fr.kh[f][0] = *reinterpret_cast<const uint4*>(r);
+      fr.kh[f][1] = *reinterpret_cast<const uint4*>(r + kHalf);
+    }
+  }
+}
+
+// <x, y> over the lane's 16 dims of two packed bf16 rows (fp32 accumulation)
+__device__ __forceinline__ float dot16_bf(uint4 x0, uint4 x1, uint4 y0, uint4 y1) {
+  float s = dot2(x0.x, y0.x, 0.f);
+  s = dot2(x0.y, y0.y, s);
+  s = dot2(x0.z, y0.z, s);
+  s = dot2(x0.w, y0.w, s);
+  s = dot2(x1.x, y1.x, s);
+  s = dot2(x1.y, y1.y, s);
+  s = dot2(x1.z, y1.z, s);
+  return dot2(x1.w, y1.w, s);
+}
+
+// acc (dims 8g+t in lo[t], 32+8g+t in hi[t]) += c * R_(-d) x for a raw packed row x, with
+// cs[t] = (cos, sin) of d * omega_(8g+t)
+__device__ __forceinline__ void add_unrot(float* lo, float* hi, float c, uint4 x0, uint4 x1, const float2* cs) {
+  float xf[16];
+  unpack8(x0, xf);
+  unpack8(x1, xf + 8);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    lo[t] = fmaf(c, xf[t] * cs[t].x + xf[8 + t] * cs[t].y, lo[t]);
+    hi[t] = fmaf(c, xf[8 + t] * cs[t].x - xf[t] * cs[t].y, hi[t]);
+  }
+}
+
+template <int MODE, int NC, int NF, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
+  constexpr int kThreads = 64 * WAVES;
+  constexpr int kT = step_rows(WAVES);
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  BqSmem& sm = *reinterpret_cast<BqSmem*>(smem_raw);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
+  const int n = l & 15;
+  const int g = l >> 4;
+  const bool diag_lane = g == (n >> 2);
+  const int jr = n >> 2;
+  const int jc = n & 3;
+  const int N = a.N;
+  const float log2e = 1.4426950408889634f;
+
+  {
+    constexpr int n_unc = MODE == 1 ? 2 * NF : NF;
+    for (int x = tid; x < n_unc * kHalf; x += kThreads) {
+      const int u = x / kHalf, j = x % kHalf;
+      sm.unc_cs[u][j] = rope_cs(a.unc_dist[u], a.rope.rev[j]);
+    }
+  }
+  float2 cs_t[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) cs_t[t] = rope_cs(16 * wave + n, a.rope.rev[8 * g + t]);
+  const float sl2 = a.scale_log2;
+  float bias0[4], bias1[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int d0 = n + 16 - 4 * g - v, d1 = n - 4 * g - v;
+    bias0[v] = d0 < a.W ? 0.f : -INFINITY;
+    bias1[v] = (d1 >= 0 && d1 < a.W) ? 0.f : -INFINITY;
+  }
+  const float bias_diag = diag_lane ? 0.f : -INFINITY;
+  uint32_t sel[4];
+  {
+    const uint32_t zero = 0x0c0c0c0cu;
+    const uint32_t a_half = (l & 1) ? 0x01000c0cu : 0x0c0c0100u;
+    const uint32_t b_half = (l & 1) ? 0x03020c0cu : 0x0c0c0302u;
+    const bool low = (l & 2) == 0;
+    sel[0] = low ? a_half : zero;
+    sel[1] = low ? zero : a_half;
+    sel[2] = low ? b_half : zero;
+    sel[3] = low ? zero : b_half;
+  }
+  const int diag_addr = 4 * (16 * (n >> 2) + n);
+  const int lane_k = n * kRow + 16 * g;
+  // transpose reads of K^: lane (jr, jc) of group g reads row 4g + jr at dims 8 jc + 4 h +
+  // 32 h2 (output block mb = 2 h2 + h), so output row 4g' + v of block mb is dim
+  // 8g' + 4h + 32h2 + v
+  const int lane_t = (4 * g + jr) * kRow + 16 * jc;
+  const int lane_off = n * kD + 8 * g;
+
+  const int64_t head = blockIdx.x / a.segs;
+  const int seg = blockIdx.x % a.segs;
+  const int s0 = seg * a.seg_len;
+  const int s1 = s0 + a.seg_len < N ? s0 + a.seg_len : N;
+  const size_t hoff = (size_t)head * (size_t)N * kD;
+  const bf16_t* Qh = a.q + hoff;
+  const bf16_t* Kh = a.k + hoff;
+  const bf16_t* Vh = a.v + hoff;
+  const bf16_t* Oh = a.o + hoff;
+  const bf16_t* Dh = a.dout + hoff;
+  const float* Lh = a.lse + (size_t)head * N;
+
+  // stores row rb + n of the lane: K^ and V, both in natural dim order
+  auto put_row = [&](int rb, uint4 k0, uint4 k1, uint4 v0, uint4 v1) {
+    const int slot = rb & (kP - 1);
+    auto put = [&](int ro) {
+      lds_write16(sm.ringK + ro + 16 * g, 0, k0);
+      lds_write16(sm.ringK + ro + 16 * g, 64, k1);
+      lds_write16(sm.ringV + ro + 16 * g, 0, v0);
+      lds_write16(sm.ringV + ro + 16 * g, 64, v1);
+    };
+    put((slot + n) * kRow);
+    if (slot < kMirror) put((slot + kP + n) * kRow);
+  };
+  // element offset of the lane's part of row rb + n (rows past the end repeat row N - 1)
+  auto row_elems = [&](int rb) -> int64_t {
+    if (rb + 15 < N) return (int64_t)rb * kD + lane_off;
+    const int r = rb + n < N ? rb + n : N - 1;
+    return (int64_t)r * kD + 8 * g;
+  };
+  auto load2 = [&](const bf16_t* base, int64_t off, uint4* x) {
+    x[0] = *reinterpret_cast<const uint4*>(base + off);
+    x[1] = *reinterpret_cast<const uint4*>(base + off + kHalf);
+  };
+
+  // ---- warm-up (as in the forward): ring rows [ws, s0)
+  const int ws = s0 - a.warm > 0 ? s0 - a.warm : 0;
+  const int n_warm = (s0 - ws) / kT;
+  if (s0 < a.warm) {
+    uint4* z = reinterpret_cast<uint4*>(sm.ringK);
+    const int n16 = (2 * (kP + kMirror) * kRow) / 16;
+    for (int x = tid; x < n16; x += kThreads) z[x] = make_uint4(0, 0, 0, 0);
+  }
+  if (tid < kHalf * (n_warm + 1)) {
+    const int j = tid / kHalf, t = tid % kHalf;
+    if (j < n_warm) sm.warm_cs[j][t] = rope_cs(ws + j * kT, a.rope.rev[t]);
+    else sm.base_cs[0][t] = rope_cs(s0, a.rope.rev[t]);
+  }
+  uint4 pq[2], pk[2], pv[2], pd[2];
+  float plse;
+  {
+    const int64_t off = row_elems(s0 + 16 * wave);
+    load2(Qh, off, pq);
+    load2(Kh, off, pk);
+    load2(Vh, off, pv);
+    load2(Dh, off, pd);
+    const int r = s0 + 16 * wave + n;
+    plse = Lh[r < N ? r : N - 1];
+  }
+  __syncthreads();
+  {
+    constexpr int kWB = WAVES == 8 ? 3 : 4;
+    for (int j0 = 0; j0 < n_warm; j0 += kWB) {
+      uint4 wk[kWB][2], wv[kWB][2];
+#pragma unroll
+      for (int jj = 0; jj < kWB; ++jj) {
+        if (j0 + jj < n_warm) {
+          const int64_t off = (int64_t)(ws + (j0 + jj) * kT + 16 * wave) * kD + lane_off;
+          load2(Kh, off, wk[jj]);
+          load2(Vh, off, wv[jj]);
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < kWB; ++jj) {
+        if (j0 + jj < n_warm) {
+          float2 cs[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const float2 b = sm.warm_cs[j0 + jj][8 * g + t];
+            cs[t] = make_float2(b.x * cs_t[t].x - b.y * cs_t[t].y, b.y * cs_t[t].x + b.x * cs_t[t].y);
+          }
+          float kf[16];
+          unpack8(wk[jj][0], kf);
+          unpack8(wk[jj][1], kf + 8);
+          uint4 kr0, kr1;
+          rotate_pack_f(kf, cs, &kr0, &kr1);
+          put_row(ws + (j0 + jj) * kT + 16 * wave, kr0, kr1, wv[jj][0], wv[jj][1]);
+        }
+      }
+    }
+  }
+  FarK<NF> fk;
+  load_far<MODE, NF>(fk, a, Kh, s0 + 16 * wave, n, g, lane_off);
+  float dal = 0.f;  // d(alpha) contributions of this lane's queries
+
+  int buf = 0;
+  for (int p0 = s0; p0 < s1; p0 += kT, buf ^= 1) {
+    // ---- insert: K^ and V of rows p0 + 16w + n; rotated Q of the step's queries
+    float2 cs[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float2 b = sm.base_cs[buf][8 * g + t];
+      cs[t] = make_float2(b.x * cs_t[t].x - b.y * cs_t[t].y, b.y * cs_t[t].x + b.x * cs_t[t].y);
+    }
+    float qf[16];
+    uint4 qh0, qh1;
+    {
+      float kf[16];
+      unpack8(pq[0], qf);
+      unpack8(pq[1], qf + 8);
+      unpack8(pk[0], kf);
+      unpack8(pk[1], kf + 8);
+      uint4 kr0, kr1;
+      rotate_pack_f(kf, cs, &kr0, &kr1);
+      rotate_pack_f(qf, cs, &qh0, &qh1);
+      put_row(p0 + 16 * wave, kr0, kr1, pv[0], pv[1]);
+    }
+    const uint4 do0 = pd[0], do1 = pd[1];
+    const float lse2 = plse * log2e;
+    __syncthreads();
+    const int pn = p0 + kT;
+    {
+      const int pr = pn < s1 ? pn : p0;
+      const int64_t off = row_elems(pr + 16 * wave);
+      load2(Qh, off, pq);
+      load2(Kh, off, pk);
+      load2(Vh, off, pv);
+      load2(Dh, off, pd);
+      const int r = pr + 16 * wave + n;
+      plse = Lh[r < N ? r : N - 1];
+    }
+    if (wave == 0 && l < kHalf) sm.base_cs[buf ^ 1][l] = rope_cs(pn, a.rope.rev[l]);
+
+    const int bw = p0 + 16 * wave;
+    const int i0w = bw;
+    const int iq = i0w + n;
+    const bool early = i0w < a.early_rows;
+    // O rows of the step's queries, for Delta (used after the logits)
+    uint4 oo[2];
+    load2(Oh, row_elems(i0w), oo);
+    const bf16x8 bq0 = as_bf8(qh0), bq1 = as_bf8(qh1);
+    const bf16x8 bd0 = as_bf8(do0), bd1 = as_bf8(do1);
+
+    // ---- window band: logits and dP for keys i0w - 16 + kappa
+    const int band = row_off(bw - 16);
+    f4 S0 = {0, 0, 0, 0}, S1 = {0, 0, 0, 0}, D0 = {0, 0, 0, 0}, D1 = {0, 0, 0, 0};
+    {
+      const int sa = band + lane_k;
+      S0 = mfma32(as_bf8(lds_read16(sm.ringK, sa)), bq0, S0);
+      S0 = mfma32(as_bf8(lds_read16(sm.ringK, sa + 64)), bq1, S0);
+      S1 = mfma32(as_bf8(lds_read16(sm.ringK, sa + 16 * kRow)), bq0, S1);
+      S1 = mfma32(as_bf8(lds_read16(sm.ringK, sa + 16 * kRow + 64)), bq1, S1);
+      D0 = mfma32(as_bf8(lds_read16(sm.ringV, sa)), bd0, D0);
+      D0 = mfma32(as_bf8(lds_read16(sm.ringV, sa + 64)), bd1, D0);
+      D1 = mfma32(as_bf8(lds_read16(sm.ringV, sa + 16 * kRow)), bd0, D1);
+      D1 = mfma32(as_bf8(lds_read16(sm.ringV, sa + 16 * kRow + 64)), bd1, D1);
+    }
+    // ---- covered entries: logits and dP (interpolated: lower and upper slab)
+    float s_e[NC], dp_e[NC], sd_e[MODE == 1 ? NC : 1], dd_e[MODE == 1 ? NC : 1];
+#pragma unroll
+    for (int e = 0; e < NC; ++e) {
+      const int sl = row_off(bw - a.dist[e]) + lane_k;
+      f4 S = {0, 0, 0, 0}, P = {0, 0, 0, 0};
+      S = mfma32(as_bf8(lds_read16(sm.ringK, sl)), bq0, S);
+      S = mfma32(as_bf8(lds_read16(sm.ringK, sl + 64)), bq1, S);
+      P = mfma32(as_bf8(lds_read16(sm.ringV, sl)), bd0, P);
+      P = mfma32(as_bf8(lds_read16(sm.ringV, sl + 64)), bd1, P);
+      s_e[e] = sel4(S, l);
+      dp_e[e] = sel4(P, l);
+      if (MODE == 1) {
+        f4 H = {0, 0, 0, 0}, Q = {0, 0, 0, 0};
+        H = mfma32(as_bf8(lds_read16(sm.ringK, sl + kRow)), bq0, H);
+        H = mfma32(as_bf8(lds_read16(sm.ringK, sl + kRow + 64)), bq1, H);
+        Q = mfma32(as_bf8(lds_read16(sm.ringV, sl + kRow)), bd0, Q);
+        Q = mfma32(as_bf8(lds_read16(sm.ringV, sl + kRow + 64)), bd1, Q);
+        sd_e[e] = sel4(H, l) - s_e[e];  // s_hi - s_lo
+        dd_e[e] = sel4(Q, l) - dp_e[e];  // dp_hi - dp_lo
+      }
+    }
+    // ---- far entries: logits (relative RoPE); their V rows for dP are requested now
+    float s_f[NF > 0 ? NF : 1], sd_f[NF > 0 ? NF : 1];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int u = MODE == 1 ? 2 * f : f;
+      uint4 r0, r1;
+      rotate_pack_f(qf, &sm.unc_cs[u][8 * g], &r0, &r1);
+      f4 S = {0, 0, 0, 0};
+      S = mfma32(as_bf8(fk.k[f][0]), as_bf8(r0), S);
+      S = mfma32(as_bf8(fk.k[f][1]), as_bf8(r1), S);
+      s_f[f] = sel4(S, l);
+      if (MODE == 1) {
+        rotate_pack_f(qf, &sm.unc_cs[u + 1][8 * g], &r0, &r1);
+        f4 H = {0, 0, 0, 0};
+        H = mfma32(as_bf8(fk.kh[f][0]), as_bf8(r0), H);
+        H = mfma32(as_bf8(fk.kh[f][1]), as_bf8(r1), H);
+        sd_f[f] = sel4(H, l) - s_f[f];
+      }
+    }
+    FarK<NF> fv;
+    load_far<MODE, NF>(fv, a, Vh, i0w, n, g, lane_off);
+
+    // ---- P, Delta, dS
+    const float dlt = quad_add(dot16_bf(do0, do1, oo[0], oo[1]));
+    float bds[8];  // band dS: sw0 (slab 0) then sw1 (slab 1), per the lane's 4 keys each
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float x0 = fmaf(S0[v], sl2, bias0[v]), x1 = fmaf(S1[v], sl2, bias1[v]);
+      if (early && n + 16 - 4 * g - v > iq) x0 = -INFINITY;
+      const float p0v = ex2(x0 - lse2), p1v = ex2(x1 - lse2);
+      bds[v] = p0v * (D0[v] - dlt);
+      bds[4 + v] = p1v * (D1[v] - dlt);
+    }
+    float dal_step = 0.f;  // this step's d(alpha) terms of the lane's query
+    float ds_e[NC];
+#pragma unroll
+    for (int e = 0; e < NC; ++e) {
+      float s = s_e[e], dp = dp_e[e];
+      if (MODE == 1) {
+        s = fmaf(a.w[e], sd_e[e], s);
+        dp = fmaf(a.w[e], dd_e[e], dp);
+      }
+      float x = fmaf(s, sl2, bias_diag);
+      if (e >= a.n_cov || (early && a.dist[e] > iq)) x = -INFINITY;
+      const float p = ex2(x - lse2);
+      ds_e[e] = p * (dp - dlt);
+      if (MODE == 1) dal_step = fmaf(-a.f[e], ds_e[e] * a.scale * sd_e[e] + p * dd_e[e], dal_step);
+    }
+
+    // ---- dQ^ = K^T dS^T (rotated frame) on MFMA: band, then covered entries
+    f4 acc[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) acc[mb] = f4{0, 0, 0, 0};
+    {
+      const bf16x8 bp = __builtin_bit_cast(
+          bf16x8, make_uint4(pack_bf2(bds[0], bds[1]), pack_bf2(bds[2], bds[3]), pack_bf2(bds[4], bds[5]),
+                             pack_bf2(bds[6], bds[7])));
+      const int r0 = band + lane_t, r1 = r0 + 16 * kRow;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int o = 8 * (mb & 1) + 64 * (mb >> 1);
+        acc[mb] = mfma32(cat_bf8(tr16(sm.ringK, r0 + o), tr16(sm.ringK, r1 + o)), bp, acc[mb]);
+      }
+    }
+    if (MODE == 0) {
+#pragma unroll
+      for (int e = 0; e < NC; e += 2) {
+        const bf16x8 bp = diag_block(pack_bf2(ds_e[e], ds_e[e + 1]), sel);
+        const int ra = row_off(bw - a.dist[e]) + lane_t, rb = row_off(bw - a.dist[e + 1]) + lane_t;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const int o = 8 * (mb & 1) + 64 * (mb >> 1);
+          acc[mb] = mfma32(cat_bf8(tr16(sm.ringK, ra + o), tr16(sm.ringK, rb + o)), bp, acc[mb]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < NC; ++e) {
+        const float ds = ds_e[e];
+        const bf16x8 bp = diag_block(pack_bf2(ds * (1.f - a.w[e]), ds * a.w[e]), sel);
+        const int ra = row_off(bw - a.dist[e]) + lane_t, rb = ra + kRow;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const int o = 8 * (mb & 1) + 64 * (mb >> 1);
+          acc[mb] = mfma32(cat_bf8(tr16(sm.ringK, ra + o), tr16(sm.ringK, rb + o)), bp, acc[mb]);
+        }
+      }
+    }
+    // undo R_i: dims 8g+t (acc[0], acc[1]) pair with 32+8g+t (acc[2], acc[3])
+    float ql[8], qhv[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float x = acc[t >> 2][t & 3], y = acc[2 + (t >> 2)][t & 3];
+      ql[t] = x * cs[t].x + y * cs[t].y;
+      qhv[t] = y * cs[t].x - x * cs[t].y;
+    }
+
+    // ---- far entries: dP on VALU, P from the diagonal lane, dS, dQ in the un-rotated frame
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int u = MODE == 1 ? 2 * f : f;
+      float s = s_f[f];
+      if (MODE == 1) s = fmaf(a.far_w[f], sd_f[f], s);
+      float x = fmaf(s, sl2, bias_diag);
+      if (early && a.far_dist[f] > iq) x = -INFINITY;
+      // P of the query, from its diagonal lane to all four
+      const float p = __uint_as_float(
+          (uint32_t)__builtin_amdgcn_ds_bpermute(diag_addr, (int)__float_as_uint(ex2(x - lse2))));
+      const float dp_lo = quad_add(dot16_bf(do0, do1, fv.k[f][0], fv.k[f][1]));
+      if (MODE == 0) {
+        const float ds = p * (dp_lo - dlt);
+        add_unrot(ql, qhv, ds, fk.k[f][0], fk.k[f][1], &sm.unc_cs[u][8 * g]);
+      } else {
+        const float dp_hi = quad_add(dot16_bf(do0, do1, fv.kh[f][0], fv.kh[f][1]));
+        const float w = a.far_w[f];
+        const float ds = p * (fmaf(w, dp_hi - dp_lo, dp_lo) - dlt);
+        add_unrot(ql, qhv, ds * (1.f - w), fk.k[f][0], fk.k[f][1], &sm.unc_cs[u][8 * g]);
+        add_unrot(ql, qhv, ds * w, fk.kh[f][0], fk.kh[f][1], &sm.unc_cs[u + 1][8 * g]);
+        // the diagonal lane holds s_hi - s_lo of its query
+        if (diag_lane) dal_step = fmaf(-a.far_f[f], ds * a.scale * sd_f[f] + p * (dp_hi - dp_lo), dal_step);
+      }
+    }
+
+    // ---- epilogue: dQ = scale * (the lane's 16 dims), Delta
+    if (iq < s1) {
+      bf16_t* dp = a.dq + hoff + (int64_t)i0w * kD + lane_off;
+      uint4 x0, x1;
+      x0.x = pack_bf2(ql[0] * a.scale, ql[1] * a.scale);
+      x0.y = pack_bf2(ql[2] * a.scale, ql[3] * a.scale);
+      x0.z = pack_bf2(ql[4] * a.scale, ql[5] * a.scale);
+      x0.w = pack_bf2(ql[6] * a.scale, ql[7] * a.scale);
+      x1.x = pack_bf2(qhv[0] * a.scale, qhv[1] * a.scale);
+      x1.y = pack_bf2(qhv[2] * a.scale, qhv[3] * a.scale);
+      x1.z = pack_bf2(qhv[4] * a.scale, qhv[5] * a.scale);
+      x1.w = pack_bf2(qhv[6] * a.scale, qhv[7] * a.scale);
+      *reinterpret_cast<uint4*>(dp) = x0;
+      *reinterpret_cast<uint4*>(dp + kHalf) = x1;
+      if (g == 0) (a.delta + (size_t)head * N + i0w)[n] = dlt;
+      dal += dal_step;  // rows past the segment's end belong to another workgroup
+    }
+    load_far<MODE, NF>(fk, a, Kh, i0w + kT, n, g, lane_off);
+    __syncthreads();
+  }
+  if (MODE == 1) {
+    // d(alpha) partial of the workgroup: fixed-order sums (wave, then across waves)
+    float x = dal;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    if (l == 0) sm.red[wave] = x;
+    __syncthreads();
+    if (tid == 0) {
+      float t = 0.f;
+      for (int w8 = 0; w8 < WAVES; ++w8) t += sm.red[w8];
+      a.dalpha_part[blockIdx.x] = t;
+    }
+  }
+}
+
+// Instances that fit 256 registers per lane, i.e. two waves per SIMD (8 waves); the others
+// run with 4 waves.
+constexpr bool fits8(int mode, int nc, int nf) {
+  return mode == 0 ? !(nc > 8 && nf > 3) : (nf == 0 || (nc <= 8 && nf <= 1));
+}
+
+template <int MODE, int NC, int NF, int WAVES>
+constexpr bool unused_instance() {
+  return WAVES == 8 && !fits8(MODE, NC, NF);
+}
+
+template <int MODE, int NC, int NF, int WAVES>
+hipError_t launch(const BqArgs& a, unsigned blocks, hipStream_t s) {
+  if constexpr (unused_instance<MODE, NC, NF, WAVES>()) {
+    return hipErrorInvalidValue;
+  } else {
+    const size_t smem = sizeof(BqSmem);
+    hipError_t e = hipFuncSetAttribute((const void*)bwdq_ring_kernel<MODE, NC, NF, WAVES>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    bwdq_ring_kernel<MODE, NC, NF, WAVES><<<blocks, 64 * WAVES, smem, s>>>(a);
+    return hipGetLastError();
+  }
+}
+
+template <int MODE, int WAVES>
+hipError_t launch_far(const BqArgs& a, int n_far, unsigned blocks, hipStream_t s) {
+  if (a.n_cov <= 8) {
+    switch (n_far) {
+      case 0: return launch<MODE, 8, 0, WAVES>(a, blocks, s);
+      case 1: return launch<MODE, 8, 1, WAVES>(a, blocks, s);
+      case 2: return launch<MODE, 8, 2, WAVES>(a, blocks, s);
+      case 3: return launch<MODE, 8, 3, WAVES>(a, blocks, s);
+      default: return launch<MODE, 8, 4, WAVES>(a, blocks, s);
+    }
+  }
+  switch (n_far) {
+    case 0: return launch<MODE, 16, 0, WAVES>(a, blocks, s);
+    case 1: return launch<MODE, 16, 1, WAVES>(a, blocks, s);
+    case 2: return launch<MODE, 16, 2, WAVES>(a, blocks, s);
+    case 3: return launch<MODE, 16, 3, WAVES>(a, blocks, s);
+    default: return launch<MODE, 16, 4, WAVES>(a, blocks, s);
+  }
+}
+
+int plan(const BwdArgs& f, int* n_cov, int* n_far) {
+  split_table(f.tab, f.N, 8, n_cov, n_far);
+  if (!fits8(f.mode, *n_cov <= 8 ? 8 : 16, *n_far)) {
+    split_table(f.tab, f.N, 4, n_cov, n_far);
+    return 4;
+  }
+  return 8;
+}
+
+constexpr int kBlocksTarget = 512;
+
+}  // namespace
+
+bool bwdq_ring_supported(const BwdArgs& f) {
+  if (f.dtype != 1 || f.W > kMaxBand || f.N > (1LL << 30)) return false;
+  int cov, far;
+  plan(f, &cov, &far);
+  return far <= kMaxFar && cov <= kMaxCov;
+}
+
+int64_t bwdq_ring_blocks(const BwdArgs& f) {
+  int cov, far;
+  const int kT = step_rows(plan(f, &cov, &far));
+  const int64_t tiles = (f.N + kT - 1) / kT;
+  int64_t segs = (kBlocksTarget + f.BH - 1) / f.BH;
+  if (segs > tiles) segs = tiles;
+  if (segs < 1) segs = 1;
+  const int64_t per = (tiles + segs - 1) / segs;
+  segs = (tiles + per - 1) / per;
+  return segs * f.BH;
+}
+
+hipError_t launch_bwdq_ring(const BwdArgs& f, float* delta, float* part) {
+  BqArgs a;
+  a.q = (const bf16_t*)f.q;
+  a.k = (const bf16_t*)f.k;
+  a.v = (const bf16_t*)f.v;
+  a.o = (const bf16_t*)f.o;
+  a.dout = (const bf16_t*)f.dout;
+  a.lse = f.lse;
+  a.dq = (bf16_t*)f.dq;
+  a.delta = delta;
+  a.dalpha_part = part;
+  a.N = (int)f.N;
+  a.W = f.W;
+  int n_far;
+  const int waves = plan(f, &a.n_cov, &n_far);
+  for (int e = 0; e < kMaxCov; ++e) {
+    a.dist[e] = e < a.n_cov ? f.tab.dist[e] : kMaxBand;
+    a.w[e] = e < a.n_cov ? f.tab.w[e] : 0.f;
+    a.f[e] = e < a.n_cov ? f.tab.f[e] : 0.f;
+  }
+  for (int x = 0; x < kMaxFar; ++x) {
+    a.far_dist[x] = x < n_far ? f.tab.dist[a.n_cov + x] : 0;
+    a.far_w[x] = x < n_far ? f.tab.w[a.n_cov + x] : 0.f;
+    a.far_f[x] = x < n_far ? f.tab.f[a.n_cov + x] : 0.f;
+  }
+  int u = 0;
+  for (int x = 0; x < n_far; ++x) {
+    a.unc_dist[u++] = a.far_dist[x];
+    if (f.mode == 1) a.unc_dist[u++] = a.far_dist[x] - 1;
+  }
+  for (; u < kMaxUnc; ++u) a.unc_dist[u] = 0;
+  const int kT = step_rows(waves);
+  int need = kMaxBand;
+  for (int e = 0; e < a.n_cov; ++e) need = f.tab.dist[e] > need ? f.tab.dist[e] : need;
+  a.warm = ((need + kT - 1) / kT) * kT;
+  int early = kMaxBand;
+  for (int e = 0; e < a.n_cov + n_far; ++e) early = f.tab.dist[e] > early ? f.tab.dist[e] : early;
+  a.early_rows = early;
+  const int64_t blocks = bwdq_ring_blocks(f);
+  a.segs = (int)(blocks / f.BH);
+  const int64_t tiles = (f.N + kT - 1) / kT;
+  a.seg_len = (int)(((tiles + a.segs - 1) / a.segs) * kT);
+  a.scale = (float)(1.0 / sqrt((double)kD));
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)kD));
+  a.rope = f.rope;
+  if (f.mode == 0) {
+    return waves == 8 ? launch_far<0, 8>(a, n_far, (unsigned)blocks, f.stream)
+                      : launch_far<0, 4>(a, n_far, (unsigned)blocks, f.stream);
+  }
+  return waves == 8 ? launch_far<1, 8>(a, n_far, (unsigned)blocks, f.stream)
+                    : launch_far<1, 4>(a, n_far, (unsigned)blocks, f.stream);
+}
+
+}  // namespace fib

@@ -34,25 +34,13 @@
 //    distinct 4-bank groups, so the A-operand reads (16 rows, one 16-byte chunk each) and the
 //    transpose reads (4 rows x 32 bytes per 16 lanes) are conflict-free, and every read of a
 //    row is one base address plus immediate offsets.
-#include "fib_common.h"
-#include "fib_launch.h"
+#include "ring_common.h"
 
 namespace fib {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) float f4;
-typedef __attribute__((ext_vector_type(4))) short s4;
+using namespace ring;
 
-constexpr int kP = 512;               // ring rows (a power of two: slot = row & (kP - 1))
-constexpr int kRow = 144;             // ring row stride in bytes (128 + 16 padding)
-// queries (and ring rows) per step: 16 per wave; the largest distance served from the ring
-constexpr int step_rows(int waves) { return 16 * waves; }
-constexpr int max_cov(int waves) { return kP - step_rows(waves); }
-constexpr int kMaxBand = 16;          // window band rows before a 16-query block
-constexpr int kMaxCov = 16;           // table entries served from the ring
-constexpr int kMaxFar = 4;            // table entries served from global memory
-constexpr int kMaxUnc = 2 * kMaxFar;  // their distances (interpolated: c and c - 1)
 constexpr int kBlocksTarget = 512;    // workgroups per launch to aim for (256 CUs)
 
 struct RingArgs {
@@ -77,10 +65,6 @@ struct RingArgs {
   Rope rope;
 };
 
-// Rows 0..kMirror-1 of the ring are also stored after its end, so that any 32 consecutive
-// ring rows (slots s..s+31, s < kP) are one base address plus constant offsets.
-constexpr int kMirror = 32;
-
 struct __align__(16) Smem {
   uint8_t ringK[(kP + kMirror) * kRow];
   uint8_t ringV[(kP + kMirror) * kRow];
@@ -88,107 +72,6 @@ struct __align__(16) Smem {
   float2 base_cs[2][kHalf];
   float2 warm_cs[8][kHalf];  // step bases of the warm-up rows
 };
-
-// byte offset of ring row `row` (any integer, negative rows included: slots are row mod kP);
-// wave-uniform arguments keep it on the scalar unit
-__device__ __forceinline__ int row_off(int row) { return (row & (kP - 1)) * kRow; }
-
-__device__ __forceinline__ uint4 lds_read16(const uint8_t* base, int off) {
-  return *reinterpret_cast<const uint4*>(base + off);
-}
-__device__ __forceinline__ void lds_write16(uint8_t* base, int off, uint4 x) {
-  *reinterpret_cast<uint4*>(base + off) = x;
-}
-__device__ __forceinline__ void lds_write8(uint8_t* base, int off, uint32_t x, uint32_t y) {
-  *reinterpret_cast<uint2*>(base + off) = make_uint2(x, y);
-}
-
-// LDS transpose read of 4 bf16: lane j (of 16) supplies the address of 4 consecutive
-// elements of row (k0 + j/4); lane i receives rows k0..k0+3 of column i.
-__device__ __forceinline__ s4 tr16(const uint8_t* base, int off) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(base + off));
-}
-
-__device__ __forceinline__ bf16x8 as_bf8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
-__device__ __forceinline__ bf16x8 cat_bf8(s4 a, s4 b) {
-  typedef __attribute__((ext_vector_type(8))) short s8;
-  s8 c = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  return __builtin_bit_cast(bf16x8, c);
-}
-
-__device__ __forceinline__ f4 mfma32(bf16x8 a, bf16x8 b, f4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ void unpack8(uint4 x, float* f) {
-  f[0] = bf_lo(x.x); f[1] = bf_hi(x.x); f[2] = bf_lo(x.y); f[3] = bf_hi(x.y);
-  f[4] = bf_lo(x.z); f[5] = bf_hi(x.z); f[6] = bf_lo(x.w); f[7] = bf_hi(x.w);
-}
-__device__ __forceinline__ uint4 pack8(const float* f) {
-  uint4 x;
-  x.x = pack_bf2(f[0], f[1]); x.y = pack_bf2(f[2], f[3]);
-  x.z = pack_bf2(f[4], f[5]); x.w = pack_bf2(f[6], f[7]);
-  return x;
-}
-
-// rotate the pairs (x[t], x[8 + t]) of 16 unpacked values by cos/sin cs[t]; packed bf16 halves
-__device__ __forceinline__ void rotate_pack_f(const float* x, const float2* cs, uint4* out_lo, uint4* out_hi) {
-  float ra[8], rb[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    ra[t] = x[t] * cs[t].x - x[8 + t] * cs[t].y;
-    rb[t] = x[8 + t] * cs[t].x + x[t] * cs[t].y;
-  }
-  *out_lo = pack8(ra);
-  *out_hi = pack8(rb);
-}
-
-// 2^x on the hardware unit (v_exp_f32); arguments here are <= 0 and results below the
-// normal range are negligible softmax weights
-__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-__device__ __forceinline__ bf16x2 as_bf2(uint32_t x) { return __builtin_bit_cast(bf16x2, x); }
-// c + x.lo * w.lo + x.hi * w.hi on bf16 pairs, fp32 accumulation (v_dot2_f32_bf16)
-__device__ __forceinline__ float dot2(uint32_t x, uint32_t w, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(as_bf2(x), as_bf2(w), c, false);
-}
-
-// select x[l & 3]
-__device__ __forceinline__ float sel4(f4 x, int l) {
-  const float a = (l & 1) ? x[1] : x[0];
-  const float b = (l & 1) ? x[3] : x[2];
-  return (l & 2) ? b : a;
-}
-
-// Reductions over the four lanes of a query (l, l ^ 16, l ^ 32, l ^ 48): each swap exchanges
-// half of two copies of x, after which the pair holds x of both partner lanes.
-__device__ __forceinline__ float quad_max(float x) {
-  const uint32_t u = __float_as_uint(x);
-  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  const uint32_t w = __float_as_uint(x);
-  auto s = __builtin_amdgcn_permlane16_swap(w, w, false, false);
-  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
-}
-__device__ __forceinline__ float quad_add(float x) {
-  const uint32_t u = __float_as_uint(x);
-  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  const uint32_t w = __float_as_uint(x);
-  auto s = __builtin_amdgcn_permlane16_swap(w, w, false, false);
-  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
-}
-
-// Diagonal P^T block of two slabs for the PV MFMA. The B operand of lane (n, g) holds slab-A
-// rows 4g..4g+3 (slots 0-3) and slab-B rows 4g..4g+3 (slots 4-7) for query n; the diagonal
-// weight of query n sits in lane g = n / 4, slot n % 4 (slab A) and 4 + n % 4 (slab B).
-// x packs (weight A, weight B) as bf16 in the query's diagonal lane and zero elsewhere;
-// sel[] are the lane's byte selectors (v_perm_b32) that place x's halves in those slots.
-__device__ __forceinline__ bf16x8 diag_block(uint32_t x, const uint32_t* sel) {
-  return __builtin_bit_cast(bf16x8, make_uint4(__builtin_amdgcn_perm(x, x, sel[0]), __builtin_amdgcn_perm(x, x, sel[1]),
-                                               __builtin_amdgcn_perm(x, x, sel[2]), __builtin_amdgcn_perm(x, x, sel[3])));
-}
 
 // Rows of the far table entries for one step, held in registers and loaded one step ahead:
 // lane (n, g) holds, per far entry, K and V row i0w - d + n, dims 8g..8g+7 and 32+8g..32+8g+7
@@ -201,16 +84,6 @@ struct FarRows {
   uint4 v[NF > 0 ? NF : 1][2];
   uint4 vh[NF > 0 ? NF : 1][2];
 };
-
-// Element offset of the lane's row of a far entry's 16-row slab for the wave's queries
-// i0w.. (row i0w - d + n; far distances exceed the ring reach, so the slab never passes row
-// N - 1). lane_off = n * D + 8 g. A slab that starts before row 0 clamps each lane's row to
-// row 0 (the queries that read rows before it are masked).
-__device__ __forceinline__ int64_t far_off(int d, int i0w, int n, int g, int lane_off) {
-  const int r0 = i0w - d;
-  if (r0 >= 0) return (int64_t)r0 * kD + lane_off;
-  return (int64_t)(r0 + n > 0 ? r0 + n : 0) * kD + 8 * g;
-}
 
 template <int MODE, int NF>
 __device__ __forceinline__ void load_far_k(FarRows<NF>& fr, const RingArgs& a, const bf16_t* Kh, int i0w, int n, int g,
@@ -671,26 +544,13 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
   }
 }
 
-// Entries usable by some query (distance < N), split into the ring-covered prefix (distance
-// <= the ring reach of a workgroup of `waves` waves) and the far rest (the table is sorted by
-// distance in both modes).
-void split_table(const FwdArgs& f, int waves, int* n_cov, int* n_far) {
-  int n = 0;
-  while (n < f.tab.n && f.tab.dist[n] < f.N) ++n;
-  const int cov_max = max_cov(waves);
-  int cov = 0;
-  while (cov < n && f.tab.dist[cov] <= cov_max) ++cov;
-  *n_cov = cov;
-  *n_far = n - cov;
-}
-
 // Waves per workgroup and the table split: 8 waves (two per SIMD) where the registers fit
 // 256 per lane, else 4 (interpolated mode with many far entries: their row pairs need twice
 // the registers).
 int plan(const FwdArgs& f, int* n_cov, int* n_far) {
-  split_table(f, 8, n_cov, n_far);
+  split_table(f.tab, f.N, 8, n_cov, n_far);
   if (f.mode == 1 && (*n_far > 3 || (*n_far == 3 && *n_cov > 8))) {
-    split_table(f, 4, n_cov, n_far);
+    split_table(f.tab, f.N, 4, n_cov, n_far);
     return 4;
   }
   return 8;

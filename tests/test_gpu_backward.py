@@ -79,6 +79,29 @@ def test_backward_edge_shapes(case, mode, dtype):
     check(qkvd, W, np.float32(alpha), base, mode, dtype)
 
 
+# cases aimed at the LDS-ring query-side kernel (bf16, W <= 16): segment edges, ring reach,
+# far entries, partial steps, 4-wave instances
+RING_BWD = [
+    # (B, H, N, W, alpha, base)
+    (1, 1, 10000, 12, 1.5, FIB_BASE),          # many segments, far entries 566/915/1480
+    (1, 3, 5000, 16, 1.0, (1, 2, 512, 513, 700)),  # distances 512 (ring) and 513, 700 (global)
+    (2, 1, 4100, 1, 1.5, POW2_BASE),           # W = 1, far rows up to 3072
+    (1, 2, 70, 6, 0.5, FIB_BASE),              # one partial step
+    (3, 5, 1500, 10, 1.3, FIB_BASE),
+    (1, 1, 2000, 12, 1.0001, (1, 2, 3, 5, 8, 13, 21, 34, 55, 89, 144, 233, 377, 511, 512, 610)),
+]
+
+
+@pytest.mark.parametrize("mode", [INT, INTERP], ids=["int", "interp"])
+@pytest.mark.parametrize("case", RING_BWD,
+                         ids=[f"B{c[0]}H{c[1]}N{c[2]}W{c[3]}a{c[4]}n{len(c[5])}" for c in RING_BWD])
+def test_backward_ring_cases(case, mode):
+    B, H, N, W, alpha, base = case
+    say("bwd ring", case, mode)
+    qkvd = inputs(5000 + N + W, (B, H, N, 64), BF16, with_dout=True)
+    check(qkvd, W, np.float32(alpha), base, mode, BF16)
+
+
 @pytest.fixture(scope="module")
 def long_inputs():
     w = BY_CONFIG[5]
