@@ -302,8 +302,13 @@ hipError_t run(const BwdArgs& a) {
     bwd_query_kernel<T, MODE><<<grid, block, 0, a.stream>>>((const T*)a.q, (const T*)a.k, (const T*)a.v,
         (const T*)a.o, (const T*)a.dout, a.lse, (T*)a.dq, delta, part, a.N, a.W, a.tab, a.rope, scale, tiles);
   }
-  bwd_key_kernel<T, MODE><<<grid, block, 0, a.stream>>>((const T*)a.q, (const T*)a.k, (const T*)a.v,
-      (const T*)a.dout, a.lse, delta, (T*)a.dk, (T*)a.dv, a.N, a.W, a.tab, a.rope, scale, tiles);
+  if (bwdk_ring_supported(a)) {
+    const hipError_t e = launch_bwdk_ring(a, delta);
+    if (e != hipSuccess) return e;
+  } else {
+    bwd_key_kernel<T, MODE><<<grid, block, 0, a.stream>>>((const T*)a.q, (const T*)a.k, (const T*)a.v,
+        (const T*)a.dout, a.lse, delta, (T*)a.dk, (T*)a.dv, a.N, a.W, a.tab, a.rope, scale, tiles);
+  }
   if (a.dalpha != nullptr) {
     if (MODE == 1)
       dalpha_reduce_kernel<<<1, 256, 0, a.stream>>>(part, n_part, a.dalpha);

@@ -1,0 +1,490 @@
+// Key side of the backward pass on an LDS ring (bf16, D = 64, W <= 16, integer offsets):
+// dK and dV.
+//
+// Operation ("Depth-Staggered Fibonacci Spacing for Sparse Attention", gist.science summaries
+// of arXiv 2606.28560, Method > Architecture and attention mechanism): key row j is read by
+// the window queries j..j+W-1 and by query j + r for each table offset r. With
+// P = exp(s - LSE_i), dP = <dO_i, V_j>, dS = P (dP - Delta_i) (Delta from the query side):
+//   dK_j = R_j^T sum_i dS q^_i / sqrt(D),  dV_j = sum_i P dO_i
+// (q^ the rotated query; R_j^T undoes the key's RoPE). Deterministic: each key's sums are
+// formed by one lane group, no atomics.
+//
+// Design: the mirror image of the query side. Per step each wave takes 16 keys (rotated K^ and
+// raw V in registers as MFMA B operands); the LDS ring holds the query rows ahead of them:
+// rotated Q^ and dO, with LSE * log2(e) and Delta in each Q^ row's padding bytes. Logits
+// S^T = Q^ K^T and dP^T = dO V^T on MFMA (window band: 32 queries x 16 keys; an offset: a
+// 16-row query slab whose diagonal is used); dK^T = Q^T dS^T and dV^T = dO^T P^T on MFMA
+// through transpose reads (addressed so that lane (n, g) accumulates dims 8g..8g+7 and
+// 32+8g..32+8g+7 of key n). The ring leads the keys by the largest covered offset: at step
+// p0 it receives the query rows p0 + kLead ... Offsets beyond the ring read raw q and dO rows
+// from global memory and use relative RoPE <R_r q_i, k_j>.
+#include "ring_common.h"
+
+namespace fib {
+namespace {
+
+using namespace ring;
+
+struct BkArgs {
+  const bf16_t* q;
+  const bf16_t* k;
+  const bf16_t* v;
+  const bf16_t* dout;
+  const float* lse;
+  const float* delta;
+  bf16_t* dk;
+  bf16_t* dv;
+  int N;
+  int W;
+  int n_cov;
+  int seg_len;
+  int segs;
+  int lead;  // ring lead: query rows [p0, p0 + lead) are in the ring before step p0 inserts
+  float scale;
+  float scale_log2;
+  int dist[kMaxCov];
+  int far_dist[kMaxFar];
+  Rope rope;
+};
+
+struct __align__(16) BkSmem {
+  uint8_t ringQ[(kP + kMirror) * kRow];  // Q^ rows; bytes 128..135: (LSE * log2 e, Delta)
+  uint8_t ringD[(kP + kMirror) * kRow];  // dO rows
+  float2 unc_cs[kMaxFar][kHalf];
+  float2 base_cs[2][2][kHalf];  // [buffer][keys, queries]
+  float2 warm_cs[8][kHalf];
+};
+
+// raw q and dO rows of the far queries j0 + r + n (row N - 1 past the end; masked), and their
+// LSE * log2 e (+inf past the end) and Delta
+template <int NF>
+struct FarQ {
+  uint4 q[NF > 0 ? NF : 1][2];
+  uint4 d[NF > 0 ? NF : 1][2];
+  float lse2[NF > 0 ? NF : 1];
+  float dlt[NF > 0 ? NF : 1];
+};
+
+template <int NF>
+__device__ __forceinline__ void load_far_q(FarQ<NF>& fq, const BkArgs& a, const bf16_t* Qh, const bf16_t* Dh,
+                                           const float* Lh, const float* Th, int j0, int n, int g, int lane_off) {
+  const float log2e = 1.4426950408889634f;
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int r0 = j0 + a.far_dist[f];
+    int64_t off;
+    int r = r0 + n;
+    if (r0 + 15 < a.N) {
+      off = (int64_t)r0 * kD + lane_off;
+    } else {
+      off = (int64_t)(r < a.N ? r : a.N - 1) * kD + 8 * g;
+    }
+    fq.q[f][0] = *reinterpret_cast<const uint4*>(Qh + off);
+    fq.q[f][1] = *reinterpret_cast<const uint4*>(Qh + off + kHalf);
+    fq.d[f][0] = *reinterpret_cast<const uint4*>(Dh + off);
+    fq.d[f][1] = *reinterpret_cast<const uint4*>(Dh + off + kHalf);
+    const int rc = r < a.N ? r : a.N - 1;
+    fq.lse2[f] = r < a.N ? Lh[rc] * log2e : INFINITY;
+    fq.dlt[f] = Th[rc];
+  }
+}
+
+// <x, y> over the lane's 16 dims of two packed bf16 rows (fp32 accumulation)
+__device__ __forceinline__ float dot16_bf(uint4 x0, uint4 x1, uint4 y0, uint4 y1) {
+  float s = dot2(x0.x, y0.x, 0.f);
+  s = dot2(x0.y, y0.y, s);
+  s = dot2(x0.z, y0.z, s);
+  s = dot2(x0.w, y0.w, s);
+  s = dot2(x1.x, y1.x, s);
+  s = dot2(x1.y, y1.y, s);
+  s = dot2(x1.z, y1.z, s);
+  return dot2(x1.w, y1.w, s);
+}
+
+template <int NC, int NF>
+__global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
+  constexpr int WAVES = 8;
+  constexpr int kThreads = 64 * WAVES;
+  constexpr int kT = step_rows(WAVES);
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  BkSmem& sm = *reinterpret_cast<BkSmem*>(smem_raw);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
+  const int n = l & 15;
+  const int g = l >> 4;
+  const bool diag_lane = g == (n >> 2);
+  const int jr = n >> 2;
+  const int jc = n & 3;
+  const int N = a.N;
+  const float log2e = 1.4426950408889634f;
+
+  for (int x = tid; x < NF * kHalf; x += kThreads) {
+    const int u = x / kHalf, j = x % kHalf;
+    sm.unc_cs[u][j] = rope_cs(a.far_dist[u], a.rope.rev[j]);
+  }
+  float2 cs_t[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) cs_t[t] = rope_cs(16 * wave + n, a.rope.rev[8 * g + t]);
+  const float sl2 = a.scale_log2;
+  // window: query row 4g + v of slab 0 (16 + 4g + v of slab 1) reads key n when
+  // 0 <= row - n < W
+  float bias0[4], bias1[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int d0 = 4 * g + v - n, d1 = 16 + 4 * g + v - n;
+    bias0[v] = (d0 >= 0 && d0 < a.W) ? 0.f : -INFINITY;
+    bias1[v] = d1 < a.W ? 0.f : -INFINITY;
+  }
+  const float bias_diag = diag_lane ? 0.f : -INFINITY;
+  uint32_t sel[4];
+  {
+    const uint32_t zero = 0x0c0c0c0cu;
+    const uint32_t a_half = (l & 1) ? 0x01000c0cu : 0x0c0c0100u;
+    const uint32_t b_half = (l & 1) ? 0x03020c0cu : 0x0c0c0302u;
+    const bool low = (l & 2) == 0;
+    sel[0] = low ? a_half : zero;
+    sel[1] = low ? zero : a_half;
+    sel[2] = low ? b_half : zero;
+    sel[3] = low ? zero : b_half;
+  }
+  const int diag_addr = 4 * (16 * (n >> 2) + n);
+  const int lane_k = n * kRow + 16 * g;
+  // transpose reads: lane (jr, jc) of group g reads row 4g + jr at dims 8 jc + 4 h + 32 h2
+  // (output block mb = 2 h2 + h): output row 4g' + v of block mb is dim 8g' + 4h + 32h2 + v
+  const int lane_t = (4 * g + jr) * kRow + 16 * jc;
+  // the lane's (LSE, Delta) pair of slab row 4g + v is at row_off + lane_lv + v * kRow
+  const int lane_lv = 4 * g * kRow + 128;
+  const int lane_off = n * kD + 8 * g;
+
+  const int64_t head = blockIdx.x / a.segs;
+  const int seg = blockIdx.x % a.segs;
+  const int s0 = seg * a.seg_len;
+  const int s1 = s0 + a.seg_len < N ? s0 + a.seg_len : N;
+  const size_t hoff = (size_t)head * (size_t)N * kD;
+  const bf16_t* Qh = a.q + hoff;
+  const bf16_t* Kh = a.k + hoff;
+  const bf16_t* Vh = a.v + hoff;
+  const bf16_t* Dh = a.dout + hoff;
+  const float* Lh = a.lse + (size_t)head * N;
+  const float* Th = a.delta + (size_t)head * N;
+
+  auto row_elems = [&](int rb) -> int64_t {
+    if (rb + 15 < N) return (int64_t)rb * kD + lane_off;
+    const int r = rb + n < N ? rb + n : N - 1;
+    return (int64_t)r * kD + 8 * g;
+  };
+  auto load2 = [&](const bf16_t* base, int64_t off, uint4* x) {
+    x[0] = *reinterpret_cast<const uint4*>(base + off);
+    x[1] = *reinterpret_cast<const uint4*>(base + off + kHalf);
+  };
+  // query row qb + n into the ring: Q^ (rotated by cs), dO, (LSE log2e, Delta); rows past
+  // the end hold zeros and LSE = +inf (P = 0)
+  auto put_query = [&](int qb, const float2* cs, const uint4* q2, const uint4* d2, float lse, float dlt) {
+    const bool live = qb + n < N;
+    float qf[16];
+    unpack8(q2[0], qf);
+    unpack8(q2[1], qf + 8);
+    uint4 r0, r1;
+    rotate_pack_f(qf, cs, &r0, &r1);
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    const uint4 d0 = live ? d2[0] : z, d1 = live ? d2[1] : z;
+    if (!live) r0 = r1 = z;
+    const float2 ld = live ? make_float2(lse * log2e, dlt) : make_float2(INFINITY, 0.f);
+    const int slot = qb & (kP - 1);
+    auto put = [&](int ro) {
+      lds_write16(sm.ringQ + ro + 16 * g, 0, r0);
+      lds_write16(sm.ringQ + ro + 16 * g, 64, r1);
+      lds_write16(sm.ringD + ro + 16 * g, 0, d0);
+      lds_write16(sm.ringD + ro + 16 * g, 64, d1);
+      if (g == 0) *reinterpret_cast<float2*>(sm.ringQ + ro + 128) = ld;
+    };
+    put((slot + n) * kRow);
+    if (slot < kMirror) put((slot + kP + n) * kRow);
+  };
+  auto compose = [&](float2 b, float2 t) {
+    return make_float2(b.x * t.x - b.y * t.y, b.y * t.x + b.x * t.y);
+  };
+
+  // ---- warm-up: query rows [s0, s0 + lead) (lead is a step multiple)
+  const int n_warm = a.lead / kT;
+  if (tid < kHalf * (n_warm + 2)) {
+    const int j = tid / kHalf, t = tid % kHalf;
+    if (j < n_warm) sm.warm_cs[j][t] = rope_cs(s0 + j * kT, a.rope.rev[t]);
+    else if (j == n_warm) sm.base_cs[0][0][t] = rope_cs(s0, a.rope.rev[t]);
+    else sm.base_cs[0][1][t] = rope_cs(s0 + a.lead, a.rope.rev[t]);
+  }
+  // this step's keys and inserted query rows, prefetched one step ahead
+  uint4 pk[2], pv[2], pq[2], pd[2];
+  float plse, pdlt;
+  auto load_step = [&](int pb) {
+    const int64_t ko = row_elems(pb + 16 * wave);
+    load2(Kh, ko, pk);
+    load2(Vh, ko, pv);
+    const int qb = pb + a.lead + 16 * wave;
+    const int64_t qo = row_elems(qb);
+    load2(Qh, qo, pq);
+    load2(Dh, qo, pd);
+    const int r = qb + n < N ? qb + n : N - 1;
+    plse = Lh[r];
+    pdlt = Th[r];
+  };
+  load_step(s0);
+  __syncthreads();
+  for (int j = 0; j < n_warm; ++j) {
+    const int qb = s0 + j * kT + 16 * wave;
+    uint4 q2[2], d2[2];
+    load2(Qh, row_elems(qb), q2);
+    load2(Dh, row_elems(qb), d2);
+    const int r = qb + n < N ? qb + n : N - 1;
+    float2 cs[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) cs[t] = compose(sm.warm_cs[j][8 * g + t], cs_t[t]);
+    put_query(qb, cs, q2, d2, Lh[r], Th[r]);
+  }
+  FarQ<NF> fq;
+  load_far_q<NF>(fq, a, Qh, Dh, Lh, Th, s0 + 16 * wave, n, g, lane_off);
+
+  int buf = 0;
+  for (int p0 = s0; p0 < s1; p0 += kT, buf ^= 1) {
+    // ---- this step's keys (rotated K^ and raw V; raw K for the far offsets) and the query
+    // rows entering the ring
+    uint4 kh0, kh1;
+    const uint4 kraw0 = pk[0], kraw1 = pk[1], v0 = pv[0], v1 = pv[1];
+    {
+      float2 csk[8], csq[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        csk[t] = compose(sm.base_cs[buf][0][8 * g + t], cs_t[t]);
+        csq[t] = compose(sm.base_cs[buf][1][8 * g + t], cs_t[t]);
+      }
+      float kf[16];
+      unpack8(pk[0], kf);
+      unpack8(pk[1], kf + 8);
+      rotate_pack_f(kf, csk, &kh0, &kh1);
+      put_query(p0 + a.lead + 16 * wave, csq, pq, pd, plse, pdlt);
+    }
+    __syncthreads();
+    const int pn = p0 + kT;
+    load_step(pn < s1 ? pn : p0);
+    if (wave == 0 && l < kHalf) {
+      sm.base_cs[buf ^ 1][0][l] = rope_cs(pn, a.rope.rev[l]);
+      sm.base_cs[buf ^ 1][1][l] = rope_cs(pn + a.lead, a.rope.rev[l]);
+    }
+
+    const int j0 = p0 + 16 * wave;
+    const int jk = j0 + n;  // this lane's key
+    const bf16x8 bk0 = as_bf8(kh0), bk1 = as_bf8(kh1);
+    const bf16x8 bv0 = as_bf8(v0), bv1 = as_bf8(v1);
+    f4 acck[4], accv[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) acck[mb] = accv[mb] = f4{0, 0, 0, 0};
+
+    // ---- window band: query rows j0 + kappa, kappa < 32
+    const int band = row_off(j0);
+    {
+      f4 S0 = {0, 0, 0, 0}, S1 = {0, 0, 0, 0}, D0 = {0, 0, 0, 0}, D1 = {0, 0, 0, 0};
+      const int sa = band + lane_k;
+      S0 = mfma32(as_bf8(lds_read16(sm.ringQ, sa)), bk0, S0);
+      S0 = mfma32(as_bf8(lds_read16(sm.ringQ, sa + 64)), bk1, S0);
+      S1 = mfma32(as_bf8(lds_read16(sm.ringQ, sa + 16 * kRow)), bk0, S1);
+      S1 = mfma32(as_bf8(lds_read16(sm.ringQ, sa + 16 * kRow + 64)), bk1, S1);
+      D0 = mfma32(as_bf8(lds_read16(sm.ringD, sa)), bv0, D0);
+      D0 = mfma32(as_bf8(lds_read16(sm.ringD, sa + 64)), bv1, D0);
+      D1 = mfma32(as_bf8(lds_read16(sm.ringD, sa + 16 * kRow)), bv0, D1);
+      D1 = mfma32(as_bf8(lds_read16(sm.ringD, sa + 16 * kRow + 64)), bv1, D1);
+      float p[8], ds[8];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float2 l0 = *reinterpret_cast<const float2*>(sm.ringQ + band + lane_lv + v * kRow);
+        const float2 l1 = *reinterpret_cast<const float2*>(sm.ringQ + band + lane_lv + (16 + v) * kRow);
+        p[v] = ex2(fmaf(S0[v], sl2, bias0[v]) - l0.x);
+        p[4 + v] = ex2(fmaf(S1[v], sl2, bias1[v]) - l1.x);
+        ds[v] = p[v] * (D0[v] - l0.y);
+        ds[4 + v] = p[4 + v] * (D1[v] - l1.y);
+      }
+      const bf16x8 bp = __builtin_bit_cast(
+          bf16x8, make_uint4(pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]), pack_bf2(p[4], p[5]), pack_bf2(p[6], p[7])));
+      const bf16x8 bs = __builtin_bit_cast(
+          bf16x8,
+          make_uint4(pack_bf2(ds[0], ds[1]), pack_bf2(ds[2], ds[3]), pack_bf2(ds[4], ds[5]), pack_bf2(ds[6], ds[7])));
+      const int r0 = band + lane_t, r1 = r0 + 16 * kRow;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int o = 8 * (mb & 1) + 64 * (mb >> 1);
+        acck[mb] = mfma32(cat_bf8(tr16(sm.ringQ, r0 + o), tr16(sm.ringQ, r1 + o)), bs, acck[mb]);
+        accv[mb] = mfma32(cat_bf8(tr16(sm.ringD, r0 + o), tr16(sm.ringD, r1 + o)), bp, accv[mb]);
+      }
+    }
+    // ---- covered offsets: query slab rows j0 + r + n (diagonal), two offsets per MFMA
+#pragma unroll
+    for (int e = 0; e < NC; e += 2) {
+      float p2[2], ds2[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int sl = row_off(j0 + a.dist[e + h]);
+        f4 S = {0, 0, 0, 0}, P = {0, 0, 0, 0};
+        S = mfma32(as_bf8(lds_read16(sm.ringQ, sl + lane_k)), bk0, S);
+        S = mfma32(as_bf8(lds_read16(sm.ringQ, sl + lane_k + 64)), bk1, S);
+        P = mfma32(as_bf8(lds_read16(sm.ringD, sl + lane_k)), bv0, P);
+        P = mfma32(as_bf8(lds_read16(sm.ringD, sl + lane_k + 64)), bv1, P);
+        // (LSE, Delta) of query row j0 + r + n
+        const float2 ld = *reinterpret_cast<const float2*>(sm.ringQ + sl + n * kRow + 128);
+        float x = fmaf(sel4(S, l), sl2, bias_diag);
+        if (e + h >= a.n_cov) x = -INFINITY;
+        p2[h] = ex2(x - ld.x);
+        ds2[h] = p2[h] * (sel4(P, l) - ld.y);
+      }
+      const bf16x8 bp = diag_block(pack_bf2(p2[0], p2[1]), sel);
+      const bf16x8 bs = diag_block(pack_bf2(ds2[0], ds2[1]), sel);
+      const int ra = row_off(j0 + a.dist[e]) + lane_t, rb = row_off(j0 + a.dist[e + 1]) + lane_t;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int o = 8 * (mb & 1) + 64 * (mb >> 1);
+        acck[mb] = mfma32(cat_bf8(tr16(sm.ringQ, ra + o), tr16(sm.ringQ, rb + o)), bs, acck[mb]);
+        accv[mb] = mfma32(cat_bf8(tr16(sm.ringD, ra + o), tr16(sm.ringD, rb + o)), bp, accv[mb]);
+      }
+    }
+    // undo R_j on dK^: dims 8g+t (acck[0], acck[1]) pair with 32+8g+t (acck[2], acck[3])
+    float kl[8], khv[8], vl[8], vhv[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      // the key's rotation, recomputed (base_cs[buf] stays valid through the step)
+      const float2 c = compose(sm.base_cs[buf][0][8 * g + t], cs_t[t]);
+      const float x = acck[t >> 2][t & 3], y = acck[2 + (t >> 2)][t & 3];
+      kl[t] = x * c.x + y * c.y;
+      khv[t] = y * c.x - x * c.y;
+      vl[t] = accv[t >> 2][t & 3];
+      vhv[t] = accv[2 + (t >> 2)][t & 3];
+    }
+    // ---- far offsets: raw q (rotated by R_r, bf16) and dO rows from global memory; dK and dV
+    // terms on VALU with the bf16 weights (dS, P) of the query's diagonal lane
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      uint4 r0, r1;
+      {
+        float qf[16];
+        unpack8(fq.q[f][0], qf);
+        unpack8(fq.q[f][1], qf + 8);
+        rotate_pack_f(qf, &sm.unc_cs[f][8 * g], &r0, &r1);
+      }
+      f4 S = {0, 0, 0, 0};
+      S = mfma32(as_bf8(r0), as_bf8(kraw0), S);
+      S = mfma32(as_bf8(r1), as_bf8(kraw1), S);
+      const float x = fmaf(sel4(S, l), sl2, bias_diag) - fq.lse2[f];
+      const float p = __uint_as_float((uint32_t)__builtin_amdgcn_ds_bpermute(diag_addr, (int)__float_as_uint(ex2(x))));
+      const float dp = quad_add(dot16_bf(fq.d[f][0], fq.d[f][1], v0, v1));
+      const uint32_t y = pack_bf2(p * (dp - fq.dlt[f]), p);  // (dS, P) in bf16
+      const uint32_t s_lo = y & 0xffffu, s_hi = y << 16, p_lo = y >> 16, p_hi = y & 0xffff0000u;
+      const uint32_t qe[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+      const uint32_t de[8] = {fq.d[f][0].x, fq.d[f][0].y, fq.d[f][0].z, fq.d[f][0].w,
+                              fq.d[f][1].x, fq.d[f][1].y, fq.d[f][1].z, fq.d[f][1].w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        kl[2 * u] = dot2(qe[u], s_lo, kl[2 * u]);
+        kl[2 * u + 1] = dot2(qe[u], s_hi, kl[2 * u + 1]);
+        khv[2 * u] = dot2(qe[4 + u], s_lo, khv[2 * u]);
+        khv[2 * u + 1] = dot2(qe[4 + u], s_hi, khv[2 * u + 1]);
+        vl[2 * u] = dot2(de[u], p_lo, vl[2 * u]);
+        vl[2 * u + 1] = dot2(de[u], p_hi, vl[2 * u + 1]);
+        vhv[2 * u] = dot2(de[4 + u], p_lo, vhv[2 * u]);
+        vhv[2 * u + 1] = dot2(de[4 + u], p_hi, vhv[2 * u + 1]);
+      }
+    }
+    load_far_q<NF>(fq, a, Qh, Dh, Lh, Th, j0 + kT, n, g, lane_off);
+
+    // ---- epilogue: dK = scale * (the lane's dims), dV
+    if (jk < s1) {
+      bf16_t* kp = a.dk + hoff + (int64_t)j0 * kD + lane_off;
+      bf16_t* vp = a.dv + hoff + (int64_t)j0 * kD + lane_off;
+      uint4 x0, x1, y0, y1;
+      x0.x = pack_bf2(kl[0] * a.scale, kl[1] * a.scale);
+      x0.y = pack_bf2(kl[2] * a.scale, kl[3] * a.scale);
+      x0.z = pack_bf2(kl[4] * a.scale, kl[5] * a.scale);
+      x0.w = pack_bf2(kl[6] * a.scale, kl[7] * a.scale);
+      x1.x = pack_bf2(khv[0] * a.scale, khv[1] * a.scale);
+      x1.y = pack_bf2(khv[2] * a.scale, khv[3] * a.scale);
+      x1.z = pack_bf2(khv[4] * a.scale, khv[5] * a.scale);
+      x1.w = pack_bf2(khv[6] * a.scale, khv[7] * a.scale);
+      y0 = pack8(vl);
+      y1 = pack8(vhv);
+      *reinterpret_cast<uint4*>(kp) = x0;
+      *reinterpret_cast<uint4*>(kp + kHalf) = x1;
+      *reinterpret_cast<uint4*>(vp) = y0;
+      *reinterpret_cast<uint4*>(vp + kHalf) = y1;
+    }
+    __syncthreads();
+  }
+}
+
+template <int NC, int NF>
+hipError_t launch(const BkArgs& a, unsigned blocks, hipStream_t s) {
+  const size_t smem = sizeof(BkSmem);
+  hipError_t e = hipFuncSetAttribute((const void*)bwdk_ring_kernel<NC, NF>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)smem);
+  if (e != hipSuccess) return e;
+  bwdk_ring_kernel<NC, NF><<<blocks, 512, smem, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int NC>
+hipError_t launch_far(const BkArgs& a, int n_far, unsigned blocks, hipStream_t s) {
+  switch (n_far) {
+    case 0: return launch<NC, 0>(a, blocks, s);
+    case 1: return launch<NC, 1>(a, blocks, s);
+    case 2: return launch<NC, 2>(a, blocks, s);
+    default: return launch<NC, 3>(a, blocks, s);
+  }
+}
+
+constexpr int kBlocksTarget = 512;
+constexpr int kMaxFarK = 3;  // far offsets whose rows fit the registers at 8 waves
+
+}  // namespace
+
+bool bwdk_ring_supported(const BwdArgs& f) {
+  if (f.dtype != 1 || f.mode != 0 || f.W > kMaxBand || f.N > (1LL << 30)) return false;
+  int cov, far;
+  split_table(f.tab, f.N, 8, &cov, &far);
+  return far <= kMaxFarK && cov <= kMaxCov;
+}
+
+hipError_t launch_bwdk_ring(const BwdArgs& f, const float* delta) {
+  BkArgs a;
+  a.q = (const bf16_t*)f.q;
+  a.k = (const bf16_t*)f.k;
+  a.v = (const bf16_t*)f.v;
+  a.dout = (const bf16_t*)f.dout;
+  a.lse = f.lse;
+  a.delta = delta;
+  a.dk = (bf16_t*)f.dk;
+  a.dv = (bf16_t*)f.dv;
+  a.N = (int)f.N;
+  a.W = f.W;
+  int n_far;
+  split_table(f.tab, f.N, 8, &a.n_cov, &n_far);
+  for (int e = 0; e < kMaxCov; ++e) a.dist[e] = e < a.n_cov ? f.tab.dist[e] : kMaxBand;
+  for (int x = 0; x < kMaxFar; ++x) a.far_dist[x] = x < n_far ? f.tab.dist[a.n_cov + x] : 0;
+  constexpr int kT = step_rows(8);
+  // After step p0's insert the ring holds the query rows [p0 + lead - (kP - kT), p0 + lead + kT);
+  // the step reads rows p0 .. p0 + kT - 1 + max(covered offset, band): lead is the largest
+  // covered offset rounded up to a step (<= kP - kT, the ring reach)
+  int need = kMaxBand;
+  for (int e = 0; e < a.n_cov; ++e) need = f.tab.dist[e] > need ? f.tab.dist[e] : need;
+  a.lead = ((need + kT - 1) / kT) * kT;
+  const int64_t tiles = (f.N + kT - 1) / kT;
+  int64_t segs = (kBlocksTarget + f.BH - 1) / f.BH;
+  if (segs > tiles) segs = tiles;
+  if (segs < 1) segs = 1;
+  const int64_t per = (tiles + segs - 1) / segs;
+  segs = (tiles + per - 1) / per;
+  a.seg_len = (int)(per * kT);
+  a.segs = (int)segs;
+  a.scale = (float)(1.0 / sqrt((double)kD));
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)kD));
+  a.rope = f.rope;
+  const unsigned blocks = (unsigned)(segs * f.BH);
+  return a.n_cov <= 8 ? launch_far<8>(a, n_far, blocks, f.stream) : launch_far<16>(a, n_far, blocks, f.stream);
+}
+
+}  // namespace fib

@@ -53,5 +53,8 @@ hipError_t launch_bwd(const BwdArgs& a);
 bool bwdq_ring_supported(const BwdArgs& a);
 int64_t bwdq_ring_blocks(const BwdArgs& a);
 hipError_t launch_bwdq_ring(const BwdArgs& a, float* delta, float* part);
+// key side on the LDS ring (bf16, integer offsets, W <= 16): dK, dV from Delta
+bool bwdk_ring_supported(const BwdArgs& a);
+hipError_t launch_bwdk_ring(const BwdArgs& a, const float* delta);
 
 }  // namespace fib
