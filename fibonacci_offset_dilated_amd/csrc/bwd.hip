@@ -266,6 +266,100 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(
   Vec8<T>::store(dv + hoff + j * kD + kHalf + 8 * c, avh);
 }
 
+// Key side in interpolated mode when the query side stored each (query, entry)'s P and dS
+// (bf16 pairs in ps[(head * kMaxEnt + e) * N + i]): the window queries are recomputed as in
+// bwd_key_kernel; for table entry e (c, w) row j is the lower row of query j + c (weight
+// 1 - w) and the upper row of query j + c - 1 (weight w), so
+//   dK_j += weight * dS * R_dist q_i / sqrt(D), dV_j += weight * P * dO_i
+// with dist = c or c - 1, and no logit of an interpolated key is recomputed.
+__global__ __launch_bounds__(256) void bwd_key_ps_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const bf16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    const uint32_t* __restrict__ ps, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int64_t N, int W, Table tab,
+    Rope rope, float scale, int tiles) {
+  __shared__ float2 cs[kCsSlots][kHalf];
+  const bool cached = fill_cs(cs, W, tab, 1, rope);
+  const int64_t head = blockIdx.x / tiles;
+  const int tile = blockIdx.x % tiles;
+  const int c = threadIdx.x & 3;
+  const int64_t j = (int64_t)tile * kRPB + (threadIdx.x >> 2);
+  const bool active = j < N;
+  const int64_t jj = active ? j : N - 1;
+  const size_t hoff = (size_t)head * (size_t)N * kD;
+  const bf16_t* qh_ = q + hoff;
+  const bf16_t* kh_ = k + hoff;
+  const bf16_t* vh_ = v + hoff;
+  const bf16_t* doh_ = dout + hoff;
+  const float* lse_h = lse + (size_t)head * N;
+  const float* dlt_h = delta + (size_t)head * N;
+  const float log2e = 1.4426950408889634f;
+  const float sl2 = scale * log2e;
+
+  float kl[8], kh[8], vl[8], vh[8];
+  Vec8<bf16_t>::load(kh_ + jj * kD + 8 * c, kl);
+  Vec8<bf16_t>::load(kh_ + jj * kD + kHalf + 8 * c, kh);
+  Vec8<bf16_t>::load(vh_ + jj * kD + 8 * c, vl);
+  Vec8<bf16_t>::load(vh_ + jj * kD + kHalf + 8 * c, vh);
+
+  float akl[8], akh[8], avl[8], avh[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) akl[t] = akh[t] = avl[t] = avh[t] = 0.f;
+
+  float ql[8], qh[8], dol[8], doh[8], rl[8], rh[8];
+  auto load_query = [&](int64_t i) {
+    Vec8<bf16_t>::load(qh_ + i * kD + 8 * c, ql);
+    Vec8<bf16_t>::load(qh_ + i * kD + kHalf + 8 * c, qh);
+    Vec8<bf16_t>::load(doh_ + i * kD + 8 * c, dol);
+    Vec8<bf16_t>::load(doh_ + i * kD + kHalf + 8 * c, doh);
+  };
+  auto accum = [&](float gk, float gv) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      akl[t] = fmaf(gk, rl[t], akl[t]);
+      akh[t] = fmaf(gk, rh[t], akh[t]);
+      avl[t] = fmaf(gv, dol[t], avl[t]);
+      avh[t] = fmaf(gv, doh[t], avh[t]);
+    }
+  };
+
+  // window queries i = j + s
+  const int64_t wmax = (int64_t)W < N - jj ? (int64_t)W : N - jj;
+  for (int64_t s = 0; s < wmax; ++s) {
+    const int64_t i = jj + s;
+    load_query(i);
+    rotate8(ql, qh, rl, rh, cs, cached, (int)s, s, c, rope);
+    const float sc = quad_sum(dot16(rl, rh, kl, kh));
+    const float p = exp2f(sc * sl2 - lse_h[i] * log2e);
+    const float dp = quad_sum(dot16(dol, doh, vl, vh));
+    accum(p * (dp - dlt_h[i]) * scale, p);
+  }
+  // table entries: stored P and dS of the queries that read row j
+  for (int e = 0; e < tab.n; ++e) {
+    const int64_t d = tab.dist[e];
+    const float w = tab.w[e];
+    const uint32_t* pse = ps + ((size_t)head * kMaxEnt + e) * N;
+    const int64_t i_lo = jj + d;      // row j is its lower row
+    const int64_t i_hi = jj + d - 1;  // row j is its upper row (its lower row j - 1 must exist)
+    if (i_lo < N) {
+      const uint32_t x = pse[i_lo];
+      load_query(i_lo);
+      rotate8(ql, qh, rl, rh, cs, cached, W + e, d, c, rope);
+      accum(bf_hi(x) * scale * (1.f - w), bf_lo(x) * (1.f - w));
+    }
+    if (i_hi < N && jj >= 1) {
+      const uint32_t x = pse[i_hi];
+      load_query(i_hi);
+      rotate8(ql, qh, rl, rh, cs, cached, W + tab.n + e, d - 1, c, rope);
+      accum(bf_hi(x) * scale * w, bf_lo(x) * w);
+    }
+  }
+  if (!active) return;
+  Vec8<bf16_t>::store(dk + hoff + j * kD + 8 * c, akl);
+  Vec8<bf16_t>::store(dk + hoff + j * kD + kHalf + 8 * c, akh);
+  Vec8<bf16_t>::store(dv + hoff + j * kD + 8 * c, avl);
+  Vec8<bf16_t>::store(dv + hoff + j * kD + kHalf + 8 * c, avh);
+}
+
 // Sums n partials in a fixed order (per-thread strided sums, then a tree); writes one float.
 __global__ __launch_bounds__(256) void dalpha_reduce_kernel(const float* __restrict__ part, int64_t n,
                                                             float* __restrict__ out) {
@@ -285,6 +379,14 @@ __global__ void store_zero_kernel(float* out) { *out = 0.f; }
 
 int64_t tiles_of(int64_t N) { return (N + kRPB - 1) / kRPB; }
 
+// Workspace: Delta [BH * N] fp32 (padded to 64 floats), one d(alpha) partial per query-side
+// workgroup (at most BH * tiles_of(N)), 64 spare floats, then, for bf16 inputs in
+// interpolated mode, the (P, dS) bf16 pairs [BH][kMaxEnt][N] (16-byte aligned).
+size_t ps_offset_bytes(int64_t BH, int64_t N) {
+  const size_t floats = (size_t)(((BH * N + 63) / 64) * 64 + BH * tiles_of(N) + 64);
+  return ((floats * sizeof(float) + 15) / 16) * 16;
+}
+
 template <typename T, int MODE>
 hipError_t run(const BwdArgs& a) {
   const int tiles = (int)tiles_of(a.N);
@@ -294,8 +396,10 @@ hipError_t run(const BwdArgs& a) {
   float* part = delta + ((a.BH * a.N + 63) / 64) * 64;
   dim3 grid((unsigned)blocks), block(256);
   int64_t n_part = blocks;
+  uint32_t* ps = nullptr;  // per-(query, entry) P and dS, stored by the ring query side
   if (bwdq_ring_supported(a)) {
-    const hipError_t e = launch_bwdq_ring(a, delta, part);
+    if (MODE == 1) ps = (uint32_t*)((char*)a.workspace + ps_offset_bytes(a.BH, a.N));
+    const hipError_t e = launch_bwdq_ring(a, delta, part, ps);
     if (e != hipSuccess) return e;
     n_part = bwdq_ring_blocks(a);
   } else {
@@ -305,6 +409,9 @@ hipError_t run(const BwdArgs& a) {
   if (bwdk_ring_supported(a)) {
     const hipError_t e = launch_bwdk_ring(a, delta);
     if (e != hipSuccess) return e;
+  } else if (ps != nullptr) {
+    bwd_key_ps_kernel<<<grid, block, 0, a.stream>>>((const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v,
+        (const bf16_t*)a.dout, a.lse, delta, ps, (bf16_t*)a.dk, (bf16_t*)a.dv, a.N, a.W, a.tab, a.rope, scale, tiles);
   } else {
     bwd_key_kernel<T, MODE><<<grid, block, 0, a.stream>>>((const T*)a.q, (const T*)a.k, (const T*)a.v,
         (const T*)a.dout, a.lse, delta, (T*)a.dk, (T*)a.dv, a.N, a.W, a.tab, a.rope, scale, tiles);
@@ -321,10 +428,8 @@ hipError_t run(const BwdArgs& a) {
 }  // namespace
 
 size_t bwd_workspace_bytes(int64_t BH, int64_t N, int dtype, int mode) {
-  (void)dtype;
-  (void)mode;
-  // Delta [BH * N] fp32 (padded to 64 floats) + one dalpha partial per query-side block
-  return (size_t)(((BH * N + 63) / 64) * 64 + BH * tiles_of(N) + 64) * sizeof(float);
+  const size_t base = ps_offset_bytes(BH, N);
+  return dtype == 1 && mode == 1 ? base + (size_t)BH * kMaxEnt * (size_t)N * sizeof(uint32_t) : base;
 }
 
 hipError_t launch_bwd(const BwdArgs& a) {

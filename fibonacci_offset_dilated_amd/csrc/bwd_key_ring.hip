@@ -437,7 +437,6 @@ hipError_t launch_far(const BkArgs& a, int n_far, unsigned blocks, hipStream_t s
   }
 }
 
-constexpr int kBlocksTarget = 512;
 constexpr int kMaxFarK = 3;  // far offsets whose rows fit the registers at 8 waves
 
 }  // namespace
@@ -473,12 +472,8 @@ hipError_t launch_bwdk_ring(const BwdArgs& f, const float* delta) {
   for (int e = 0; e < a.n_cov; ++e) need = f.tab.dist[e] > need ? f.tab.dist[e] : need;
   a.lead = ((need + kT - 1) / kT) * kT;
   const int64_t tiles = (f.N + kT - 1) / kT;
-  int64_t segs = (kBlocksTarget + f.BH - 1) / f.BH;
-  if (segs > tiles) segs = tiles;
-  if (segs < 1) segs = 1;
-  const int64_t per = (tiles + segs - 1) / segs;
-  segs = (tiles + per - 1) / per;
-  a.seg_len = (int)(per * kT);
+  const int64_t segs = ring_segments(f.BH, tiles);
+  a.seg_len = (int)(((tiles + segs - 1) / segs) * kT);
   a.segs = (int)segs;
   a.scale = (float)(1.0 / sqrt((double)kD));
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)kD));

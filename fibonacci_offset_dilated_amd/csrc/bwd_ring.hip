@@ -36,6 +36,7 @@ struct BqArgs {
   bf16_t* dq;
   float* delta;
   float* dalpha_part;  // one per workgroup (interpolated mode)
+  uint32_t* ps;        // interpolated mode: bf16 (P, dS) per [head][entry][query], or null
   int N;
   int W;
   int n_cov;
@@ -380,6 +381,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
     }
     float dal_step = 0.f;  // this step's d(alpha) terms of the lane's query
     float ds_e[NC];
+    uint32_t ps_e[MODE == 1 ? NC : 1];  // interpolated: (P, dS) of each entry, stored at the end
 #pragma unroll
     for (int e = 0; e < NC; ++e) {
       float s = s_e[e], dp = dp_e[e];
@@ -391,7 +393,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
       if (e >= a.n_cov || (early && a.dist[e] > iq)) x = -INFINITY;
       const float p = ex2(x - lse2);
       ds_e[e] = p * (dp - dlt);
-      if (MODE == 1) dal_step = fmaf(-a.f[e], ds_e[e] * a.scale * sd_e[e] + p * dd_e[e], dal_step);
+      if (MODE == 1) {
+        dal_step = fmaf(-a.f[e], ds_e[e] * a.scale * sd_e[e] + p * dd_e[e], dal_step);
+        ps_e[e] = pack_bf2(p, ds_e[e]);
+      }
     }
 
     // ---- dQ^ = K^T dS^T (rotated frame) on MFMA: band, then covered entries
@@ -443,6 +448,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
     }
 
     // ---- far entries: dP on VALU, P from the diagonal lane, dS, dQ in the un-rotated frame
+    uint32_t ps_f[MODE == 1 && NF > 0 ? NF : 1];
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const int u = MODE == 1 ? 2 * f : f;
@@ -465,6 +471,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
         add_unrot(ql, qhv, ds * w, fk.kh[f][0], fk.kh[f][1], &sm.unc_cs[u + 1][8 * g]);
         // the diagonal lane holds s_hi - s_lo of its query
         if (diag_lane) dal_step = fmaf(-a.far_f[f], ds * a.scale * sd_f[f] + p * (dp_hi - dp_lo), dal_step);
+        ps_f[f] = pack_bf2(p, ds);
       }
     }
 
@@ -484,6 +491,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
       *reinterpret_cast<uint4*>(dp + kHalf) = x1;
       if (g == 0) (a.delta + (size_t)head * N + i0w)[n] = dlt;
       dal += dal_step;  // rows past the segment's end belong to another workgroup
+      if (MODE == 1 && a.ps != nullptr && diag_lane) {
+        // (P, dS) per entry, entry-major: the 16 queries of a wave are 64 contiguous bytes
+        uint32_t* pq = a.ps + (size_t)head * kMaxEnt * N + iq;
+#pragma unroll
+        for (int e = 0; e < NC; ++e)
+          if (e < a.n_cov) pq[(size_t)e * N] = ps_e[e];
+#pragma unroll
+        for (int f = 0; f < NF; ++f) pq[(size_t)(a.n_cov + f) * N] = ps_f[f];
+      }
     }
     load_far<MODE, NF>(fk, a, Kh, i0w + kT, n, g, lane_off);
     __syncthreads();
@@ -557,7 +573,6 @@ int plan(const BwdArgs& f, int* n_cov, int* n_far) {
   return 8;
 }
 
-constexpr int kBlocksTarget = 512;
 
 }  // namespace
 
@@ -572,15 +587,10 @@ int64_t bwdq_ring_blocks(const BwdArgs& f) {
   int cov, far;
   const int kT = step_rows(plan(f, &cov, &far));
   const int64_t tiles = (f.N + kT - 1) / kT;
-  int64_t segs = (kBlocksTarget + f.BH - 1) / f.BH;
-  if (segs > tiles) segs = tiles;
-  if (segs < 1) segs = 1;
-  const int64_t per = (tiles + segs - 1) / segs;
-  segs = (tiles + per - 1) / per;
-  return segs * f.BH;
+  return ring_segments(f.BH, tiles) * f.BH;
 }
 
-hipError_t launch_bwdq_ring(const BwdArgs& f, float* delta, float* part) {
+hipError_t launch_bwdq_ring(const BwdArgs& f, float* delta, float* part, uint32_t* ps) {
   BqArgs a;
   a.q = (const bf16_t*)f.q;
   a.k = (const bf16_t*)f.k;
@@ -591,6 +601,7 @@ hipError_t launch_bwdq_ring(const BwdArgs& f, float* delta, float* part) {
   a.dq = (bf16_t*)f.dq;
   a.delta = delta;
   a.dalpha_part = part;
+  a.ps = ps;
   a.N = (int)f.N;
   a.W = f.W;
   int n_far;

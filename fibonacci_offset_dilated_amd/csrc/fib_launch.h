@@ -48,11 +48,13 @@ hipError_t launch_index_set(int32_t* out, int64_t N, int W, const Table& tab, in
 
 size_t bwd_workspace_bytes(int64_t BH, int64_t N, int dtype, int mode);
 hipError_t launch_bwd(const BwdArgs& a);
-// query side of the backward on the LDS ring (bf16, W <= 16): dQ, Delta [BH * N] and one
-// d(alpha) partial per workgroup (bwdq_ring_blocks of them)
+// query side of the backward on the LDS ring (bf16, W <= 16): dQ, Delta [BH * N], one
+// d(alpha) partial per workgroup (bwdq_ring_blocks of them) and, in interpolated mode when ps
+// is not null, each (query, table entry)'s softmax weight P and dS as a bf16 pair in
+// ps[(head * kMaxEnt + entry) * N + query]
 bool bwdq_ring_supported(const BwdArgs& a);
 int64_t bwdq_ring_blocks(const BwdArgs& a);
-hipError_t launch_bwdq_ring(const BwdArgs& a, float* delta, float* part);
+hipError_t launch_bwdq_ring(const BwdArgs& a, float* delta, float* part, uint32_t* ps);
 // key side on the LDS ring (bf16, integer offsets, W <= 16): dK, dV from Delta
 bool bwdk_ring_supported(const BwdArgs& a);
 hipError_t launch_bwdk_ring(const BwdArgs& a, const float* delta);

@@ -41,7 +41,6 @@ namespace {
 
 using namespace ring;
 
-constexpr int kBlocksTarget = 512;    // workgroups per launch to aim for (256 CUs)
 
 struct RingArgs {
   const bf16_t* q;
@@ -640,15 +639,10 @@ hipError_t launch_fwd_ring(const FwdArgs& f) {
   int early = kMaxBand;
   for (int e = 0; e < a.n_cov + n_far; ++e) early = f.tab.dist[e] > early ? f.tab.dist[e] : early;
   a.early_rows = early;
-  // Segments: about two workgroups per CU in total (one runs per CU at a time; the second
-  // round evens out the finishing times of the CUs)
+  // segments per head: see ring_segments
   const int64_t tiles = (f.N + kT - 1) / kT;
-  int64_t segs = (kBlocksTarget + f.BH - 1) / f.BH;
-  if (segs > tiles) segs = tiles;
-  if (segs < 1) segs = 1;
-  const int64_t per = (tiles + segs - 1) / segs;
-  segs = (tiles + per - 1) / per;
-  a.seg_len = (int)(per * kT);
+  const int64_t segs = ring_segments(f.BH, tiles);
+  a.seg_len = (int)(((tiles + segs - 1) / segs) * kT);
   a.segs = (int)segs;
   const unsigned blocks = (unsigned)(segs * f.BH);
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)kD));

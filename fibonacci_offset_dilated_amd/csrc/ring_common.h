@@ -153,5 +153,18 @@ inline void split_table(const Table& tab, int64_t N, int waves, int* n_cov, int*
   *n_far = n - cov;
 }
 
+// Segments per head for a launch of BH heads of `tiles` steps. Long sequences: about 512
+// workgroups (two rounds over the 256 CUs; the second evens out the finishing times). When
+// that would leave fewer than 8 steps per segment, each segment's warm-up (up to 3 steps of
+// ring rows) weighs too much: one round of at most 256 workgroups instead.
+inline int64_t ring_segments(int64_t BH, int64_t tiles) {
+  int64_t segs = (512 + BH - 1) / BH;
+  if ((tiles + segs - 1) / segs < 8) segs = 256 / BH;
+  if (segs > tiles) segs = tiles;
+  if (segs < 1) segs = 1;
+  const int64_t per = (tiles + segs - 1) / segs;
+  return (tiles + per - 1) / per;
+}
+
 }  // namespace ring
 }  // namespace fib
