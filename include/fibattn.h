@@ -122,7 +122,10 @@ int fib_sparse_attn_bwd(const void* q, const void* k, const void* v, const void*
                         float rope_theta, int mode,
                         void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace fib_sparse_attn_bwd needs for these sizes (0 on bad sizes). */
+/* Bytes of device workspace fib_sparse_attn_bwd needs for these sizes (0 on bad sizes):
+ * about 4 bytes per (b, h, n) row for Delta = <dO, O> and the d(alpha) partials, plus, for
+ * bf16 inputs in FIB_INTERP mode, 128 bytes per row in which the query side hands each
+ * (query, table entry) pair's softmax weight and dS (bf16) to the key side. */
 size_t fib_sparse_attn_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D,
                                           int dtype, int mode);
 
