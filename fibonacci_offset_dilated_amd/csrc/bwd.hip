@@ -267,7 +267,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(
 }
 
 // Key side in interpolated mode when the query side stored each (query, entry)'s P and dS
-// (bf16 pairs in ps[(head * kMaxEnt + e) * N + i]): the window queries are recomputed as in
+// (ps_pack words in ps[(head * kMaxEnt + e) * N + i]): the window queries are recomputed as in
 // bwd_key_kernel; for table entry e (c, w) row j is the lower row of query j + c (weight
 // 1 - w) and the upper row of query j + c - 1 (weight w), so
 //   dK_j += weight * dS * R_dist q_i / sqrt(D), dV_j += weight * P * dO_i
@@ -344,13 +344,13 @@ __global__ __launch_bounds__(256) void bwd_key_ps_kernel(
       const uint32_t x = pse[i_lo];
       load_query(i_lo);
       rotate8(ql, qh, rl, rh, cs, cached, W + e, d, c, rope);
-      accum(bf_hi(x) * scale * (1.f - w), bf_lo(x) * (1.f - w));
+      accum(ps_ds(x) * scale * (1.f - w), ps_p(x) * (1.f - w));
     }
     if (i_hi < N && jj >= 1) {
       const uint32_t x = pse[i_hi];
       load_query(i_hi);
       rotate8(ql, qh, rl, rh, cs, cached, W + tab.n + e, d - 1, c, rope);
-      accum(bf_hi(x) * scale * w, bf_lo(x) * w);
+      accum(ps_ds(x) * scale * w, ps_p(x) * w);
     }
   }
   if (!active) return;
@@ -381,7 +381,7 @@ int64_t tiles_of(int64_t N) { return (N + kRPB - 1) / kRPB; }
 
 // Workspace: Delta [BH * N] fp32 (padded to 64 floats), one d(alpha) partial per query-side
 // workgroup (at most BH * tiles_of(N)), 64 spare floats, then, for bf16 inputs in
-// interpolated mode, the (P, dS) bf16 pairs [BH][kMaxEnt][N] (16-byte aligned).
+// interpolated mode, the (P, dS) words (ps_pack) [BH][kMaxEnt][N] (16-byte aligned).
 size_t ps_offset_bytes(int64_t BH, int64_t N) {
   const size_t floats = (size_t)(((BH * N + 63) / 64) * 64 + BH * tiles_of(N) + 64);
   return ((floats * sizeof(float) + 15) / 16) * 16;
@@ -406,8 +406,8 @@ hipError_t run(const BwdArgs& a) {
     bwd_query_kernel<T, MODE><<<grid, block, 0, a.stream>>>((const T*)a.q, (const T*)a.k, (const T*)a.v,
         (const T*)a.o, (const T*)a.dout, a.lse, (T*)a.dq, delta, part, a.N, a.W, a.tab, a.rope, scale, tiles);
   }
-  if (bwdk_ring_supported(a)) {
-    const hipError_t e = launch_bwdk_ring(a, delta);
+  if (bwdk_ring_supported(a) && (MODE == 0 || ps != nullptr)) {
+    const hipError_t e = launch_bwdk_ring(a, delta, ps);
     if (e != hipSuccess) return e;
   } else if (ps != nullptr) {
     bwd_key_ps_kernel<<<grid, block, 0, a.stream>>>((const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v,

@@ -1,5 +1,5 @@
-// Key side of the backward pass on an LDS ring (bf16, D = 64, W <= 16, integer offsets):
-// dK and dV.
+// Key side of the backward pass on an LDS ring (bf16, D = 64, W <= 16, integer and
+// interpolated offsets): dK and dV.
 //
 // Operation ("Depth-Staggered Fibonacci Spacing for Sparse Attention", gist.science summaries
 // of arXiv 2606.28560, Method > Architecture and attention mechanism): key row j is read by
@@ -18,6 +18,15 @@
 // 32+8g..32+8g+7 of key n). The ring leads the keys by the largest covered offset: at step
 // p0 it receives the query rows p0 + kLead ... Offsets beyond the ring read raw q and dO rows
 // from global memory and use relative RoPE <R_r q_i, k_j>.
+//
+// Interpolated offsets: key j is the lower row (weight 1 - w) of query j + c and the upper
+// row (weight w) of query j + c - 1, for each entry (c = ceil(d), w = c - d). The query side
+// has stored each (query, entry)'s P and dS (ps_pack), so no logit of an entry is
+// recomputed here: the two query slabs j0 + c + n and j0 + c - 1 + n pair up in one MFMA per
+// output block with the diagonal weights ((1 - w) dS_lo, w dS_hi) and ((1 - w) P_lo, w P_hi).
+// A far entry's upper query row of key n is the lower row of key n - 1: each lane loads one
+// row, takes its neighbour's with a DPP row shift, and the one row that no lane of the wave
+// holds (j0 + c - 1, for key j0) is loaded spread over the wave, one dword per lane.
 #include "ring_common.h"
 
 namespace fib {
@@ -32,6 +41,7 @@ struct BkArgs {
   const bf16_t* dout;
   const float* lse;
   const float* delta;
+  const uint32_t* ps;  // interpolated: (P, dS) per (query, entry), [head][kMaxEnt][N]
   bf16_t* dk;
   bf16_t* dv;
   int N;
@@ -43,14 +53,16 @@ struct BkArgs {
   float scale;
   float scale_log2;
   int dist[kMaxCov];
+  float w[kMaxCov];
   int far_dist[kMaxFar];
+  float far_w[kMaxFar];
   Rope rope;
 };
 
 struct __align__(16) BkSmem {
   uint8_t ringQ[(kP + kMirror) * kRow];  // Q^ rows; bytes 128..135: (LSE * log2 e, Delta)
   uint8_t ringD[(kP + kMirror) * kRow];  // dO rows
-  float2 unc_cs[kMaxFar][kHalf];
+  float2 unc_cs[kMaxUnc][kHalf];  // far distances (interpolated: c and c - 1)
   float2 base_cs[2][2][kHalf];  // [buffer][keys, queries]
   float2 warm_cs[8][kHalf];
 };
@@ -89,6 +101,57 @@ __device__ __forceinline__ void load_far_q(FarQ<NF>& fq, const BkArgs& a, const 
   }
 }
 
+// Interpolated far entries, per entry: the lower query row j0 + c + n of the lane's key (raw
+// q and dO, the lane's dims), the row j0 + c - 1 spread over the wave (lane l: dword l & 31
+// of q if l < 32, else of dO) and the stored (P, dS) of the key's lower and upper query.
+template <int NF>
+struct FarQI {
+  uint4 q[NF > 0 ? NF : 1][2];
+  uint4 d[NF > 0 ? NF : 1][2];
+  uint32_t ex[NF > 0 ? NF : 1];
+  uint32_t pl[NF > 0 ? NF : 1];
+  uint32_t ph[NF > 0 ? NF : 1];
+};
+
+// loads at a wave-uniform base plus a small per-lane byte offset (the base stays in scalar
+// registers; only the 32-bit offset is per lane)
+__device__ __forceinline__ uint4 ld16(const void* base, uint32_t off) {
+  return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(base) + off);
+}
+__device__ __forceinline__ uint32_t ld4(const void* base, uint32_t off) {
+  return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(base) + off);
+}
+
+template <int NF>
+__device__ __forceinline__ void load_far_qi(FarQI<NF>& fq, const BkArgs& a, const bf16_t* Qh, const bf16_t* Dh,
+                                            const uint32_t* Sh, int n_cov, int j0, int l, int n, int g) {
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int r0 = j0 + a.far_dist[f];
+    // rows past the end repeat row N - 1 (their weights are zero)
+    const int rb = r0 < a.N ? r0 : a.N - 1;
+    const int r = r0 + n;
+    const uint32_t off = (uint32_t)(((r < a.N ? r : a.N - 1) - rb) * kD + 8 * g) * 2u;
+    const bf16_t* qb = Qh + (int64_t)rb * kD;
+    const bf16_t* db = Dh + (int64_t)rb * kD;
+    fq.q[f][0] = ld16(qb, off);
+    fq.q[f][1] = ld16(qb, off + 2 * kHalf);
+    fq.d[f][0] = ld16(db, off);
+    fq.d[f][1] = ld16(db, off + 2 * kHalf);
+    // (no branches here: every load is in bounds, the unused values are selected away)
+    const int re = r0 - 1 < a.N ? r0 - 1 : a.N - 1;
+    const uint32_t eq = ld4(Qh + (int64_t)re * kD, 4u * (uint32_t)(l & 31));
+    const uint32_t ed = ld4(Dh + (int64_t)re * kD, 4u * (uint32_t)(l & 31));
+    fq.ex[f] = l < 32 ? eq : ed;
+    const uint32_t* se = Sh + (size_t)(n_cov + f) * a.N + rb;
+    uint32_t x = ld4(se, (uint32_t)((r < a.N ? r : a.N - 1) - rb) * 4u);
+    uint32_t y = ld4(se - 1, (uint32_t)((r - 1 < a.N ? r - 1 : a.N - 1) - rb + 1) * 4u);
+    asm volatile("" : "+v"(x), "+v"(y));  // keeps the loads unconditional (no branches)
+    fq.pl[f] = r < a.N ? x : 0u;
+    fq.ph[f] = r - 1 < a.N ? y : 0u;
+  }
+}
+
 // <x, y> over the lane's 16 dims of two packed bf16 rows (fp32 accumulation)
 __device__ __forceinline__ float dot16_bf(uint4 x0, uint4 x1, uint4 y0, uint4 y1) {
   float s = dot2(x0.x, y0.x, 0.f);
@@ -101,7 +164,7 @@ __device__ __forceinline__ float dot16_bf(uint4 x0, uint4 x1, uint4 y0, uint4 y1
   return dot2(x1.w, y1.w, s);
 }
 
-template <int NC, int NF>
+template <int MODE, int NC, int NF>
 __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
   constexpr int WAVES = 8;
   constexpr int kThreads = 64 * WAVES;
@@ -119,35 +182,43 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
   const int N = a.N;
   const float log2e = 1.4426950408889634f;
 
-  for (int x = tid; x < NF * kHalf; x += kThreads) {
+  constexpr int n_unc = MODE == 1 ? 2 * NF : NF;
+  for (int x = tid; x < n_unc * kHalf; x += kThreads) {
     const int u = x / kHalf, j = x % kHalf;
-    sm.unc_cs[u][j] = rope_cs(a.far_dist[u], a.rope.rev[j]);
+    const int d = MODE == 1 ? a.far_dist[u >> 1] - (u & 1) : a.far_dist[u];
+    sm.unc_cs[u][j] = rope_cs(d, a.rope.rev[j]);
   }
   float2 cs_t[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) cs_t[t] = rope_cs(16 * wave + n, a.rope.rev[8 * g + t]);
   const float sl2 = a.scale_log2;
-  // window: query row 4g + v of slab 0 (16 + 4g + v of slab 1) reads key n when
-  // 0 <= row - n < W
-  float bias0[4], bias1[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int d0 = 4 * g + v - n, d1 = 16 + 4 * g + v - n;
-    bias0[v] = (d0 >= 0 && d0 < a.W) ? 0.f : -INFINITY;
-    bias1[v] = d1 < a.W ? 0.f : -INFINITY;
-  }
   const float bias_diag = diag_lane ? 0.f : -INFINITY;
-  uint32_t sel[4];
-  {
+  // Lane constants formed anew in every step (a few VALU operations) rather than held in
+  // registers through the loop: the window masks (query row 4g + v of slab 0, 16 + 4g + v of
+  // slab 1, reads key n when 0 <= row - n < W) and the selectors of diag_block. (The empty asm
+  // makes W opaque, so the compiler does not hoist them out of the loop.)
+  auto window_bias = [&](float* bias0, float* bias1) {
+    int Wp = a.W;
+    asm volatile("" : "+s"(Wp));
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int d0 = 4 * g + v - n, d1 = 16 + 4 * g + v - n;
+      bias0[v] = (d0 >= 0 && d0 < Wp) ? 0.f : -INFINITY;
+      bias1[v] = d1 < Wp ? 0.f : -INFINITY;
+    }
+  };
+  auto diag_sel = [&](uint32_t* sel) {
+    int lp = l;
+    asm volatile("" : "+v"(lp));
     const uint32_t zero = 0x0c0c0c0cu;
-    const uint32_t a_half = (l & 1) ? 0x01000c0cu : 0x0c0c0100u;
-    const uint32_t b_half = (l & 1) ? 0x03020c0cu : 0x0c0c0302u;
-    const bool low = (l & 2) == 0;
+    const uint32_t a_half = (lp & 1) ? 0x01000c0cu : 0x0c0c0100u;
+    const uint32_t b_half = (lp & 1) ? 0x03020c0cu : 0x0c0c0302u;
+    const bool low = (lp & 2) == 0;
     sel[0] = low ? a_half : zero;
     sel[1] = low ? zero : a_half;
     sel[2] = low ? b_half : zero;
     sel[3] = low ? zero : b_half;
-  }
+  };
   const int diag_addr = 4 * (16 * (n >> 2) + n);
   const int lane_k = n * kRow + 16 * g;
   // transpose reads: lane (jr, jc) of group g reads row 4g + jr at dims 8 jc + 4 h + 32 h2
@@ -168,6 +239,7 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
   const bf16_t* Dh = a.dout + hoff;
   const float* Lh = a.lse + (size_t)head * N;
   const float* Th = a.delta + (size_t)head * N;
+  const uint32_t* Sh = MODE == 1 ? a.ps + (size_t)head * kMaxEnt * N : nullptr;
 
   auto row_elems = [&](int rb) -> int64_t {
     if (rb + 15 < N) return (int64_t)rb * kD + lane_off;
@@ -217,6 +289,27 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
   // this step's keys and inserted query rows, prefetched one step ahead
   uint4 pk[2], pv[2], pq[2], pd[2];
   float plse, pdlt;
+  // interpolated: the stored (P, dS) of the covered entries' lower and upper query of the
+  // lane's key (in its diagonal lane; zero elsewhere and past the end)
+  uint32_t psl[MODE == 1 ? NC : 1], psh[MODE == 1 ? NC : 1];
+  auto load_ps = [&](int pb) {
+    if constexpr (MODE == 1) {
+      // (no branches: loads at clamped rows, unused values selected away)
+      const int jb = pb + 16 * wave;
+#pragma unroll
+      for (int e = 0; e < NC; ++e) {
+        const int b = jb + a.dist[e] - 1 < N ? jb + a.dist[e] - 1 : N - 1;  // >= 0
+        const int ilo = jb + a.dist[e] + n;
+        const uint32_t* se = Sh + (size_t)e * N + b;
+        uint32_t x = ld4(se, (uint32_t)((ilo < N ? ilo : N - 1) - b) * 4u);
+        uint32_t y = ld4(se, (uint32_t)((ilo - 1 < N ? ilo - 1 : N - 1) - b) * 4u);
+        asm volatile("" : "+v"(x), "+v"(y));  // keeps the loads unconditional (no branches)
+        const bool use = diag_lane && e < a.n_cov;
+        psl[e] = use && ilo < N ? x : 0u;
+        psh[e] = use && ilo - 1 < N ? y : 0u;
+      }
+    }
+  };
   auto load_step = [&](int pb) {
     const int64_t ko = row_elems(pb + 16 * wave);
     load2(Kh, ko, pk);
@@ -230,6 +323,7 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
     pdlt = Th[r];
   };
   load_step(s0);
+  load_ps(s0);
   __syncthreads();
   for (int j = 0; j < n_warm; ++j) {
     const int qb = s0 + j * kT + 16 * wave;
@@ -242,8 +336,12 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
     for (int t = 0; t < 8; ++t) cs[t] = compose(sm.warm_cs[j][8 * g + t], cs_t[t]);
     put_query(qb, cs, q2, d2, Lh[r], Th[r]);
   }
-  FarQ<NF> fq;
-  load_far_q<NF>(fq, a, Qh, Dh, Lh, Th, s0 + 16 * wave, n, g, lane_off);
+  FarQ<MODE == 0 ? NF : 0> fq;
+  FarQI<MODE == 1 ? NF : 0> fi;
+  if constexpr (MODE == 0)
+    load_far_q<NF>(fq, a, Qh, Dh, Lh, Th, s0 + 16 * wave, n, g, lane_off);
+  else
+    load_far_qi<NF>(fi, a, Qh, Dh, Sh, a.n_cov, s0 + 16 * wave, l, n, g);
 
   int buf = 0;
   for (int p0 = s0; p0 < s1; p0 += kT, buf ^= 1) {
@@ -282,6 +380,8 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
 
     // ---- window band: query rows j0 + kappa, kappa < 32
     const int band = row_off(j0);
+    uint32_t sel[4];
+    diag_sel(sel);
     {
       f4 S0 = {0, 0, 0, 0}, S1 = {0, 0, 0, 0}, D0 = {0, 0, 0, 0}, D1 = {0, 0, 0, 0};
       const int sa = band + lane_k;
@@ -293,7 +393,8 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
       D0 = mfma32(as_bf8(lds_read16(sm.ringD, sa + 64)), bv1, D0);
       D1 = mfma32(as_bf8(lds_read16(sm.ringD, sa + 16 * kRow)), bv0, D1);
       D1 = mfma32(as_bf8(lds_read16(sm.ringD, sa + 16 * kRow + 64)), bv1, D1);
-      float p[8], ds[8];
+      float p[8], ds[8], bias0[4], bias1[4];
+      window_bias(bias0, bias1);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const float2 l0 = *reinterpret_cast<const float2*>(sm.ringQ + band + lane_lv + v * kRow);
@@ -305,18 +406,28 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
       }
       const bf16x8 bp = __builtin_bit_cast(
           bf16x8, make_uint4(pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]), pack_bf2(p[4], p[5]), pack_bf2(p[6], p[7])));
-      const bf16x8 bs = __builtin_bit_cast(
-          bf16x8,
-          make_uint4(pack_bf2(ds[0], ds[1]), pack_bf2(ds[2], ds[3]), pack_bf2(ds[4], ds[5]), pack_bf2(ds[6], ds[7])));
+      // dS as bf16 plus its rounding residual (a second MFMA): the window's dS (whose
+      // weights P reach 1 near the sequence start) are not rounded to 8 significant bits
+      uint32_t hs[4], ls[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        hs[x] = pack_bf2(ds[2 * x], ds[2 * x + 1]);
+        ls[x] = pack_bf2(ds[2 * x] - bf_lo(hs[x]), ds[2 * x + 1] - bf_hi(hs[x]));
+      }
+      const bf16x8 bs = __builtin_bit_cast(bf16x8, make_uint4(hs[0], hs[1], hs[2], hs[3]));
+      const bf16x8 bs2 = __builtin_bit_cast(bf16x8, make_uint4(ls[0], ls[1], ls[2], ls[3]));
       const int r0 = band + lane_t, r1 = r0 + 16 * kRow;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         const int o = 8 * (mb & 1) + 64 * (mb >> 1);
-        acck[mb] = mfma32(cat_bf8(tr16(sm.ringQ, r0 + o), tr16(sm.ringQ, r1 + o)), bs, acck[mb]);
+        const bf16x8 aq = cat_bf8(tr16(sm.ringQ, r0 + o), tr16(sm.ringQ, r1 + o));
+        acck[mb] = mfma32(aq, bs, acck[mb]);
+        acck[mb] = mfma32(aq, bs2, acck[mb]);
         accv[mb] = mfma32(cat_bf8(tr16(sm.ringD, r0 + o), tr16(sm.ringD, r1 + o)), bp, accv[mb]);
       }
     }
     // ---- covered offsets: query slab rows j0 + r + n (diagonal), two offsets per MFMA
+    if constexpr (MODE == 0) {
 #pragma unroll
     for (int e = 0; e < NC; e += 2) {
       float p2[2], ds2[2];
@@ -345,6 +456,30 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
         accv[mb] = mfma32(cat_bf8(tr16(sm.ringD, ra + o), tr16(sm.ringD, rb + o)), bp, accv[mb]);
       }
     }
+    } else {
+      // interpolated: the lower query slab j0 + c + n and the upper one j0 + c - 1 + n of an
+      // entry in one MFMA, with the stored P and dS (entries past n_cov have zero weights).
+      // The weighted dS ((1 - w) dS_lo, w dS_hi) enter as a bf16 pair plus the pair of their
+      // rounding residuals (two MFMAs): the weights keep the stored dS's 12 significant bits.
+#pragma unroll
+      for (int e = 0; e < NC; ++e) {
+        const float w = a.w[e];
+        const float xs = ps_ds(psl[e]) * (1.f - w), ys = ps_ds(psh[e]) * w;
+        const uint32_t hs = pack_bf2(xs, ys);
+        const bf16x8 bs = diag_block(hs, sel);
+        const bf16x8 bs2 = diag_block(pack_bf2(xs - bf_lo(hs), ys - bf_hi(hs)), sel);
+        const bf16x8 bp = diag_block(pack_bf2(ps_p(psl[e]) * (1.f - w), ps_p(psh[e]) * w), sel);
+        const int ra = row_off(j0 + a.dist[e]) + lane_t, rb = row_off(j0 + a.dist[e] - 1) + lane_t;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const int o = 8 * (mb & 1) + 64 * (mb >> 1);
+          const bf16x8 aq = cat_bf8(tr16(sm.ringQ, ra + o), tr16(sm.ringQ, rb + o));
+          acck[mb] = mfma32(aq, bs, acck[mb]);
+          acck[mb] = mfma32(aq, bs2, acck[mb]);
+          accv[mb] = mfma32(cat_bf8(tr16(sm.ringD, ra + o), tr16(sm.ringD, rb + o)), bp, accv[mb]);
+        }
+      }
+    }
     // undo R_j on dK^: dims 8g+t (acck[0], acck[1]) pair with 32+8g+t (acck[2], acck[3])
     float kl[8], khv[8], vl[8], vhv[8];
 #pragma unroll
@@ -359,6 +494,7 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
     }
     // ---- far offsets: raw q (rotated by R_r, bf16) and dO rows from global memory; dK and dV
     // terms on VALU with the bf16 weights (dS, P) of the query's diagonal lane
+    if constexpr (MODE == 0) {
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       uint4 r0, r1;
@@ -392,8 +528,84 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
       }
     }
     load_far_q<NF>(fq, a, Qh, Dh, Lh, Th, j0 + kT, n, g, lane_off);
+    } else {
+      // interpolated far entries: the lower query row (the lane's, rotated by R_c) and the
+      // upper row (rotated by R_(c-1)) in fp32, weighted by the stored (P, dS) in fp32.
+      // (Scheduling barriers keep each entry's cross-lane moves and unpacked values from
+      // spreading over the other entries and the MFMA part, where they would hold registers.)
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const float w = a.far_w[f];
+        const float al = ps_ds(fi.pl[f]) * (1.f - w), ah = ps_ds(fi.ph[f]) * w;
+        const float pl = ps_p(fi.pl[f]) * (1.f - w), ph = ps_p(fi.ph[f]) * w;
+#pragma unroll
+        for (int tsr = 0; tsr < 2; ++tsr) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          // words 2hh, 2hh + 1 of each 16-byte half of the lane's slice: dims 8g + 4hh..+3 and
+          // 32 + 8g + 4hh..+3 (rotation partners)
+          const uint4 a0 = tsr == 0 ? fi.q[f][0] : fi.d[f][0], a1 = tsr == 0 ? fi.q[f][1] : fi.d[f][1];
+          uint32_t lo[4] = {hh == 0 ? a0.x : a0.z, hh == 0 ? a0.y : a0.w, hh == 0 ? a1.x : a1.z, hh == 0 ? a1.y : a1.w};
+          uint32_t ex = fi.ex[f];
+          // (empty asm: pins the uses of these registers below this point)
+#pragma unroll
+          for (int x = 0; x < 4; ++x) asm volatile("" : "+v"(lo[x]));
+          asm volatile("" : "+v"(ex));
+          uint32_t hi[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            // the same word of row j0 + c - 1 (tensor tsr, 16-byte half x / 2, word 2hh + x % 2),
+            // for the lanes of key 0; every other lane takes lane n - 1's row
+            const int src = 32 * tsr + 16 * (x >> 1) + 4 * g + 2 * hh + (x & 1);
+            const int e = __builtin_amdgcn_ds_bpermute(4 * src, (int)ex);
+            hi[x] = (uint32_t)__builtin_amdgcn_update_dpp(e, (int)lo[x], 0x111, 0xf, 0xf, false);
+          }
+          // xl[0..3]: dims 8g + 4hh + t, xl[4..7]: dims 32 + 8g + 4hh + t (t < 4)
+          float xl[8], xh[8];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            xl[(x >> 1) * 4 + 2 * (x & 1)] = bf_lo(lo[x]);
+            xl[(x >> 1) * 4 + 2 * (x & 1) + 1] = bf_hi(lo[x]);
+            xh[(x >> 1) * 4 + 2 * (x & 1)] = bf_lo(hi[x]);
+            xh[(x >> 1) * 4 + 2 * (x & 1) + 1] = bf_hi(hi[x]);
+          }
+          if (tsr == 0) {
+            const float2* cl = &sm.unc_cs[2 * f][8 * g + 4 * hh];
+            const float2* ch = &sm.unc_cs[2 * f + 1][8 * g + 4 * hh];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const float2 c0 = cl[t], c1 = ch[t];
+              const int u = 4 * hh + t;
+              kl[u] = fmaf(al, xl[t] * c0.x - xl[4 + t] * c0.y, kl[u]);
+              khv[u] = fmaf(al, xl[4 + t] * c0.x + xl[t] * c0.y, khv[u]);
+              kl[u] = fmaf(ah, xh[t] * c1.x - xh[4 + t] * c1.y, kl[u]);
+              khv[u] = fmaf(ah, xh[4 + t] * c1.x + xh[t] * c1.y, khv[u]);
+            }
+          } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int u = 4 * hh + t;
+              vl[u] = fmaf(pl, xl[t], fmaf(ph, xh[t], vl[u]));
+              vhv[u] = fmaf(pl, xl[4 + t], fmaf(ph, xh[4 + t], vhv[u]));
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        }
+      }
+    }
 
     // ---- epilogue: dK = scale * (the lane's dims), dV
+    // interpolated: the next step's (P, dS), requested after the far terms (which is where the
+    // registers run short); they are first used after the next step's window band
+    load_ps(pn < s1 ? pn : p0);
+    if constexpr (MODE == 1) {
+      // (empty asm: the sums are formed here, not sunk into the conditional store below
+      // past the loads that follow it)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) asm volatile("" : "+v"(kl[t]), "+v"(khv[t]), "+v"(vl[t]), "+v"(vhv[t]));
+    }
     if (jk < s1) {
       bf16_t* kp = a.dk + hoff + (int64_t)j0 * kD + lane_off;
       bf16_t* vp = a.dv + hoff + (int64_t)j0 * kD + lane_off;
@@ -413,27 +625,30 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
       *reinterpret_cast<uint4*>(vp) = y0;
       *reinterpret_cast<uint4*>(vp + kHalf) = y1;
     }
+    // interpolated: the next step's far rows, requested after the stores (the far terms above
+    // feed only the stores; requested earlier, the new rows would be held alongside them)
+    if constexpr (MODE == 1) load_far_qi<NF>(fi, a, Qh, Dh, Sh, a.n_cov, j0 + kT, l, n, g);
     __syncthreads();
   }
 }
 
-template <int NC, int NF>
+template <int MODE, int NC, int NF>
 hipError_t launch(const BkArgs& a, unsigned blocks, hipStream_t s) {
   const size_t smem = sizeof(BkSmem);
-  hipError_t e = hipFuncSetAttribute((const void*)bwdk_ring_kernel<NC, NF>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)smem);
+  hipError_t e = hipFuncSetAttribute((const void*)bwdk_ring_kernel<MODE, NC, NF>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
-  bwdk_ring_kernel<NC, NF><<<blocks, 512, smem, s>>>(a);
+  bwdk_ring_kernel<MODE, NC, NF><<<blocks, 512, smem, s>>>(a);
   return hipGetLastError();
 }
 
-template <int NC>
+template <int MODE, int NC>
 hipError_t launch_far(const BkArgs& a, int n_far, unsigned blocks, hipStream_t s) {
   switch (n_far) {
-    case 0: return launch<NC, 0>(a, blocks, s);
-    case 1: return launch<NC, 1>(a, blocks, s);
-    case 2: return launch<NC, 2>(a, blocks, s);
-    default: return launch<NC, 3>(a, blocks, s);
+    case 0: return launch<MODE, NC, 0>(a, blocks, s);
+    case 1: return launch<MODE, NC, 1>(a, blocks, s);
+    case 2: return launch<MODE, NC, 2>(a, blocks, s);
+    default: return launch<MODE, NC, 3>(a, blocks, s);
   }
 }
 
@@ -442,13 +657,14 @@ constexpr int kMaxFarK = 3;  // far offsets whose rows fit the registers at 8 wa
 }  // namespace
 
 bool bwdk_ring_supported(const BwdArgs& f) {
-  if (f.dtype != 1 || f.mode != 0 || f.W > kMaxBand || f.N > (1LL << 30)) return false;
+  if (f.dtype != 1 || f.W > kMaxBand || f.N > (1LL << 30)) return false;
   int cov, far;
   split_table(f.tab, f.N, 8, &cov, &far);
   return far <= kMaxFarK && cov <= kMaxCov;
 }
 
-hipError_t launch_bwdk_ring(const BwdArgs& f, const float* delta) {
+hipError_t launch_bwdk_ring(const BwdArgs& f, const float* delta, const uint32_t* ps) {
+  if (f.mode == 1 && ps == nullptr) return hipErrorInvalidValue;
   BkArgs a;
   a.q = (const bf16_t*)f.q;
   a.k = (const bf16_t*)f.k;
@@ -456,14 +672,21 @@ hipError_t launch_bwdk_ring(const BwdArgs& f, const float* delta) {
   a.dout = (const bf16_t*)f.dout;
   a.lse = f.lse;
   a.delta = delta;
+  a.ps = ps;
   a.dk = (bf16_t*)f.dk;
   a.dv = (bf16_t*)f.dv;
   a.N = (int)f.N;
   a.W = f.W;
   int n_far;
   split_table(f.tab, f.N, 8, &a.n_cov, &n_far);
-  for (int e = 0; e < kMaxCov; ++e) a.dist[e] = e < a.n_cov ? f.tab.dist[e] : kMaxBand;
-  for (int x = 0; x < kMaxFar; ++x) a.far_dist[x] = x < n_far ? f.tab.dist[a.n_cov + x] : 0;
+  for (int e = 0; e < kMaxCov; ++e) {
+    a.dist[e] = e < a.n_cov ? f.tab.dist[e] : kMaxBand;
+    a.w[e] = e < a.n_cov ? f.tab.w[e] : 0.f;
+  }
+  for (int x = 0; x < kMaxFar; ++x) {
+    a.far_dist[x] = x < n_far ? f.tab.dist[a.n_cov + x] : 0;
+    a.far_w[x] = x < n_far ? f.tab.w[a.n_cov + x] : 0.f;
+  }
   constexpr int kT = step_rows(8);
   // After step p0's insert the ring holds the query rows [p0 + lead - (kP - kT), p0 + lead + kT);
   // the step reads rows p0 .. p0 + kT - 1 + max(covered offset, band): lead is the largest
@@ -479,7 +702,9 @@ hipError_t launch_bwdk_ring(const BwdArgs& f, const float* delta) {
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)kD));
   a.rope = f.rope;
   const unsigned blocks = (unsigned)(segs * f.BH);
-  return a.n_cov <= 8 ? launch_far<8>(a, n_far, blocks, f.stream) : launch_far<16>(a, n_far, blocks, f.stream);
+  if (f.mode == 0)
+    return a.n_cov <= 8 ? launch_far<0, 8>(a, n_far, blocks, f.stream) : launch_far<0, 16>(a, n_far, blocks, f.stream);
+  return a.n_cov <= 8 ? launch_far<1, 8>(a, n_far, blocks, f.stream) : launch_far<1, 16>(a, n_far, blocks, f.stream);
 }
 
 }  // namespace fib

@@ -36,7 +36,7 @@ struct BqArgs {
   bf16_t* dq;
   float* delta;
   float* dalpha_part;  // one per workgroup (interpolated mode)
-  uint32_t* ps;        // interpolated mode: bf16 (P, dS) per [head][entry][query], or null
+  uint32_t* ps;        // interpolated mode: (P, dS) (ps_pack) per [head][entry][query], or null
   int N;
   int W;
   int n_cov;
@@ -395,7 +395,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
       ds_e[e] = p * (dp - dlt);
       if (MODE == 1) {
         dal_step = fmaf(-a.f[e], ds_e[e] * a.scale * sd_e[e] + p * dd_e[e], dal_step);
-        ps_e[e] = pack_bf2(p, ds_e[e]);
+        ps_e[e] = ps_pack(p, ds_e[e]);
       }
     }
 
@@ -471,7 +471,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
         add_unrot(ql, qhv, ds * w, fk.kh[f][0], fk.kh[f][1], &sm.unc_cs[u + 1][8 * g]);
         // the diagonal lane holds s_hi - s_lo of its query
         if (diag_lane) dal_step = fmaf(-a.far_f[f], ds * a.scale * sd_f[f] + p * (dp_hi - dp_lo), dal_step);
-        ps_f[f] = pack_bf2(p, ds);
+        ps_f[f] = ps_pack(p, ds);
       }
     }
 

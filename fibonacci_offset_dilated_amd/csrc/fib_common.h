@@ -55,6 +55,19 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
 }
 __device__ __forceinline__ uint32_t f2bf(float x) { return pack_bf2(x, 0.f) & 0xffffu; }
 
+// (P, dS) of one (query, table entry) in 32 bits, handed from the query side of the
+// interpolated backward to its key side: dS as an fp32 whose mantissa is rounded (to
+// nearest even) to 11 bits (bits 31..12: 12 significant bits, against bf16's 8), P in [0, 1]
+// as a 12-bit fixed-point fraction P * 4095 (bits 11..0; absolute error <= 1.3e-4).
+__device__ __forceinline__ uint32_t ps_pack(float p, float ds) {
+  uint32_t u = __float_as_uint(ds);
+  u = (u + 0x7ffu + ((u >> 12) & 1u)) & 0xfffff000u;
+  const uint32_t q = (uint32_t)__builtin_rintf(fminf(fmaxf(p, 0.f), 1.f) * 4095.f);
+  return u | q;
+}
+__device__ __forceinline__ float ps_ds(uint32_t x) { return __uint_as_float(x & 0xfffff000u); }
+__device__ __forceinline__ float ps_p(uint32_t x) { return (float)(x & 0xfffu) * (1.f / 4095.f); }
+
 // 8 consecutive elements <-> 8 floats
 template <typename T> struct Vec8;
 template <> struct Vec8<float> {

@@ -50,13 +50,14 @@ size_t bwd_workspace_bytes(int64_t BH, int64_t N, int dtype, int mode);
 hipError_t launch_bwd(const BwdArgs& a);
 // query side of the backward on the LDS ring (bf16, W <= 16): dQ, Delta [BH * N], one
 // d(alpha) partial per workgroup (bwdq_ring_blocks of them) and, in interpolated mode when ps
-// is not null, each (query, table entry)'s softmax weight P and dS as a bf16 pair in
+// is not null, each (query, table entry)'s softmax weight P and dS (one ps_pack word) in
 // ps[(head * kMaxEnt + entry) * N + query]
 bool bwdq_ring_supported(const BwdArgs& a);
 int64_t bwdq_ring_blocks(const BwdArgs& a);
 hipError_t launch_bwdq_ring(const BwdArgs& a, float* delta, float* part, uint32_t* ps);
-// key side on the LDS ring (bf16, integer offsets, W <= 16): dK, dV from Delta
+// key side on the LDS ring (bf16, W <= 16): dK, dV from Delta; in interpolated mode also
+// from the (P, dS) pairs ps that the ring query side stored (required there)
 bool bwdk_ring_supported(const BwdArgs& a);
-hipError_t launch_bwdk_ring(const BwdArgs& a, const float* delta);
+hipError_t launch_bwdk_ring(const BwdArgs& a, const float* delta, const uint32_t* ps);
 
 }  // namespace fib

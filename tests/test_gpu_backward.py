@@ -89,6 +89,8 @@ RING_BWD = [
     (1, 2, 70, 6, 0.5, FIB_BASE),              # one partial step
     (3, 5, 1500, 10, 1.3, FIB_BASE),
     (1, 1, 2000, 12, 1.0001, (1, 2, 3, 5, 8, 13, 21, 34, 55, 89, 144, 233, 377, 511, 512, 610)),
+    (1, 2, 3001, 7, 1.37, FIB_BASE),           # interpolation weights of every size, ragged end
+    (2, 2, 700, 12, 1.45, FIB_BASE),           # one far entry (c = 547) read by few queries
 ]
 
 
