@@ -65,26 +65,53 @@ struct __align__(16) BqSmem {
   float red[16];
 };
 
-template <int NF>
+// Rows of the far entries for the wave's queries i0w + n, of K or V: lane (n, g) holds row
+// i0w - d + n (the lower row in interpolated mode), dims 8g..8g+7 and 32+8g..32+8g+7. In
+// interpolated mode the upper row of query n is the lower row of query n + 1 (upper_rows);
+// the one that no lane holds, row i0w - d + 16, is kept spread over the wave, lane l holding
+// its dword l % 32.
+template <int MODE, int NF>
 struct FarK {
   uint4 k[NF > 0 ? NF : 1][2];
-  uint4 kh[NF > 0 ? NF : 1][2];
+  uint32_t ex[MODE == 1 && NF > 0 ? NF : 1];
 };
 
 template <int MODE, int NF>
-__device__ __forceinline__ void load_far(FarK<NF>& fr, const BqArgs& a, const bf16_t* X, int i0w, int n, int g,
-                                         int lane_off) {
+__device__ __forceinline__ void load_far(FarK<MODE, NF>& fr, const BqArgs& a, const bf16_t* X, int i0w, int l,
+                                         int n, int g, int lane_off) {
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     const bf16_t* p = X + far_off(a.far_dist[f], i0w, n, g, lane_off);
     fr.k[f][0] = *reinterpret_cast<const uint4*>(p);
     fr.k[f][1] = *reinterpret_cast<const uint4*>(p + kHalf);
-    if (MODE == 1) {
-      const bf16_t* r = X + far_off(a.far_dist[f] - 1, i0w, n, g, lane_off);
-      fr.kh[f][0] = *reinterpret_cast<const uint4*>(r);
-      fr.kh[f][1] = *reinterpret_cast<const uint4*>(r + kHalf);
+    if constexpr (MODE == 1) {
+      // row i0w - d + 16 (< N: far distances exceed 16); rows before 0 only meet masked queries
+      const int r = i0w - a.far_dist[f] + 16;
+      fr.ex[f] = reinterpret_cast<const uint32_t*>(X + (int64_t)(r > 0 ? r : 0) * kD)[l & 31];
     }
   }
+}
+
+// Interpolated far entry: the upper rows (i0w - d + 1 + n) from the lower rows. Lane n takes
+// lane n + 1's row (DPP row shift within the 16 lanes of a dim group); lane 15 takes row
+// i0w - d + 16 from the dwords spread over the wave.
+__device__ __forceinline__ void upper_rows(const uint4* lo, uint32_t ex, int g, uint4* hi) {
+  uint32_t w[8] = {lo[0].x, lo[0].y, lo[0].z, lo[0].w, lo[1].x, lo[1].y, lo[1].z, lo[1].w};
+  // (empty asm: the moves happen here, not hoisted to where their results would hold
+  // registers through other work)
+#pragma unroll
+  for (int x = 0; x < 8; ++x) asm volatile("" : "+v"(w[x]));
+  asm volatile("" : "+v"(ex));
+  uint32_t h[8];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    // dword x of the lane's slice: 16-byte half x / 4 (dims 8g.. or 32 + 8g..), word x % 4
+    const int src = 16 * (x >> 2) + 4 * g + (x & 3);
+    const int e = __builtin_amdgcn_ds_bpermute(4 * src, (int)ex);
+    h[x] = (uint32_t)__builtin_amdgcn_update_dpp(e, (int)w[x], 0x101, 0xf, 0xf, false);
+  }
+  hi[0] = make_uint4(h[0], h[1], h[2], h[3]);
+  hi[1] = make_uint4(h[4], h[5], h[6], h[7]);
 }
 
 // <x, y> over the lane's 16 dims of two packed bf16 rows (fp32 accumulation)
@@ -140,25 +167,33 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
 #pragma unroll
   for (int t = 0; t < 8; ++t) cs_t[t] = rope_cs(16 * wave + n, a.rope.rev[8 * g + t]);
   const float sl2 = a.scale_log2;
-  float bias0[4], bias1[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int d0 = n + 16 - 4 * g - v, d1 = n - 4 * g - v;
-    bias0[v] = d0 < a.W ? 0.f : -INFINITY;
-    bias1[v] = (d1 >= 0 && d1 < a.W) ? 0.f : -INFINITY;
-  }
   const float bias_diag = diag_lane ? 0.f : -INFINITY;
-  uint32_t sel[4];
-  {
+  // Lane constants formed anew in every step (a few VALU operations) rather than held in
+  // registers through the loop: the window masks (band key kappa of the lane at distance
+  // n + 16 - 4g - v in block 0 and n - 4g - v in block 1) and the selectors of diag_block.
+  // (The empty asm makes W and the lane opaque, so the compiler does not hoist them.)
+  auto window_bias = [&](float* bias0, float* bias1) {
+    int Wp = a.W;
+    asm volatile("" : "+s"(Wp));
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int d0 = n + 16 - 4 * g - v, d1 = n - 4 * g - v;
+      bias0[v] = d0 < Wp ? 0.f : -INFINITY;
+      bias1[v] = (d1 >= 0 && d1 < Wp) ? 0.f : -INFINITY;
+    }
+  };
+  auto diag_sel = [&](uint32_t* sel) {
+    int lp = l;
+    asm volatile("" : "+v"(lp));
     const uint32_t zero = 0x0c0c0c0cu;
-    const uint32_t a_half = (l & 1) ? 0x01000c0cu : 0x0c0c0100u;
-    const uint32_t b_half = (l & 1) ? 0x03020c0cu : 0x0c0c0302u;
-    const bool low = (l & 2) == 0;
+    const uint32_t a_half = (lp & 1) ? 0x01000c0cu : 0x0c0c0100u;
+    const uint32_t b_half = (lp & 1) ? 0x03020c0cu : 0x0c0c0302u;
+    const bool low = (lp & 2) == 0;
     sel[0] = low ? a_half : zero;
     sel[1] = low ? zero : a_half;
     sel[2] = low ? b_half : zero;
     sel[3] = low ? zero : b_half;
-  }
+  };
   const int diag_addr = 4 * (16 * (n >> 2) + n);
   const int lane_k = n * kRow + 16 * g;
   // transpose reads of K^: lane (jr, jc) of group g reads row 4g + jr at dims 8 jc + 4 h +
@@ -258,8 +293,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
       }
     }
   }
-  FarK<NF> fk;
-  load_far<MODE, NF>(fk, a, Kh, s0 + 16 * wave, n, g, lane_off);
+  FarK<MODE, NF> fk;
+  load_far<MODE, NF>(fk, a, Kh, s0 + 16 * wave, l, n, g, lane_off);
   float dal = 0.f;  // d(alpha) contributions of this lane's queries
 
   int buf = 0;
@@ -328,7 +363,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
     float s_e[NC], dp_e[NC], sd_e[MODE == 1 ? NC : 1], dd_e[MODE == 1 ? NC : 1];
 #pragma unroll
     for (int e = 0; e < NC; ++e) {
-      const int sl = row_off(bw - a.dist[e]) + lane_k;
+      int sl = row_off(bw - a.dist[e]) + lane_k;
+      if (MODE == 1 && (e & 1) == 0) asm volatile("" : "+v"(sl));
       f4 S = {0, 0, 0, 0}, P = {0, 0, 0, 0};
       S = mfma32(as_bf8(lds_read16(sm.ringK, sl)), bq0, S);
       S = mfma32(as_bf8(lds_read16(sm.ringK, sl + 64)), bq1, S);
@@ -344,6 +380,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
         Q = mfma32(as_bf8(lds_read16(sm.ringV, sl + kRow + 64)), bd1, Q);
         sd_e[e] = sel4(H, l) - s_e[e];  // s_hi - s_lo
         dd_e[e] = sel4(Q, l) - dp_e[e];  // dp_hi - dp_lo
+        // at most two entries' accumulators (16 registers each) in flight at a time: left to
+        // itself the compiler issues every entry's MFMAs back to back and runs out of
+        // registers. (Empty asm: the results of entries e - 1 and e are taken before the
+        // slab address of entry e + 1 is formed.)
+        if (e & 1) asm volatile("" : "+v"(s_e[e]), "+v"(dp_e[e]), "+v"(sd_e[e]), "+v"(dd_e[e]),
+                                "+v"(s_e[e - 1]), "+v"(dp_e[e - 1]), "+v"(sd_e[e - 1]), "+v"(dd_e[e - 1]));
       }
     }
     // ---- far entries: logits (relative RoPE); their V rows for dP are requested now
@@ -359,18 +401,22 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
       s_f[f] = sel4(S, l);
       if (MODE == 1) {
         rotate_pack_f(qf, &sm.unc_cs[u + 1][8 * g], &r0, &r1);
+        uint4 kh[2];
+        upper_rows(fk.k[f], fk.ex[f], g, kh);
         f4 H = {0, 0, 0, 0};
-        H = mfma32(as_bf8(fk.kh[f][0]), as_bf8(r0), H);
-        H = mfma32(as_bf8(fk.kh[f][1]), as_bf8(r1), H);
+        H = mfma32(as_bf8(kh[0]), as_bf8(r0), H);
+        H = mfma32(as_bf8(kh[1]), as_bf8(r1), H);
         sd_f[f] = sel4(H, l) - s_f[f];
       }
     }
-    FarK<NF> fv;
-    load_far<MODE, NF>(fv, a, Vh, i0w, n, g, lane_off);
+    FarK<MODE, NF> fv;
+    load_far<MODE, NF>(fv, a, Vh, i0w, l, n, g, lane_off);
 
     // ---- P, Delta, dS
     const float dlt = quad_add(dot16_bf(do0, do1, oo[0], oo[1]));
     float bds[8];  // band dS: sw0 (slab 0) then sw1 (slab 1), per the lane's 4 keys each
+    float bias0[4], bias1[4];
+    window_bias(bias0, bias1);
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       float x0 = fmaf(S0[v], sl2, bias0[v]), x1 = fmaf(S1[v], sl2, bias1[v]);
@@ -400,6 +446,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
     }
 
     // ---- dQ^ = K^T dS^T (rotated frame) on MFMA: band, then covered entries
+    uint32_t sel[4];
+    diag_sel(sel);
     f4 acc[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) acc[mb] = f4{0, 0, 0, 0};
@@ -449,6 +497,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
 
     // ---- far entries: dP on VALU, P from the diagonal lane, dS, dQ in the un-rotated frame
     uint32_t ps_f[MODE == 1 && NF > 0 ? NF : 1];
+    if constexpr (MODE == 1) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const int u = MODE == 1 ? 2 * f : f;
@@ -464,11 +513,14 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
         const float ds = p * (dp_lo - dlt);
         add_unrot(ql, qhv, ds, fk.k[f][0], fk.k[f][1], &sm.unc_cs[u][8 * g]);
       } else {
-        const float dp_hi = quad_add(dot16_bf(do0, do1, fv.kh[f][0], fv.kh[f][1]));
+        uint4 vh[2], kh[2];
+        upper_rows(fv.k[f], fv.ex[f], g, vh);
+        const float dp_hi = quad_add(dot16_bf(do0, do1, vh[0], vh[1]));
         const float w = a.far_w[f];
         const float ds = p * (fmaf(w, dp_hi - dp_lo, dp_lo) - dlt);
         add_unrot(ql, qhv, ds * (1.f - w), fk.k[f][0], fk.k[f][1], &sm.unc_cs[u][8 * g]);
-        add_unrot(ql, qhv, ds * w, fk.kh[f][0], fk.kh[f][1], &sm.unc_cs[u + 1][8 * g]);
+        upper_rows(fk.k[f], fk.ex[f], g, kh);
+        add_unrot(ql, qhv, ds * w, kh[0], kh[1], &sm.unc_cs[u + 1][8 * g]);
         // the diagonal lane holds s_hi - s_lo of its query
         if (diag_lane) dal_step = fmaf(-a.far_f[f], ds * a.scale * sd_f[f] + p * (dp_hi - dp_lo), dal_step);
         ps_f[f] = ps_pack(p, ds);
@@ -476,6 +528,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
     }
 
     // ---- epilogue: dQ = scale * (the lane's 16 dims), Delta
+    if constexpr (MODE == 1) {
+      // (empty asm: the sums are formed here, not sunk into the conditional stores below)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) asm volatile("" : "+v"(ql[t]), "+v"(qhv[t]));
+    }
     if (iq < s1) {
       bf16_t* dp = a.dq + hoff + (int64_t)i0w * kD + lane_off;
       uint4 x0, x1;
@@ -501,7 +558,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
         for (int f = 0; f < NF; ++f) pq[(size_t)(a.n_cov + f) * N] = ps_f[f];
       }
     }
-    load_far<MODE, NF>(fk, a, Kh, i0w + kT, n, g, lane_off);
+    load_far<MODE, NF>(fk, a, Kh, i0w + kT, l, n, g, lane_off);
     __syncthreads();
   }
   if (MODE == 1) {
@@ -522,7 +579,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
 // Instances that fit 256 registers per lane, i.e. two waves per SIMD (8 waves); the others
 // run with 4 waves.
 constexpr bool fits8(int mode, int nc, int nf) {
-  return mode == 0 ? !(nc > 8 && nf > 3) : (nf == 0 || (nc <= 8 && nf <= 1));
+  return !(nc > 8 && nf > 3);
 }
 
 template <int MODE, int NC, int NF, int WAVES>
