@@ -125,16 +125,20 @@ def test_long_context_sampled_rows(long_inputs, mode):
     a = alpha_of(w, 15)
     say(f"long context N=131072 H=32 alpha={a} mode={mode}")
     o, lse = run_fwd(long_inputs, 12, a, FIB_BASE, mode)
-    rng = np.random.default_rng(mode)
-    rows = np.unique(np.concatenate([np.arange(0, 40), np.arange(980, 1500), rng.integers(0, w.N, 600),
-                                     np.arange(w.N - 70, w.N)]))
     (_, q64), (_, k64), (_, v64) = long_inputs[:3]
+    o_h, lse_h = host(o[0]), host(lse[0])
     eo = el = 0.0
-    for h in (0, 7, 19, 31):
+    # every head: the sequence start, the rows where the far entries start (980..1500), the
+    # end, and random rows; four heads with a denser random sample
+    for h in range(w.H):
+        rng = np.random.default_rng(100 * h + mode)
+        n_rand = 600 if h in (0, 7, 19, 31) else 150
+        rows = np.unique(np.concatenate([np.arange(0, 40), np.arange(980, 1500, 1 if h in (0, 31) else 7),
+                                         rng.integers(0, w.N, n_rand), np.arange(w.N - 70, w.N)]))
         ro, rl = O.forward_rows(q64[0, h], k64[0, h], v64[0, h], rows, 12, a, FIB_BASE, 10000.0, mode)
-        eo = max(eo, maxabs(host(o[0, h])[rows], ro))
-        el = max(el, maxabs(host(lse[0, h])[rows], rl))
-    say("  max err O", eo, "LSE", el)
+        eo = max(eo, maxabs(o_h[h][rows], ro))
+        el = max(el, maxabs(lse_h[h][rows], rl))
+    say("  max err O", eo, "LSE", el, "over all", w.H, "heads")
     assert eo <= TOL[BF16] and el <= TOL[BF16]
     assert torch.isfinite(o.float()).all().item()
     check_index_set(w.N, 12, a, FIB_BASE, mode)
