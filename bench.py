@@ -36,13 +36,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# device sources of the timed kernel (the ring forward): the stored HBM byte counts hold
+# only while these are unchanged
+TIMED_KERNEL_SOURCES = ("fwd_ring.hip", "ring_common.h", "fib_common.h")
+
+
 def kernel_sources_sha() -> str:
     csrc = os.path.join(ROOT, "fibonacci_offset_dilated_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            h.update(f.encode())
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in TIMED_KERNEL_SOURCES:
+        h.update(f.encode())
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -196,6 +200,22 @@ def small_configs(dev, stream, args):
     out["b8h8n1024_interp_over_int"] = round(us_interp / us_int, 3)
     out["b8h8n1024_bwd_interp_us_per_layer"] = round(us_bwd, 2)
     out["b8h8n1024_fwd_int_hbm_frac"] = round(rows2 * (4 * D * 2 + 4) / (us_int * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    del q, k, v, do, o, lse, outs, dq, dk, dv, ws
+
+    # decode: one new query per (batch, head) against a cache at the pages' evaluation length
+    # (B8 H8, N = 4096), integer offsets at the linear schedule's layers vs interpolated at the
+    # learned-dilation alphas (the comparison of Results 2)
+    (qc, kc, vc), _ = make_inputs(8, 8, 4096, seed_for(3, 0, 12, 1), False, dev)
+    qd = qc[:, :, -1, :].contiguous()
+    od = torch.empty_like(qd)
+    ld = torch.empty((8, 8), dtype=torch.float32, device=dev)
+    us_di = per_layer_us(lambda l: (lambda: F.decode(qd, kc, vc, 12, al2[l], FIB_BASE, 10000.0, INT, out=od, lse=ld)),
+                         range(16))
+    us_dp = per_layer_us(lambda l: (lambda: F.decode(qd, kc, vc, 12, al3[l], FIB_BASE, 10000.0, INTERP, out=od,
+                                                     lse=ld)), range(16))
+    out["decode_b8h8n4096_int_us_per_layer"] = round(us_di, 2)
+    out["decode_b8h8n4096_interp_us_per_layer"] = round(us_dp, 2)
+    out["decode_b8h8n4096_interp_over_int"] = round(us_dp / us_di, 3)
     return out
 
 

@@ -36,6 +36,10 @@ _SIGS = {
                                        _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int,
                                        _c.c_int, _c.c_float, _c.c_void_p, _c.c_int, _c.c_float, _c.c_int,
                                        _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "fib_sparse_attn_decode": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                          _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int,
+                                          _c.c_int, _c.c_float, _c.c_void_p, _c.c_int, _c.c_float, _c.c_int,
+                                          _c.c_void_p]),
     "fib_sparse_attn_bwd_workspace_size": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64,
                                                          _c.c_int, _c.c_int]),
     "fib_status_string": (_c.c_char_p, [_c.c_int]),
@@ -160,6 +164,31 @@ def fwd(q, k, v, W: int, alpha, base: Sequence[int], theta: float = 10000.0, mod
                                    int(W), ctypes.c_float(float(np.float32(alpha))), b, n,
                                    ctypes.c_float(float(theta)), int(mode), _stream(stream))
     _check(st, "fib_sparse_attn_fwd")
+    return out, lse
+
+
+def decode(q, k_cache, v_cache, W: int, alpha, base: Sequence[int], theta: float = 10000.0, mode: int = INT,
+           out=None, lse=None, with_lse: bool = True, stream=None):
+    """One decode step: q [B, H, D] at position N - 1 of the caches [B, H, N, D]; returns
+    (O [B, H, D], LSE [B, H] or None)."""
+    torch = _torch()
+    _check_qkv(k_cache, v_cache)
+    B, H, N, D = k_cache.shape
+    for t in (q, out):
+        if t is None:
+            continue
+        if (not isinstance(t, torch.Tensor) or not t.is_cuda or t.shape != (B, H, D) or t.dtype != k_cache.dtype
+                or t.device != k_cache.device or not t.is_contiguous()):
+            raise ValueError("q and o must be contiguous [B, H, D] tensors of the caches' dtype and device")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and with_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    b, n = _base_array(base)
+    st = lib().fib_sparse_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), B, H, N, D,
+                                      _dtype_code(q), int(W), ctypes.c_float(float(np.float32(alpha))), b, n,
+                                      ctypes.c_float(float(theta)), int(mode), _stream(stream))
+    _check(st, "fib_sparse_attn_decode")
     return out, lse
 
 

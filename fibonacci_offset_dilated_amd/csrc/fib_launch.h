@@ -45,6 +45,9 @@ hipError_t launch_fwd_generic(const FwdArgs& a);
 bool fwd_ring_supported(const FwdArgs& a);
 hipError_t launch_fwd_ring(const FwdArgs& a);
 hipError_t launch_index_set(int32_t* out, int64_t N, int W, const Table& tab, int64_t cols, hipStream_t s);
+// one query per (batch, head) at position N - 1 of a K/V cache of N rows: q and o are
+// [BH, D], k and v [BH, N, D], lse [BH]
+hipError_t launch_decode(const FwdArgs& a);
 
 size_t bwd_workspace_bytes(int64_t BH, int64_t N, int dtype, int mode);
 hipError_t launch_bwd(const BwdArgs& a);

@@ -212,6 +212,28 @@ int fib_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   return e == hipSuccess ? FIB_OK : FIB_ERR_LAUNCH;
 }
 
+int fib_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                           int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                           int W, float alpha, const int32_t* base, int n_base,
+                           float rope_theta, int mode, void* stream) {
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || o == nullptr) return FIB_ERR_NULL;
+  int st = check_shape(B, H, N, D, dtype);
+  if (st) return st;
+  st = check_base(base, n_base);
+  if (st) return st;
+  st = check_scalars(W, alpha, rope_theta, mode);
+  if (st) return st;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || ((uintptr_t)lse & 3u))
+    return FIB_ERR_ALIGN;
+  FwdArgs a;
+  a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = lse;
+  a.BH = B * H; a.N = N; a.dtype = dtype; a.mode = mode; a.W = W;
+  build_table(alpha, base, n_base, W, mode, &a.tab);
+  a.rope = make_rope(rope_theta);
+  a.stream = (hipStream_t)stream;
+  return launch_decode(a) == hipSuccess ? FIB_OK : FIB_ERR_LAUNCH;
+}
+
 size_t fib_sparse_attn_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, int mode) {
   if (check_shape(B, H, N, D, dtype) != FIB_OK) return 0;
   if (mode != FIB_INT && mode != FIB_INTERP) return 0;

@@ -125,9 +125,26 @@ int fib_sparse_attn_bwd(const void* q, const void* k, const void* v, const void*
 /* Bytes of device workspace fib_sparse_attn_bwd needs for these sizes (0 on bad sizes):
  * about 4 bytes per (b, h, n) row for Delta = <dO, O> and the d(alpha) partials, plus, for
  * bf16 inputs in FIB_INTERP mode, 128 bytes per row in which the query side hands each
- * (query, table entry) pair's softmax weight and dS (bf16) to the key side. */
+ * (query, table entry) pair's softmax weight and dS (32 bits per pair) to the key side. */
 size_t fib_sparse_attn_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D,
                                           int dtype, int mode);
+
+/*
+ * Decode step: the newest position of a key/value cache attends its window and offset keys
+ * ([FIB] Method > Architecture and attention mechanism; Results 2 compares the inference
+ * cost of the integer and interpolated gathers). The result equals row N - 1 of
+ * fib_sparse_attn_fwd over the cache with this query at position N - 1.
+ *   q        device, [B, H, D] of `dtype`: the query of position N - 1, un-rotated.
+ *   k_cache, v_cache  device, [B, H, N, D] of `dtype`: keys and values of positions
+ *            0..N-1 (the new position's included), un-rotated.
+ *   o        device, [B, H, D] of `dtype`, written.
+ *   lse      device, [B, H] fp32, written; may be NULL.
+ * The other arguments, the errors and the ownership rules are those of fib_sparse_attn_fwd.
+ */
+int fib_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                           int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                           int W, float alpha, const int32_t* base, int n_base,
+                           float rope_theta, int mode, void* stream);
 
 /* Static, human-readable text of a status code. */
 const char* fib_status_string(int status);

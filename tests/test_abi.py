@@ -104,6 +104,25 @@ def test_fwd_argument_errors(kw, status):
     assert _fwd_raw(**kw) == status
 
 
+def test_decode_argument_errors():
+    L = F.lib()
+    b = (ctypes.c_int32 * 15)(*FIB_BASE)
+    p = 16
+
+    def call(q=p, kc=p, o=p, lse=0, B=1, N=8, D=64, dtype=1, W=12, alpha=1.0, mode=0, nb=15):
+        return L.fib_sparse_attn_decode(q, kc, p, o, lse, B, 1, N, D, dtype, W, ctypes.c_float(alpha), b, nb,
+                                        ctypes.c_float(10000.0), mode, None)
+    assert call(q=None) == -1 and call(kc=None) == -1 and call(o=None) == -1
+    assert call(B=0) == -2 and call(N=0) == -2
+    assert call(D=32) == -3
+    assert call(dtype=5) == -4
+    assert call(W=0) == -5
+    assert call(alpha=float("nan")) == -6
+    assert call(nb=0) == -7
+    assert call(mode=3) == -9
+    assert call(o=0x1004) == -10 and call(lse=0x1001) == -10
+
+
 def test_bwd_argument_errors():
     L = F.lib()
     b = (ctypes.c_int32 * 15)(*FIB_BASE)
