@@ -23,6 +23,10 @@
 //      upper-row queries j + c - 1) and accumulate dK_j, dV_j in registers;
 //   3. a single block sums the dalpha partials in a fixed order.
 // Lane layout as in the general forward kernel: a quad of 4 lanes per row, 16 dims per lane.
+// For bf16 with W <= 16 the query and key sides run on the LDS-ring kernels of bwd_ring.hip
+// and bwd_key_ring.hip instead (run() below picks them); this file also holds the workspace
+// layout and the key side that reads the interpolated (P, dS) words when the ring key side
+// does not apply (more than 3 far entries).
 #include "fib_common.h"
 #include "fib_launch.h"
 

@@ -577,14 +577,14 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
 }
 
 // Instances that fit 256 registers per lane, i.e. two waves per SIMD (8 waves); the others
-// run with 4 waves.
-constexpr bool fits8(int mode, int nc, int nf) {
-  return !(nc > 8 && nf > 3);
-}
+// (16 covered and 4 far entries) run with 4 waves.
+constexpr bool fits8(int nc, int nf) { return !(nc > 8 && nf > 3); }
 
+// instances that plan() never picks (not compiled); at 4 waves the table is split again
+// with the longer ring reach, so any 4-wave instance can occur
 template <int MODE, int NC, int NF, int WAVES>
 constexpr bool unused_instance() {
-  return WAVES == 8 && !fits8(MODE, NC, NF);
+  return WAVES == 8 && !fits8(NC, NF);
 }
 
 template <int MODE, int NC, int NF, int WAVES>
@@ -623,7 +623,7 @@ hipError_t launch_far(const BqArgs& a, int n_far, unsigned blocks, hipStream_t s
 
 int plan(const BwdArgs& f, int* n_cov, int* n_far) {
   split_table(f.tab, f.N, 8, n_cov, n_far);
-  if (!fits8(f.mode, *n_cov <= 8 ? 8 : 16, *n_far)) {
+  if (!fits8(*n_cov <= 8 ? 8 : 16, *n_far)) {
     split_table(f.tab, f.N, 4, n_cov, n_far);
     return 4;
   }
