@@ -40,6 +40,21 @@ _SIGS = {
                                           _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int,
                                           _c.c_int, _c.c_float, _c.c_void_p, _c.c_int, _c.c_float, _c.c_int,
                                           _c.c_void_p]),
+    "fib_sparse_attn_plan_bytes": (_c.c_size_t, []),
+    "fib_sparse_attn_fwd_dev": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                           _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int,
+                                           _c.c_int, _c.c_void_p, _c.c_float, _c.c_float, _c.c_void_p, _c.c_int,
+                                           _c.c_float, _c.c_int, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "fib_sparse_attn_decode_dev": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                              _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int,
+                                              _c.c_int, _c.c_void_p, _c.c_float, _c.c_float, _c.c_void_p, _c.c_int,
+                                              _c.c_float, _c.c_int, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "fib_sparse_attn_bwd_dev": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                           _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                           _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int,
+                                           _c.c_int, _c.c_void_p, _c.c_float, _c.c_float, _c.c_void_p, _c.c_int,
+                                           _c.c_float, _c.c_int, _c.c_void_p, _c.c_size_t, _c.c_void_p, _c.c_size_t,
+                                           _c.c_void_p]),
     "fib_sparse_attn_bwd_workspace_size": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64,
                                                          _c.c_int, _c.c_int]),
     "fib_status_string": (_c.c_char_p, [_c.c_int]),
@@ -189,6 +204,112 @@ def decode(q, k_cache, v_cache, W: int, alpha, base: Sequence[int], theta: float
                                       _dtype_code(q), int(W), ctypes.c_float(float(np.float32(alpha))), b, n,
                                       ctypes.c_float(float(theta)), int(mode), _stream(stream))
     _check(st, "fib_sparse_attn_decode")
+    return out, lse
+
+
+def plan_bytes() -> int:
+    """Device bytes of the plan buffer of the device-alpha calls."""
+    return int(lib().fib_sparse_attn_plan_bytes())
+
+
+def _alpha_dev(alpha, device):
+    torch = _torch()
+    if (not isinstance(alpha, torch.Tensor) or alpha.dtype != torch.float32 or alpha.numel() != 1
+            or alpha.device != device):
+        raise ValueError("alpha must be a one-element float32 tensor on the inputs' device")
+    return alpha
+
+
+def _plan_buffer(plan, device):
+    torch = _torch()
+    need = plan_bytes()
+    if plan is None:
+        plan = torch.empty(need, dtype=torch.uint8, device=device)
+    if plan.numel() * plan.element_size() < need:
+        raise ValueError("plan buffer too small")
+    return plan
+
+
+def fwd_dev(q, k, v, W: int, alpha, alpha_range, base: Sequence[int], theta: float = 10000.0, mode: int = INT,
+            out=None, lse=None, with_lse: bool = True, plan=None, stream=None):
+    """Forward with alpha a one-element float32 device tensor (no host copy of alpha);
+    alpha_range = (lo, hi) bounds it (the kernels clamp it into the range)."""
+    torch = _torch()
+    _check_qkv(q, k, v)
+    B, H, N, D = q.shape
+    alpha = _alpha_dev(alpha, q.device)
+    plan = _plan_buffer(plan, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_qkv(q, out)
+    if lse is None and with_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    b, n = _base_array(base)
+    lo, hi = alpha_range
+    st = lib().fib_sparse_attn_fwd_dev(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, D, _dtype_code(q),
+                                       int(W), _ptr(alpha), ctypes.c_float(float(lo)), ctypes.c_float(float(hi)),
+                                       b, n, ctypes.c_float(float(theta)), int(mode), _ptr(plan),
+                                       plan.numel() * plan.element_size(), _stream(stream))
+    _check(st, "fib_sparse_attn_fwd_dev")
+    return out, lse
+
+
+def bwd_dev(q, k, v, o, lse, dout, W: int, alpha, alpha_range, base: Sequence[int], theta: float = 10000.0,
+            mode: int = INT, dq=None, dk=None, dv=None, dalpha=None, workspace=None, want_dalpha: bool = True,
+            plan=None, stream=None):
+    """Backward with alpha in device memory (see fwd_dev); returns (dQ, dK, dV, dalpha [1] or None)."""
+    torch = _torch()
+    _check_qkv(q, k, v, o, dout)
+    B, H, N, D = q.shape
+    alpha = _alpha_dev(alpha, q.device)
+    plan = _plan_buffer(plan, q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    _check_qkv(q, dq, dk, dv)
+    if dalpha is None and want_dalpha:
+        dalpha = torch.empty(1, dtype=torch.float32, device=q.device)
+    need = bwd_workspace_size(B, H, N, D, _dtype_code(q), mode)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    b, n = _base_array(base)
+    lo, hi = alpha_range
+    st = lib().fib_sparse_attn_bwd_dev(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dalpha), B, H, N, D, _dtype_code(q),
+                                       int(W), _ptr(alpha), ctypes.c_float(float(lo)), ctypes.c_float(float(hi)),
+                                       b, n, ctypes.c_float(float(theta)), int(mode), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _ptr(plan),
+                                       plan.numel() * plan.element_size(), _stream(stream))
+    _check(st, "fib_sparse_attn_bwd_dev")
+    return dq, dk, dv, dalpha
+
+
+def decode_dev(q, k_cache, v_cache, W: int, alpha, alpha_range, base: Sequence[int], theta: float = 10000.0,
+               mode: int = INT, out=None, lse=None, with_lse: bool = True, plan=None, stream=None):
+    """Decode step with alpha in device memory (see fwd_dev and decode)."""
+    torch = _torch()
+    _check_qkv(k_cache, v_cache)
+    B, H, N, D = k_cache.shape
+    for t in (q, out):
+        if t is None:
+            continue
+        if (not isinstance(t, torch.Tensor) or not t.is_cuda or t.shape != (B, H, D) or t.dtype != k_cache.dtype
+                or t.device != k_cache.device or not t.is_contiguous()):
+            raise ValueError("q and o must be contiguous [B, H, D] tensors of the caches' dtype and device")
+    alpha = _alpha_dev(alpha, q.device)
+    plan = _plan_buffer(plan, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and with_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    b, n = _base_array(base)
+    lo, hi = alpha_range
+    st = lib().fib_sparse_attn_decode_dev(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), B, H, N, D,
+                                          _dtype_code(q), int(W), _ptr(alpha), ctypes.c_float(float(lo)),
+                                          ctypes.c_float(float(hi)), b, n, ctypes.c_float(float(theta)), int(mode),
+                                          _ptr(plan), plan.numel() * plan.element_size(), _stream(stream))
+    _check(st, "fib_sparse_attn_decode_dev")
     return out, lse
 
 

@@ -35,11 +35,13 @@ namespace {
 
 constexpr int kRPB = 64;  // rows per block
 
-template <typename T, int MODE>
+template <typename T, int MODE, bool DEV>
 __global__ __launch_bounds__(256) void bwd_query_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ o,
     const T* __restrict__ dout, const float* __restrict__ lse, T* __restrict__ dq, float* __restrict__ delta,
-    float* __restrict__ dalpha_part, int64_t N, int W, Table tab, Rope rope, float scale, int tiles) {
+    float* __restrict__ dalpha_part, int64_t N, int W, Table tab_arg, Rope rope, float scale, int tiles,
+    const DevPlan* __restrict__ plan) {
+  const Table& tab = call_table<DEV>(tab_arg, plan);
   __shared__ float2 cs[kCsSlots][kHalf];
   __shared__ float red[256];
   const bool cached = fill_cs(cs, W, tab, MODE, rope);
@@ -144,11 +146,12 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
   }
 }
 
-template <typename T, int MODE>
+template <typename T, int MODE, bool DEV>
 __global__ __launch_bounds__(256) void bwd_key_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta, T* __restrict__ dk, T* __restrict__ dv,
-    int64_t N, int W, Table tab, Rope rope, float scale, int tiles) {
+    int64_t N, int W, Table tab_arg, Rope rope, float scale, int tiles, const DevPlan* __restrict__ plan) {
+  const Table& tab = call_table<DEV>(tab_arg, plan);
   __shared__ float2 cs[kCsSlots][kHalf];
   const bool cached = fill_cs(cs, W, tab, MODE, rope);
   const int64_t head = blockIdx.x / tiles;
@@ -276,11 +279,13 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(
 // 1 - w) and the upper row of query j + c - 1 (weight w), so
 //   dK_j += weight * dS * R_dist q_i / sqrt(D), dV_j += weight * P * dO_i
 // with dist = c or c - 1, and no logit of an interpolated key is recomputed.
+template <bool DEV>
 __global__ __launch_bounds__(256) void bwd_key_ps_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
-    const uint32_t* __restrict__ ps, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int64_t N, int W, Table tab,
-    Rope rope, float scale, int tiles) {
+    const uint32_t* __restrict__ ps, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int64_t N, int W,
+    Table tab_arg, Rope rope, float scale, int tiles, const DevPlan* __restrict__ plan) {
+  const Table& tab = call_table<DEV>(tab_arg, plan);
   __shared__ float2 cs[kCsSlots][kHalf];
   const bool cached = fill_cs(cs, W, tab, 1, rope);
   const int64_t head = blockIdx.x / tiles;
@@ -391,7 +396,7 @@ size_t ps_offset_bytes(int64_t BH, int64_t N) {
   return ((floats * sizeof(float) + 15) / 16) * 16;
 }
 
-template <typename T, int MODE>
+template <typename T, int MODE, bool DEV>
 hipError_t run(const BwdArgs& a) {
   const int tiles = (int)tiles_of(a.N);
   const int64_t blocks = (int64_t)tiles * a.BH;
@@ -407,18 +412,20 @@ hipError_t run(const BwdArgs& a) {
     if (e != hipSuccess) return e;
     n_part = bwdq_ring_blocks(a);
   } else {
-    bwd_query_kernel<T, MODE><<<grid, block, 0, a.stream>>>((const T*)a.q, (const T*)a.k, (const T*)a.v,
-        (const T*)a.o, (const T*)a.dout, a.lse, (T*)a.dq, delta, part, a.N, a.W, a.tab, a.rope, scale, tiles);
+    bwd_query_kernel<T, MODE, DEV><<<grid, block, 0, a.stream>>>((const T*)a.q, (const T*)a.k, (const T*)a.v,
+        (const T*)a.o, (const T*)a.dout, a.lse, (T*)a.dq, delta, part, a.N, a.W, a.tab, a.rope, scale, tiles,
+        a.plan);
   }
   if (bwdk_ring_supported(a) && (MODE == 0 || ps != nullptr)) {
     const hipError_t e = launch_bwdk_ring(a, delta, ps);
     if (e != hipSuccess) return e;
   } else if (ps != nullptr) {
-    bwd_key_ps_kernel<<<grid, block, 0, a.stream>>>((const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v,
-        (const bf16_t*)a.dout, a.lse, delta, ps, (bf16_t*)a.dk, (bf16_t*)a.dv, a.N, a.W, a.tab, a.rope, scale, tiles);
+    bwd_key_ps_kernel<DEV><<<grid, block, 0, a.stream>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
+        (const bf16_t*)a.v, (const bf16_t*)a.dout, a.lse, delta, ps, (bf16_t*)a.dk, (bf16_t*)a.dv, a.N, a.W, a.tab,
+        a.rope, scale, tiles, a.plan);
   } else {
-    bwd_key_kernel<T, MODE><<<grid, block, 0, a.stream>>>((const T*)a.q, (const T*)a.k, (const T*)a.v,
-        (const T*)a.dout, a.lse, delta, (T*)a.dk, (T*)a.dv, a.N, a.W, a.tab, a.rope, scale, tiles);
+    bwd_key_kernel<T, MODE, DEV><<<grid, block, 0, a.stream>>>((const T*)a.q, (const T*)a.k, (const T*)a.v,
+        (const T*)a.dout, a.lse, delta, (T*)a.dk, (T*)a.dv, a.N, a.W, a.tab, a.rope, scale, tiles, a.plan);
   }
   if (a.dalpha != nullptr) {
     if (MODE == 1)
@@ -437,8 +444,12 @@ size_t bwd_workspace_bytes(int64_t BH, int64_t N, int dtype, int mode) {
 }
 
 hipError_t launch_bwd(const BwdArgs& a) {
-  if (a.dtype == 0) return a.mode == 0 ? run<float, 0>(a) : run<float, 1>(a);
-  return a.mode == 0 ? run<bf16_t, 0>(a) : run<bf16_t, 1>(a);
+  if (a.plan != nullptr) {
+    if (a.dtype == 0) return a.mode == 0 ? run<float, 0, true>(a) : run<float, 1, true>(a);
+    return a.mode == 0 ? run<bf16_t, 0, true>(a) : run<bf16_t, 1, true>(a);
+  }
+  if (a.dtype == 0) return a.mode == 0 ? run<float, 0, false>(a) : run<float, 1, false>(a);
+  return a.mode == 0 ? run<bf16_t, 0, false>(a) : run<bf16_t, 1, false>(a);
 }
 
 }  // namespace fib

@@ -57,6 +57,8 @@ struct BkArgs {
   int far_dist[kMaxFar];
   float far_w[kMaxFar];
   Rope rope;
+  const DevPlan* plan;  // alpha in device memory: the split above comes from here (DEV instances)
+  int n_far;            // far entries in use (DEV instances: NF is an upper bound)
 };
 
 struct __align__(16) BkSmem {
@@ -78,12 +80,12 @@ struct FarQ {
 };
 
 template <int NF>
-__device__ __forceinline__ void load_far_q(FarQ<NF>& fq, const BkArgs& a, const bf16_t* Qh, const bf16_t* Dh,
+__device__ __forceinline__ void load_far_q(const int* fdist, FarQ<NF>& fq, const BkArgs& a, const bf16_t* Qh, const bf16_t* Dh,
                                            const float* Lh, const float* Th, int j0, int n, int g, int lane_off) {
   const float log2e = 1.4426950408889634f;
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    const int r0 = j0 + a.far_dist[f];
+    const int r0 = j0 + fdist[f];
     int64_t off;
     int r = r0 + n;
     if (r0 + 15 < a.N) {
@@ -123,11 +125,11 @@ __device__ __forceinline__ uint32_t ld4(const void* base, uint32_t off) {
 }
 
 template <int NF>
-__device__ __forceinline__ void load_far_qi(FarQI<NF>& fq, const BkArgs& a, const bf16_t* Qh, const bf16_t* Dh,
+__device__ __forceinline__ void load_far_qi(const int* fdist, FarQI<NF>& fq, const BkArgs& a, const bf16_t* Qh, const bf16_t* Dh,
                                             const uint32_t* Sh, int n_cov, int j0, int l, int n, int g) {
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    const int r0 = j0 + a.far_dist[f];
+    const int r0 = j0 + fdist[f];
     // rows past the end repeat row N - 1 (their weights are zero)
     const int rb = r0 < a.N ? r0 : a.N - 1;
     const int r = r0 + n;
@@ -164,7 +166,7 @@ __device__ __forceinline__ float dot16_bf(uint4 x0, uint4 x1, uint4 y0, uint4 y1
   return dot2(x1.w, y1.w, s);
 }
 
-template <int MODE, int NC, int NF>
+template <int MODE, int NC, int NF, bool DEV>
 __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
   constexpr int WAVES = 8;
   constexpr int kThreads = 64 * WAVES;
@@ -182,10 +184,27 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
   const int N = a.N;
   const float log2e = 1.4426950408889634f;
 
+  // alpha-dependent launch data: the kernel arguments, or (DEV instances, alpha in device
+  // memory) the split built on the device, read once into registers (the arguments struct
+  // itself is never written, so it stays in the kernel-argument segment)
+  RingSplit lcl;
+  if constexpr (DEV) lcl = a.plan->s8;
+  const int S_n_cov = DEV ? lcl.n_cov : a.n_cov;
+  const int S_n_far = DEV ? lcl.n_far : a.n_far;
+  const int S_lead = DEV ? ((lcl.need + kT - 1) / kT) * kT : a.lead;
+  auto S_dist = [&](int x) -> int { if constexpr (DEV) return lcl.dist[x]; else return a.dist[x]; };
+  auto S_w = [&](int x) -> float { if constexpr (DEV) return lcl.w[x]; else return a.w[x]; };
+  auto S_far_dist = [&](int x) -> int { if constexpr (DEV) return lcl.far_dist[x]; else return a.far_dist[x]; };
+  auto S_far_w = [&](int x) -> float { if constexpr (DEV) return lcl.far_w[x]; else return a.far_w[x]; };
+
+
   constexpr int n_unc = MODE == 1 ? 2 * NF : NF;
   for (int x = tid; x < n_unc * kHalf; x += kThreads) {
     const int u = x / kHalf, j = x % kHalf;
-    const int d = MODE == 1 ? a.far_dist[u >> 1] - (u & 1) : a.far_dist[u];
+    int fd;
+    if constexpr (DEV) fd = a.plan->s8.far_dist[MODE == 1 ? u >> 1 : u];
+    else fd = S_far_dist(MODE == 1 ? u >> 1 : u);  // (a's arrays: constant indices in DEV instances)
+    const int d = MODE == 1 ? fd - (u & 1) : fd;
     sm.unc_cs[u][j] = rope_cs(d, a.rope.rev[j]);
   }
   float2 cs_t[8];
@@ -279,12 +298,12 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
   };
 
   // ---- warm-up: query rows [s0, s0 + lead) (lead is a step multiple)
-  const int n_warm = a.lead / kT;
+  const int n_warm = S_lead / kT;
   if (tid < kHalf * (n_warm + 2)) {
     const int j = tid / kHalf, t = tid % kHalf;
     if (j < n_warm) sm.warm_cs[j][t] = rope_cs(s0 + j * kT, a.rope.rev[t]);
     else if (j == n_warm) sm.base_cs[0][0][t] = rope_cs(s0, a.rope.rev[t]);
-    else sm.base_cs[0][1][t] = rope_cs(s0 + a.lead, a.rope.rev[t]);
+    else sm.base_cs[0][1][t] = rope_cs(s0 + S_lead, a.rope.rev[t]);
   }
   // this step's keys and inserted query rows, prefetched one step ahead
   uint4 pk[2], pv[2], pq[2], pd[2];
@@ -298,13 +317,13 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
       const int jb = pb + 16 * wave;
 #pragma unroll
       for (int e = 0; e < NC; ++e) {
-        const int b = jb + a.dist[e] - 1 < N ? jb + a.dist[e] - 1 : N - 1;  // >= 0
-        const int ilo = jb + a.dist[e] + n;
+        const int b = jb + S_dist(e) - 1 < N ? jb + S_dist(e) - 1 : N - 1;  // >= 0
+        const int ilo = jb + S_dist(e) + n;
         const uint32_t* se = Sh + (size_t)e * N + b;
         uint32_t x = ld4(se, (uint32_t)((ilo < N ? ilo : N - 1) - b) * 4u);
         uint32_t y = ld4(se, (uint32_t)((ilo - 1 < N ? ilo - 1 : N - 1) - b) * 4u);
         asm volatile("" : "+v"(x), "+v"(y));  // keeps the loads unconditional (no branches)
-        const bool use = diag_lane && e < a.n_cov;
+        const bool use = diag_lane && e < S_n_cov;
         psl[e] = use && ilo < N ? x : 0u;
         psh[e] = use && ilo - 1 < N ? y : 0u;
       }
@@ -314,7 +333,7 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
     const int64_t ko = row_elems(pb + 16 * wave);
     load2(Kh, ko, pk);
     load2(Vh, ko, pv);
-    const int qb = pb + a.lead + 16 * wave;
+    const int qb = pb + S_lead + 16 * wave;
     const int64_t qo = row_elems(qb);
     load2(Qh, qo, pq);
     load2(Dh, qo, pd);
@@ -339,9 +358,9 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
   FarQ<MODE == 0 ? NF : 0> fq;
   FarQI<MODE == 1 ? NF : 0> fi;
   if constexpr (MODE == 0)
-    load_far_q<NF>(fq, a, Qh, Dh, Lh, Th, s0 + 16 * wave, n, g, lane_off);
+    load_far_q<NF>(DEV ? lcl.far_dist : a.far_dist, fq, a, Qh, Dh, Lh, Th, s0 + 16 * wave, n, g, lane_off);
   else
-    load_far_qi<NF>(fi, a, Qh, Dh, Sh, a.n_cov, s0 + 16 * wave, l, n, g);
+    load_far_qi<NF>(DEV ? lcl.far_dist : a.far_dist, fi, a, Qh, Dh, Sh, S_n_cov, s0 + 16 * wave, l, n, g);
 
   int buf = 0;
   for (int p0 = s0; p0 < s1; p0 += kT, buf ^= 1) {
@@ -360,14 +379,14 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
       unpack8(pk[0], kf);
       unpack8(pk[1], kf + 8);
       rotate_pack_f(kf, csk, &kh0, &kh1);
-      put_query(p0 + a.lead + 16 * wave, csq, pq, pd, plse, pdlt);
+      put_query(p0 + S_lead + 16 * wave, csq, pq, pd, plse, pdlt);
     }
     __syncthreads();
     const int pn = p0 + kT;
     load_step(pn < s1 ? pn : p0);
     if (wave == 0 && l < kHalf) {
       sm.base_cs[buf ^ 1][0][l] = rope_cs(pn, a.rope.rev[l]);
-      sm.base_cs[buf ^ 1][1][l] = rope_cs(pn + a.lead, a.rope.rev[l]);
+      sm.base_cs[buf ^ 1][1][l] = rope_cs(pn + S_lead, a.rope.rev[l]);
     }
 
     const int j0 = p0 + 16 * wave;
@@ -433,7 +452,7 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
       float p2[2], ds2[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int sl = row_off(j0 + a.dist[e + h]);
+        const int sl = row_off(j0 + S_dist(e + h));
         f4 S = {0, 0, 0, 0}, P = {0, 0, 0, 0};
         S = mfma32(as_bf8(lds_read16(sm.ringQ, sl + lane_k)), bk0, S);
         S = mfma32(as_bf8(lds_read16(sm.ringQ, sl + lane_k + 64)), bk1, S);
@@ -442,13 +461,13 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
         // (LSE, Delta) of query row j0 + r + n
         const float2 ld = *reinterpret_cast<const float2*>(sm.ringQ + sl + n * kRow + 128);
         float x = fmaf(sel4(S, l), sl2, bias_diag);
-        if (e + h >= a.n_cov) x = -INFINITY;
+        if (e + h >= S_n_cov) x = -INFINITY;
         p2[h] = ex2(x - ld.x);
         ds2[h] = p2[h] * (sel4(P, l) - ld.y);
       }
       const bf16x8 bp = diag_block(pack_bf2(p2[0], p2[1]), sel);
       const bf16x8 bs = diag_block(pack_bf2(ds2[0], ds2[1]), sel);
-      const int ra = row_off(j0 + a.dist[e]) + lane_t, rb = row_off(j0 + a.dist[e + 1]) + lane_t;
+      const int ra = row_off(j0 + S_dist(e)) + lane_t, rb = row_off(j0 + S_dist(e + 1)) + lane_t;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         const int o = 8 * (mb & 1) + 64 * (mb >> 1);
@@ -463,13 +482,13 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
       // rounding residuals (two MFMAs): the weights keep the stored dS's 12 significant bits.
 #pragma unroll
       for (int e = 0; e < NC; ++e) {
-        const float w = a.w[e];
+        const float w = S_w(e);
         const float xs = ps_ds(psl[e]) * (1.f - w), ys = ps_ds(psh[e]) * w;
         const uint32_t hs = pack_bf2(xs, ys);
         const bf16x8 bs = diag_block(hs, sel);
         const bf16x8 bs2 = diag_block(pack_bf2(xs - bf_lo(hs), ys - bf_hi(hs)), sel);
         const bf16x8 bp = diag_block(pack_bf2(ps_p(psl[e]) * (1.f - w), ps_p(psh[e]) * w), sel);
-        const int ra = row_off(j0 + a.dist[e]) + lane_t, rb = row_off(j0 + a.dist[e] - 1) + lane_t;
+        const int ra = row_off(j0 + S_dist(e)) + lane_t, rb = row_off(j0 + S_dist(e) - 1) + lane_t;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
           const int o = 8 * (mb & 1) + 64 * (mb >> 1);
@@ -507,7 +526,8 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
       f4 S = {0, 0, 0, 0};
       S = mfma32(as_bf8(r0), as_bf8(kraw0), S);
       S = mfma32(as_bf8(r1), as_bf8(kraw1), S);
-      const float x = fmaf(sel4(S, l), sl2, bias_diag) - fq.lse2[f];
+      float x = fmaf(sel4(S, l), sl2, bias_diag) - fq.lse2[f];
+      if (DEV && f >= S_n_far) x = -INFINITY;  // slot beyond the table
       const float p = __uint_as_float((uint32_t)__builtin_amdgcn_ds_bpermute(diag_addr, (int)__float_as_uint(ex2(x))));
       const float dp = quad_add(dot16_bf(fq.d[f][0], fq.d[f][1], v0, v1));
       const uint32_t y = pack_bf2(p * (dp - fq.dlt[f]), p);  // (dS, P) in bf16
@@ -527,7 +547,7 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
         vhv[2 * u + 1] = dot2(de[4 + u], p_hi, vhv[2 * u + 1]);
       }
     }
-    load_far_q<NF>(fq, a, Qh, Dh, Lh, Th, j0 + kT, n, g, lane_off);
+    load_far_q<NF>(DEV ? lcl.far_dist : a.far_dist, fq, a, Qh, Dh, Lh, Th, j0 + kT, n, g, lane_off);
     } else {
       // interpolated far entries: the lower query row (the lane's, rotated by R_c) and the
       // upper row (rotated by R_(c-1)) in fp32, weighted by the stored (P, dS) in fp32.
@@ -536,9 +556,11 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
-        const float w = a.far_w[f];
-        const float al = ps_ds(fi.pl[f]) * (1.f - w), ah = ps_ds(fi.ph[f]) * w;
-        const float pl = ps_p(fi.pl[f]) * (1.f - w), ph = ps_p(fi.ph[f]) * w;
+        const float w = S_far_w(f);
+        // (a slot beyond the table weighs nothing)
+        const float keep = DEV && f >= S_n_far ? 0.f : 1.f;
+        const float al = keep * ps_ds(fi.pl[f]) * (1.f - w), ah = keep * ps_ds(fi.ph[f]) * w;
+        const float pl = keep * ps_p(fi.pl[f]) * (1.f - w), ph = keep * ps_p(fi.ph[f]) * w;
 #pragma unroll
         for (int tsr = 0; tsr < 2; ++tsr) {
 #pragma unroll
@@ -627,39 +649,54 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
     }
     // interpolated: the next step's far rows, requested after the stores (the far terms above
     // feed only the stores; requested earlier, the new rows would be held alongside them)
-    if constexpr (MODE == 1) load_far_qi<NF>(fi, a, Qh, Dh, Sh, a.n_cov, j0 + kT, l, n, g);
+    if constexpr (MODE == 1) load_far_qi<NF>(DEV ? lcl.far_dist : a.far_dist, fi, a, Qh, Dh, Sh, S_n_cov, j0 + kT, l, n, g);
     __syncthreads();
   }
 }
 
-template <int MODE, int NC, int NF>
+template <int MODE, int NC, int NF, bool DEV>
 hipError_t launch(const BkArgs& a, unsigned blocks, hipStream_t s) {
-  const size_t smem = sizeof(BkSmem);
-  hipError_t e = hipFuncSetAttribute((const void*)bwdk_ring_kernel<MODE, NC, NF>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  if (e != hipSuccess) return e;
-  bwdk_ring_kernel<MODE, NC, NF><<<blocks, 512, smem, s>>>(a);
-  return hipGetLastError();
+  if constexpr (DEV && NC != 16) {
+    return hipErrorInvalidValue;
+  } else {
+    const size_t smem = sizeof(BkSmem);
+    hipError_t e = hipFuncSetAttribute((const void*)bwdk_ring_kernel<MODE, NC, NF, DEV>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    bwdk_ring_kernel<MODE, NC, NF, DEV><<<blocks, 512, smem, s>>>(a);
+    return hipGetLastError();
+  }
 }
 
-template <int MODE, int NC>
+template <int MODE, int NC, bool DEV>
 hipError_t launch_far(const BkArgs& a, int n_far, unsigned blocks, hipStream_t s) {
   switch (n_far) {
-    case 0: return launch<MODE, NC, 0>(a, blocks, s);
-    case 1: return launch<MODE, NC, 1>(a, blocks, s);
-    case 2: return launch<MODE, NC, 2>(a, blocks, s);
-    default: return launch<MODE, NC, 3>(a, blocks, s);
+    case 0: return launch<MODE, NC, 0, DEV>(a, blocks, s);
+    case 1: return launch<MODE, NC, 1, DEV>(a, blocks, s);
+    case 2: return launch<MODE, NC, 2, DEV>(a, blocks, s);
+    default: return launch<MODE, NC, 3, DEV>(a, blocks, s);
   }
 }
 
 constexpr int kMaxFarK = 3;  // far offsets whose rows fit the registers at 8 waves
+
+// covered and far counts (with alpha in device memory: bounds over the alpha range, and 16
+// covered slots)
+void split(const BwdArgs& f, int* n_cov, int* n_far) {
+  if (f.plan != nullptr) {
+    range_counts(f.alpha_lo, f.alpha_hi, f.base, f.n_base, f.W, f.mode, f.N, 8, n_cov, n_far);
+    if (*n_cov <= kMaxCov) *n_cov = kMaxCov;
+  } else {
+    split_table(f.tab, f.N, 8, n_cov, n_far);
+  }
+}
 
 }  // namespace
 
 bool bwdk_ring_supported(const BwdArgs& f) {
   if (f.dtype != 1 || f.W > kMaxBand || f.N > (1LL << 30)) return false;
   int cov, far;
-  split_table(f.tab, f.N, 8, &cov, &far);
+  split(f, &cov, &far);
   return far <= kMaxFarK && cov <= kMaxCov;
 }
 
@@ -678,7 +715,9 @@ hipError_t launch_bwdk_ring(const BwdArgs& f, const float* delta, const uint32_t
   a.N = (int)f.N;
   a.W = f.W;
   int n_far;
-  split_table(f.tab, f.N, 8, &a.n_cov, &n_far);
+  split(f, &a.n_cov, &n_far);
+  a.plan = f.plan;
+  a.n_far = n_far;
   for (int e = 0; e < kMaxCov; ++e) {
     a.dist[e] = e < a.n_cov ? f.tab.dist[e] : kMaxBand;
     a.w[e] = e < a.n_cov ? f.tab.w[e] : 0.f;
@@ -702,9 +741,14 @@ hipError_t launch_bwdk_ring(const BwdArgs& f, const float* delta, const uint32_t
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)kD));
   a.rope = f.rope;
   const unsigned blocks = (unsigned)(segs * f.BH);
+  if (f.plan != nullptr)
+    return f.mode == 0 ? launch_far<0, 16, true>(a, n_far, blocks, f.stream)
+                       : launch_far<1, 16, true>(a, n_far, blocks, f.stream);
   if (f.mode == 0)
-    return a.n_cov <= 8 ? launch_far<0, 8>(a, n_far, blocks, f.stream) : launch_far<0, 16>(a, n_far, blocks, f.stream);
-  return a.n_cov <= 8 ? launch_far<1, 8>(a, n_far, blocks, f.stream) : launch_far<1, 16>(a, n_far, blocks, f.stream);
+    return a.n_cov <= 8 ? launch_far<0, 8, false>(a, n_far, blocks, f.stream)
+                        : launch_far<0, 16, false>(a, n_far, blocks, f.stream);
+  return a.n_cov <= 8 ? launch_far<1, 8, false>(a, n_far, blocks, f.stream)
+                      : launch_far<1, 16, false>(a, n_far, blocks, f.stream);
 }
 
 }  // namespace fib

@@ -54,6 +54,8 @@ struct BqArgs {
   float far_f[kMaxFar];
   int unc_dist[kMaxUnc];
   Rope rope;
+  const DevPlan* plan;  // alpha in device memory: the split above comes from here (DEV instances)
+  int n_far;            // far entries in use (DEV instances: NF is an upper bound)
 };
 
 struct __align__(16) BqSmem {
@@ -77,16 +79,16 @@ struct FarK {
 };
 
 template <int MODE, int NF>
-__device__ __forceinline__ void load_far(FarK<MODE, NF>& fr, const BqArgs& a, const bf16_t* X, int i0w, int l,
+__device__ __forceinline__ void load_far(const int* fdist, FarK<MODE, NF>& fr, const BqArgs& a, const bf16_t* X, int i0w, int l,
                                          int n, int g, int lane_off) {
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    const bf16_t* p = X + far_off(a.far_dist[f], i0w, n, g, lane_off);
+    const bf16_t* p = X + far_off(fdist[f], i0w, n, g, lane_off);
     fr.k[f][0] = *reinterpret_cast<const uint4*>(p);
     fr.k[f][1] = *reinterpret_cast<const uint4*>(p + kHalf);
     if constexpr (MODE == 1) {
       // row i0w - d + 16 (< N: far distances exceed 16); rows before 0 only meet masked queries
-      const int r = i0w - a.far_dist[f] + 16;
+      const int r = i0w - fdist[f] + 16;
       fr.ex[f] = reinterpret_cast<const uint32_t*>(X + (int64_t)(r > 0 ? r : 0) * kD)[l & 31];
     }
   }
@@ -139,7 +141,7 @@ __device__ __forceinline__ void add_unrot(float* lo, float* hi, float c, uint4 x
   }
 }
 
-template <int MODE, int NC, int NF, int WAVES>
+template <int MODE, int NC, int NF, int WAVES, bool DEV>
 __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
   constexpr int kThreads = 64 * WAVES;
   constexpr int kT = step_rows(WAVES);
@@ -155,12 +157,31 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
   const int jc = n & 3;
   const int N = a.N;
   const float log2e = 1.4426950408889634f;
+  // alpha-dependent launch data: the kernel arguments, or (DEV instances, alpha in device
+  // memory) the split built on the device, read once into registers (the arguments struct
+  // itself is never written, so it stays in the kernel-argument segment)
+  RingSplit lcl;
+  if constexpr (DEV) lcl = (WAVES == 8 ? a.plan->s8 : a.plan->s4);
+  const int S_n_cov = DEV ? lcl.n_cov : a.n_cov;
+  const int S_n_far = DEV ? lcl.n_far : a.n_far;
+  const int S_early_rows = DEV ? lcl.early_rows : a.early_rows;
+  const int S_warm = DEV ? ((lcl.need + kT - 1) / kT) * kT : a.warm;
+  auto S_dist = [&](int x) -> int { if constexpr (DEV) return lcl.dist[x]; else return a.dist[x]; };
+  auto S_w = [&](int x) -> float { if constexpr (DEV) return lcl.w[x]; else return a.w[x]; };
+  auto S_f = [&](int x) -> float { if constexpr (DEV) return lcl.f[x]; else return a.f[x]; };
+  auto S_far_dist = [&](int x) -> int { if constexpr (DEV) return lcl.far_dist[x]; else return a.far_dist[x]; };
+  auto S_far_w = [&](int x) -> float { if constexpr (DEV) return lcl.far_w[x]; else return a.far_w[x]; };
+  auto S_far_f = [&](int x) -> float { if constexpr (DEV) return lcl.far_f[x]; else return a.far_f[x]; };
+
 
   {
     constexpr int n_unc = MODE == 1 ? 2 * NF : NF;
     for (int x = tid; x < n_unc * kHalf; x += kThreads) {
       const int u = x / kHalf, j = x % kHalf;
-      sm.unc_cs[u][j] = rope_cs(a.unc_dist[u], a.rope.rev[j]);
+      int d;
+      if constexpr (DEV) d = (WAVES == 8 ? a.plan->s8 : a.plan->s4).unc_dist[u];
+      else d = a.unc_dist[u];  // (a's arrays are indexed by constants only in DEV instances)
+      sm.unc_cs[u][j] = rope_cs(d, a.rope.rev[j]);
     }
   }
   float2 cs_t[8];
@@ -238,9 +259,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
   };
 
   // ---- warm-up (as in the forward): ring rows [ws, s0)
-  const int ws = s0 - a.warm > 0 ? s0 - a.warm : 0;
+  const int ws = s0 - S_warm > 0 ? s0 - S_warm : 0;
   const int n_warm = (s0 - ws) / kT;
-  if (s0 < a.warm) {
+  if (s0 < S_warm) {
     uint4* z = reinterpret_cast<uint4*>(sm.ringK);
     const int n16 = (2 * (kP + kMirror) * kRow) / 16;
     for (int x = tid; x < n16; x += kThreads) z[x] = make_uint4(0, 0, 0, 0);
@@ -294,7 +315,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
     }
   }
   FarK<MODE, NF> fk;
-  load_far<MODE, NF>(fk, a, Kh, s0 + 16 * wave, l, n, g, lane_off);
+  load_far<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, fk, a, Kh, s0 + 16 * wave, l, n, g, lane_off);
   float dal = 0.f;  // d(alpha) contributions of this lane's queries
 
   int buf = 0;
@@ -338,7 +359,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
     const int bw = p0 + 16 * wave;
     const int i0w = bw;
     const int iq = i0w + n;
-    const bool early = i0w < a.early_rows;
+    const bool early = i0w < S_early_rows;
     // O rows of the step's queries, for Delta (used after the logits)
     uint4 oo[2];
     load2(Oh, row_elems(i0w), oo);
@@ -363,7 +384,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
     float s_e[NC], dp_e[NC], sd_e[MODE == 1 ? NC : 1], dd_e[MODE == 1 ? NC : 1];
 #pragma unroll
     for (int e = 0; e < NC; ++e) {
-      int sl = row_off(bw - a.dist[e]) + lane_k;
+      int sl = row_off(bw - S_dist(e)) + lane_k;
       if (MODE == 1 && (e & 1) == 0) asm volatile("" : "+v"(sl));
       f4 S = {0, 0, 0, 0}, P = {0, 0, 0, 0};
       S = mfma32(as_bf8(lds_read16(sm.ringK, sl)), bq0, S);
@@ -410,7 +431,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
       }
     }
     FarK<MODE, NF> fv;
-    load_far<MODE, NF>(fv, a, Vh, i0w, l, n, g, lane_off);
+    load_far<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, fv, a, Vh, i0w, l, n, g, lane_off);
 
     // ---- P, Delta, dS
     const float dlt = quad_add(dot16_bf(do0, do1, oo[0], oo[1]));
@@ -432,15 +453,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
     for (int e = 0; e < NC; ++e) {
       float s = s_e[e], dp = dp_e[e];
       if (MODE == 1) {
-        s = fmaf(a.w[e], sd_e[e], s);
-        dp = fmaf(a.w[e], dd_e[e], dp);
+        s = fmaf(S_w(e), sd_e[e], s);
+        dp = fmaf(S_w(e), dd_e[e], dp);
       }
       float x = fmaf(s, sl2, bias_diag);
-      if (e >= a.n_cov || (early && a.dist[e] > iq)) x = -INFINITY;
+      if (e >= S_n_cov || (early && S_dist(e) > iq)) x = -INFINITY;
       const float p = ex2(x - lse2);
       ds_e[e] = p * (dp - dlt);
       if (MODE == 1) {
-        dal_step = fmaf(-a.f[e], ds_e[e] * a.scale * sd_e[e] + p * dd_e[e], dal_step);
+        dal_step = fmaf(-S_f(e), ds_e[e] * a.scale * sd_e[e] + p * dd_e[e], dal_step);
         ps_e[e] = ps_pack(p, ds_e[e]);
       }
     }
@@ -466,7 +487,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
 #pragma unroll
       for (int e = 0; e < NC; e += 2) {
         const bf16x8 bp = diag_block(pack_bf2(ds_e[e], ds_e[e + 1]), sel);
-        const int ra = row_off(bw - a.dist[e]) + lane_t, rb = row_off(bw - a.dist[e + 1]) + lane_t;
+        const int ra = row_off(bw - S_dist(e)) + lane_t, rb = row_off(bw - S_dist(e + 1)) + lane_t;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
           const int o = 8 * (mb & 1) + 64 * (mb >> 1);
@@ -477,8 +498,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
 #pragma unroll
       for (int e = 0; e < NC; ++e) {
         const float ds = ds_e[e];
-        const bf16x8 bp = diag_block(pack_bf2(ds * (1.f - a.w[e]), ds * a.w[e]), sel);
-        const int ra = row_off(bw - a.dist[e]) + lane_t, rb = ra + kRow;
+        const bf16x8 bp = diag_block(pack_bf2(ds * (1.f - S_w(e)), ds * S_w(e)), sel);
+        const int ra = row_off(bw - S_dist(e)) + lane_t, rb = ra + kRow;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
           const int o = 8 * (mb & 1) + 64 * (mb >> 1);
@@ -502,9 +523,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
     for (int f = 0; f < NF; ++f) {
       const int u = MODE == 1 ? 2 * f : f;
       float s = s_f[f];
-      if (MODE == 1) s = fmaf(a.far_w[f], sd_f[f], s);
+      if (MODE == 1) s = fmaf(S_far_w(f), sd_f[f], s);
       float x = fmaf(s, sl2, bias_diag);
-      if (early && a.far_dist[f] > iq) x = -INFINITY;
+      if (early && S_far_dist(f) > iq) x = -INFINITY;
+      if (DEV && f >= S_n_far) x = -INFINITY;  // slot beyond the table
       // P of the query, from its diagonal lane to all four
       const float p = __uint_as_float(
           (uint32_t)__builtin_amdgcn_ds_bpermute(diag_addr, (int)__float_as_uint(ex2(x - lse2))));
@@ -516,13 +538,13 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
         uint4 vh[2], kh[2];
         upper_rows(fv.k[f], fv.ex[f], g, vh);
         const float dp_hi = quad_add(dot16_bf(do0, do1, vh[0], vh[1]));
-        const float w = a.far_w[f];
+        const float w = S_far_w(f);
         const float ds = p * (fmaf(w, dp_hi - dp_lo, dp_lo) - dlt);
         add_unrot(ql, qhv, ds * (1.f - w), fk.k[f][0], fk.k[f][1], &sm.unc_cs[u][8 * g]);
         upper_rows(fk.k[f], fk.ex[f], g, kh);
         add_unrot(ql, qhv, ds * w, kh[0], kh[1], &sm.unc_cs[u + 1][8 * g]);
         // the diagonal lane holds s_hi - s_lo of its query
-        if (diag_lane) dal_step = fmaf(-a.far_f[f], ds * a.scale * sd_f[f] + p * (dp_hi - dp_lo), dal_step);
+        if (diag_lane) dal_step = fmaf(-S_far_f(f), ds * a.scale * sd_f[f] + p * (dp_hi - dp_lo), dal_step);
         ps_f[f] = ps_pack(p, ds);
       }
     }
@@ -553,12 +575,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
         uint32_t* pq = a.ps + (size_t)head * kMaxEnt * N + iq;
 #pragma unroll
         for (int e = 0; e < NC; ++e)
-          if (e < a.n_cov) pq[(size_t)e * N] = ps_e[e];
+          if (e < S_n_cov) pq[(size_t)e * N] = ps_e[e];
 #pragma unroll
-        for (int f = 0; f < NF; ++f) pq[(size_t)(a.n_cov + f) * N] = ps_f[f];
+        for (int f = 0; f < NF; ++f) pq[(size_t)(S_n_cov + f) * N] = ps_f[f];
       }
     }
-    load_far<MODE, NF>(fk, a, Kh, i0w + kT, l, n, g, lane_off);
+    load_far<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, fk, a, Kh, i0w + kT, l, n, g, lane_off);
     __syncthreads();
   }
   if (MODE == 1) {
@@ -587,44 +609,56 @@ constexpr bool unused_instance() {
   return WAVES == 8 && !fits8(NC, NF);
 }
 
-template <int MODE, int NC, int NF, int WAVES>
+template <int MODE, int NC, int NF, int WAVES, bool DEV>
 hipError_t launch(const BqArgs& a, unsigned blocks, hipStream_t s) {
-  if constexpr (unused_instance<MODE, NC, NF, WAVES>()) {
+  if constexpr (unused_instance<MODE, NC, NF, WAVES>() || (DEV && NC != 16)) {
     return hipErrorInvalidValue;
   } else {
     const size_t smem = sizeof(BqSmem);
-    hipError_t e = hipFuncSetAttribute((const void*)bwdq_ring_kernel<MODE, NC, NF, WAVES>,
+    hipError_t e = hipFuncSetAttribute((const void*)bwdq_ring_kernel<MODE, NC, NF, WAVES, DEV>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
-    bwdq_ring_kernel<MODE, NC, NF, WAVES><<<blocks, 64 * WAVES, smem, s>>>(a);
+    bwdq_ring_kernel<MODE, NC, NF, WAVES, DEV><<<blocks, 64 * WAVES, smem, s>>>(a);
     return hipGetLastError();
   }
 }
 
-template <int MODE, int WAVES>
+// kernel instance by (covered entries rounded up to 8 or 16, far entries); with alpha in
+// device memory (DEV) always 16 covered slots
+template <int MODE, int WAVES, bool DEV = false>
 hipError_t launch_far(const BqArgs& a, int n_far, unsigned blocks, hipStream_t s) {
-  if (a.n_cov <= 8) {
+  if (DEV || a.n_cov > 8) {
     switch (n_far) {
-      case 0: return launch<MODE, 8, 0, WAVES>(a, blocks, s);
-      case 1: return launch<MODE, 8, 1, WAVES>(a, blocks, s);
-      case 2: return launch<MODE, 8, 2, WAVES>(a, blocks, s);
-      case 3: return launch<MODE, 8, 3, WAVES>(a, blocks, s);
-      default: return launch<MODE, 8, 4, WAVES>(a, blocks, s);
+      case 0: return launch<MODE, 16, 0, WAVES, DEV>(a, blocks, s);
+      case 1: return launch<MODE, 16, 1, WAVES, DEV>(a, blocks, s);
+      case 2: return launch<MODE, 16, 2, WAVES, DEV>(a, blocks, s);
+      case 3: return launch<MODE, 16, 3, WAVES, DEV>(a, blocks, s);
+      default: return launch<MODE, 16, 4, WAVES, DEV>(a, blocks, s);
     }
   }
   switch (n_far) {
-    case 0: return launch<MODE, 16, 0, WAVES>(a, blocks, s);
-    case 1: return launch<MODE, 16, 1, WAVES>(a, blocks, s);
-    case 2: return launch<MODE, 16, 2, WAVES>(a, blocks, s);
-    case 3: return launch<MODE, 16, 3, WAVES>(a, blocks, s);
-    default: return launch<MODE, 16, 4, WAVES>(a, blocks, s);
+    case 0: return launch<MODE, 8, 0, WAVES, DEV>(a, blocks, s);
+    case 1: return launch<MODE, 8, 1, WAVES, DEV>(a, blocks, s);
+    case 2: return launch<MODE, 8, 2, WAVES, DEV>(a, blocks, s);
+    case 3: return launch<MODE, 8, 3, WAVES, DEV>(a, blocks, s);
+    default: return launch<MODE, 8, 4, WAVES, DEV>(a, blocks, s);
   }
 }
 
+// With alpha in device memory the counts are upper bounds over the alpha range, and the
+// covered slots are always 16.
 int plan(const BwdArgs& f, int* n_cov, int* n_far) {
-  split_table(f.tab, f.N, 8, n_cov, n_far);
+  auto split = [&](int waves) {
+    if (f.plan != nullptr) {
+      range_counts(f.alpha_lo, f.alpha_hi, f.base, f.n_base, f.W, f.mode, f.N, waves, n_cov, n_far);
+      if (*n_cov <= kMaxCov) *n_cov = kMaxCov;
+    } else {
+      split_table(f.tab, f.N, waves, n_cov, n_far);
+    }
+  };
+  split(8);
   if (!fits8(*n_cov <= 8 ? 8 : 16, *n_far)) {
-    split_table(f.tab, f.N, 4, n_cov, n_far);
+    split(4);
     return 4;
   }
   return 8;
@@ -659,6 +693,7 @@ hipError_t launch_bwdq_ring(const BwdArgs& f, float* delta, float* part, uint32_
   a.delta = delta;
   a.dalpha_part = part;
   a.ps = ps;
+  a.plan = f.plan;
   a.N = (int)f.N;
   a.W = f.W;
   int n_far;
@@ -693,6 +728,15 @@ hipError_t launch_bwdq_ring(const BwdArgs& f, float* delta, float* part, uint32_
   a.scale = (float)(1.0 / sqrt((double)kD));
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)kD));
   a.rope = f.rope;
+  a.n_far = n_far;
+  if (f.plan != nullptr) {
+    if (f.mode == 0) {
+      return waves == 8 ? launch_far<0, 8, true>(a, n_far, (unsigned)blocks, f.stream)
+                        : launch_far<0, 4, true>(a, n_far, (unsigned)blocks, f.stream);
+    }
+    return waves == 8 ? launch_far<1, 8, true>(a, n_far, (unsigned)blocks, f.stream)
+                      : launch_far<1, 4, true>(a, n_far, (unsigned)blocks, f.stream);
+  }
   if (f.mode == 0) {
     return waves == 8 ? launch_far<0, 8>(a, n_far, (unsigned)blocks, f.stream)
                       : launch_far<0, 4>(a, n_far, (unsigned)blocks, f.stream);

@@ -23,11 +23,12 @@ namespace {
 
 constexpr int kQuads = 64;
 
-template <typename T, int MODE>
+template <typename T, int MODE, bool DEV>
 __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                      const T* __restrict__ v, T* __restrict__ o,
-                                                     float* __restrict__ lse, int64_t N, int W, Table tab,
-                                                     Rope rope, float scale_log2) {
+                                                     float* __restrict__ lse, int64_t N, int W, Table tab_arg,
+                                                     Rope rope, float scale_log2, const DevPlan* __restrict__ plan) {
+  const Table& tab = call_table<DEV>(tab_arg, plan);
   __shared__ float2 cs[kCsSlots][kHalf];
   __shared__ float red_m[kQuads], red_l[kQuads];
   __shared__ float red_o[kQuads][kD];
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
     m = mn;
   }
 
-  // merge the quads' states: quads without keys hold m = -inf, l = 0, acc = 0 and weigh 0
+  // merge the states of the quads that took keys (quads 0..nv-1, all 64 when nv >= 64)
   if (c == 0) {
     red_m[u] = m;
     red_l[u] = l;
@@ -119,10 +120,11 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
   __syncthreads();
   if (threadIdx.x < kD) {
     const int dim = threadIdx.x;
+    const int nq = nv < kQuads ? (int)nv : kQuads;  // quads that took a key
     float M = -INFINITY;
-    for (int x = 0; x < kQuads; ++x) M = fmaxf(M, red_m[x]);  // finite: distance 0 always exists
+    for (int x = 0; x < nq; ++x) M = fmaxf(M, red_m[x]);  // finite: distance 0 always exists
     float L = 0.f, Od = 0.f;
-    for (int x = 0; x < kQuads; ++x) {
+    for (int x = 0; x < nq; ++x) {
       const float sc = exp2f(red_m[x] - M);
       L = fmaf(red_l[x], sc, L);
       Od = fmaf(red_o[x][dim], sc, Od);
@@ -137,29 +139,32 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
   }
 }
 
-}  // namespace
-
-hipError_t launch_decode(const FwdArgs& a) {
+template <bool DEV>
+hipError_t launch_decode_t(const FwdArgs& a) {
   dim3 grid((unsigned)a.BH), block(256);
   const float sl2 = (float)(1.4426950408889634 / sqrt((double)kD));
   if (a.dtype == 0) {
     if (a.mode == 0)
-      decode_kernel<float, 0><<<grid, block, 0, a.stream>>>((const float*)a.q, (const float*)a.k, (const float*)a.v,
-                                                           (float*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2);
+      decode_kernel<float, 0, DEV><<<grid, block, 0, a.stream>>>((const float*)a.q, (const float*)a.k,
+          (const float*)a.v, (float*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, a.plan);
     else
-      decode_kernel<float, 1><<<grid, block, 0, a.stream>>>((const float*)a.q, (const float*)a.k, (const float*)a.v,
-                                                           (float*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2);
+      decode_kernel<float, 1, DEV><<<grid, block, 0, a.stream>>>((const float*)a.q, (const float*)a.k,
+          (const float*)a.v, (float*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, a.plan);
   } else {
     if (a.mode == 0)
-      decode_kernel<bf16_t, 0><<<grid, block, 0, a.stream>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
-                                                            (const bf16_t*)a.v, (bf16_t*)a.o, a.lse, a.N, a.W,
-                                                            a.tab, a.rope, sl2);
+      decode_kernel<bf16_t, 0, DEV><<<grid, block, 0, a.stream>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
+          (const bf16_t*)a.v, (bf16_t*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, a.plan);
     else
-      decode_kernel<bf16_t, 1><<<grid, block, 0, a.stream>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
-                                                            (const bf16_t*)a.v, (bf16_t*)a.o, a.lse, a.N, a.W,
-                                                            a.tab, a.rope, sl2);
+      decode_kernel<bf16_t, 1, DEV><<<grid, block, 0, a.stream>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
+          (const bf16_t*)a.v, (bf16_t*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, a.plan);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const FwdArgs& a) {
+  return a.plan != nullptr ? launch_decode_t<true>(a) : launch_decode_t<false>(a);
 }
 
 }  // namespace fib

@@ -7,6 +7,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 namespace fib {
@@ -25,6 +26,50 @@ struct Table {
   float w[kMaxEnt];
   float f[kMaxEnt];
 };
+
+// Offset table of one call ("Depth-Staggered Fibonacci Spacing for Sparse Attention", Method >
+// Architecture and attention mechanism: d = alpha f per base offset f). mode 0 (integer):
+// r = round-half-to-even(alpha f), kept when r >= W, equal offsets collapse; mode 1
+// (interpolated): kept when alpha f >= W, c = ceil(alpha f), w = c - alpha f. alpha * f is
+// exact in fp64 (a 24-bit significand times f <= 2^24), so the rounding (rint: ties to even
+// in the default rounding mode) and the ceiling act on the true product. The same code
+// builds the table on the host and, for an alpha held in device memory, on the device.
+__host__ __device__ inline void build_table(float alpha, const int32_t* base, int n_base, int W, int mode,
+                                            Table* t) {
+  t->n = 0;
+  for (int e = 0; e < kMaxEnt; ++e) {
+    t->dist[e] = 0;
+    t->w[e] = 0.f;
+    t->f[e] = 0.f;
+  }
+  for (int e = 0; e < n_base; ++e) {
+    const double d = (double)alpha * (double)base[e];
+    if (mode == 0) {
+      const double r = rint(d);
+      if (r < (double)W || r > 2147483647.0) continue;
+      if (t->n > 0 && t->dist[t->n - 1] == (int)r) continue;  // r is non-decreasing in f
+      t->dist[t->n] = (int)r;
+      t->n++;
+    } else {
+      if (d < (double)W) continue;
+      const double c = ceil(d);
+      if (c > 2147483647.0) continue;
+      t->dist[t->n] = (int)c;
+      t->w[t->n] = (float)(c - d);
+      t->f[t->n] = (float)base[e];
+      t->n++;
+    }
+  }
+}
+
+// The table of a call: the kernel argument, or (DEV instances, alpha in device memory) the
+// one built on the device. The pointer is a read-only kernel argument, so its loads are
+// uniform (scalar) loads.
+template <bool DEV, typename Plan>
+__device__ __forceinline__ const Table& call_table(const Table& arg, const Plan* plan) {
+  if constexpr (DEV) return plan->tab;
+  else return arg;
+}
 
 // RoPE rates in revolutions per position: omega_j / (2 pi), omega_j = theta^(-2j/D), fp64.
 struct Rope {

@@ -9,6 +9,87 @@
 
 namespace fib {
 
+// ---- split of the offset table for the LDS-ring kernels --------------------------------
+// A ring kernel of `waves` waves takes 16 * waves queries per step and keeps the last
+// kRingRows rows in LDS, so it serves table entries up to kRingRows - 16 * waves from the
+// ring ("covered", a prefix of the sorted table) and reads the rest ("far", up to distance
+// N - 1) from global memory. RingSplit holds the per-entry arrays the ring kernels take;
+// unused slots hold harmless in-bounds distances and zero weights.
+constexpr int kRingRows = 512;
+constexpr int kSplitCov = 16;  // covered slots
+constexpr int kSplitFar = 4;   // far slots
+constexpr int kBandRows = 16;  // window rows ahead of a 16-query block
+
+struct RingSplit {
+  int n_cov, n_far;
+  int need;        // rows before a step that the ring must hold: max(16, largest covered distance)
+  int early_rows;  // max(16, largest usable distance): steps below it need position checks
+  int dist[kSplitCov];
+  float w[kSplitCov];
+  float f[kSplitCov];
+  int far_dist[kSplitFar];
+  float far_w[kSplitFar];
+  float far_f[kSplitFar];
+  int unc_dist[2 * kSplitFar];  // far distances (interpolated: c and c - 1 per entry)
+};
+
+__host__ __device__ inline int ring_reach(int waves) { return kRingRows - 16 * waves; }
+
+// Fills s from table t for sequences of N rows (entries at distance >= N are unusable).
+// Counts beyond the slots are left in n_cov / n_far for the caller to check.
+__host__ __device__ inline void make_split(const Table& t, int64_t N, int waves, int mode, RingSplit* s) {
+  int n = 0;
+  while (n < t.n && (int64_t)t.dist[n] < N) ++n;
+  const int reach = ring_reach(waves);
+  int cov = 0;
+  while (cov < n && t.dist[cov] <= reach) ++cov;
+  s->n_cov = cov;
+  s->n_far = n - cov;
+  s->need = kBandRows;
+  for (int e = 0; e < cov; ++e) s->need = t.dist[e] > s->need ? t.dist[e] : s->need;
+  s->early_rows = kBandRows;
+  for (int e = 0; e < n; ++e) s->early_rows = t.dist[e] > s->early_rows ? t.dist[e] : s->early_rows;
+  for (int e = 0; e < kSplitCov; ++e) {
+    const bool use = e < cov;
+    s->dist[e] = use ? t.dist[e] : kBandRows;
+    s->w[e] = use ? t.w[e] : 0.f;
+    s->f[e] = use ? t.f[e] : 0.f;
+  }
+  for (int x = 0; x < kSplitFar; ++x) {
+    const bool use = x < n - cov && cov + x < kMaxEnt;
+    s->far_dist[x] = use ? t.dist[cov + x] : reach + 1;
+    s->far_w[x] = use ? t.w[cov + x] : 0.f;
+    s->far_f[x] = use ? t.f[cov + x] : 0.f;
+  }
+  for (int x = 0; x < kSplitFar; ++x) {
+    if (mode == 1) {
+      s->unc_dist[2 * x] = s->far_dist[x];
+      s->unc_dist[2 * x + 1] = s->far_dist[x] - 1;
+    } else {
+      s->unc_dist[x] = s->far_dist[x];
+      s->unc_dist[kSplitFar + x] = 0;
+    }
+  }
+}
+
+// ---- alpha in device memory ------------------------------------------------------------
+// The alpha-dependent launch data, built on the device from *alpha by launch_dev_plan: the
+// table and its ring splits for 8-wave and 4-wave kernels. Kernels launched for an alpha
+// range read it from here instead of their arguments.
+struct DevPlan {
+  Table tab;
+  RingSplit s8;
+  RingSplit s4;
+};
+struct BaseList {
+  int32_t v[kMaxEnt];
+};
+hipError_t launch_dev_plan(DevPlan* out, const float* alpha, float alpha_lo, float alpha_hi, const BaseList& base,
+                           int n_base, int W, int mode, int64_t N, hipStream_t s);
+// Upper bounds, over alpha in [lo, hi], of the covered and far counts of make_split (host).
+void range_counts(float lo, float hi, const int32_t* base, int n_base, int W, int mode, int64_t N, int waves,
+                  int* n_cov, int* n_far);
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -20,6 +101,13 @@ struct FwdArgs {
   Table tab;
   Rope rope;
   hipStream_t stream;
+  // alpha in device memory (null: tab holds the table): the kernels read the table and its
+  // splits from *plan; the launch picks kernel instances that fit every alpha in
+  // [alpha_lo, alpha_hi] (base/n_base give the range bounds)
+  const DevPlan* plan = nullptr;
+  float alpha_lo = 0.f, alpha_hi = 0.f;
+  const int32_t* base = nullptr;
+  int n_base = 0;
 };
 
 struct BwdArgs {
@@ -39,6 +127,10 @@ struct BwdArgs {
   Rope rope;
   void* workspace;
   hipStream_t stream;
+  const DevPlan* plan = nullptr;  // as in FwdArgs
+  float alpha_lo = 0.f, alpha_hi = 0.f;
+  const int32_t* base = nullptr;
+  int n_base = 0;
 };
 
 hipError_t launch_fwd_generic(const FwdArgs& a);

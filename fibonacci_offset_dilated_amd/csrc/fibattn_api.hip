@@ -51,33 +51,6 @@ int check_scalars(int W, float alpha, float theta, int mode) {
   return FIB_OK;
 }
 
-// Offset table. alpha * f is exact in fp64 (a 24-bit significand times f <= 2^24), so the
-// rounding (ties to even, the default rounding mode of nearbyint) and the ceiling act on the
-// true product.
-void build_table(float alpha, const int32_t* base, int n_base, int W, int mode, Table* t) {
-  memset(t, 0, sizeof(*t));
-  for (int e = 0; e < n_base; ++e) {
-    const double d = (double)alpha * (double)base[e];
-    if (mode == FIB_INT) {
-      const double r = nearbyint(d);
-      if (r < (double)W || r > 2147483647.0) continue;
-      if (t->n > 0 && t->dist[t->n - 1] == (int)r) continue;  // r is non-decreasing in f
-      t->dist[t->n] = (int)r;
-      t->w[t->n] = 0.f;
-      t->f[t->n] = 0.f;
-      t->n++;
-    } else {
-      if (d < (double)W) continue;
-      const double c = ceil(d);
-      if (c > 2147483647.0) continue;
-      t->dist[t->n] = (int)c;
-      t->w[t->n] = (float)(c - d);
-      t->f[t->n] = (float)base[e];
-      t->n++;
-    }
-  }
-}
-
 Rope make_rope(float theta) {
   Rope r;
   for (int j = 0; j < kHalf; ++j)
@@ -189,49 +162,134 @@ int fib_sparse_attn_index_set(int64_t N, int W, float alpha, const int32_t* base
   return FIB_OK;
 }
 
-int fib_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                        int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
-                        int W, float alpha, const int32_t* base, int n_base,
-                        float rope_theta, int mode, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Where alpha comes from: a host value, or device memory together with the range the launch
+// is planned for and a device buffer that receives the plan (the table built from *alpha).
+struct AlphaArg {
+  bool dev;
+  float host;
+  const float* ptr;
+  float lo, hi;
+  void* plan;
+  size_t plan_bytes;
+};
+
+int check_alpha(const AlphaArg& al) {
+  if (!al.dev) return isfinite(al.host) && al.host > 0.f ? FIB_OK : FIB_ERR_ALPHA;
+  if (al.ptr == nullptr || al.plan == nullptr) return FIB_ERR_NULL;
+  if (!isfinite(al.lo) || !isfinite(al.hi) || al.lo <= 0.f || al.hi < al.lo) return FIB_ERR_ALPHA;
+  if (((uintptr_t)al.ptr & 3u) || !aligned16(al.plan)) return FIB_ERR_ALIGN;
+  if (al.plan_bytes < sizeof(DevPlan)) return FIB_ERR_WORKSPACE;
+  return FIB_OK;
+}
+
+// The call's table: built on the host, or (alpha in device memory) by a one-thread kernel
+// enqueued on the stream ahead of the attention kernels, which then read it from the plan.
+template <typename Args>
+int set_table(Args& a, const AlphaArg& al, const int32_t* base, int n_base) {
+  if (!al.dev) {
+    build_table(al.host, base, n_base, a.W, a.mode, &a.tab);
+    return FIB_OK;
+  }
+  memset(&a.tab, 0, sizeof(a.tab));
+  BaseList bl;
+  memset(&bl, 0, sizeof(bl));
+  for (int e = 0; e < n_base; ++e) bl.v[e] = base[e];
+  if (launch_dev_plan((DevPlan*)al.plan, al.ptr, al.lo, al.hi, bl, n_base, a.W, a.mode, a.N, a.stream) !=
+      hipSuccess)
+    return FIB_ERR_LAUNCH;
+  a.plan = (const DevPlan*)al.plan;
+  a.alpha_lo = al.lo;
+  a.alpha_hi = al.hi;
+  a.base = base;
+  a.n_base = n_base;
+  return FIB_OK;
+}
+
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
+             int64_t D, int dtype, int W, const AlphaArg& al, const int32_t* base, int n_base, float rope_theta,
+             int mode, void* stream, bool decode) {
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return FIB_ERR_NULL;
   int st = check_shape(B, H, N, D, dtype);
   if (st) return st;
   st = check_base(base, n_base);
   if (st) return st;
-  st = check_scalars(W, alpha, rope_theta, mode);
+  st = check_scalars(W, 1.f, rope_theta, mode);
+  if (st) return st;
+  st = check_alpha(al);
   if (st) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u))
     return FIB_ERR_ALIGN;
   FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
   a.BH = B * H; a.N = N; a.dtype = dtype; a.mode = mode; a.W = W;
-  build_table(alpha, base, n_base, W, mode, &a.tab);
   a.rope = make_rope(rope_theta);
   a.stream = (hipStream_t)stream;
-  hipError_t e = fwd_ring_supported(a) ? launch_fwd_ring(a) : launch_fwd_generic(a);
+  st = set_table(a, al, base, n_base);
+  if (st) return st;
+  hipError_t e = decode ? launch_decode(a) : fwd_ring_supported(a) ? launch_fwd_ring(a) : launch_fwd_generic(a);
   return e == hipSuccess ? FIB_OK : FIB_ERR_LAUNCH;
+}
+
+int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             void* dq, void* dk, void* dv, float* dalpha, int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+             int W, const AlphaArg& al, const int32_t* base, int n_base, float rope_theta, int mode,
+             void* workspace, size_t workspace_bytes, void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || dout == nullptr || lse == nullptr ||
+      dq == nullptr || dk == nullptr || dv == nullptr)
+    return FIB_ERR_NULL;
+  int st = check_shape(B, H, N, D, dtype);
+  if (st) return st;
+  st = check_base(base, n_base);
+  if (st) return st;
+  st = check_scalars(W, 1.f, rope_theta, mode);
+  if (st) return st;
+  st = check_alpha(al);
+  if (st) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 3u) || ((uintptr_t)dalpha & 3u))
+    return FIB_ERR_ALIGN;
+  const size_t need = bwd_workspace_bytes(B * H, N, dtype, mode);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FIB_ERR_WORKSPACE;
+  if (workspace != nullptr && !aligned16(workspace)) return FIB_ERR_ALIGN;
+  BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dalpha = dalpha;
+  a.BH = B * H; a.N = N; a.dtype = dtype; a.mode = mode; a.W = W;
+  a.rope = make_rope(rope_theta);
+  a.workspace = workspace;
+  a.stream = (hipStream_t)stream;
+  st = set_table(a, al, base, n_base);
+  if (st) return st;
+  return launch_bwd(a) == hipSuccess ? FIB_OK : FIB_ERR_LAUNCH;
+}
+
+AlphaArg host_alpha(float alpha) { return AlphaArg{false, alpha, nullptr, 0.f, 0.f, nullptr, 0}; }
+AlphaArg dev_alpha(const float* alpha, float lo, float hi, void* plan, size_t plan_bytes) {
+  return AlphaArg{true, 0.f, alpha, lo, hi, plan, plan_bytes};
+}
+
+}  // namespace
+
+extern "C" {
+
+int fib_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                        int W, float alpha, const int32_t* base, int n_base,
+                        float rope_theta, int mode, void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, N, D, dtype, W, host_alpha(alpha), base, n_base, rope_theta, mode, stream,
+                  false);
 }
 
 int fib_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
                            int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
                            int W, float alpha, const int32_t* base, int n_base,
                            float rope_theta, int mode, void* stream) {
-  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || o == nullptr) return FIB_ERR_NULL;
-  int st = check_shape(B, H, N, D, dtype);
-  if (st) return st;
-  st = check_base(base, n_base);
-  if (st) return st;
-  st = check_scalars(W, alpha, rope_theta, mode);
-  if (st) return st;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || ((uintptr_t)lse & 3u))
-    return FIB_ERR_ALIGN;
-  FwdArgs a;
-  a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = lse;
-  a.BH = B * H; a.N = N; a.dtype = dtype; a.mode = mode; a.W = W;
-  build_table(alpha, base, n_base, W, mode, &a.tab);
-  a.rope = make_rope(rope_theta);
-  a.stream = (hipStream_t)stream;
-  return launch_decode(a) == hipSuccess ? FIB_OK : FIB_ERR_LAUNCH;
+  return fwd_impl(q, k_cache, v_cache, o, lse, B, H, N, D, dtype, W, host_alpha(alpha), base, n_base, rope_theta,
+                  mode, stream, true);
 }
 
 size_t fib_sparse_attn_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, int mode) {
@@ -247,30 +305,41 @@ int fib_sparse_attn_bwd(const void* q, const void* k, const void* v, const void*
                         int W, float alpha, const int32_t* base, int n_base,
                         float rope_theta, int mode,
                         void* workspace, size_t workspace_bytes, void* stream) {
-  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || dout == nullptr || lse == nullptr ||
-      dq == nullptr || dk == nullptr || dv == nullptr)
-    return FIB_ERR_NULL;
-  int st = check_shape(B, H, N, D, dtype);
-  if (st) return st;
-  st = check_base(base, n_base);
-  if (st) return st;
-  st = check_scalars(W, alpha, rope_theta, mode);
-  if (st) return st;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
-      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 3u) || ((uintptr_t)dalpha & 3u))
-    return FIB_ERR_ALIGN;
-  const size_t need = bwd_workspace_bytes(B * H, N, dtype, mode);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FIB_ERR_WORKSPACE;
-  if (workspace != nullptr && !aligned16(workspace)) return FIB_ERR_ALIGN;
-  BwdArgs a;
-  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
-  a.dq = dq; a.dk = dk; a.dv = dv; a.dalpha = dalpha;
-  a.BH = B * H; a.N = N; a.dtype = dtype; a.mode = mode; a.W = W;
-  build_table(alpha, base, n_base, W, mode, &a.tab);
-  a.rope = make_rope(rope_theta);
-  a.workspace = workspace;
-  a.stream = (hipStream_t)stream;
-  return launch_bwd(a) == hipSuccess ? FIB_OK : FIB_ERR_LAUNCH;
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, dalpha, B, H, N, D, dtype, W, host_alpha(alpha), base, n_base,
+                  rope_theta, mode, workspace, workspace_bytes, stream);
+}
+
+size_t fib_sparse_attn_plan_bytes(void) { return sizeof(DevPlan); }
+
+int fib_sparse_attn_fwd_dev(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                            int W, const float* alpha, float alpha_lo, float alpha_hi,
+                            const int32_t* base, int n_base, float rope_theta, int mode,
+                            void* plan, size_t plan_bytes, void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, N, D, dtype, W, dev_alpha(alpha, alpha_lo, alpha_hi, plan, plan_bytes),
+                  base, n_base, rope_theta, mode, stream, false);
+}
+
+int fib_sparse_attn_decode_dev(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                               int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                               int W, const float* alpha, float alpha_lo, float alpha_hi,
+                               const int32_t* base, int n_base, float rope_theta, int mode,
+                               void* plan, size_t plan_bytes, void* stream) {
+  return fwd_impl(q, k_cache, v_cache, o, lse, B, H, N, D, dtype, W,
+                  dev_alpha(alpha, alpha_lo, alpha_hi, plan, plan_bytes), base, n_base, rope_theta, mode, stream,
+                  true);
+}
+
+int fib_sparse_attn_bwd_dev(const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const float* lse,
+                            void* dq, void* dk, void* dv, float* dalpha,
+                            int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                            int W, const float* alpha, float alpha_lo, float alpha_hi,
+                            const int32_t* base, int n_base, float rope_theta, int mode,
+                            void* workspace, size_t workspace_bytes, void* plan, size_t plan_bytes, void* stream) {
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, dalpha, B, H, N, D, dtype, W,
+                  dev_alpha(alpha, alpha_lo, alpha_hi, plan, plan_bytes), base, n_base, rope_theta, mode, workspace,
+                  workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -20,10 +20,12 @@ namespace {
 
 constexpr int kQPB = 64;  // queries per block
 
-template <typename T, int MODE>
+template <typename T, int MODE, bool DEV>
 __global__ __launch_bounds__(256) void fwd_generic_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ o,
-    float* __restrict__ lse, int64_t N, int W, Table tab, Rope rope, float scale_log2, int tiles) {
+    float* __restrict__ lse, int64_t N, int W, Table tab_arg, Rope rope, float scale_log2, int tiles,
+    const DevPlan* __restrict__ plan) {
+  const Table& tab = call_table<DEV>(tab_arg, plan);
   __shared__ float2 cs[kCsSlots][kHalf];
   const bool cached = fill_cs(cs, W, tab, MODE, rope);
   const int64_t head = blockIdx.x / tiles;
@@ -116,28 +118,33 @@ __global__ __launch_bounds__(256) void fwd_generic_kernel(
   if (lse != nullptr && c == 0) lse[(size_t)head * N + i] = (m + log2f(l)) * 0.69314718055994530942f;
 }
 
-}  // namespace
-
-hipError_t launch_fwd_generic(const FwdArgs& a) {
+template <bool DEV>
+hipError_t launch_generic(const FwdArgs& a) {
   const int tiles = (int)((a.N + kQPB - 1) / kQPB);
   dim3 grid((unsigned)(tiles * a.BH)), block(256);
   const float sl2 = (float)(1.4426950408889634 / sqrt((double)kD));
   if (a.dtype == 0) {
     if (a.mode == 0)
-      fwd_generic_kernel<float, 0><<<grid, block, 0, a.stream>>>((const float*)a.q, (const float*)a.k,
-          (const float*)a.v, (float*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, tiles);
+      fwd_generic_kernel<float, 0, DEV><<<grid, block, 0, a.stream>>>((const float*)a.q, (const float*)a.k,
+          (const float*)a.v, (float*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, tiles, a.plan);
     else
-      fwd_generic_kernel<float, 1><<<grid, block, 0, a.stream>>>((const float*)a.q, (const float*)a.k,
-          (const float*)a.v, (float*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, tiles);
+      fwd_generic_kernel<float, 1, DEV><<<grid, block, 0, a.stream>>>((const float*)a.q, (const float*)a.k,
+          (const float*)a.v, (float*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, tiles, a.plan);
   } else {
     if (a.mode == 0)
-      fwd_generic_kernel<bf16_t, 0><<<grid, block, 0, a.stream>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
-          (const bf16_t*)a.v, (bf16_t*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, tiles);
+      fwd_generic_kernel<bf16_t, 0, DEV><<<grid, block, 0, a.stream>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
+          (const bf16_t*)a.v, (bf16_t*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, tiles, a.plan);
     else
-      fwd_generic_kernel<bf16_t, 1><<<grid, block, 0, a.stream>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
-          (const bf16_t*)a.v, (bf16_t*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, tiles);
+      fwd_generic_kernel<bf16_t, 1, DEV><<<grid, block, 0, a.stream>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
+          (const bf16_t*)a.v, (bf16_t*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, tiles, a.plan);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_generic(const FwdArgs& a) {
+  return a.plan != nullptr ? launch_generic<true>(a) : launch_generic<false>(a);
 }
 
 // Debug export of the attended rows (same table and validity code as the kernels).

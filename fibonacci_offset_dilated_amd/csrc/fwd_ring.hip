@@ -62,6 +62,8 @@ struct RingArgs {
   float far_w[kMaxFar];
   int unc_dist[kMaxUnc];
   Rope rope;
+  const DevPlan* plan;  // alpha in device memory: the split above comes from here (DEV instances)
+  int n_far;            // far entries in use (DEV instances: NF is an upper bound)
 };
 
 struct __align__(16) Smem {
@@ -85,15 +87,15 @@ struct FarRows {
 };
 
 template <int MODE, int NF>
-__device__ __forceinline__ void load_far_k(FarRows<NF>& fr, const RingArgs& a, const bf16_t* Kh, int i0w, int n, int g,
+__device__ __forceinline__ void load_far_k(const int* fdist, FarRows<NF>& fr, const RingArgs& a, const bf16_t* Kh, int i0w, int n, int g,
                                            int lane_off) {
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    const bf16_t* kp = Kh + far_off(a.far_dist[f], i0w, n, g, lane_off);
+    const bf16_t* kp = Kh + far_off(fdist[f], i0w, n, g, lane_off);
     fr.k[f][0] = *reinterpret_cast<const uint4*>(kp);
     fr.k[f][1] = *reinterpret_cast<const uint4*>(kp + kHalf);
     if (MODE == 1) {
-      const bf16_t* kq = Kh + far_off(a.far_dist[f] - 1, i0w, n, g, lane_off);
+      const bf16_t* kq = Kh + far_off(fdist[f] - 1, i0w, n, g, lane_off);
       fr.kh[f][0] = *reinterpret_cast<const uint4*>(kq);
       fr.kh[f][1] = *reinterpret_cast<const uint4*>(kq + kHalf);
     }
@@ -101,15 +103,15 @@ __device__ __forceinline__ void load_far_k(FarRows<NF>& fr, const RingArgs& a, c
 }
 
 template <int MODE, int NF>
-__device__ __forceinline__ void load_far_v(FarRows<NF>& fr, const RingArgs& a, const bf16_t* Vh, int i0w, int n, int g,
+__device__ __forceinline__ void load_far_v(const int* fdist, FarRows<NF>& fr, const RingArgs& a, const bf16_t* Vh, int i0w, int n, int g,
                                            int lane_off) {
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    const bf16_t* vp = Vh + far_off(a.far_dist[f], i0w, n, g, lane_off);
+    const bf16_t* vp = Vh + far_off(fdist[f], i0w, n, g, lane_off);
     fr.v[f][0] = *reinterpret_cast<const uint4*>(vp);
     fr.v[f][1] = *reinterpret_cast<const uint4*>(vp + kHalf);
     if (MODE == 1) {
-      const bf16_t* vq = Vh + far_off(a.far_dist[f] - 1, i0w, n, g, lane_off);
+      const bf16_t* vq = Vh + far_off(fdist[f] - 1, i0w, n, g, lane_off);
       fr.vh[f][0] = *reinterpret_cast<const uint4*>(vq);
       fr.vh[f][1] = *reinterpret_cast<const uint4*>(vq + kHalf);
     }
@@ -143,7 +145,7 @@ __device__ __forceinline__ void far_pv_interp(f4* acc, uint4 x0, uint4 x1, uint4
   }
 }
 
-template <int MODE, int NC, int NF, int WAVES>
+template <int MODE, int NC, int NF, int WAVES, bool DEV>
 __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
   constexpr int kThreads = 64 * WAVES;
   constexpr int kT = step_rows(WAVES);
@@ -160,13 +162,30 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
   const int jc = n & 3;   // transpose-read 4-column group
 
   const int N = a.N;
+  // alpha-dependent launch data: the kernel arguments, or (DEV instances, alpha in device
+  // memory) the split built on the device, read once into registers (the arguments struct
+  // itself is never written, so it stays in the kernel-argument segment)
+  RingSplit lcl;
+  if constexpr (DEV) lcl = (WAVES == 8 ? a.plan->s8 : a.plan->s4);
+  const int S_n_cov = DEV ? lcl.n_cov : a.n_cov;
+  const int S_n_far = DEV ? lcl.n_far : a.n_far;
+  const int S_early_rows = DEV ? lcl.early_rows : a.early_rows;
+  const int S_warm = DEV ? ((lcl.need + kT - 1) / kT) * kT : a.warm;
+  auto S_dist = [&](int x) -> int { if constexpr (DEV) return lcl.dist[x]; else return a.dist[x]; };
+  auto S_w = [&](int x) -> float { if constexpr (DEV) return lcl.w[x]; else return a.w[x]; };
+  auto S_far_dist = [&](int x) -> int { if constexpr (DEV) return lcl.far_dist[x]; else return a.far_dist[x]; };
+  auto S_far_w = [&](int x) -> float { if constexpr (DEV) return lcl.far_w[x]; else return a.far_w[x]; };
+
   // ---- per-launch set-up: cos/sin of the far distances; per-lane rotation by t = 16 wave + n
   // (the row's offset from a step base)
   {
     constexpr int n_unc = MODE == 1 ? 2 * NF : NF;
     for (int x = tid; x < n_unc * kHalf; x += kThreads) {
       const int u = x / kHalf, j = x % kHalf;
-      sm.unc_cs[u][j] = rope_cs(a.unc_dist[u], a.rope.rev[j]);
+      int d;
+      if constexpr (DEV) d = (WAVES == 8 ? a.plan->s8 : a.plan->s4).unc_dist[u];
+      else d = a.unc_dist[u];  // (a's arrays are indexed by constants only in DEV instances)
+      sm.unc_cs[u][j] = rope_cs(d, a.rope.rev[j]);
     }
   }
   float2 cs_t[8];
@@ -257,9 +276,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
 
   // ---- warm-up: ring rows [ws, s0), the band and covered rows of the first steps. Rows
   // before 0 are never stored: their slots must read as zero (finite, and masked).
-  const int ws = s0 - a.warm > 0 ? s0 - a.warm : 0;
+  const int ws = s0 - S_warm > 0 ? s0 - S_warm : 0;
   const int n_warm = (s0 - ws) / kT;  // whole steps (s0 and the warm-up are step multiples)
-  if (s0 < a.warm) {
+  if (s0 < S_warm) {
     uint4* z = reinterpret_cast<uint4*>(sm.ringK);
     const int n16 = (2 * (kP + kMirror) * kRow) / 16;
     for (int x = tid; x < n16; x += kThreads) z[x] = make_uint4(0, 0, 0, 0);
@@ -309,7 +328,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
   // (the first step's barrier orders these stores before any read of them)
   // far K rows of the first step (requested after the warm-up rows, whose registers they reuse)
   FarRows<NF> fr;
-  load_far_k<MODE, NF>(fr, a, Kh, s0 + 16 * wave, n, g, lane_off);
+  load_far_k<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, fr, a, Kh, s0 + 16 * wave, n, g, lane_off);
 
   int buf = 0;
   for (int p0 = s0; p0 < s1; p0 += kT, buf ^= 1) {
@@ -342,7 +361,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
       const bf16x8 bq0 = as_bf8(qh0), bq1 = as_bf8(qh1);
       // keys before position 0 (and table distances longer than the query position) occur
       // only in the first steps of a sequence; afterwards the masks are the fixed biases
-      const bool early = i0w < a.early_rows;
+      const bool early = i0w < S_early_rows;
 
       // ---- window band: keys i0w - 16 + kappa, kappa < 32
       f4 S0 = {0, 0, 0, 0}, S1 = {0, 0, 0, 0};
@@ -358,7 +377,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
       float s_ent[NC];
 #pragma unroll
       for (int e = 0; e < NC; ++e) {
-        const int sl = row_off(bw - a.dist[e]) + lane_k;
+        const int sl = row_off(bw - S_dist(e)) + lane_k;
         f4 S = {0, 0, 0, 0};
         S = mfma32(as_bf8(lds_read16(sm.ringK, sl)), bq0, S);
         S = mfma32(as_bf8(lds_read16(sm.ringK, sl + 64)), bq1, S);
@@ -368,14 +387,14 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
           f4 H = {0, 0, 0, 0};
           H = mfma32(as_bf8(lds_read16(sm.ringK, sl + kRow)), bq0, H);
           H = mfma32(as_bf8(lds_read16(sm.ringK, sl + kRow + 64)), bq1, H);
-          s = fmaf(a.w[e], sel4(H, l) - s, s);
+          s = fmaf(S_w(e), sel4(H, l) - s, s);
         }
         s_ent[e] = fmaf(s, sl2, bias_diag);
       }
-      if (a.n_cov < NC) {
+      if (S_n_cov < NC) {
 #pragma unroll
         for (int e = 0; e < NC; ++e)
-          if (e >= a.n_cov) s_ent[e] = -INFINITY;
+          if (e >= S_n_cov) s_ent[e] = -INFINITY;
       }
 
       // ---- far entries: their K rows were requested at the end of the previous step
@@ -394,12 +413,13 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
           f4 H = {0, 0, 0, 0};
           H = mfma32(as_bf8(fr.kh[f][0]), as_bf8(r0), H);
           H = mfma32(as_bf8(fr.kh[f][1]), as_bf8(r1), H);
-          s = fmaf(a.far_w[f], sel4(H, l) - s, s);
+          s = fmaf(S_far_w(f), sel4(H, l) - s, s);
         }
         s_far[f] = fmaf(s, sl2, bias_diag);
+        if (DEV && f >= S_n_far) s_far[f] = -INFINITY;  // slot beyond the table
       }
       // their V rows, for the end of this step (K and V rows are never held together)
-      load_far_v<MODE, NF>(fr, a, Vh, i0w, n, g, lane_off);
+      load_far_v<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, fr, a, Vh, i0w, n, g, lane_off);
 
 
       // ---- softmax over the window band and the entries (base-2 logits)
@@ -415,10 +435,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
           if (n + 16 - 4 * g - v > iq) sw0[v] = -INFINITY;
 #pragma unroll
         for (int e = 0; e < NC; ++e)
-          if (a.dist[e] > iq) s_ent[e] = -INFINITY;
+          if (S_dist(e) > iq) s_ent[e] = -INFINITY;
 #pragma unroll
         for (int f = 0; f < NF; ++f)
-          if (a.far_dist[f] > iq) s_far[f] = -INFINITY;
+          if (S_far_dist(f) > iq) s_far[f] = -INFINITY;
       }
       float m = fmaxf(fmaxf(sw0[0], sw0[1]), fmaxf(sw0[2], sw0[3]));
 #pragma unroll
@@ -477,7 +497,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
 #pragma unroll
         for (int e = 0; e < NC; e += 2) {
           const bf16x8 bp = diag_block(pack_bf2(s_ent[e], s_ent[e + 1]), sel);
-          const int ra = row_off(bw - a.dist[e]) + lane_v, rb = row_off(bw - a.dist[e + 1]) + lane_v;
+          const int ra = row_off(bw - S_dist(e)) + lane_v, rb = row_off(bw - S_dist(e + 1)) + lane_v;
 #pragma unroll
           for (int mb = 0; mb < 4; ++mb)
             acc[mb] = mfma32(cat_bf8(tr16(sm.ringV, ra + 32 * mb), tr16(sm.ringV, rb + 32 * mb)), bp, acc[mb]);
@@ -487,8 +507,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
 #pragma unroll
         for (int e = 0; e < NC; ++e) {
           const float p = s_ent[e];
-          const bf16x8 bp = diag_block(pack_bf2(p * (1.f - a.w[e]), p * a.w[e]), sel);
-          const int ra = row_off(bw - a.dist[e]) + lane_v, rb = ra + kRow;
+          const bf16x8 bp = diag_block(pack_bf2(p * (1.f - S_w(e)), p * S_w(e)), sel);
+          const int ra = row_off(bw - S_dist(e)) + lane_v, rb = ra + kRow;
 #pragma unroll
           for (int mb = 0; mb < 4; ++mb)
             acc[mb] = mfma32(cat_bf8(tr16(sm.ringV, ra + 32 * mb), tr16(sm.ringV, rb + 32 * mb)), bp, acc[mb]);
@@ -511,7 +531,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
           const float p = s_far[f];
-          const uint32_t x = pack_bf2(p * (1.f - a.far_w[f]), p * a.far_w[f]);
+          const uint32_t x = pack_bf2(p * (1.f - S_far_w(f)), p * S_far_w(f));
           const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute(diag_addr, (int)x);
           lnorm_far = dot2(y, kOnes, lnorm_far);
           far_pv_interp(acc, fr.v[f][0], fr.v[f][1], fr.vh[f][0], fr.vh[f][1], y);
@@ -537,7 +557,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
         if (g == 0 && a.lse != nullptr) (a.lse + (size_t)head * N + i0w)[n] = (m + log2f(lsum)) * 0.69314718055994530942f;
       }
       // far K rows of the next step (the last step loads rows that are never used)
-      load_far_k<MODE, NF>(fr, a, Kh, i0w + kT, n, g, lane_off);
+      load_far_k<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, fr, a, Kh, i0w + kT, n, g, lane_off);
     }
     __syncthreads();
   }
@@ -546,10 +566,20 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
 // Waves per workgroup and the table split: 8 waves (two per SIMD) where the registers fit
 // 256 per lane, else 4 (interpolated mode with many far entries: their row pairs need twice
 // the registers).
+// With alpha in device memory the counts are upper bounds over the alpha range, and the
+// covered slots are always 16.
 int plan(const FwdArgs& f, int* n_cov, int* n_far) {
-  split_table(f.tab, f.N, 8, n_cov, n_far);
+  auto split = [&](int waves) {
+    if (f.plan != nullptr) {
+      range_counts(f.alpha_lo, f.alpha_hi, f.base, f.n_base, f.W, f.mode, f.N, waves, n_cov, n_far);
+      if (*n_cov <= kMaxCov) *n_cov = kMaxCov;
+    } else {
+      split_table(f.tab, f.N, waves, n_cov, n_far);
+    }
+  };
+  split(8);
   if (f.mode == 1 && (*n_far > 3 || (*n_far == 3 && *n_cov > 8))) {
-    split_table(f.tab, f.N, 4, n_cov, n_far);
+    split(4);
     return 4;
   }
   return 8;
@@ -561,38 +591,48 @@ constexpr bool unused_instance() {
   return MODE == 1 && WAVES == 8 && (NF > 3 || (NF == 3 && NC > 8));
 }
 
-template <int MODE, int NC, int NF, int WAVES>
+template <int MODE, int NC, int NF, int WAVES, bool DEV>
 hipError_t launch(const RingArgs& a, unsigned blocks, hipStream_t s) {
-  if constexpr (unused_instance<MODE, NC, NF, WAVES>()) {
+  if constexpr (unused_instance<MODE, NC, NF, WAVES>() || (DEV && NC != 16)) {
     return hipErrorInvalidValue;
   } else {
   const size_t smem = sizeof(Smem);
-  hipError_t e = hipFuncSetAttribute((const void*)fwd_ring_kernel<MODE, NC, NF, WAVES>,
+  hipError_t e = hipFuncSetAttribute((const void*)fwd_ring_kernel<MODE, NC, NF, WAVES, DEV>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
-  fwd_ring_kernel<MODE, NC, NF, WAVES><<<blocks, 64 * WAVES, smem, s>>>(a);
+  fwd_ring_kernel<MODE, NC, NF, WAVES, DEV><<<blocks, 64 * WAVES, smem, s>>>(a);
   return hipGetLastError();
   }
 }
 
-// kernel instance by (covered entries rounded up to 8 or 16, far entries, waves)
-template <int MODE, int WAVES>
+// kernel instance by (covered entries rounded up to 8 or 16, far entries, waves); with alpha
+// in device memory (DEV) always 16 covered slots
+template <int MODE, int WAVES, bool DEV = false>
 hipError_t launch_mode(const RingArgs& a, int n_far, unsigned blocks, hipStream_t s) {
+  if constexpr (DEV) {
+    switch (n_far) {
+      case 0: return launch<MODE, 16, 0, WAVES, true>(a, blocks, s);
+      case 1: return launch<MODE, 16, 1, WAVES, true>(a, blocks, s);
+      case 2: return launch<MODE, 16, 2, WAVES, true>(a, blocks, s);
+      case 3: return launch<MODE, 16, 3, WAVES, true>(a, blocks, s);
+      default: return launch<MODE, 16, 4, WAVES, true>(a, blocks, s);
+    }
+  }
   if (a.n_cov <= 8) {
     switch (n_far) {
-      case 0: return launch<MODE, 8, 0, WAVES>(a, blocks, s);
-      case 1: return launch<MODE, 8, 1, WAVES>(a, blocks, s);
-      case 2: return launch<MODE, 8, 2, WAVES>(a, blocks, s);
-      case 3: return launch<MODE, 8, 3, WAVES>(a, blocks, s);
-      default: return launch<MODE, 8, 4, WAVES>(a, blocks, s);
+      case 0: return launch<MODE, 8, 0, WAVES, false>(a, blocks, s);
+      case 1: return launch<MODE, 8, 1, WAVES, false>(a, blocks, s);
+      case 2: return launch<MODE, 8, 2, WAVES, false>(a, blocks, s);
+      case 3: return launch<MODE, 8, 3, WAVES, false>(a, blocks, s);
+      default: return launch<MODE, 8, 4, WAVES, false>(a, blocks, s);
     }
   }
   switch (n_far) {
-    case 0: return launch<MODE, 16, 0, WAVES>(a, blocks, s);
-    case 1: return launch<MODE, 16, 1, WAVES>(a, blocks, s);
-    case 2: return launch<MODE, 16, 2, WAVES>(a, blocks, s);
-    case 3: return launch<MODE, 16, 3, WAVES>(a, blocks, s);
-    default: return launch<MODE, 16, 4, WAVES>(a, blocks, s);
+    case 0: return launch<MODE, 16, 0, WAVES, false>(a, blocks, s);
+    case 1: return launch<MODE, 16, 1, WAVES, false>(a, blocks, s);
+    case 2: return launch<MODE, 16, 2, WAVES, false>(a, blocks, s);
+    case 3: return launch<MODE, 16, 3, WAVES, false>(a, blocks, s);
+    default: return launch<MODE, 16, 4, WAVES, false>(a, blocks, s);
   }
 }
 
@@ -607,6 +647,7 @@ bool fwd_ring_supported(const FwdArgs& f) {
 
 hipError_t launch_fwd_ring(const FwdArgs& f) {
   RingArgs a;
+  a.plan = f.plan;
   a.q = (const bf16_t*)f.q;
   a.k = (const bf16_t*)f.k;
   a.v = (const bf16_t*)f.v;
@@ -647,6 +688,12 @@ hipError_t launch_fwd_ring(const FwdArgs& f) {
   const unsigned blocks = (unsigned)(segs * f.BH);
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)kD));
   a.rope = f.rope;
+  a.n_far = n_far;
+  if (f.plan != nullptr) {
+    if (f.mode == 0) return launch_mode<0, 8, true>(a, n_far, blocks, f.stream);
+    if (waves == 8) return launch_mode<1, 8, true>(a, n_far, blocks, f.stream);
+    return launch_mode<1, 4, true>(a, n_far, blocks, f.stream);
+  }
   if (f.mode == 0) return launch_mode<0, 8>(a, n_far, blocks, f.stream);
   if (waves == 8) return launch_mode<1, 8>(a, n_far, blocks, f.stream);
   return launch_mode<1, 4>(a, n_far, blocks, f.stream);

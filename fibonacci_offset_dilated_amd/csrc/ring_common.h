@@ -28,6 +28,8 @@ constexpr int kMaxUnc = 2 * kMaxFar;  // their distances (interpolated: c and c 
 // Rows 0..kMirror-1 of the ring are also stored after its end, so that any 32 consecutive
 // ring rows (slots s..s+31, s < kP) are one base address plus constant offsets.
 constexpr int kMirror = 32;
+static_assert(kP == kRingRows && kMaxBand == kBandRows && kMaxCov == kSplitCov && kMaxFar == kSplitFar,
+              "ring geometry and RingSplit must agree");
 
 // byte offset of ring row `row` (any integer, negative rows included: slots are row mod kP);
 // wave-uniform arguments keep it on the scalar unit

@@ -146,6 +146,45 @@ int fib_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cac
                            int W, float alpha, const int32_t* base, int n_base,
                            float rope_theta, int mode, void* stream);
 
+/*
+ * alpha in device memory (the Learned schedule of [FIB] Method > Experimental variables
+ * trains alpha on the device): the same operations with alpha read from `alpha` (device,
+ * one fp32) instead of a host value, so a call needs no device-to-host copy and no stream
+ * synchronization. The offset table is built on the device, by a small kernel enqueued on
+ * `stream` ahead of the attention kernels, into `plan` (device, at least
+ * fib_sparse_attn_plan_bytes() bytes, 16-byte aligned, overwritten; its contents on entry
+ * are ignored; it must not be shared by calls that overlap). Kernel instances are chosen on
+ * the host to fit every alpha in [alpha_lo, alpha_hi] (0 < alpha_lo <= alpha_hi, finite);
+ * the device value is clamped into that range (a NaN becomes alpha_lo). A wide range can
+ * select slower instances than the exact alpha would. Results equal the host-alpha calls'
+ * up to floating-point summation order.
+ * Errors as for the host-alpha calls, plus FIB_ERR_NULL for a NULL alpha or plan,
+ * FIB_ERR_ALPHA for a bad range, FIB_ERR_ALIGN for a misaligned alpha or plan and
+ * FIB_ERR_WORKSPACE for plan_bytes below fib_sparse_attn_plan_bytes().
+ */
+size_t fib_sparse_attn_plan_bytes(void);
+
+int fib_sparse_attn_fwd_dev(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                            int W, const float* alpha, float alpha_lo, float alpha_hi,
+                            const int32_t* base, int n_base, float rope_theta, int mode,
+                            void* plan, size_t plan_bytes, void* stream);
+
+int fib_sparse_attn_bwd_dev(const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const float* lse,
+                            void* dq, void* dk, void* dv, float* dalpha,
+                            int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                            int W, const float* alpha, float alpha_lo, float alpha_hi,
+                            const int32_t* base, int n_base, float rope_theta, int mode,
+                            void* workspace, size_t workspace_bytes, void* plan, size_t plan_bytes,
+                            void* stream);
+
+int fib_sparse_attn_decode_dev(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                               int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                               int W, const float* alpha, float alpha_lo, float alpha_hi,
+                               const int32_t* base, int n_base, float rope_theta, int mode,
+                               void* plan, size_t plan_bytes, void* stream);
+
 /* Static, human-readable text of a status code. */
 const char* fib_status_string(int status);
 

@@ -123,6 +123,30 @@ def test_decode_argument_errors():
     assert call(o=0x1004) == -10 and call(lse=0x1001) == -10
 
 
+def test_device_alpha_argument_errors():
+    L = F.lib()
+    b = (ctypes.c_int32 * 15)(*FIB_BASE)
+    p = 16
+    need = F.plan_bytes()
+    assert need > 0
+
+    def fwd(alpha=p, lo=0.5, hi=1.5, plan=p, nbytes=need):
+        return L.fib_sparse_attn_fwd_dev(p, p, p, p, None, 1, 1, 8, 64, 1, 12, alpha, ctypes.c_float(lo),
+                                         ctypes.c_float(hi), b, 15, ctypes.c_float(10000.0), 1, plan, nbytes, None)
+    assert fwd(alpha=None) == -1 and fwd(plan=None) == -1
+    assert fwd(lo=0.0) == -6 and fwd(lo=1.6) == -6 and fwd(hi=float("inf")) == -6
+    assert fwd(alpha=0x1002) == -10 and fwd(plan=0x1008) == -10
+    assert fwd(nbytes=need - 1) == -11
+
+    def bwd(alpha=p, plan=p, nbytes=need, ws=p, ws_bytes=1 << 40):
+        return L.fib_sparse_attn_bwd_dev(p, p, p, p, p, p, p, p, p, p, 1, 1, 8, 64, 1, 12, alpha, ctypes.c_float(0.5),
+                                         ctypes.c_float(1.5), b, 15, ctypes.c_float(10000.0), 1, ws, ws_bytes, plan,
+                                         nbytes, None)
+    assert bwd(alpha=None) == -1 and bwd(ws=None) == -11 and bwd(nbytes=3) == -11
+    assert L.fib_sparse_attn_decode_dev(p, p, p, p, None, 1, 1, 8, 64, 1, 12, None, ctypes.c_float(0.5),
+                                        ctypes.c_float(1.5), b, 15, ctypes.c_float(10000.0), 0, p, need, None) == -1
+
+
 def test_bwd_argument_errors():
     L = F.lib()
     b = (ctypes.c_int32 * 15)(*FIB_BASE)
