@@ -216,6 +216,77 @@ def small_configs(dev, stream, args):
     out["decode_b8h8n4096_int_us_per_layer"] = round(us_di, 2)
     out["decode_b8h8n4096_interp_us_per_layer"] = round(us_dp, 2)
     out["decode_b8h8n4096_interp_over_int"] = round(us_dp / us_di, 3)
+    del qc, kc, vc, qd, od, ld
+
+    # a 16-layer stack in one call (fwd_layers / bwd_layers: [16, B, H, N, D] inputs, distinct
+    # per layer, so no layer's rows are cache-resident: 0.8 GB of Q, K, V at B4 H8 N4096) vs
+    # 16 single-layer calls over the same stack; N(0, 1) draws made on the device
+    out.update(layer_stacks(dev, stream, args, al4, al2, al3))
+    return out
+
+
+def layer_stacks(dev, stream, args, al4, al2, al3):
+    import torch
+
+    import fibonacci_offset_dilated_amd as F
+    from fibonacci_offset_dilated_amd.synthetic import seed_for
+    from fibonacci_offset_dilated_amd.workloads import BY_CONFIG, FIB_BASE, INT, INTERP
+
+    reps = max(5, args.steps // 5)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed_for(4, 0, 12, 16))
+    L = 16
+
+    def stack(w, n):
+        return [torch.randn((L, w.B, w.H, w.N, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(n)]
+
+    out = {}
+    plan = torch.empty(F.layers_plan_bytes(L), dtype=torch.uint8, device=dev)
+    w4 = BY_CONFIG[4]
+    q, k, v = stack(w4, 3)
+    o = torch.empty_like(q)
+    lse = torch.empty((L, w4.B, w4.H, w4.N), dtype=torch.float32, device=dev)
+    a4 = np.array(al4, dtype=np.float32)
+    us_f = time_calls(lambda: F.fwd_layers(q, k, v, 12, a4, FIB_BASE, 10000.0, INT, out=o, lse=lse, plan=plan),
+                      reps, 2, stream) * 1e3 / L
+    us_s = time_calls(lambda: [F.fwd(q[l], k[l], v[l], 12, a4[l], FIB_BASE, 10000.0, INT, out=o[l], lse=lse[l])
+                               for l in range(L)], reps, 2, stream) * 1e3 / L
+    rows4 = w4.B * w4.H * w4.N
+    out["c4_stack16_fwd_int_us_per_layer"] = round(us_f, 2)
+    out["c4_stack16_fwd_int_hbm_frac"] = round(rows4 * (4 * D * 2 + 4) / (us_f * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    out["c4_stack16_separate_calls_us_per_layer"] = round(us_s, 2)
+    del q, k, v, o, lse
+
+    w2 = BY_CONFIG[3]
+    q, k, v, do = stack(w2, 4)
+    o = torch.empty_like(q)
+    lse = torch.empty((L, w2.B, w2.H, w2.N), dtype=torch.float32, device=dev)
+    a2 = np.array(al2, dtype=np.float32)
+    a3 = np.asarray(al3, dtype=np.float32)
+    us_fi = time_calls(lambda: F.fwd_layers(q, k, v, 12, a2, FIB_BASE, 10000.0, INT, out=o, lse=lse, plan=plan),
+                       reps, 2, stream) * 1e3 / L
+    us_si = time_calls(lambda: [F.fwd(q[l], k[l], v[l], 12, a2[l], FIB_BASE, 10000.0, INT, out=o[l], lse=lse[l])
+                                for l in range(L)], reps, 2, stream) * 1e3 / L
+    us_fp = time_calls(lambda: F.fwd_layers(q, k, v, 12, a3, FIB_BASE, 10000.0, INTERP, out=o, lse=lse, plan=plan),
+                       reps, 2, stream) * 1e3 / L
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dal = torch.empty(L, dtype=torch.float32, device=dev)
+    ws = torch.empty(F.bwd_workspace_size(L * w2.B, w2.H, w2.N, D, F.BF16, INTERP), dtype=torch.uint8, device=dev)
+    us_fb = time_calls(lambda: F.bwd_layers(q, k, v, o, lse, do, 12, a3, FIB_BASE, 10000.0, INTERP, dq=dq, dk=dk,
+                                            dv=dv, dalpha=dal, workspace=ws, plan=plan), reps, 2, stream) * 1e3 / L
+    ws1 = torch.empty(F.bwd_workspace_size(w2.B, w2.H, w2.N, D, F.BF16, INTERP), dtype=torch.uint8, device=dev)
+    dal1 = torch.empty(1, dtype=torch.float32, device=dev)
+    us_sb = time_calls(lambda: [F.bwd(q[l], k[l], v[l], o[l], lse[l], do[l], 12, a3[l], FIB_BASE, 10000.0, INTERP,
+                                      dq=dq[l], dk=dk[l], dv=dv[l], dalpha=dal1, workspace=ws1) for l in range(L)],
+                       reps, 2, stream) * 1e3 / L
+    rows2 = w2.B * w2.H * w2.N
+    out["b8h8n1024_stack16_fwd_int_us_per_layer"] = round(us_fi, 2)
+    out["b8h8n1024_stack16_fwd_int_hbm_frac"] = round(rows2 * (4 * D * 2 + 4) / (us_fi * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                                      4)
+    out["b8h8n1024_stack16_separate_calls_fwd_int_us_per_layer"] = round(us_si, 2)
+    out["b8h8n1024_stack16_fwd_interp_us_per_layer"] = round(us_fp, 2)
+    out["b8h8n1024_stack16_bwd_interp_us_per_layer"] = round(us_fb, 2)
+    out["b8h8n1024_stack16_separate_calls_bwd_interp_us_per_layer"] = round(us_sb, 2)
     return out
 
 

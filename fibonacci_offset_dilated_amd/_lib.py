@@ -57,6 +57,27 @@ _SIGS = {
                                            _c.c_void_p]),
     "fib_sparse_attn_bwd_workspace_size": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64,
                                                          _c.c_int, _c.c_int]),
+    "fib_sparse_attn_layers_plan_bytes": (_c.c_size_t, [_c.c_int64]),
+    "fib_sparse_attn_fwd_layers": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                              _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int,
+                                              _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_float, _c.c_int,
+                                              _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "fib_sparse_attn_fwd_layers_dev": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                                  _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64,
+                                                  _c.c_int, _c.c_int, _c.c_void_p, _c.c_float, _c.c_float,
+                                                  _c.c_void_p, _c.c_int, _c.c_float, _c.c_int, _c.c_void_p,
+                                                  _c.c_size_t, _c.c_void_p]),
+    "fib_sparse_attn_bwd_layers": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                              _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                              _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int,
+                                              _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_float, _c.c_int,
+                                              _c.c_void_p, _c.c_size_t, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "fib_sparse_attn_bwd_layers_dev": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                                  _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                                  _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64,
+                                                  _c.c_int, _c.c_int, _c.c_void_p, _c.c_float, _c.c_float,
+                                                  _c.c_void_p, _c.c_int, _c.c_float, _c.c_int, _c.c_void_p,
+                                                  _c.c_size_t, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "fib_status_string": (_c.c_char_p, [_c.c_int]),
     "fib_sparse_attn_offset_table": (_c.c_int, [_c.c_float, _c.c_void_p, _c.c_int, _c.c_int, _c.c_int,
                                                 _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p]),
@@ -311,6 +332,118 @@ def decode_dev(q, k_cache, v_cache, W: int, alpha, alpha_range, base: Sequence[i
                                           _ptr(plan), plan.numel() * plan.element_size(), _stream(stream))
     _check(st, "fib_sparse_attn_decode_dev")
     return out, lse
+
+
+def layers_plan_bytes(n_layers: int) -> int:
+    """Device bytes of the plan buffer of a call over n_layers layers (0 if out of range)."""
+    return int(lib().fib_sparse_attn_layers_plan_bytes(int(n_layers)))
+
+
+def _check_layers(*ts):
+    torch = _torch()
+    ref = ts[0]
+    for t in ts:
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError("tensors must be CUDA (HIP) tensors")
+        if t.dim() != 5 or t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError("layer tensors must share shape [L, B, H, N, D], dtype and device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _layers_alpha(alpha, L, alpha_range, device):
+    """(host float32 array or None, device tensor or None, lo, hi) of a call over L layers."""
+    torch = _torch()
+    if alpha_range is None:
+        a = np.ascontiguousarray(np.asarray(alpha, dtype=np.float32).reshape(-1))
+        if a.size != L:
+            raise ValueError(f"alpha must hold {L} values (one per layer)")
+        return a, None, 0.0, 0.0
+    if (not isinstance(alpha, torch.Tensor) or alpha.dtype != torch.float32 or alpha.numel() != L
+            or alpha.device != device or not alpha.is_contiguous()):
+        raise ValueError(f"alpha must be a contiguous float32 tensor of {L} values on the inputs' device")
+    return None, alpha, float(alpha_range[0]), float(alpha_range[1])
+
+
+def _layers_plan(plan, L, device):
+    torch = _torch()
+    need = layers_plan_bytes(L)
+    if need == 0:
+        raise ValueError("layer count out of range")
+    if plan is None:
+        plan = torch.empty(need, dtype=torch.uint8, device=device)
+    if plan.numel() * plan.element_size() < need:
+        raise ValueError("plan buffer too small")
+    return plan
+
+
+def fwd_layers(q, k, v, W: int, alpha, base: Sequence[int], theta: float = 10000.0, mode: int = INT,
+               alpha_range=None, out=None, lse=None, with_lse: bool = True, plan=None, stream=None):
+    """Forward of L layers in one call: q, k, v [L, B, H, N, D]; alpha: L host values, or
+    (with alpha_range = (lo, hi)) a float32 device tensor of L values. Returns (O, LSE [L, B,
+    H, N] or None)."""
+    torch = _torch()
+    _check_layers(q, k, v)
+    L, B, H, N, D = q.shape
+    ah, ad, lo, hi = _layers_alpha(alpha, L, alpha_range, q.device)
+    plan = _layers_plan(plan, L, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_layers(q, out)
+    if lse is None and with_lse:
+        lse = torch.empty((L, B, H, N), dtype=torch.float32, device=q.device)
+    b, n = _base_array(base)
+    pb = plan.numel() * plan.element_size()
+    if ad is None:
+        st = lib().fib_sparse_attn_fwd_layers(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), L, B, H, N, D,
+                                              _dtype_code(q), int(W), ah.ctypes.data_as(ctypes.c_void_p), b, n,
+                                              ctypes.c_float(float(theta)), int(mode), _ptr(plan), pb,
+                                              _stream(stream))
+        _check(st, "fib_sparse_attn_fwd_layers")
+    else:
+        st = lib().fib_sparse_attn_fwd_layers_dev(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), L, B, H, N, D,
+                                                  _dtype_code(q), int(W), _ptr(ad), ctypes.c_float(lo),
+                                                  ctypes.c_float(hi), b, n, ctypes.c_float(float(theta)), int(mode),
+                                                  _ptr(plan), pb, _stream(stream))
+        _check(st, "fib_sparse_attn_fwd_layers_dev")
+    return out, lse
+
+
+def bwd_layers(q, k, v, o, lse, dout, W: int, alpha, base: Sequence[int], theta: float = 10000.0, mode: int = INT,
+               alpha_range=None, dq=None, dk=None, dv=None, dalpha=None, workspace=None, want_dalpha: bool = True,
+               plan=None, stream=None):
+    """Backward of L layers in one call (see fwd_layers); returns (dQ, dK, dV, dalpha [L] or None)."""
+    torch = _torch()
+    _check_layers(q, k, v, o, dout)
+    L, B, H, N, D = q.shape
+    ah, ad, lo, hi = _layers_alpha(alpha, L, alpha_range, q.device)
+    plan = _layers_plan(plan, L, q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    _check_layers(q, dq, dk, dv)
+    if dalpha is None and want_dalpha:
+        dalpha = torch.empty(L, dtype=torch.float32, device=q.device)
+    need = bwd_workspace_size(L * B, H, N, D, _dtype_code(q), mode)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    b, n = _base_array(base)
+    pb = plan.numel() * plan.element_size()
+    wb = workspace.numel() * workspace.element_size()
+    common = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dalpha),
+              L, B, H, N, D, _dtype_code(q), int(W))
+    if ad is None:
+        st = lib().fib_sparse_attn_bwd_layers(*common, ah.ctypes.data_as(ctypes.c_void_p), b, n,
+                                              ctypes.c_float(float(theta)), int(mode), _ptr(workspace), wb,
+                                              _ptr(plan), pb, _stream(stream))
+        _check(st, "fib_sparse_attn_bwd_layers")
+    else:
+        st = lib().fib_sparse_attn_bwd_layers_dev(*common, _ptr(ad), ctypes.c_float(lo), ctypes.c_float(hi), b, n,
+                                                  ctypes.c_float(float(theta)), int(mode), _ptr(workspace), wb,
+                                                  _ptr(plan), pb, _stream(stream))
+        _check(st, "fib_sparse_attn_bwd_layers_dev")
+    return dq, dk, dv, dalpha
 
 
 def bwd_workspace_size(B, H, N, D, dtype_code: int, mode: int) -> int:

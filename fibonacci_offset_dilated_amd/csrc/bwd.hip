@@ -40,8 +40,8 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ o,
     const T* __restrict__ dout, const float* __restrict__ lse, T* __restrict__ dq, float* __restrict__ delta,
     float* __restrict__ dalpha_part, int64_t N, int W, Table tab_arg, Rope rope, float scale, int tiles,
-    const DevPlan* __restrict__ plan) {
-  const Table& tab = call_table<DEV>(tab_arg, plan);
+    const DevPlan* __restrict__ plan, int heads_per_plan) {
+  const Table& tab = call_table<DEV>(tab_arg, plan, (int)(blockIdx.x / tiles) / heads_per_plan);
   __shared__ float2 cs[kCsSlots][kHalf];
   __shared__ float red[256];
   const bool cached = fill_cs(cs, W, tab, MODE, rope);
@@ -150,8 +150,9 @@ template <typename T, int MODE, bool DEV>
 __global__ __launch_bounds__(256) void bwd_key_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta, T* __restrict__ dk, T* __restrict__ dv,
-    int64_t N, int W, Table tab_arg, Rope rope, float scale, int tiles, const DevPlan* __restrict__ plan) {
-  const Table& tab = call_table<DEV>(tab_arg, plan);
+    int64_t N, int W, Table tab_arg, Rope rope, float scale, int tiles, const DevPlan* __restrict__ plan,
+    int heads_per_plan) {
+  const Table& tab = call_table<DEV>(tab_arg, plan, (int)(blockIdx.x / tiles) / heads_per_plan);
   __shared__ float2 cs[kCsSlots][kHalf];
   const bool cached = fill_cs(cs, W, tab, MODE, rope);
   const int64_t head = blockIdx.x / tiles;
@@ -284,8 +285,9 @@ __global__ __launch_bounds__(256) void bwd_key_ps_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     const uint32_t* __restrict__ ps, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int64_t N, int W,
-    Table tab_arg, Rope rope, float scale, int tiles, const DevPlan* __restrict__ plan) {
-  const Table& tab = call_table<DEV>(tab_arg, plan);
+    Table tab_arg, Rope rope, float scale, int tiles, const DevPlan* __restrict__ plan,
+    int heads_per_plan) {
+  const Table& tab = call_table<DEV>(tab_arg, plan, (int)(blockIdx.x / tiles) / heads_per_plan);
   __shared__ float2 cs[kCsSlots][kHalf];
   const bool cached = fill_cs(cs, W, tab, 1, rope);
   const int64_t head = blockIdx.x / tiles;
@@ -369,10 +371,13 @@ __global__ __launch_bounds__(256) void bwd_key_ps_kernel(
   Vec8<bf16_t>::store(dv + hoff + j * kD + kHalf + 8 * c, avh);
 }
 
-// Sums n partials in a fixed order (per-thread strided sums, then a tree); writes one float.
+// Sums n partials in a fixed order (per-thread strided sums, then a tree); block b sums the
+// b-th run of n partials (one layer's workgroups) into out[b].
 __global__ __launch_bounds__(256) void dalpha_reduce_kernel(const float* __restrict__ part, int64_t n,
                                                             float* __restrict__ out) {
   __shared__ double red[256];
+  part += (int64_t)blockIdx.x * n;
+  out += blockIdx.x;
   double s = 0.0;
   for (int64_t x = threadIdx.x; x < n; x += 256) s += (double)part[x];
   red[threadIdx.x] = s;
@@ -384,7 +389,9 @@ __global__ __launch_bounds__(256) void dalpha_reduce_kernel(const float* __restr
   if (threadIdx.x == 0) *out = (float)red[0];
 }
 
-__global__ void store_zero_kernel(float* out) { *out = 0.f; }
+__global__ void store_zero_kernel(float* out, int n) {
+  for (int x = threadIdx.x; x < n; x += blockDim.x) out[x] = 0.f;
+}
 
 int64_t tiles_of(int64_t N) { return (N + kRPB - 1) / kRPB; }
 
@@ -414,7 +421,7 @@ hipError_t run(const BwdArgs& a) {
   } else {
     bwd_query_kernel<T, MODE, DEV><<<grid, block, 0, a.stream>>>((const T*)a.q, (const T*)a.k, (const T*)a.v,
         (const T*)a.o, (const T*)a.dout, a.lse, (T*)a.dq, delta, part, a.N, a.W, a.tab, a.rope, scale, tiles,
-        a.plan);
+        a.plan, a.heads_per_plan);
   }
   if (bwdk_ring_supported(a) && (MODE == 0 || ps != nullptr)) {
     const hipError_t e = launch_bwdk_ring(a, delta, ps);
@@ -422,16 +429,17 @@ hipError_t run(const BwdArgs& a) {
   } else if (ps != nullptr) {
     bwd_key_ps_kernel<DEV><<<grid, block, 0, a.stream>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
         (const bf16_t*)a.v, (const bf16_t*)a.dout, a.lse, delta, ps, (bf16_t*)a.dk, (bf16_t*)a.dv, a.N, a.W, a.tab,
-        a.rope, scale, tiles, a.plan);
+        a.rope, scale, tiles, a.plan, a.heads_per_plan);
   } else {
     bwd_key_kernel<T, MODE, DEV><<<grid, block, 0, a.stream>>>((const T*)a.q, (const T*)a.k, (const T*)a.v,
-        (const T*)a.dout, a.lse, delta, (T*)a.dk, (T*)a.dv, a.N, a.W, a.tab, a.rope, scale, tiles, a.plan);
+        (const T*)a.dout, a.lse, delta, (T*)a.dk, (T*)a.dv, a.N, a.W, a.tab, a.rope, scale, tiles, a.plan, a.heads_per_plan);
   }
   if (a.dalpha != nullptr) {
+    // the query-side workgroups are head-major, so each layer's partials are one run
     if (MODE == 1)
-      dalpha_reduce_kernel<<<1, 256, 0, a.stream>>>(part, n_part, a.dalpha);
+      dalpha_reduce_kernel<<<a.layers, 256, 0, a.stream>>>(part, n_part / a.layers, a.dalpha);
     else
-      store_zero_kernel<<<1, 1, 0, a.stream>>>(a.dalpha);
+      store_zero_kernel<<<1, 256, 0, a.stream>>>(a.dalpha, a.layers);
   }
   return hipGetLastError();
 }

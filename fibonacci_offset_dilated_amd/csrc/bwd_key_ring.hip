@@ -59,6 +59,7 @@ struct BkArgs {
   Rope rope;
   const DevPlan* plan;  // alpha in device memory: the split above comes from here (DEV instances)
   int n_far;            // far entries in use (DEV instances: NF is an upper bound)
+  int heads_per_plan;   // DEV instances: head h reads plan[h / heads_per_plan]
 };
 
 struct __align__(16) BkSmem {
@@ -79,12 +80,21 @@ struct FarQ {
   float dlt[NF > 0 ? NF : 1];
 };
 
+// n_use: far slots in use (NF, or fewer in DEV instances: the unused slots get zero rows and
+// an infinite LSE, i.e. weight 0, without a load; n_use is wave-uniform)
 template <int NF>
-__device__ __forceinline__ void load_far_q(const int* fdist, FarQ<NF>& fq, const BkArgs& a, const bf16_t* Qh, const bf16_t* Dh,
-                                           const float* Lh, const float* Th, int j0, int n, int g, int lane_off) {
+__device__ __forceinline__ void load_far_q(const int* fdist, int n_use, FarQ<NF>& fq, const BkArgs& a,
+                                           const bf16_t* Qh, const bf16_t* Dh, const float* Lh, const float* Th, int j0,
+                                           int n, int g, int lane_off) {
   const float log2e = 1.4426950408889634f;
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
+    if (f >= n_use) {
+      fq.q[f][0] = fq.q[f][1] = fq.d[f][0] = fq.d[f][1] = make_uint4(0, 0, 0, 0);
+      fq.lse2[f] = INFINITY;
+      fq.dlt[f] = 0.f;
+      continue;
+    }
     const int r0 = j0 + fdist[f];
     int64_t off;
     int r = r0 + n;
@@ -125,10 +135,16 @@ __device__ __forceinline__ uint32_t ld4(const void* base, uint32_t off) {
 }
 
 template <int NF>
-__device__ __forceinline__ void load_far_qi(const int* fdist, FarQI<NF>& fq, const BkArgs& a, const bf16_t* Qh, const bf16_t* Dh,
-                                            const uint32_t* Sh, int n_cov, int j0, int l, int n, int g) {
+__device__ __forceinline__ void load_far_qi(const int* fdist, int n_use, FarQI<NF>& fq, const BkArgs& a,
+                                            const bf16_t* Qh, const bf16_t* Dh, const uint32_t* Sh, int n_cov, int j0,
+                                            int l, int n, int g) {
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
+    if (f >= n_use) {  // (as in load_far_q: (P, dS) = 0 gives the slot weight 0)
+      fq.q[f][0] = fq.q[f][1] = fq.d[f][0] = fq.d[f][1] = make_uint4(0, 0, 0, 0);
+      fq.ex[f] = fq.pl[f] = fq.ph[f] = 0u;
+      continue;
+    }
     const int r0 = j0 + fdist[f];
     // rows past the end repeat row N - 1 (their weights are zero)
     const int rb = r0 < a.N ? r0 : a.N - 1;
@@ -188,7 +204,11 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
   // memory) the split built on the device, read once into registers (the arguments struct
   // itself is never written, so it stays in the kernel-argument segment)
   RingSplit lcl;
-  if constexpr (DEV) lcl = a.plan->s8;
+  const DevPlan* pl = a.plan;
+  if constexpr (DEV) {
+    pl += (int)(blockIdx.x / a.segs) / a.heads_per_plan;
+    lcl = pl->s8;
+  }
   const int S_n_cov = DEV ? lcl.n_cov : a.n_cov;
   const int S_n_far = DEV ? lcl.n_far : a.n_far;
   const int S_lead = DEV ? ((lcl.need + kT - 1) / kT) * kT : a.lead;
@@ -202,7 +222,7 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
   for (int x = tid; x < n_unc * kHalf; x += kThreads) {
     const int u = x / kHalf, j = x % kHalf;
     int fd;
-    if constexpr (DEV) fd = a.plan->s8.far_dist[MODE == 1 ? u >> 1 : u];
+    if constexpr (DEV) fd = pl->s8.far_dist[MODE == 1 ? u >> 1 : u];
     else fd = S_far_dist(MODE == 1 ? u >> 1 : u);  // (a's arrays: constant indices in DEV instances)
     const int d = MODE == 1 ? fd - (u & 1) : fd;
     sm.unc_cs[u][j] = rope_cs(d, a.rope.rev[j]);
@@ -358,9 +378,9 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
   FarQ<MODE == 0 ? NF : 0> fq;
   FarQI<MODE == 1 ? NF : 0> fi;
   if constexpr (MODE == 0)
-    load_far_q<NF>(DEV ? lcl.far_dist : a.far_dist, fq, a, Qh, Dh, Lh, Th, s0 + 16 * wave, n, g, lane_off);
+    load_far_q<NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fq, a, Qh, Dh, Lh, Th, s0 + 16 * wave, n, g, lane_off);
   else
-    load_far_qi<NF>(DEV ? lcl.far_dist : a.far_dist, fi, a, Qh, Dh, Sh, S_n_cov, s0 + 16 * wave, l, n, g);
+    load_far_qi<NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fi, a, Qh, Dh, Sh, S_n_cov, s0 + 16 * wave, l, n, g);
 
   int buf = 0;
   for (int p0 = s0; p0 < s1; p0 += kT, buf ^= 1) {
@@ -547,7 +567,7 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
         vhv[2 * u + 1] = dot2(de[4 + u], p_hi, vhv[2 * u + 1]);
       }
     }
-    load_far_q<NF>(DEV ? lcl.far_dist : a.far_dist, fq, a, Qh, Dh, Lh, Th, j0 + kT, n, g, lane_off);
+    load_far_q<NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fq, a, Qh, Dh, Lh, Th, j0 + kT, n, g, lane_off);
     } else {
       // interpolated far entries: the lower query row (the lane's, rotated by R_c) and the
       // upper row (rotated by R_(c-1)) in fp32, weighted by the stored (P, dS) in fp32.
@@ -649,23 +669,19 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
     }
     // interpolated: the next step's far rows, requested after the stores (the far terms above
     // feed only the stores; requested earlier, the new rows would be held alongside them)
-    if constexpr (MODE == 1) load_far_qi<NF>(DEV ? lcl.far_dist : a.far_dist, fi, a, Qh, Dh, Sh, S_n_cov, j0 + kT, l, n, g);
+    if constexpr (MODE == 1) load_far_qi<NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fi, a, Qh, Dh, Sh, S_n_cov, j0 + kT, l, n, g);
     __syncthreads();
   }
 }
 
 template <int MODE, int NC, int NF, bool DEV>
 hipError_t launch(const BkArgs& a, unsigned blocks, hipStream_t s) {
-  if constexpr (DEV && NC != 16) {
-    return hipErrorInvalidValue;
-  } else {
-    const size_t smem = sizeof(BkSmem);
-    hipError_t e = hipFuncSetAttribute((const void*)bwdk_ring_kernel<MODE, NC, NF, DEV>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    bwdk_ring_kernel<MODE, NC, NF, DEV><<<blocks, 512, smem, s>>>(a);
-    return hipGetLastError();
-  }
+  const size_t smem = sizeof(BkSmem);
+  hipError_t e = hipFuncSetAttribute((const void*)bwdk_ring_kernel<MODE, NC, NF, DEV>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
+  bwdk_ring_kernel<MODE, NC, NF, DEV><<<blocks, 512, smem, s>>>(a);
+  return hipGetLastError();
 }
 
 template <int MODE, int NC, bool DEV>
@@ -680,12 +696,10 @@ hipError_t launch_far(const BkArgs& a, int n_far, unsigned blocks, hipStream_t s
 
 constexpr int kMaxFarK = 3;  // far offsets whose rows fit the registers at 8 waves
 
-// covered and far counts (with alpha in device memory: bounds over the alpha range, and 16
-// covered slots)
+// covered and far counts (with alpha in device memory: bounds over the alpha range)
 void split(const BwdArgs& f, int* n_cov, int* n_far) {
   if (f.plan != nullptr) {
     range_counts(f.alpha_lo, f.alpha_hi, f.base, f.n_base, f.W, f.mode, f.N, 8, n_cov, n_far);
-    if (*n_cov <= kMaxCov) *n_cov = kMaxCov;
   } else {
     split_table(f.tab, f.N, 8, n_cov, n_far);
   }
@@ -698,6 +712,13 @@ bool bwdk_ring_supported(const BwdArgs& f) {
   int cov, far;
   split(f, &cov, &far);
   return far <= kMaxFarK && cov <= kMaxCov;
+}
+
+int bwdk_instance_key(const BwdArgs& f) {
+  if (!bwdk_ring_supported(f)) return -1;
+  int cov, far;
+  split(f, &cov, &far);
+  return (cov <= 8 ? 8 : 16) * 10 + far;
 }
 
 hipError_t launch_bwdk_ring(const BwdArgs& f, const float* delta, const uint32_t* ps) {
@@ -718,6 +739,7 @@ hipError_t launch_bwdk_ring(const BwdArgs& f, const float* delta, const uint32_t
   split(f, &a.n_cov, &n_far);
   a.plan = f.plan;
   a.n_far = n_far;
+  a.heads_per_plan = f.heads_per_plan;
   for (int e = 0; e < kMaxCov; ++e) {
     a.dist[e] = e < a.n_cov ? f.tab.dist[e] : kMaxBand;
     a.w[e] = e < a.n_cov ? f.tab.w[e] : 0.f;
@@ -741,9 +763,13 @@ hipError_t launch_bwdk_ring(const BwdArgs& f, const float* delta, const uint32_t
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)kD));
   a.rope = f.rope;
   const unsigned blocks = (unsigned)(segs * f.BH);
-  if (f.plan != nullptr)
-    return f.mode == 0 ? launch_far<0, 16, true>(a, n_far, blocks, f.stream)
-                       : launch_far<1, 16, true>(a, n_far, blocks, f.stream);
+  if (f.plan != nullptr) {
+    if (f.mode == 0)
+      return a.n_cov <= 8 ? launch_far<0, 8, true>(a, n_far, blocks, f.stream)
+                          : launch_far<0, 16, true>(a, n_far, blocks, f.stream);
+    return a.n_cov <= 8 ? launch_far<1, 8, true>(a, n_far, blocks, f.stream)
+                        : launch_far<1, 16, true>(a, n_far, blocks, f.stream);
+  }
   if (f.mode == 0)
     return a.n_cov <= 8 ? launch_far<0, 8, false>(a, n_far, blocks, f.stream)
                         : launch_far<0, 16, false>(a, n_far, blocks, f.stream);

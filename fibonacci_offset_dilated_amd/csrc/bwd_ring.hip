@@ -56,6 +56,7 @@ struct BqArgs {
   Rope rope;
   const DevPlan* plan;  // alpha in device memory: the split above comes from here (DEV instances)
   int n_far;            // far entries in use (DEV instances: NF is an upper bound)
+  int heads_per_plan;   // DEV instances: head h reads plan[h / heads_per_plan]
 };
 
 struct __align__(16) BqSmem {
@@ -78,11 +79,19 @@ struct FarK {
   uint32_t ex[MODE == 1 && NF > 0 ? NF : 1];
 };
 
+// n_use: far slots to load (the rest are zero-filled). The kernel passes NF: in DEV
+// instances the unused slots load in-bounds rows and are masked, since skipping their loads
+// by a branch costs this kernel its register fit.
 template <int MODE, int NF>
-__device__ __forceinline__ void load_far(const int* fdist, FarK<MODE, NF>& fr, const BqArgs& a, const bf16_t* X, int i0w, int l,
-                                         int n, int g, int lane_off) {
+__device__ __forceinline__ void load_far(const int* fdist, int n_use, FarK<MODE, NF>& fr, const BqArgs& a,
+                                         const bf16_t* X, int i0w, int l, int n, int g, int lane_off) {
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
+    if (f >= n_use) {
+      fr.k[f][0] = fr.k[f][1] = make_uint4(0, 0, 0, 0);
+      if constexpr (MODE == 1) fr.ex[f] = 0u;
+      continue;
+    }
     const bf16_t* p = X + far_off(fdist[f], i0w, n, g, lane_off);
     fr.k[f][0] = *reinterpret_cast<const uint4*>(p);
     fr.k[f][1] = *reinterpret_cast<const uint4*>(p + kHalf);
@@ -161,7 +170,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
   // memory) the split built on the device, read once into registers (the arguments struct
   // itself is never written, so it stays in the kernel-argument segment)
   RingSplit lcl;
-  if constexpr (DEV) lcl = (WAVES == 8 ? a.plan->s8 : a.plan->s4);
+  const DevPlan* pl = a.plan;
+  if constexpr (DEV) {
+    pl += (int)(blockIdx.x / a.segs) / a.heads_per_plan;
+    lcl = (WAVES == 8 ? pl->s8 : pl->s4);
+  }
   const int S_n_cov = DEV ? lcl.n_cov : a.n_cov;
   const int S_n_far = DEV ? lcl.n_far : a.n_far;
   const int S_early_rows = DEV ? lcl.early_rows : a.early_rows;
@@ -179,7 +192,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
     for (int x = tid; x < n_unc * kHalf; x += kThreads) {
       const int u = x / kHalf, j = x % kHalf;
       int d;
-      if constexpr (DEV) d = (WAVES == 8 ? a.plan->s8 : a.plan->s4).unc_dist[u];
+      if constexpr (DEV) d = (WAVES == 8 ? pl->s8 : pl->s4).unc_dist[u];
       else d = a.unc_dist[u];  // (a's arrays are indexed by constants only in DEV instances)
       sm.unc_cs[u][j] = rope_cs(d, a.rope.rev[j]);
     }
@@ -315,7 +328,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
     }
   }
   FarK<MODE, NF> fk;
-  load_far<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, fk, a, Kh, s0 + 16 * wave, l, n, g, lane_off);
+  load_far<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, NF, fk, a, Kh, s0 + 16 * wave, l, n, g, lane_off);
   float dal = 0.f;  // d(alpha) contributions of this lane's queries
 
   int buf = 0;
@@ -431,7 +444,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
       }
     }
     FarK<MODE, NF> fv;
-    load_far<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, fv, a, Vh, i0w, l, n, g, lane_off);
+    load_far<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, NF, fv, a, Vh, i0w, l, n, g, lane_off);
 
     // ---- P, Delta, dS
     const float dlt = quad_add(dot16_bf(do0, do1, oo[0], oo[1]));
@@ -580,7 +593,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
         for (int f = 0; f < NF; ++f) pq[(size_t)(S_n_cov + f) * N] = ps_f[f];
       }
     }
-    load_far<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, fk, a, Kh, i0w + kT, l, n, g, lane_off);
+    load_far<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, NF, fk, a, Kh, i0w + kT, l, n, g, lane_off);
     __syncthreads();
   }
   if (MODE == 1) {
@@ -611,7 +624,7 @@ constexpr bool unused_instance() {
 
 template <int MODE, int NC, int NF, int WAVES, bool DEV>
 hipError_t launch(const BqArgs& a, unsigned blocks, hipStream_t s) {
-  if constexpr (unused_instance<MODE, NC, NF, WAVES>() || (DEV && NC != 16)) {
+  if constexpr (unused_instance<MODE, NC, NF, WAVES>()) {
     return hipErrorInvalidValue;
   } else {
     const size_t smem = sizeof(BqSmem);
@@ -624,10 +637,10 @@ hipError_t launch(const BqArgs& a, unsigned blocks, hipStream_t s) {
 }
 
 // kernel instance by (covered entries rounded up to 8 or 16, far entries); with alpha in
-// device memory (DEV) always 16 covered slots
+// device memory (DEV) the counts are bounds over the alpha range
 template <int MODE, int WAVES, bool DEV = false>
 hipError_t launch_far(const BqArgs& a, int n_far, unsigned blocks, hipStream_t s) {
-  if (DEV || a.n_cov > 8) {
+  if (a.n_cov > 8) {
     switch (n_far) {
       case 0: return launch<MODE, 16, 0, WAVES, DEV>(a, blocks, s);
       case 1: return launch<MODE, 16, 1, WAVES, DEV>(a, blocks, s);
@@ -645,13 +658,11 @@ hipError_t launch_far(const BqArgs& a, int n_far, unsigned blocks, hipStream_t s
   }
 }
 
-// With alpha in device memory the counts are upper bounds over the alpha range, and the
-// covered slots are always 16.
+// With alpha in device memory the counts are upper bounds over the alpha range.
 int plan(const BwdArgs& f, int* n_cov, int* n_far) {
   auto split = [&](int waves) {
     if (f.plan != nullptr) {
       range_counts(f.alpha_lo, f.alpha_hi, f.base, f.n_base, f.W, f.mode, f.N, waves, n_cov, n_far);
-      if (*n_cov <= kMaxCov) *n_cov = kMaxCov;
     } else {
       split_table(f.tab, f.N, waves, n_cov, n_far);
     }
@@ -672,6 +683,13 @@ bool bwdq_ring_supported(const BwdArgs& f) {
   int cov, far;
   plan(f, &cov, &far);
   return far <= kMaxFar && cov <= kMaxCov;
+}
+
+int bwdq_instance_key(const BwdArgs& f) {
+  if (!bwdq_ring_supported(f)) return -1;
+  int cov, far;
+  const int waves = plan(f, &cov, &far);
+  return waves * 1000 + (cov <= 8 ? 8 : 16) * 10 + far;
 }
 
 int64_t bwdq_ring_blocks(const BwdArgs& f) {
@@ -729,6 +747,7 @@ hipError_t launch_bwdq_ring(const BwdArgs& f, float* delta, float* part, uint32_
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)kD));
   a.rope = f.rope;
   a.n_far = n_far;
+  a.heads_per_plan = f.heads_per_plan;
   if (f.plan != nullptr) {
     if (f.mode == 0) {
       return waves == 8 ? launch_far<0, 8, true>(a, n_far, (unsigned)blocks, f.stream)

@@ -27,8 +27,9 @@ template <typename T, int MODE, bool DEV>
 __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                      const T* __restrict__ v, T* __restrict__ o,
                                                      float* __restrict__ lse, int64_t N, int W, Table tab_arg,
-                                                     Rope rope, float scale_log2, const DevPlan* __restrict__ plan) {
-  const Table& tab = call_table<DEV>(tab_arg, plan);
+                                                     Rope rope, float scale_log2, const DevPlan* __restrict__ plan,
+                                                     int heads_per_plan) {
+  const Table& tab = call_table<DEV>(tab_arg, plan, (int)blockIdx.x / heads_per_plan);
   __shared__ float2 cs[kCsSlots][kHalf];
   __shared__ float red_m[kQuads], red_l[kQuads];
   __shared__ float red_o[kQuads][kD];
@@ -146,17 +147,17 @@ hipError_t launch_decode_t(const FwdArgs& a) {
   if (a.dtype == 0) {
     if (a.mode == 0)
       decode_kernel<float, 0, DEV><<<grid, block, 0, a.stream>>>((const float*)a.q, (const float*)a.k,
-          (const float*)a.v, (float*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, a.plan);
+          (const float*)a.v, (float*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, a.plan, a.heads_per_plan);
     else
       decode_kernel<float, 1, DEV><<<grid, block, 0, a.stream>>>((const float*)a.q, (const float*)a.k,
-          (const float*)a.v, (float*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, a.plan);
+          (const float*)a.v, (float*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, a.plan, a.heads_per_plan);
   } else {
     if (a.mode == 0)
       decode_kernel<bf16_t, 0, DEV><<<grid, block, 0, a.stream>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
-          (const bf16_t*)a.v, (bf16_t*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, a.plan);
+          (const bf16_t*)a.v, (bf16_t*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, a.plan, a.heads_per_plan);
     else
       decode_kernel<bf16_t, 1, DEV><<<grid, block, 0, a.stream>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
-          (const bf16_t*)a.v, (bf16_t*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, a.plan);
+          (const bf16_t*)a.v, (bf16_t*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, a.plan, a.heads_per_plan);
   }
   return hipGetLastError();
 }

@@ -63,11 +63,11 @@ __host__ __device__ inline void build_table(float alpha, const int32_t* base, in
 }
 
 // The table of a call: the kernel argument, or (DEV instances, alpha in device memory) the
-// one built on the device. The pointer is a read-only kernel argument, so its loads are
-// uniform (scalar) loads.
+// one built on the device for the block's layer. The pointer is a read-only kernel argument
+// and the layer is uniform, so its loads are uniform (scalar) loads.
 template <bool DEV, typename Plan>
-__device__ __forceinline__ const Table& call_table(const Table& arg, const Plan* plan) {
-  if constexpr (DEV) return plan->tab;
+__device__ __forceinline__ const Table& call_table(const Table& arg, const Plan* plan, int layer) {
+  if constexpr (DEV) return plan[layer].tab;
   else return arg;
 }
 

@@ -84,8 +84,18 @@ struct DevPlan {
 struct BaseList {
   int32_t v[kMaxEnt];
 };
-hipError_t launch_dev_plan(DevPlan* out, const float* alpha, float alpha_lo, float alpha_hi, const BaseList& base,
-                           int n_base, int W, int mode, int64_t N, hipStream_t s);
+// Several layers in one call: layer l's tensors are the l-th [B, H, N, D] block of
+// [L, B, H, N, D] inputs and its plan is plan[l]; the kernels take head h's plan from
+// plan[h / heads_per_plan] (heads_per_plan = B * H).
+constexpr int kMaxLayers = 256;
+struct AlphaList {
+  float v[kMaxLayers];
+};
+// Builds plans out[0..L-1]: from alpha[l] in device memory clamped into [lo, hi] (alpha not
+// null), else from host[l] as given.
+hipError_t launch_dev_plan(DevPlan* out, const float* alpha, const AlphaList& host, int L, float alpha_lo,
+                           float alpha_hi, const BaseList& base, int n_base, int W, int mode, int64_t N,
+                           hipStream_t s);
 // Upper bounds, over alpha in [lo, hi], of the covered and far counts of make_split (host).
 void range_counts(float lo, float hi, const int32_t* base, int n_base, int W, int mode, int64_t N, int waves,
                   int* n_cov, int* n_far);
@@ -108,6 +118,8 @@ struct FwdArgs {
   float alpha_lo = 0.f, alpha_hi = 0.f;
   const int32_t* base = nullptr;
   int n_base = 0;
+  int heads_per_plan = 0x7fffffff;  // several layers: B * H (see AlphaList)
+  int layers = 1;
 };
 
 struct BwdArgs {
@@ -131,10 +143,17 @@ struct BwdArgs {
   float alpha_lo = 0.f, alpha_hi = 0.f;
   const int32_t* base = nullptr;
   int n_base = 0;
+  int heads_per_plan = 0x7fffffff;
+  int layers = 1;  // dalpha holds one value per layer
 };
 
 hipError_t launch_fwd_generic(const FwdArgs& a);
 bool fwd_ring_supported(const FwdArgs& a);
+// the kernel instance a launch would pick (-1: the general kernel); calls over several
+// layers launch runs of consecutive layers whose instances agree
+int fwd_instance_key(const FwdArgs& a);
+int bwdq_instance_key(const BwdArgs& a);
+int bwdk_instance_key(const BwdArgs& a);
 hipError_t launch_fwd_ring(const FwdArgs& a);
 hipError_t launch_index_set(int32_t* out, int64_t N, int W, const Table& tab, int64_t cols, hipStream_t s);
 // one query per (batch, head) at position N - 1 of a K/V cache of N rows: q and o are

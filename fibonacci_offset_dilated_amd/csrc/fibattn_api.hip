@@ -11,6 +11,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "../../include/fibattn.h"
 #include "fib_launch.h"
 
@@ -166,31 +168,45 @@ int fib_sparse_attn_index_set(int64_t N, int W, float alpha, const int32_t* base
 
 namespace {
 
-// Where alpha comes from: a host value, or device memory together with the range the launch
-// is planned for and a device buffer that receives the plan (the table built from *alpha).
+// Where alpha comes from: one host value; or device memory (one value per layer) together
+// with the range the launch is planned for; or (calls over several layers) one host value
+// per layer. The last two build their tables on the device into the caller's plan buffer
+// (one DevPlan per layer).
 struct AlphaArg {
   bool dev;
   float host;
-  const float* ptr;
+  const float* ptr;        // device alphas [layers]
+  const float* host_list;  // host alphas [layers]
+  int64_t layers;
   float lo, hi;
   void* plan;
   size_t plan_bytes;
+  bool uses_plan() const { return dev || host_list != nullptr; }
 };
 
 int check_alpha(const AlphaArg& al) {
-  if (!al.dev) return isfinite(al.host) && al.host > 0.f ? FIB_OK : FIB_ERR_ALPHA;
-  if (al.ptr == nullptr || al.plan == nullptr) return FIB_ERR_NULL;
-  if (!isfinite(al.lo) || !isfinite(al.hi) || al.lo <= 0.f || al.hi < al.lo) return FIB_ERR_ALPHA;
-  if (((uintptr_t)al.ptr & 3u) || !aligned16(al.plan)) return FIB_ERR_ALIGN;
-  if (al.plan_bytes < sizeof(DevPlan)) return FIB_ERR_WORKSPACE;
+  if (al.layers < 1 || al.layers > kMaxLayers) return FIB_ERR_SHAPE;
+  if (!al.uses_plan()) return isfinite(al.host) && al.host > 0.f ? FIB_OK : FIB_ERR_ALPHA;
+  if (al.plan == nullptr || (al.dev && al.ptr == nullptr)) return FIB_ERR_NULL;
+  if (al.dev) {
+    if (!isfinite(al.lo) || !isfinite(al.hi) || al.lo <= 0.f || al.hi < al.lo) return FIB_ERR_ALPHA;
+    if ((uintptr_t)al.ptr & 3u) return FIB_ERR_ALIGN;
+  } else {
+    for (int64_t l = 0; l < al.layers; ++l)
+      if (!isfinite(al.host_list[l]) || al.host_list[l] <= 0.f) return FIB_ERR_ALPHA;
+  }
+  if (!aligned16(al.plan)) return FIB_ERR_ALIGN;
+  if (al.plan_bytes < (size_t)al.layers * sizeof(DevPlan)) return FIB_ERR_WORKSPACE;
   return FIB_OK;
 }
 
-// The call's table: built on the host, or (alpha in device memory) by a one-thread kernel
-// enqueued on the stream ahead of the attention kernels, which then read it from the plan.
+// The call's table: built on the host, or by a kernel (one thread per layer) enqueued on the
+// stream ahead of the attention kernels, which then read it from the plan.
 template <typename Args>
 int set_table(Args& a, const AlphaArg& al, const int32_t* base, int n_base) {
-  if (!al.dev) {
+  a.layers = (int)al.layers;
+  a.heads_per_plan = (int)(a.BH / al.layers);
+  if (!al.uses_plan()) {
     build_table(al.host, base, n_base, a.W, a.mode, &a.tab);
     return FIB_OK;
   }
@@ -198,15 +214,89 @@ int set_table(Args& a, const AlphaArg& al, const int32_t* base, int n_base) {
   BaseList bl;
   memset(&bl, 0, sizeof(bl));
   for (int e = 0; e < n_base; ++e) bl.v[e] = base[e];
-  if (launch_dev_plan((DevPlan*)al.plan, al.ptr, al.lo, al.hi, bl, n_base, a.W, a.mode, a.N, a.stream) !=
-      hipSuccess)
+  AlphaList hl;
+  memset(&hl, 0, sizeof(hl));
+  float lo = al.lo, hi = al.hi;
+  if (!al.dev) {
+    // host values: the kernels are planned for exactly their range
+    lo = hi = al.host_list[0];
+    for (int64_t l = 0; l < al.layers; ++l) {
+      hl.v[l] = al.host_list[l];
+      lo = fminf(lo, hl.v[l]);
+      hi = fmaxf(hi, hl.v[l]);
+    }
+  }
+  if (launch_dev_plan((DevPlan*)al.plan, al.dev ? al.ptr : nullptr, hl, (int)al.layers, lo, hi, bl, n_base, a.W,
+                      a.mode, a.N, a.stream) != hipSuccess)
     return FIB_ERR_LAUNCH;
   a.plan = (const DevPlan*)al.plan;
-  a.alpha_lo = al.lo;
-  a.alpha_hi = al.hi;
+  a.alpha_lo = lo;
+  a.alpha_hi = hi;
   a.base = base;
   a.n_base = n_base;
   return FIB_OK;
+}
+
+// Calls over several layers with host alphas launch runs of consecutive layers: a run grows
+// while the kernel instance picked for its alpha range stays the one its first layer gets
+// alone, so no layer runs a wider instance than a single-layer call would (with device
+// alphas the host cannot see them, and one launch covers the declared range).
+template <typename Args, typename Key>
+int64_t run_end(const Args& a, const AlphaArg& al, int64_t s, Key key) {
+  Args t = a;
+  t.BH = a.heads_per_plan;
+  float lo = al.host_list[s], hi = lo;
+  t.alpha_lo = t.alpha_hi = lo;
+  const int k0 = key(t);
+  int64_t e = s + 1;
+  for (; e < al.layers; ++e) {
+    t.alpha_lo = fminf(lo, al.host_list[e]);
+    t.alpha_hi = fmaxf(hi, al.host_list[e]);
+    if (key(t) != k0) break;
+    lo = t.alpha_lo;
+    hi = t.alpha_hi;
+  }
+  return e;
+}
+
+// Args of layers [s, e) of a call over several layers: tensors and plans offset by s layers.
+// A run of one layer takes the host-built table as a kernel argument instead (the kernels
+// then need not read the plan from memory), i.e. exactly the single-layer call.
+template <typename Args>
+Args layer_run(const Args& a, const AlphaArg& al, const int32_t* base, int n_base, int64_t s, int64_t e) {
+  Args b = a;
+  const int64_t hpp = a.heads_per_plan;
+  const size_t rows = (size_t)(s * hpp) * (size_t)a.N;
+  const size_t bytes = rows * kD * (a.dtype == 0 ? 4 : 2);
+  auto off = [&](auto p) { return p == nullptr ? p : (decltype(p))((const char*)p + bytes); };
+  b.q = off(a.q);
+  b.k = off(a.k);
+  b.v = off(a.v);
+  if (a.lse != nullptr) b.lse = a.lse + rows;
+  if constexpr (std::is_same_v<Args, BwdArgs>) {
+    b.o = off(a.o);
+    b.dout = off(a.dout);
+    b.dq = off(a.dq);
+    b.dk = off(a.dk);
+    b.dv = off(a.dv);
+    if (a.dalpha != nullptr) b.dalpha = a.dalpha + s;
+  } else {
+    b.o = off(a.o);
+  }
+  b.plan = a.plan + s;
+  b.BH = (e - s) * hpp;
+  b.layers = (int)(e - s);
+  b.alpha_lo = b.alpha_hi = al.host_list[s];
+  for (int64_t l = s; l < e; ++l) {
+    b.alpha_lo = fminf(b.alpha_lo, al.host_list[l]);
+    b.alpha_hi = fmaxf(b.alpha_hi, al.host_list[l]);
+  }
+  if (e - s == 1) {
+    b.plan = nullptr;
+    b.heads_per_plan = 0x7fffffff;
+    build_table(al.host_list[s], base, n_base, a.W, a.mode, &b.tab);
+  }
+  return b;
 }
 
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
@@ -230,8 +320,16 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   a.stream = (hipStream_t)stream;
   st = set_table(a, al, base, n_base);
   if (st) return st;
-  hipError_t e = decode ? launch_decode(a) : fwd_ring_supported(a) ? launch_fwd_ring(a) : launch_fwd_generic(a);
-  return e == hipSuccess ? FIB_OK : FIB_ERR_LAUNCH;
+  auto launch = [&](const FwdArgs& b) {
+    return decode ? launch_decode(b) : fwd_ring_supported(b) ? launch_fwd_ring(b) : launch_fwd_generic(b);
+  };
+  if (al.dev || al.host_list == nullptr || al.layers == 1) return launch(a) == hipSuccess ? FIB_OK : FIB_ERR_LAUNCH;
+  for (int64_t s0 = 0; s0 < al.layers;) {
+    const int64_t e0 = run_end(a, al, s0, [](const FwdArgs& t) { return fwd_instance_key(t); });
+    if (launch(layer_run(a, al, base, n_base, s0, e0)) != hipSuccess) return FIB_ERR_LAUNCH;
+    s0 = e0;
+  }
+  return FIB_OK;
 }
 
 int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
@@ -264,12 +362,29 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   a.stream = (hipStream_t)stream;
   st = set_table(a, al, base, n_base);
   if (st) return st;
-  return launch_bwd(a) == hipSuccess ? FIB_OK : FIB_ERR_LAUNCH;
+  if (al.dev || al.host_list == nullptr || al.layers == 1) return launch_bwd(a) == hipSuccess ? FIB_OK : FIB_ERR_LAUNCH;
+  // runs share the workspace: they execute one after another on the stream
+  for (int64_t s0 = 0; s0 < al.layers;) {
+    const int64_t e0 = run_end(a, al, s0, [](const BwdArgs& t) {
+      return bwdq_instance_key(t) * 1000 + bwdk_instance_key(t);
+    });
+    if (launch_bwd(layer_run(a, al, base, n_base, s0, e0)) != hipSuccess) return FIB_ERR_LAUNCH;
+    s0 = e0;
+  }
+  return FIB_OK;
 }
 
-AlphaArg host_alpha(float alpha) { return AlphaArg{false, alpha, nullptr, 0.f, 0.f, nullptr, 0}; }
-AlphaArg dev_alpha(const float* alpha, float lo, float hi, void* plan, size_t plan_bytes) {
-  return AlphaArg{true, 0.f, alpha, lo, hi, plan, plan_bytes};
+AlphaArg host_alpha(float alpha) { return AlphaArg{false, alpha, nullptr, nullptr, 1, 0.f, 0.f, nullptr, 0}; }
+AlphaArg dev_alpha(const float* alpha, float lo, float hi, void* plan, size_t plan_bytes, int64_t layers = 1) {
+  return AlphaArg{true, 0.f, alpha, nullptr, layers, lo, hi, plan, plan_bytes};
+}
+AlphaArg host_alphas(const float* alpha, int64_t layers, void* plan, size_t plan_bytes) {
+  return AlphaArg{false, 0.f, nullptr, alpha, layers, 0.f, 0.f, plan, plan_bytes};
+}
+
+// [L, B, H, N, D] inputs are L * B batches of the single-layer shape
+int64_t layer_batches(int64_t L, int64_t B) {
+  return (L < 1 || L > kMaxLayers || B < 1 || B > (1LL << 31)) ? 0 : L * B;
 }
 
 }  // namespace
@@ -310,6 +425,62 @@ int fib_sparse_attn_bwd(const void* q, const void* k, const void* v, const void*
 }
 
 size_t fib_sparse_attn_plan_bytes(void) { return sizeof(DevPlan); }
+
+size_t fib_sparse_attn_layers_plan_bytes(int64_t n_layers) {
+  return n_layers < 1 || n_layers > kMaxLayers ? 0 : (size_t)n_layers * sizeof(DevPlan);
+}
+
+int fib_sparse_attn_fwd_layers(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int64_t L, int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                               int W, const float* alpha, const int32_t* base, int n_base,
+                               float rope_theta, int mode, void* plan, size_t plan_bytes, void* stream) {
+  if (alpha == nullptr) return FIB_ERR_NULL;
+  const int64_t LB = layer_batches(L, B);
+  if (LB == 0) return FIB_ERR_SHAPE;
+  return fwd_impl(q, k, v, o, lse, LB, H, N, D, dtype, W, host_alphas(alpha, L, plan, plan_bytes), base, n_base,
+                  rope_theta, mode, stream, false);
+}
+
+int fib_sparse_attn_fwd_layers_dev(const void* q, const void* k, const void* v, void* o, float* lse,
+                                   int64_t L, int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                                   int W, const float* alpha, float alpha_lo, float alpha_hi,
+                                   const int32_t* base, int n_base, float rope_theta, int mode,
+                                   void* plan, size_t plan_bytes, void* stream) {
+  const int64_t LB = layer_batches(L, B);
+  if (LB == 0) return FIB_ERR_SHAPE;
+  return fwd_impl(q, k, v, o, lse, LB, H, N, D, dtype, W, dev_alpha(alpha, alpha_lo, alpha_hi, plan, plan_bytes, L),
+                  base, n_base, rope_theta, mode, stream, false);
+}
+
+int fib_sparse_attn_bwd_layers(const void* q, const void* k, const void* v, const void* o,
+                               const void* dout, const float* lse,
+                               void* dq, void* dk, void* dv, float* dalpha,
+                               int64_t L, int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                               int W, const float* alpha, const int32_t* base, int n_base,
+                               float rope_theta, int mode, void* workspace, size_t workspace_bytes,
+                               void* plan, size_t plan_bytes, void* stream) {
+  if (alpha == nullptr) return FIB_ERR_NULL;
+  const int64_t LB = layer_batches(L, B);
+  if (LB == 0) return FIB_ERR_SHAPE;
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, dalpha, LB, H, N, D, dtype, W,
+                  host_alphas(alpha, L, plan, plan_bytes), base, n_base, rope_theta, mode, workspace,
+                  workspace_bytes, stream);
+}
+
+int fib_sparse_attn_bwd_layers_dev(const void* q, const void* k, const void* v, const void* o,
+                                   const void* dout, const float* lse,
+                                   void* dq, void* dk, void* dv, float* dalpha,
+                                   int64_t L, int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                                   int W, const float* alpha, float alpha_lo, float alpha_hi,
+                                   const int32_t* base, int n_base, float rope_theta, int mode,
+                                   void* workspace, size_t workspace_bytes, void* plan, size_t plan_bytes,
+                                   void* stream) {
+  const int64_t LB = layer_batches(L, B);
+  if (LB == 0) return FIB_ERR_SHAPE;
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, dalpha, LB, H, N, D, dtype, W,
+                  dev_alpha(alpha, alpha_lo, alpha_hi, plan, plan_bytes, L), base, n_base, rope_theta, mode,
+                  workspace, workspace_bytes, stream);
+}
 
 int fib_sparse_attn_fwd_dev(const void* q, const void* k, const void* v, void* o, float* lse,
                             int64_t B, int64_t H, int64_t N, int64_t D, int dtype,

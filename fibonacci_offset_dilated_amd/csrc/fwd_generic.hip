@@ -24,8 +24,8 @@ template <typename T, int MODE, bool DEV>
 __global__ __launch_bounds__(256) void fwd_generic_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ o,
     float* __restrict__ lse, int64_t N, int W, Table tab_arg, Rope rope, float scale_log2, int tiles,
-    const DevPlan* __restrict__ plan) {
-  const Table& tab = call_table<DEV>(tab_arg, plan);
+    const DevPlan* __restrict__ plan, int heads_per_plan) {
+  const Table& tab = call_table<DEV>(tab_arg, plan, (int)(blockIdx.x / tiles) / heads_per_plan);
   __shared__ float2 cs[kCsSlots][kHalf];
   const bool cached = fill_cs(cs, W, tab, MODE, rope);
   const int64_t head = blockIdx.x / tiles;
@@ -126,17 +126,17 @@ hipError_t launch_generic(const FwdArgs& a) {
   if (a.dtype == 0) {
     if (a.mode == 0)
       fwd_generic_kernel<float, 0, DEV><<<grid, block, 0, a.stream>>>((const float*)a.q, (const float*)a.k,
-          (const float*)a.v, (float*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, tiles, a.plan);
+          (const float*)a.v, (float*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, tiles, a.plan, a.heads_per_plan);
     else
       fwd_generic_kernel<float, 1, DEV><<<grid, block, 0, a.stream>>>((const float*)a.q, (const float*)a.k,
-          (const float*)a.v, (float*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, tiles, a.plan);
+          (const float*)a.v, (float*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, tiles, a.plan, a.heads_per_plan);
   } else {
     if (a.mode == 0)
       fwd_generic_kernel<bf16_t, 0, DEV><<<grid, block, 0, a.stream>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
-          (const bf16_t*)a.v, (bf16_t*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, tiles, a.plan);
+          (const bf16_t*)a.v, (bf16_t*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, tiles, a.plan, a.heads_per_plan);
     else
       fwd_generic_kernel<bf16_t, 1, DEV><<<grid, block, 0, a.stream>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
-          (const bf16_t*)a.v, (bf16_t*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, tiles, a.plan);
+          (const bf16_t*)a.v, (bf16_t*)a.o, a.lse, a.N, a.W, a.tab, a.rope, sl2, tiles, a.plan, a.heads_per_plan);
   }
   return hipGetLastError();
 }

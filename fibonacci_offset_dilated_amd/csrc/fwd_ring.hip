@@ -64,6 +64,7 @@ struct RingArgs {
   Rope rope;
   const DevPlan* plan;  // alpha in device memory: the split above comes from here (DEV instances)
   int n_far;            // far entries in use (DEV instances: NF is an upper bound)
+  int heads_per_plan;   // DEV instances: head h reads plan[h / heads_per_plan]
 };
 
 struct __align__(16) Smem {
@@ -86,11 +87,17 @@ struct FarRows {
   uint4 vh[NF > 0 ? NF : 1][2];
 };
 
+// n_use: far slots in use (NF, or fewer in DEV instances: the unused slots are zero-filled
+// without a load; n_use is wave-uniform, so the test is a scalar branch)
 template <int MODE, int NF>
-__device__ __forceinline__ void load_far_k(const int* fdist, FarRows<NF>& fr, const RingArgs& a, const bf16_t* Kh, int i0w, int n, int g,
-                                           int lane_off) {
+__device__ __forceinline__ void load_far_k(const int* fdist, int n_use, FarRows<NF>& fr, const RingArgs& a,
+                                           const bf16_t* Kh, int i0w, int n, int g, int lane_off) {
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
+    if (f >= n_use) {
+      fr.k[f][0] = fr.k[f][1] = fr.kh[f][0] = fr.kh[f][1] = make_uint4(0, 0, 0, 0);
+      continue;
+    }
     const bf16_t* kp = Kh + far_off(fdist[f], i0w, n, g, lane_off);
     fr.k[f][0] = *reinterpret_cast<const uint4*>(kp);
     fr.k[f][1] = *reinterpret_cast<const uint4*>(kp + kHalf);
@@ -103,10 +110,14 @@ __device__ __forceinline__ void load_far_k(const int* fdist, FarRows<NF>& fr, co
 }
 
 template <int MODE, int NF>
-__device__ __forceinline__ void load_far_v(const int* fdist, FarRows<NF>& fr, const RingArgs& a, const bf16_t* Vh, int i0w, int n, int g,
-                                           int lane_off) {
+__device__ __forceinline__ void load_far_v(const int* fdist, int n_use, FarRows<NF>& fr, const RingArgs& a,
+                                           const bf16_t* Vh, int i0w, int n, int g, int lane_off) {
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
+    if (f >= n_use) {
+      fr.v[f][0] = fr.v[f][1] = fr.vh[f][0] = fr.vh[f][1] = make_uint4(0, 0, 0, 0);
+      continue;
+    }
     const bf16_t* vp = Vh + far_off(fdist[f], i0w, n, g, lane_off);
     fr.v[f][0] = *reinterpret_cast<const uint4*>(vp);
     fr.v[f][1] = *reinterpret_cast<const uint4*>(vp + kHalf);
@@ -166,7 +177,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
   // memory) the split built on the device, read once into registers (the arguments struct
   // itself is never written, so it stays in the kernel-argument segment)
   RingSplit lcl;
-  if constexpr (DEV) lcl = (WAVES == 8 ? a.plan->s8 : a.plan->s4);
+  const DevPlan* pl = a.plan;
+  if constexpr (DEV) {
+    pl += (int)(blockIdx.x / a.segs) / a.heads_per_plan;
+    lcl = (WAVES == 8 ? pl->s8 : pl->s4);
+  }
   const int S_n_cov = DEV ? lcl.n_cov : a.n_cov;
   const int S_n_far = DEV ? lcl.n_far : a.n_far;
   const int S_early_rows = DEV ? lcl.early_rows : a.early_rows;
@@ -183,7 +198,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
     for (int x = tid; x < n_unc * kHalf; x += kThreads) {
       const int u = x / kHalf, j = x % kHalf;
       int d;
-      if constexpr (DEV) d = (WAVES == 8 ? a.plan->s8 : a.plan->s4).unc_dist[u];
+      if constexpr (DEV) d = (WAVES == 8 ? pl->s8 : pl->s4).unc_dist[u];
       else d = a.unc_dist[u];  // (a's arrays are indexed by constants only in DEV instances)
       sm.unc_cs[u][j] = rope_cs(d, a.rope.rev[j]);
     }
@@ -328,7 +343,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
   // (the first step's barrier orders these stores before any read of them)
   // far K rows of the first step (requested after the warm-up rows, whose registers they reuse)
   FarRows<NF> fr;
-  load_far_k<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, fr, a, Kh, s0 + 16 * wave, n, g, lane_off);
+  load_far_k<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fr, a, Kh, s0 + 16 * wave, n, g,
+                       lane_off);
 
   int buf = 0;
   for (int p0 = s0; p0 < s1; p0 += kT, buf ^= 1) {
@@ -419,7 +435,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
         if (DEV && f >= S_n_far) s_far[f] = -INFINITY;  // slot beyond the table
       }
       // their V rows, for the end of this step (K and V rows are never held together)
-      load_far_v<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, fr, a, Vh, i0w, n, g, lane_off);
+      load_far_v<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fr, a, Vh, i0w, n, g, lane_off);
 
 
       // ---- softmax over the window band and the entries (base-2 logits)
@@ -557,7 +573,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
         if (g == 0 && a.lse != nullptr) (a.lse + (size_t)head * N + i0w)[n] = (m + log2f(lsum)) * 0.69314718055994530942f;
       }
       // far K rows of the next step (the last step loads rows that are never used)
-      load_far_k<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, fr, a, Kh, i0w + kT, n, g, lane_off);
+      load_far_k<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fr, a, Kh, i0w + kT, n, g,
+                           lane_off);
     }
     __syncthreads();
   }
@@ -566,13 +583,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
 // Waves per workgroup and the table split: 8 waves (two per SIMD) where the registers fit
 // 256 per lane, else 4 (interpolated mode with many far entries: their row pairs need twice
 // the registers).
-// With alpha in device memory the counts are upper bounds over the alpha range, and the
-// covered slots are always 16.
+// With alpha in device memory the counts are upper bounds over the alpha range.
 int plan(const FwdArgs& f, int* n_cov, int* n_far) {
   auto split = [&](int waves) {
     if (f.plan != nullptr) {
       range_counts(f.alpha_lo, f.alpha_hi, f.base, f.n_base, f.W, f.mode, f.N, waves, n_cov, n_far);
-      if (*n_cov <= kMaxCov) *n_cov = kMaxCov;
     } else {
       split_table(f.tab, f.N, waves, n_cov, n_far);
     }
@@ -593,7 +608,7 @@ constexpr bool unused_instance() {
 
 template <int MODE, int NC, int NF, int WAVES, bool DEV>
 hipError_t launch(const RingArgs& a, unsigned blocks, hipStream_t s) {
-  if constexpr (unused_instance<MODE, NC, NF, WAVES>() || (DEV && NC != 16)) {
+  if constexpr (unused_instance<MODE, NC, NF, WAVES>()) {
     return hipErrorInvalidValue;
   } else {
   const size_t smem = sizeof(Smem);
@@ -606,33 +621,24 @@ hipError_t launch(const RingArgs& a, unsigned blocks, hipStream_t s) {
 }
 
 // kernel instance by (covered entries rounded up to 8 or 16, far entries, waves); with alpha
-// in device memory (DEV) always 16 covered slots
+// in device memory (DEV) the counts are bounds over the alpha range
 template <int MODE, int WAVES, bool DEV = false>
 hipError_t launch_mode(const RingArgs& a, int n_far, unsigned blocks, hipStream_t s) {
-  if constexpr (DEV) {
-    switch (n_far) {
-      case 0: return launch<MODE, 16, 0, WAVES, true>(a, blocks, s);
-      case 1: return launch<MODE, 16, 1, WAVES, true>(a, blocks, s);
-      case 2: return launch<MODE, 16, 2, WAVES, true>(a, blocks, s);
-      case 3: return launch<MODE, 16, 3, WAVES, true>(a, blocks, s);
-      default: return launch<MODE, 16, 4, WAVES, true>(a, blocks, s);
-    }
-  }
   if (a.n_cov <= 8) {
     switch (n_far) {
-      case 0: return launch<MODE, 8, 0, WAVES, false>(a, blocks, s);
-      case 1: return launch<MODE, 8, 1, WAVES, false>(a, blocks, s);
-      case 2: return launch<MODE, 8, 2, WAVES, false>(a, blocks, s);
-      case 3: return launch<MODE, 8, 3, WAVES, false>(a, blocks, s);
-      default: return launch<MODE, 8, 4, WAVES, false>(a, blocks, s);
+      case 0: return launch<MODE, 8, 0, WAVES, DEV>(a, blocks, s);
+      case 1: return launch<MODE, 8, 1, WAVES, DEV>(a, blocks, s);
+      case 2: return launch<MODE, 8, 2, WAVES, DEV>(a, blocks, s);
+      case 3: return launch<MODE, 8, 3, WAVES, DEV>(a, blocks, s);
+      default: return launch<MODE, 8, 4, WAVES, DEV>(a, blocks, s);
     }
   }
   switch (n_far) {
-    case 0: return launch<MODE, 16, 0, WAVES, false>(a, blocks, s);
-    case 1: return launch<MODE, 16, 1, WAVES, false>(a, blocks, s);
-    case 2: return launch<MODE, 16, 2, WAVES, false>(a, blocks, s);
-    case 3: return launch<MODE, 16, 3, WAVES, false>(a, blocks, s);
-    default: return launch<MODE, 16, 4, WAVES, false>(a, blocks, s);
+    case 0: return launch<MODE, 16, 0, WAVES, DEV>(a, blocks, s);
+    case 1: return launch<MODE, 16, 1, WAVES, DEV>(a, blocks, s);
+    case 2: return launch<MODE, 16, 2, WAVES, DEV>(a, blocks, s);
+    case 3: return launch<MODE, 16, 3, WAVES, DEV>(a, blocks, s);
+    default: return launch<MODE, 16, 4, WAVES, DEV>(a, blocks, s);
   }
 }
 
@@ -643,6 +649,13 @@ bool fwd_ring_supported(const FwdArgs& f) {
   int cov, far;
   plan(f, &cov, &far);
   return far <= kMaxFar && cov <= kMaxCov;
+}
+
+int fwd_instance_key(const FwdArgs& f) {
+  if (!fwd_ring_supported(f)) return -1;
+  int cov, far;
+  const int waves = plan(f, &cov, &far);
+  return waves * 1000 + (cov <= 8 ? 8 : 16) * 10 + far;
 }
 
 hipError_t launch_fwd_ring(const FwdArgs& f) {
@@ -689,6 +702,7 @@ hipError_t launch_fwd_ring(const FwdArgs& f) {
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)kD));
   a.rope = f.rope;
   a.n_far = n_far;
+  a.heads_per_plan = f.heads_per_plan;
   if (f.plan != nullptr) {
     if (f.mode == 0) return launch_mode<0, 8, true>(a, n_far, blocks, f.stream);
     if (waves == 8) return launch_mode<1, 8, true>(a, n_far, blocks, f.stream);

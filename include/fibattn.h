@@ -185,6 +185,57 @@ int fib_sparse_attn_decode_dev(const void* q, const void* k_cache, const void* v
                                const int32_t* base, int n_base, float rope_theta, int mode,
                                void* plan, size_t plan_bytes, void* stream);
 
+/*
+ * Several layers in one call (one launch per kernel for the whole stack of layers; each
+ * layer has its own alpha, e.g. the Staggered-linear, Staggered-coprime or Learned
+ * schedules of [FIB] Method > Experimental variables, which assign one alpha per layer).
+ * Layer l computes exactly what the single-layer call with alpha[l] computes, on the l-th
+ * [B, H, N, D] block of the inputs:
+ *   q, k, v, o, dout, dq, dk, dv: [L, B, H, N, D] contiguous; lse: [L, B, H, N];
+ *   dalpha (backward, may be NULL): device float[L], dL/dalpha of each layer;
+ *   alpha: fib_sparse_attn_fwd_layers / _bwd_layers: host float[L], read during the call
+ *          (each finite and > 0); the kernels are planned for [min alpha, max alpha];
+ *          ..._dev: device float[L], clamped into [alpha_lo, alpha_hi] as in the
+ *          device-alpha calls above;
+ *   plan: device buffer of fib_sparse_attn_layers_plan_bytes(L) bytes, 16-byte aligned,
+ *         overwritten (one offset table per layer, built on the device); calls that
+ *         overlap must not share it;
+ *   workspace (backward): fib_sparse_attn_bwd_workspace_size(L * B, H, N, D, dtype, mode)
+ *         bytes.
+ * 1 <= L <= 256. Errors as for the single-layer calls; FIB_ERR_SHAPE for L outside
+ * [1, 256]; FIB_ERR_WORKSPACE for a plan smaller than fib_sparse_attn_layers_plan_bytes(L).
+ * fib_sparse_attn_layers_plan_bytes returns 0 for L outside [1, 256].
+ */
+size_t fib_sparse_attn_layers_plan_bytes(int64_t n_layers);
+
+int fib_sparse_attn_fwd_layers(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int64_t L, int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                               int W, const float* alpha, const int32_t* base, int n_base,
+                               float rope_theta, int mode, void* plan, size_t plan_bytes, void* stream);
+
+int fib_sparse_attn_fwd_layers_dev(const void* q, const void* k, const void* v, void* o, float* lse,
+                                   int64_t L, int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                                   int W, const float* alpha, float alpha_lo, float alpha_hi,
+                                   const int32_t* base, int n_base, float rope_theta, int mode,
+                                   void* plan, size_t plan_bytes, void* stream);
+
+int fib_sparse_attn_bwd_layers(const void* q, const void* k, const void* v, const void* o,
+                               const void* dout, const float* lse,
+                               void* dq, void* dk, void* dv, float* dalpha,
+                               int64_t L, int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                               int W, const float* alpha, const int32_t* base, int n_base,
+                               float rope_theta, int mode, void* workspace, size_t workspace_bytes,
+                               void* plan, size_t plan_bytes, void* stream);
+
+int fib_sparse_attn_bwd_layers_dev(const void* q, const void* k, const void* v, const void* o,
+                                   const void* dout, const float* lse,
+                                   void* dq, void* dk, void* dv, float* dalpha,
+                                   int64_t L, int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                                   int W, const float* alpha, float alpha_lo, float alpha_hi,
+                                   const int32_t* base, int n_base, float rope_theta, int mode,
+                                   void* workspace, size_t workspace_bytes, void* plan, size_t plan_bytes,
+                                   void* stream);
+
 /* Static, human-readable text of a status code. */
 const char* fib_status_string(int status);
 

@@ -147,6 +147,44 @@ def test_device_alpha_argument_errors():
                                         ctypes.c_float(1.5), b, 15, ctypes.c_float(10000.0), 0, p, need, None) == -1
 
 
+def test_layers_argument_errors():
+    L = F.lib()
+    b = (ctypes.c_int32 * 15)(*FIB_BASE)
+    p = 16
+    need = F.layers_plan_bytes(4)
+    assert need == 4 * F.plan_bytes()
+    assert F.layers_plan_bytes(0) == 0 and F.layers_plan_bytes(257) == 0 and F.layers_plan_bytes(256) > 0
+    alphas = (ctypes.c_float * 4)(0.5, 0.8, 1.2, 1.5)
+
+    def fwd(nl=4, alpha=alphas, plan=p, nbytes=need, B=1):
+        return L.fib_sparse_attn_fwd_layers(p, p, p, p, None, nl, B, 1, 8, 64, 1, 12, alpha, b, 15,
+                                            ctypes.c_float(10000.0), 0, plan, nbytes, None)
+    assert fwd(alpha=None) == -1 and fwd(plan=None) == -1
+    assert fwd(nl=0) == -2 and fwd(nl=257) == -2 and fwd(B=0) == -2
+    assert fwd(nbytes=need - 1) == -11 and fwd(plan=0x1008) == -10
+    bad = (ctypes.c_float * 4)(0.5, float("nan"), 1.2, 1.5)
+    assert fwd(alpha=bad) == -6
+    neg = (ctypes.c_float * 4)(0.5, 0.8, -1.0, 1.5)
+    assert fwd(alpha=neg) == -6
+
+    def fwd_dev(alpha=p, lo=0.5, hi=1.5, nbytes=need):
+        return L.fib_sparse_attn_fwd_layers_dev(p, p, p, p, None, 4, 1, 1, 8, 64, 1, 12, alpha, ctypes.c_float(lo),
+                                                ctypes.c_float(hi), b, 15, ctypes.c_float(10000.0), 1, p, nbytes,
+                                                None)
+    assert fwd_dev(alpha=None) == -1 and fwd_dev(lo=2.0) == -6 and fwd_dev(nbytes=need - 1) == -11
+
+    def bwd(ws=p, ws_bytes=1 << 40, nbytes=need, alpha=alphas):
+        return L.fib_sparse_attn_bwd_layers(p, p, p, p, p, p, p, p, p, p, 4, 1, 1, 8, 64, 1, 12, alpha, b, 15,
+                                            ctypes.c_float(10000.0), 1, ws, ws_bytes, p, nbytes, None)
+    assert bwd(alpha=None) == -1 and bwd(ws=None) == -11 and bwd(nbytes=need - 1) == -11
+    # the workspace of L layers is the single-layer size at L * B batches
+    ws_need = F.bwd_workspace_size(4, 1, 8, 64, F.BF16, F.INTERP)
+    assert bwd(ws_bytes=ws_need - 1) == -11
+    assert L.fib_sparse_attn_bwd_layers_dev(p, p, p, p, p, p, p, p, p, p, 4, 1, 1, 8, 64, 1, 12, None,
+                                            ctypes.c_float(0.5), ctypes.c_float(1.5), b, 15, ctypes.c_float(10000.0),
+                                            1, p, 1 << 40, p, need, None) == -1
+
+
 def test_bwd_argument_errors():
     L = F.lib()
     b = (ctypes.c_int32 * 15)(*FIB_BASE)

@@ -17,6 +17,7 @@ import torch
 import fibonacci_offset_dilated_amd as F
 import oracle as O
 from fibonacci_offset_dilated_amd.autograd import fib_sparse_attention
+from fibonacci_offset_dilated_amd.synthetic import random_alpha_grid
 from fibonacci_offset_dilated_amd.workloads import BF16, F32, FIB_BASE, INT, INTERP, POW2_BASE
 from gpu_util import TOL, TOL_DALPHA, grad_excess, host, inputs, maxabs, say
 
@@ -196,3 +197,64 @@ def test_autograd_device_alpha_path(mode):
     assert torch.equal(o.detach(), of)
     assert torch.equal(qq.grad, dq) and torch.equal(kk.grad, dk) and torch.equal(vv.grad, dv)
     assert float(alpha.grad.item()) == float(da.item())
+
+
+# Layout of one plan (the library's internal DevPlan): the table {int n; int dist[32];
+# float w[32]; float f[32]} and two ring splits {int n_cov, n_far, need, early_rows; int
+# dist[16]; float w[16], f[16]; int far_dist[4]; float far_w[4], far_f[4]; int unc_dist[8]}
+# for 8- and 4-wave kernels.
+PLAN_WORDS = 97 + 2 * 72
+
+
+def decode_plan(words):
+    n = int(words[0])
+    dist = words[1:33].astype(np.int32)
+    w = words[33:65].view(np.float32)
+    f = words[65:97].view(np.float32)
+    splits = []
+    for s0 in (97, 97 + 72):
+        sw = words[s0:s0 + 72]
+        splits.append(dict(n_cov=int(sw[0]), n_far=int(sw[1]), need=int(sw[2]), early_rows=int(sw[3]),
+                           dist=sw[4:20].astype(np.int32), far_dist=sw[52:56].astype(np.int32)))
+    return n, dist, w, f, splits
+
+
+@pytest.mark.parametrize("mode", [INT, INTERP], ids=["int", "interp"])
+@pytest.mark.parametrize("W,base,N", [(12, FIB_BASE, 4096), (1, FIB_BASE, 131072), (40, POW2_BASE, 3000),
+                                      (3, (1, 2, 3, 4, 5, 6, 7, 8), 100),
+                                      (12, (1, 2, 3, 5, 8, 13, 21, 34, 55, 89, 144, 233, 377, 511, 512, 610), 900)],
+                         ids=["fib-W12", "fib-W1", "pow2-W40", "dense-base", "near-dup"])
+def test_device_built_tables_equal_host_and_oracle_tables(W, base, N, mode):
+    """The plans the device builds (one per layer of a 256-layer call) hold exactly the host
+    table and the oracle's offsets, and the ring splits follow the table."""
+    assert F.plan_bytes() == 4 * PLAN_WORDS
+    L = 256
+    al = random_alpha_grid(9900 + W + N, L, 0.3, 3.0)
+    al[:4] = [0.5, 1.0, 1.5, 2.0 / 3.0]  # exact halves: rounding ties
+    plan = torch.empty(F.layers_plan_bytes(L), dtype=torch.uint8, device="cuda")
+    # only the plans are inspected (the splits depend on N)
+    kk = torch.zeros((L, 1, 1, N, 64), dtype=torch.bfloat16, device="cuda")
+    F.fwd_layers(kk, kk, kk, W, torch.from_numpy(al).cuda(), base, 10000.0, mode, alpha_range=(0.3, 3.0), plan=plan,
+                 with_lse=False)
+    torch.cuda.synchronize()
+    words = plan.cpu().numpy().view(np.uint32).reshape(L, PLAN_WORDS)
+    for l in range(L):
+        n, dist, w, f, splits = decode_plan(words[l])
+        hd, hw, hf = F.offset_table(al[l], base, W, mode)
+        assert n == len(hd), (l, al[l])
+        assert list(dist[:n]) == hd and np.array_equal(w[:n], np.array(hw, dtype=np.float32))
+        if mode == INTERP:
+            assert list(f[:n].astype(np.int64)) == hf
+            od = [c for _, c, _ in O.interp_entries(al[l], base, W)]
+        else:
+            od = O.int_offsets(al[l], base, W)
+        assert list(dist[:n]) == [int(x) for x in od]
+        usable = sum(1 for x in hd if x < N)
+        for sp, waves in zip(splits, (8, 4)):
+            reach = 512 - 16 * waves
+            cov = sum(1 for x in hd[:usable] if x <= reach)
+            assert sp["n_cov"] == cov and sp["n_far"] == usable - cov
+            assert sp["need"] == max([16] + hd[:cov]) and sp["early_rows"] == max([16] + hd[:usable])
+            assert list(sp["dist"][:cov]) == hd[:cov]
+            far = hd[cov:usable][:4]
+            assert list(sp["far_dist"][:len(far)]) == far

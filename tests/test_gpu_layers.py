@@ -1,0 +1,145 @@
+"""GPU parity of the calls over several layers (one launch per kernel for a stack of layers,
+one alpha per layer) against the single-layer calls and the CPU oracle, via the C ABI.
+
+Layer l of an [L, B, H, N, D] call must compute what the single-layer call computes on the
+l-th block with alpha[l]. The layer call plans its kernels for the whole alpha range of the
+stack, so its ring kernels may split a layer's table differently from the single-layer call
+(fp32 summation order only): the comparison bounds are the oracle bounds (O, LSE: 1e-4 fp32,
+2e-2 bf16; gradients: the same plus one ulp; dalpha: relative 1e-2 bf16 / 1e-4 fp32).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import fibonacci_offset_dilated_amd as F
+import oracle as O
+from fibonacci_offset_dilated_amd.synthetic import uniform_alphas
+from fibonacci_offset_dilated_amd.workloads import (BF16, F32, FIB_BASE, INT, INTERP, POW2_BASE, UNIFORM_ALPHA_RANGE,
+                                                    UNIFORM_ALPHA_SEED)
+from gpu_util import TOL, TOL_DALPHA, grad_excess, host, inputs, maxabs, say
+
+pytestmark = pytest.mark.gpu
+WORKERS = min(16, len(os.sched_getaffinity(0)))
+
+
+def schedule(kind, L):
+    return np.array([F.schedule_alpha(kind, l, L) for l in range(L)], dtype=np.float32)
+
+
+def stack_inputs(seed, L, B, H, N, dtype, with_dout=False):
+    """[L, B, H, N, D] device tensors and their fp64 copies (layer-major draws)."""
+    arrs = inputs(seed, (L * B, H, N, 64), dtype, with_dout=with_dout)
+    return [(t.view(L, B, H, N, 64), a.reshape(L, B, H, N, 64)) for t, a in arrs]
+
+
+FWD = [
+    # (L, B, H, N, W, alphas, base, dtype)
+    ("linear16", 16, 2, 2, 1024, 12, "linear", FIB_BASE, BF16),     # 16-layer staggered-linear stack
+    ("coprime16", 16, 1, 2, 4096, 12, "coprime", FIB_BASE, BF16),   # coprime stack at 4x length
+    ("pow2", 4, 1, 2, 4096, 12, "coprime", POW2_BASE, BF16),
+    ("uniform", 16, 2, 2, 1024, 12, "uniform", FIB_BASE, BF16),     # learned-dilation alphas
+    ("w6", 3, 2, 1, 700, 6, "linear", FIB_BASE, BF16),
+    ("f32", 4, 2, 2, 600, 12, "linear", FIB_BASE, F32),             # general kernel
+    ("wide", 2, 1, 2, 500, 40, "linear", POW2_BASE, BF16),          # general kernel (W > 16)
+    ("one", 1, 2, 3, 900, 12, "uniform", FIB_BASE, BF16),
+]
+
+
+def alphas_for(kind, L):
+    if kind == "uniform":
+        return uniform_alphas(UNIFORM_ALPHA_SEED, L, *UNIFORM_ALPHA_RANGE).astype(np.float32)
+    if L < 2:
+        return np.array([1.25], dtype=np.float32)
+    return schedule(F.SCHED_LINEAR if kind == "linear" else F.SCHED_COPRIME, L)
+
+
+@pytest.mark.parametrize("mode", [INT, INTERP], ids=["int", "interp"])
+@pytest.mark.parametrize("case", FWD, ids=[c[0] for c in FWD])
+def test_forward_layers(case, mode):
+    name, L, B, H, N, W, kind, base, dtype = case
+    al = alphas_for(kind, L)
+    say("fwd_layers", name, (L, B, H, N, W), "mode", mode, "alphas", al.min(), al.max())
+    (q, q64), (k, k64), (v, v64) = stack_inputs(9100 + N + W + L, L, B, H, N, dtype)
+    o, lse = F.fwd_layers(q, k, v, W, al, base, 10000.0, mode)
+    # the same stack with the alphas in device memory (planned for [0.5, 1.5])
+    od, lsed = F.fwd_layers(q, k, v, W, torch.from_numpy(al).cuda(), base, 10000.0, mode, alpha_range=(0.5, 1.5))
+    torch.cuda.synchronize()
+    e_single = e_oracle = e_dev = 0.0
+    for l in range(L):
+        os_, ls_ = F.fwd(q[l], k[l], v[l], W, al[l], base, 10000.0, mode)
+        torch.cuda.synchronize()
+        e_single = max(e_single, maxabs(host(o[l]), host(os_)), maxabs(host(lse[l]), host(ls_)))
+        e_dev = max(e_dev, maxabs(host(od[l]), host(o[l])), maxabs(host(lsed[l]), host(lse[l])))
+        if l in (0, L // 2, L - 1):
+            ro, rl = O.forward(q64[l], k64[l], v64[l], W, al[l], base, 10000.0, mode, workers=WORKERS)
+            e_oracle = max(e_oracle, maxabs(host(o[l]), ro), maxabs(host(lse[l]), rl))
+    say(f"  vs single-layer calls {e_single:.3e}; vs oracle (3 layers) {e_oracle:.3e}; device alphas {e_dev:.3e}")
+    assert e_single <= TOL[dtype] and e_oracle <= TOL[dtype] and e_dev <= TOL[dtype]
+
+
+BWD = [
+    ("uniform16", 16, 2, 2, 1024, 12, "uniform", FIB_BASE, BF16),   # learned-dilation stack
+    ("linear8", 8, 1, 2, 2000, 12, "linear", FIB_BASE, BF16),
+    ("f32", 3, 2, 2, 500, 12, "linear", FIB_BASE, F32),             # general kernels
+    ("wide", 2, 1, 1, 300, 40, "linear", POW2_BASE, BF16),
+]
+
+
+@pytest.mark.parametrize("mode", [INT, INTERP], ids=["int", "interp"])
+@pytest.mark.parametrize("case", BWD, ids=[c[0] for c in BWD])
+def test_backward_layers(case, mode):
+    name, L, B, H, N, W, kind, base, dtype = case
+    al = alphas_for(kind, L)
+    say("bwd_layers", name, (L, B, H, N, W), "mode", mode)
+    (q, q64), (k, k64), (v, v64), (do, d64) = stack_inputs(9300 + N + W + L, L, B, H, N, dtype, with_dout=True)
+    o, lse = F.fwd_layers(q, k, v, W, al, base, 10000.0, mode)
+    dq, dk, dv, da = F.bwd_layers(q, k, v, o, lse, do, W, al, base, 10000.0, mode)
+    ad = torch.from_numpy(al).cuda()
+    _, _, _, da_dev = F.bwd_layers(q, k, v, o, lse, do, W, ad, base, 10000.0, mode, alpha_range=(0.5, 1.5))
+    torch.cuda.synchronize()
+    da_h, da_dev_h = host(da), host(da_dev)
+    eg = 0.0
+    ea = 0.0
+    for l in range(L):
+        rq, rk, rv, ra, rabs = O.backward(q64[l], k64[l], v64[l], d64[l], W, al[l], base, 10000.0, mode,
+                                          workers=WORKERS, return_abs=True)
+        eg = max(eg, grad_excess(host(dq[l]), rq, dtype), grad_excess(host(dk[l]), rk, dtype),
+                 grad_excess(host(dv[l]), rv, dtype))
+        if mode == INT:
+            assert da_h[l] == 0.0 and da_dev_h[l] == 0.0
+        else:
+            ea = max(ea, abs(da_h[l] - ra) / max(rabs, 1e-30), abs(da_dev_h[l] - ra) / max(rabs, 1e-30))
+    say(f"  grad excess {eg:.3e}; dalpha rel err {ea:.3e}")
+    assert eg <= TOL[dtype]
+    assert ea <= TOL_DALPHA[dtype]
+
+
+def test_layers_match_single_layer_exactly_on_general_kernels():
+    """fp32 runs the general kernels, which read the same table either way: bit-identical."""
+    L = 3
+    al = schedule(F.SCHED_LINEAR, 16)[[0, 7, 15]]
+    (q, _), (k, _), (v, _), (do, _) = stack_inputs(9500, L, 1, 2, 400, F32, with_dout=True)
+    o, lse = F.fwd_layers(q, k, v, 12, al, FIB_BASE, 10000.0, INTERP)
+    dq, dk, dv, da = F.bwd_layers(q, k, v, o, lse, do, 12, al, FIB_BASE, 10000.0, INTERP)
+    torch.cuda.synchronize()
+    for l in range(L):
+        os_, ls_ = F.fwd(q[l], k[l], v[l], 12, al[l], FIB_BASE, 10000.0, INTERP)
+        gq, gk, gv, ga = F.bwd(q[l], k[l], v[l], os_, ls_, do[l], 12, al[l], FIB_BASE, 10000.0, INTERP)
+        torch.cuda.synchronize()
+        assert torch.equal(o[l], os_) and torch.equal(lse[l], ls_)
+        assert torch.equal(dq[l], gq) and torch.equal(dk[l], gk) and torch.equal(dv[l], gv)
+        assert float(da[l].item()) == float(ga.item())
+
+
+def test_layers_rejects_bad_arguments():
+    q = torch.zeros((2, 1, 1, 8, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        F.fwd_layers(q, q, q, 12, [1.0], FIB_BASE)                       # 1 alpha for 2 layers
+    with pytest.raises(ValueError):
+        F.fwd_layers(q[0], q[0], q[0], 12, [1.0], FIB_BASE)              # not [L, B, H, N, D]
+    with pytest.raises(F.FibError):
+        F.fwd_layers(q, q, q, 12, [1.0, 0.0], FIB_BASE)                  # alpha <= 0
+    with pytest.raises(ValueError):
+        F.fwd_layers(q, q, q, 12, torch.ones(2, device="cuda", dtype=torch.float64), FIB_BASE, alpha_range=(0.5, 1.5))
