@@ -18,6 +18,9 @@ content). Sections used:
   * Results 2 (learned dilation is inert), efficiency bullet: static (integer) offsets run on
     a fused boolean-mask path, non-integer ones on an interpolated gather.
   * Significance: vanilla RoPE without scaling.
+The dropped-attention-mass diagnostic follows "SSA: Sparse Sparse Attention" (arXiv
+2511.20102, gist.science Korean summary), 1. Problem definition, item 1 (attention gap): the
+attention weight that full attention gives to keys the sparse mechanism does not select.
 
 Readings taken where the pages leave a step open (each is the plainest one consistent with
 the rest; the same list is kept with the design notes):
@@ -53,6 +56,7 @@ __all__ = [
     "exact_alpha", "f32_nearest", "schedule_linear", "schedule_coprime",
     "int_offsets", "interp_entries", "rope_omega", "rope", "rope_inverse",
     "attended", "index_sets", "forward", "backward", "forward_rows",
+    "dense_causal_lse", "dropped_mass",
 ]
 
 
@@ -458,3 +462,44 @@ def backward(q, k, v, dout, W, alpha, base, theta=10000.0, mode=INT, workers=1, 
     if return_abs:
         return dq, dk, dv, dalpha, dalpha_abs
     return dq, dk, dv, dalpha
+
+
+# ---------------------------------------------------------------------------------------
+# dense causal attention and the mass it puts outside the sparse set (diagnostic)
+# ---------------------------------------------------------------------------------------
+
+def dense_causal_lse(q, k, theta=10000.0):
+    """LSE [..., N] (natural log, fp64) of dense causal attention logits: for query i, log of
+    the sum over keys j <= i of exp(<R_i q_i, R_j k_j> / sqrt(D)); inputs [..., N, D]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    N, D = q.shape[-2], q.shape[-1]
+    qr, kr = rope(q, theta), rope(k, theta)
+    s = np.matmul(qr, np.swapaxes(kr, -1, -2)) / math.sqrt(D)
+    future = np.triu(np.ones((N, N), dtype=bool), k=1)
+    s = np.where(future, -np.inf, s)
+    m = np.max(s, axis=-1, keepdims=True)
+    return (m + np.log(np.sum(np.exp(s - m), axis=-1, keepdims=True)))[..., 0]
+
+
+def dropped_mass(q, k, W, alpha, base, theta=10000.0):
+    """Per query, the dense causal softmax mass on keys outside the integer-mode attended set
+    (window plus kept offsets): 1 - sum over j in S_i of softmax_dense(i, j). Inputs
+    [..., N, D]; output [..., N] in fp64. (Interpolated entries blend two rows, so the set is
+    defined for integer offsets only.)"""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    N, D = q.shape[-2], q.shape[-1]
+    qr, kr = rope(q, theta), rope(k, theta)
+    s = np.matmul(qr, np.swapaxes(kr, -1, -2)) / math.sqrt(D)
+    future = np.triu(np.ones((N, N), dtype=bool), k=1)
+    s = np.where(future, -np.inf, s)
+    m = np.max(s, axis=-1, keepdims=True)
+    p = np.exp(s - m)
+    p = p / np.sum(p, axis=-1, keepdims=True)
+    inset = np.zeros((N, N), dtype=bool)
+    rows = index_sets(N, W, alpha, base, INT)
+    for i in range(N):
+        cols = rows[i][rows[i] >= 0]
+        inset[i, cols] = True
+    return 1.0 - np.sum(np.where(inset, p, 0.0), axis=-1)
