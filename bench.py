@@ -222,6 +222,34 @@ def small_configs(dev, stream, args):
     # per layer, so no layer's rows are cache-resident: 0.8 GB of Q, K, V at B4 H8 N4096) vs
     # 16 single-layer calls over the same stack; N(0, 1) draws made on the device
     out.update(layer_stacks(dev, stream, args, al4, al2, al3))
+    out.update(dropped_mass_diag(dev, stream, args))
+    return out
+
+
+def dropped_mass_diag(dev, stream, args):
+    """The dropped-attention-mass diagnostic at the 4x-extrapolation shape (B4 H8 N4096, alpha 1):
+    the dense causal LSE kernel (bf16 MFMA, causal half of Q K^T) timed alone, and the mean
+    dropped mass of the Fibonacci and power-of-two bases."""
+    import torch
+
+    import fibonacci_offset_dilated_amd as F
+    from fibonacci_offset_dilated_amd.synthetic import seed_for
+    from fibonacci_offset_dilated_amd.workloads import BY_CONFIG, FIB_BASE, POW2_BASE
+
+    w = BY_CONFIG[4]
+    (q, k, v), _ = make_inputs(w.B, w.H, w.N, seed_for(4, 0, 12, 0), False, dev)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    ws = torch.empty(int(F.lib().fib_dense_lse_workspace_size(w.B, w.H, w.N, D, F.BF16)), dtype=torch.uint8,
+                     device=dev)
+    reps = max(5, args.steps // 5)
+    ms = time_calls(lambda: F.dense_lse(q, k, 10000.0, lse=lse, workspace=ws), reps, 2, stream)
+    flops = w.B * w.H * (w.N * (w.N + 1) / 2) * D * 2
+    out = {"dense_lse_b4h8n4096_us": round(ms * 1e3, 2),
+           "dense_lse_b4h8n4096_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+           "dense_lse_b4h8n4096_mfma_frac": round(flops / (ms * 1e-3) / 1e12 / 2500.0, 4)}
+    for name, base in (("fib", FIB_BASE), ("pow2", POW2_BASE)):
+        dm = F.dropped_mass(q, k, v, 12, 1.0, base)
+        out[f"dropped_mass_b4h8n4096_{name}_mean"] = round(float(dm.mean().item()), 4)
     return out
 
 

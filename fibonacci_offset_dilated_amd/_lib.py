@@ -58,6 +58,10 @@ _SIGS = {
     "fib_sparse_attn_bwd_workspace_size": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64,
                                                          _c.c_int, _c.c_int]),
     "fib_sparse_attn_layers_plan_bytes": (_c.c_size_t, [_c.c_int64]),
+    "fib_dense_lse_workspace_size": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int]),
+    "fib_dense_causal_lse": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64,
+                                        _c.c_int64, _c.c_int, _c.c_float, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "fib_sparse_attn_dropped_mass": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_void_p]),
     "fib_sparse_attn_fwd_layers": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                               _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int,
                                               _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_float, _c.c_int,
@@ -444,6 +448,36 @@ def bwd_layers(q, k, v, o, lse, dout, W: int, alpha, base: Sequence[int], theta:
                                                   _ptr(plan), pb, _stream(stream))
         _check(st, "fib_sparse_attn_bwd_layers_dev")
     return dq, dk, dv, dalpha
+
+
+def dense_lse(q, k, theta: float = 10000.0, lse=None, workspace=None, stream=None):
+    """LSE [B, H, N] of dense causal attention over q, k [B, H, N, D] (bf16 MFMA; see
+    fib_dense_causal_lse)."""
+    torch = _torch()
+    _check_qkv(q, k)
+    B, H, N, D = q.shape
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    need = int(lib().fib_dense_lse_workspace_size(B, H, N, D, _dtype_code(q)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = lib().fib_dense_causal_lse(_ptr(q), _ptr(k), _ptr(lse), B, H, N, D, _dtype_code(q),
+                                    ctypes.c_float(float(theta)), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "fib_dense_causal_lse")
+    return lse
+
+
+def dropped_mass(q, k, v, W: int, alpha, base: Sequence[int], theta: float = 10000.0, stream=None):
+    """Per query, the dense causal softmax mass outside the integer-mode attended set:
+    1 - exp(LSE_sparse - LSE_dense) [B, H, N] (three kernels: sparse forward, dense LSE, map)."""
+    torch = _torch()
+    _, lse_s = fwd(q, k, v, W, alpha, base, theta, INT, stream=stream)
+    lse_d = dense_lse(q, k, theta, stream=stream)
+    out = torch.empty_like(lse_s)
+    st = lib().fib_sparse_attn_dropped_mass(_ptr(lse_s), _ptr(lse_d), _ptr(out), lse_s.numel(), _stream(stream))
+    _check(st, "fib_sparse_attn_dropped_mass")
+    return out
 
 
 def bwd_workspace_size(B, H, N, D, dtype_code: int, mode: int) -> int:

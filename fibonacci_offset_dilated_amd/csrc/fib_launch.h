@@ -160,6 +160,14 @@ hipError_t launch_index_set(int32_t* out, int64_t N, int W, const Table& tab, in
 // [BH, D], k and v [BH, N, D], lse [BH]
 hipError_t launch_decode(const FwdArgs& a);
 
+// dense causal LSE (bf16 MFMA on rotated bf16 copies of q and k in the workspace) and the
+// dropped mass 1 - exp(lse_sparse - lse_dense)
+size_t dense_lse_workspace_bytes(int64_t BH, int64_t N);
+hipError_t launch_dense_lse(const void* q, const void* k, float* lse, int64_t BH, int64_t N, int dtype,
+                            const Rope& rope, void* workspace, hipStream_t s);
+hipError_t launch_dropped_mass(const float* lse_sparse, const float* lse_dense, float* out, int64_t n,
+                               hipStream_t s);
+
 size_t bwd_workspace_bytes(int64_t BH, int64_t N, int dtype, int mode);
 hipError_t launch_bwd(const BwdArgs& a);
 // query side of the backward on the LDS ring (bf16, W <= 16): dQ, Delta [BH * N], one

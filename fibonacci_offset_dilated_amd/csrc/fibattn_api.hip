@@ -424,6 +424,36 @@ int fib_sparse_attn_bwd(const void* q, const void* k, const void* v, const void*
                   rope_theta, mode, workspace, workspace_bytes, stream);
 }
 
+size_t fib_dense_lse_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D, int dtype) {
+  if (check_shape(B, H, N, D, dtype) != FIB_OK) return 0;
+  return dense_lse_workspace_bytes(B * H, N);
+}
+
+int fib_dense_causal_lse(const void* q, const void* k, float* lse, int64_t B, int64_t H, int64_t N, int64_t D,
+                         int dtype, float rope_theta, void* workspace, size_t workspace_bytes, void* stream) {
+  if (q == nullptr || k == nullptr || lse == nullptr) return FIB_ERR_NULL;
+  int st = check_shape(B, H, N, D, dtype);
+  if (st) return st;
+  if (!isfinite(rope_theta) || rope_theta <= 0.f) return FIB_ERR_THETA;
+  if ((double)(B * H) * (double)((N + 127) / 128) > 2147483647.0) return FIB_ERR_SHAPE;
+  if (workspace == nullptr || workspace_bytes < dense_lse_workspace_bytes(B * H, N)) return FIB_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(workspace) || ((uintptr_t)lse & 3u)) return FIB_ERR_ALIGN;
+  return launch_dense_lse(q, k, lse, B * H, N, dtype, make_rope(rope_theta), workspace, (hipStream_t)stream) ==
+                 hipSuccess
+             ? FIB_OK
+             : FIB_ERR_LAUNCH;
+}
+
+int fib_sparse_attn_dropped_mass(const float* lse_sparse, const float* lse_dense, float* dropped, int64_t count,
+                                 void* stream) {
+  if (lse_sparse == nullptr || lse_dense == nullptr || dropped == nullptr) return FIB_ERR_NULL;
+  if (count < 1 || count > (1LL << 40)) return FIB_ERR_SHAPE;
+  if (((uintptr_t)lse_sparse & 3u) || ((uintptr_t)lse_dense & 3u) || ((uintptr_t)dropped & 3u)) return FIB_ERR_ALIGN;
+  return launch_dropped_mass(lse_sparse, lse_dense, dropped, count, (hipStream_t)stream) == hipSuccess
+             ? FIB_OK
+             : FIB_ERR_LAUNCH;
+}
+
 size_t fib_sparse_attn_plan_bytes(void) { return sizeof(DevPlan); }
 
 size_t fib_sparse_attn_layers_plan_bytes(int64_t n_layers) {

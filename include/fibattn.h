@@ -236,6 +236,32 @@ int fib_sparse_attn_bwd_layers_dev(const void* q, const void* k, const void* v, 
                                    void* workspace, size_t workspace_bytes, void* plan, size_t plan_bytes,
                                    void* stream);
 
+/*
+ * Dropped attention mass (diagnostic): the softmax weight that dense causal attention puts
+ * on keys outside the sparse set, the attention-gap measure of "SSA: Sparse Sparse
+ * Attention" (arXiv 2511.20102, gist.science summary, 1. Problem definition, item 1)
+ * applied to this pattern. For query i with integer offsets:
+ *   dropped[i] = 1 - exp(lse_sparse[i] - lse_dense[i]),
+ * lse_sparse from fib_sparse_attn_fwd (mode FIB_INT) and lse_dense from
+ * fib_dense_causal_lse on the same q, k and rope_theta.
+ *
+ * fib_dense_causal_lse: lse [B, H, N] (natural log, fp32) of the dense causal logits
+ * <R_i q_i, R_j k_j> / sqrt(D), j <= i. O(N^2) work per head on bf16 MFMA: q and k are
+ * rotated in fp32 and rounded to bf16 (fp32 inputs too) into the workspace
+ * (fib_dense_lse_workspace_size bytes, caller-owned, 16-byte aligned), products accumulate
+ * in fp32. Errors: FIB_ERR_NULL, FIB_ERR_SHAPE, FIB_ERR_HEAD_DIM, FIB_ERR_DTYPE,
+ * FIB_ERR_THETA, FIB_ERR_WORKSPACE, FIB_ERR_ALIGN, FIB_ERR_LAUNCH.
+ * fib_sparse_attn_dropped_mass: the elementwise map above over `count` device floats.
+ * fib_dense_lse_workspace_size returns 0 for a bad shape.
+ */
+size_t fib_dense_lse_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D, int dtype);
+
+int fib_dense_causal_lse(const void* q, const void* k, float* lse, int64_t B, int64_t H, int64_t N, int64_t D,
+                         int dtype, float rope_theta, void* workspace, size_t workspace_bytes, void* stream);
+
+int fib_sparse_attn_dropped_mass(const float* lse_sparse, const float* lse_dense, float* dropped, int64_t count,
+                                 void* stream);
+
 /* Static, human-readable text of a status code. */
 const char* fib_status_string(int status);
 

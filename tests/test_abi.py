@@ -185,6 +185,24 @@ def test_layers_argument_errors():
                                             1, p, 1 << 40, p, need, None) == -1
 
 
+def test_dense_lse_argument_errors():
+    L = F.lib()
+    p = 16
+    need = L.fib_dense_lse_workspace_size(1, 2, 100, 64, 1)
+    assert need == 2 * 2 * 100 * 64 * 2
+    assert L.fib_dense_lse_workspace_size(1, 2, 100, 32, 1) == 0
+
+    def call(q=p, lse=p, ws=p, ws_bytes=need, theta=10000.0, D=64, dtype=1):
+        return L.fib_dense_causal_lse(q, p, lse, 1, 2, 100, D, dtype, ctypes.c_float(theta), ws, ws_bytes, None)
+    assert call(q=None) == -1 and call(lse=None) == -1
+    assert call(ws=None) == -11 and call(ws_bytes=need - 1) == -11
+    assert call(theta=0.0) == -8 and call(D=32) == -3 and call(dtype=7) == -4
+    assert call(q=0x1008) == -10
+    assert L.fib_sparse_attn_dropped_mass(None, p, p, 10, None) == -1
+    assert L.fib_sparse_attn_dropped_mass(p, p, p, 0, None) == -2
+    assert L.fib_sparse_attn_dropped_mass(p, 0x1002, p, 10, None) == -10
+
+
 def test_bwd_argument_errors():
     L = F.lib()
     b = (ctypes.c_int32 * 15)(*FIB_BASE)
