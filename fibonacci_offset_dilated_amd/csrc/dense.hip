@@ -122,25 +122,27 @@ __global__ __launch_bounds__(256) void dense_lse_kernel(const bf16_t* __restrict
     const bool diag = (int64_t)t * kDT + kDT - 1 > i0;
 #pragma unroll
     for (int qg = 0; qg < 2; ++qg) {
-      float x[16];
-      float tmax = -INFINITY;
+      if (diag) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float s = acc[qg][kb][v] * scale_log2;
-          if (diag) {
+          for (int v = 0; v < 4; ++v) {
             const int64_t j = (int64_t)t * kDT + 16 * kb + 4 * g + v;
-            s = j > qi[qg] ? -INFINITY : s;
+            acc[qg][kb][v] = j > qi[qg] ? -INFINITY : acc[qg][kb][v];
           }
-          x[4 * kb + v] = s;
-          tmax = fmaxf(tmax, s);
-        }
       }
-      const float mn = fmaxf(m[qg], tmax);
-      float acc_s = sum[qg] * exp2f(m[qg] - mn);
+      // raw logits: the scale (> 0) is applied in the exponent, exp2(s * scale_log2 - m)
+      float tmax = acc[qg][0][0];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) acc_s += exp2f(x[u] - mn);
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) tmax = fmaxf(tmax, acc[qg][kb][v]);
+      const float mn = fmaxf(m[qg], tmax * scale_log2);
+      float acc_s = sum[qg] * ex2(m[qg] - mn);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc_s += ex2(fmaf(acc[qg][kb][v], scale_log2, -mn));
       sum[qg] = acc_s;
       m[qg] = mn;
     }
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(256) void dense_lse_kernel(const bf16_t* __restrict
 #pragma unroll
   for (int qg = 0; qg < 2; ++qg) {
     const float M = quad_max(m[qg]);
-    const float L = quad_add(sum[qg] * exp2f(m[qg] - M));
+    const float L = quad_add(sum[qg] * ex2(m[qg] - M));
     if (g == 0 && qi[qg] < N) lse[head * N + qi[qg]] = (M + log2f(L)) * 0.69314718055994530942f;
   }
 }
