@@ -315,6 +315,17 @@ def layer_stacks(dev, stream, args, al4, al2, al3):
     out["b8h8n1024_stack16_fwd_interp_us_per_layer"] = round(us_fp, 2)
     out["b8h8n1024_stack16_bwd_interp_us_per_layer"] = round(us_fb, 2)
     out["b8h8n1024_stack16_separate_calls_bwd_interp_us_per_layer"] = round(us_sb, 2)
+    del q, k, v, do, o, lse, dq, dk, dv, ws
+
+    # decode over a 16-layer cache stack at B8 H8 N4096 in one launch
+    kc, vc = [torch.randn((L, 8, 8, 4096, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(2)]
+    qd = torch.randn((L, 8, 8, D), generator=gen, device=dev).to(torch.bfloat16)
+    od = torch.empty_like(qd)
+    ld = torch.empty((L, 8, 8), dtype=torch.float32, device=dev)
+    for mode, a, name in ((INT, a2, "int"), (INTERP, a3, "interp")):
+        us_d = time_calls(lambda: F.decode_layers(qd, kc, vc, 12, a, FIB_BASE, 10000.0, mode, out=od, lse=ld,
+                                                  plan=plan), reps, 2, stream) * 1e3 / L
+        out[f"decode_b8h8n4096_stack16_{name}_us_per_layer"] = round(us_d, 2)
     return out
 
 

@@ -66,6 +66,15 @@ _SIGS = {
                                               _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int,
                                               _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_float, _c.c_int,
                                               _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "fib_sparse_attn_decode_layers": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                                 _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64,
+                                                 _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_float,
+                                                 _c.c_int, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "fib_sparse_attn_decode_layers_dev": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                                     _c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64,
+                                                     _c.c_int64, _c.c_int, _c.c_int, _c.c_void_p, _c.c_float,
+                                                     _c.c_float, _c.c_void_p, _c.c_int, _c.c_float, _c.c_int,
+                                                     _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "fib_sparse_attn_fwd_layers_dev": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                                   _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64,
                                                   _c.c_int, _c.c_int, _c.c_void_p, _c.c_float, _c.c_float,
@@ -411,6 +420,42 @@ def fwd_layers(q, k, v, W: int, alpha, base: Sequence[int], theta: float = 10000
                                                   ctypes.c_float(hi), b, n, ctypes.c_float(float(theta)), int(mode),
                                                   _ptr(plan), pb, _stream(stream))
         _check(st, "fib_sparse_attn_fwd_layers_dev")
+    return out, lse
+
+
+def decode_layers(q, k_cache, v_cache, W: int, alpha, base: Sequence[int], theta: float = 10000.0, mode: int = INT,
+                  alpha_range=None, out=None, lse=None, with_lse: bool = True, plan=None, stream=None):
+    """One decode step of L layers in one launch: q [L, B, H, D] at position N - 1 of the caches
+    [L, B, H, N, D]; alpha as in fwd_layers. Returns (O [L, B, H, D], LSE [L, B, H] or None)."""
+    torch = _torch()
+    _check_layers(k_cache, v_cache)
+    L, B, H, N, D = k_cache.shape
+    for t in (q, out):
+        if t is None:
+            continue
+        if (not isinstance(t, torch.Tensor) or not t.is_cuda or t.shape != (L, B, H, D)
+                or t.dtype != k_cache.dtype or t.device != k_cache.device or not t.is_contiguous()):
+            raise ValueError("q and o must be contiguous [L, B, H, D] tensors of the caches' dtype and device")
+    ah, ad, lo, hi = _layers_alpha(alpha, L, alpha_range, q.device)
+    plan = _layers_plan(plan, L, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and with_lse:
+        lse = torch.empty((L, B, H), dtype=torch.float32, device=q.device)
+    b, n = _base_array(base)
+    pb = plan.numel() * plan.element_size()
+    if ad is None:
+        st = lib().fib_sparse_attn_decode_layers(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), L, B, H,
+                                                 N, D, _dtype_code(q), int(W), ah.ctypes.data_as(ctypes.c_void_p), b,
+                                                 n, ctypes.c_float(float(theta)), int(mode), _ptr(plan), pb,
+                                                 _stream(stream))
+        _check(st, "fib_sparse_attn_decode_layers")
+    else:
+        st = lib().fib_sparse_attn_decode_layers_dev(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), L,
+                                                     B, H, N, D, _dtype_code(q), int(W), _ptr(ad), ctypes.c_float(lo),
+                                                     ctypes.c_float(hi), b, n, ctypes.c_float(float(theta)),
+                                                     int(mode), _ptr(plan), pb, _stream(stream))
+        _check(st, "fib_sparse_attn_decode_layers_dev")
     return out, lse
 
 

@@ -323,7 +323,9 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   auto launch = [&](const FwdArgs& b) {
     return decode ? launch_decode(b) : fwd_ring_supported(b) ? launch_fwd_ring(b) : launch_fwd_generic(b);
   };
-  if (al.dev || al.host_list == nullptr || al.layers == 1) return launch(a) == hipSuccess ? FIB_OK : FIB_ERR_LAUNCH;
+  // (the decode kernel is one instance for every table: one launch serves any stack)
+  if (decode || al.dev || al.host_list == nullptr || al.layers == 1)
+    return launch(a) == hipSuccess ? FIB_OK : FIB_ERR_LAUNCH;
   for (int64_t s0 = 0; s0 < al.layers;) {
     const int64_t e0 = run_end(a, al, s0, [](const FwdArgs& t) { return fwd_instance_key(t); });
     if (launch(layer_run(a, al, base, n_base, s0, e0)) != hipSuccess) return FIB_ERR_LAUNCH;
@@ -469,6 +471,29 @@ int fib_sparse_attn_fwd_layers(const void* q, const void* k, const void* v, void
   if (LB == 0) return FIB_ERR_SHAPE;
   return fwd_impl(q, k, v, o, lse, LB, H, N, D, dtype, W, host_alphas(alpha, L, plan, plan_bytes), base, n_base,
                   rope_theta, mode, stream, false);
+}
+
+int fib_sparse_attn_decode_layers(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                                  int64_t L, int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                                  int W, const float* alpha, const int32_t* base, int n_base,
+                                  float rope_theta, int mode, void* plan, size_t plan_bytes, void* stream) {
+  if (alpha == nullptr) return FIB_ERR_NULL;
+  const int64_t LB = layer_batches(L, B);
+  if (LB == 0) return FIB_ERR_SHAPE;
+  return fwd_impl(q, k_cache, v_cache, o, lse, LB, H, N, D, dtype, W, host_alphas(alpha, L, plan, plan_bytes), base,
+                  n_base, rope_theta, mode, stream, true);
+}
+
+int fib_sparse_attn_decode_layers_dev(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                                      int64_t L, int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                                      int W, const float* alpha, float alpha_lo, float alpha_hi,
+                                      const int32_t* base, int n_base, float rope_theta, int mode,
+                                      void* plan, size_t plan_bytes, void* stream) {
+  const int64_t LB = layer_batches(L, B);
+  if (LB == 0) return FIB_ERR_SHAPE;
+  return fwd_impl(q, k_cache, v_cache, o, lse, LB, H, N, D, dtype, W,
+                  dev_alpha(alpha, alpha_lo, alpha_hi, plan, plan_bytes, L), base, n_base, rope_theta, mode, stream,
+                  true);
 }
 
 int fib_sparse_attn_fwd_layers_dev(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -202,6 +202,9 @@ int fib_sparse_attn_decode_dev(const void* q, const void* k_cache, const void* v
  *         overlap must not share it;
  *   workspace (backward): fib_sparse_attn_bwd_workspace_size(L * B, H, N, D, dtype, mode)
  *         bytes.
+ * Decode over a stack (fib_sparse_attn_decode_layers, ..._dev): q and o [L, B, H, D], the
+ * caches [L, B, H, N, D], lse [L, B, H]; layer l is fib_sparse_attn_decode with alpha[l]
+ * (one launch for the whole stack).
  * 1 <= L <= 256. Errors as for the single-layer calls; FIB_ERR_SHAPE for L outside
  * [1, 256]; FIB_ERR_WORKSPACE for a plan smaller than fib_sparse_attn_layers_plan_bytes(L).
  * fib_sparse_attn_layers_plan_bytes returns 0 for L outside [1, 256].
@@ -212,6 +215,17 @@ int fib_sparse_attn_fwd_layers(const void* q, const void* k, const void* v, void
                                int64_t L, int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
                                int W, const float* alpha, const int32_t* base, int n_base,
                                float rope_theta, int mode, void* plan, size_t plan_bytes, void* stream);
+
+int fib_sparse_attn_decode_layers(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                                  int64_t L, int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                                  int W, const float* alpha, const int32_t* base, int n_base,
+                                  float rope_theta, int mode, void* plan, size_t plan_bytes, void* stream);
+
+int fib_sparse_attn_decode_layers_dev(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                                      int64_t L, int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                                      int W, const float* alpha, float alpha_lo, float alpha_hi,
+                                      const int32_t* base, int n_base, float rope_theta, int mode,
+                                      void* plan, size_t plan_bytes, void* stream);
 
 int fib_sparse_attn_fwd_layers_dev(const void* q, const void* k, const void* v, void* o, float* lse,
                                    int64_t L, int64_t B, int64_t H, int64_t N, int64_t D, int dtype,

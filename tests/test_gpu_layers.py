@@ -133,6 +133,35 @@ def test_layers_match_single_layer_exactly_on_general_kernels():
         assert float(da[l].item()) == float(ga.item())
 
 
+@pytest.mark.parametrize("mode", [INT, INTERP], ids=["int", "interp"])
+@pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "f32"])
+def test_decode_layers(mode, dtype):
+    """One decode launch over a 16-layer cache stack equals the 16 single-layer decode calls
+    (the same kernel and tables: exactly) and the oracle's row N - 1."""
+    L, B, H, N, W = 16, 2, 3, 1500, 12
+    al = alphas_for("linear", L) if mode == INT else alphas_for("uniform", L)
+    (q, q64), (k, k64), (v, v64) = stack_inputs(9700 + mode + 2 * dtype, L, B, H, N, dtype)
+    qd = q[:, :, :, N - 1, :].contiguous()
+    o, lse = F.decode_layers(qd, k, v, W, al, FIB_BASE, 10000.0, mode)
+    od, lsed = F.decode_layers(qd, k, v, W, torch.from_numpy(al).cuda(), FIB_BASE, 10000.0, mode,
+                               alpha_range=(0.5, 1.5))
+    torch.cuda.synchronize()
+    assert torch.equal(o, od) and torch.equal(lse, lsed)
+    e = 0.0
+    for l in range(L):
+        os_, ls_ = F.decode(qd[l], k[l], v[l], W, al[l], FIB_BASE, 10000.0, mode)
+        torch.cuda.synchronize()
+        assert torch.equal(o[l], os_) and torch.equal(lse[l], ls_)
+        if l in (0, 9, 15):
+            for b in range(B):
+                for h in range(H):
+                    ro, rl = O.forward_rows(q64[l, b, h], k64[l, b, h], v64[l, b, h], np.array([N - 1]), W, al[l],
+                                            FIB_BASE, 10000.0, mode)
+                    e = max(e, maxabs(host(o[l, b, h]), ro[0]), maxabs(host(lse[l, b, h]), rl[0]))
+    say(f"decode stack vs oracle {e:.3e}")
+    assert e <= TOL[dtype]
+
+
 def test_layers_rejects_bad_arguments():
     q = torch.zeros((2, 1, 1, 8, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ValueError):
