@@ -1,4 +1,5 @@
-"""torch.autograd wrapper of the sparse attention op and the Learned-schedule parameter.
+"""torch.autograd wrapper of the sparse attention op, the Learned-schedule parameter and an
+attention layer with its projections.
 
 The attention layer of "Depth-Staggered Fibonacci Spacing for Sparse Attention" (gist.science
 summaries of arXiv 2606.28560, Method > Architecture and attention mechanism; Method >
@@ -12,6 +13,11 @@ device together with an ``alpha_range`` = (lo, hi) stays on the device: the devi
 entry points build the offset table on the GPU, so the call involves no host copy of alpha
 and no stream synchronization. Any other tensor is read once per call on the host.
 
+``FibSparseSelfAttention`` is the attention sub-layer of the pages' models (Method >
+Architecture and attention mechanism: hidden 512 = 8 heads x 64): a bias-free QKV projection,
+the sparse attention (RoPE inside the op) and a bias-free output projection; the projections
+are plain library GEMMs (torch.nn.Linear).
+
 ``LearnedDilation`` is the per-layer free parameter theta of the Learned schedule. The pages
 give no map from theta to alpha beyond alpha in [0.5, 1.5] initialised at 1; this module
 uses alpha = 1 + 0.5 tanh(theta) (theta = 0 gives alpha = 1; the range is the open interval
@@ -19,12 +25,12 @@ uses alpha = 1 + 0.5 tanh(theta) (theta = 0 gives alpha = 1; the range is the op
 """
 from __future__ import annotations
 
-from typing import Sequence
+from typing import Optional, Sequence
 
 import numpy as np
 import torch
 
-from ._lib import INTERP, bwd, bwd_dev, fwd, fwd_dev
+from ._lib import INT, INTERP, bwd, bwd_dev, fwd, fwd_dev
 
 FIB_BASE_987 = (1, 2, 3, 5, 8, 13, 21, 34, 55, 89, 144, 233, 377, 610, 987)
 
@@ -105,3 +111,38 @@ class LearnedDilation(torch.nn.Module):
     def forward(self, q, k, v, W: int = 12, base: Sequence[int] = FIB_BASE_987, rope_theta: float = 10000.0):
         # alpha lies in [0.5, 1.5] by construction, so it can stay on the device
         return fib_sparse_attention(q, k, v, self.alpha(), W, base, rope_theta, INTERP, alpha_range=(0.5, 1.5))
+
+
+class FibSparseSelfAttention(torch.nn.Module):
+    """x [B, N, hidden] -> Linear(hidden, 3 hidden) -> per-head q, k, v [B, H, N, D] -> sparse
+    attention -> Linear(hidden, hidden). ``alpha``: a fixed per-layer float (static schedules:
+    integer offsets by default), or "learned" (a LearnedDilation parameter, interpolated
+    offsets, alpha kept on the device)."""
+
+    def __init__(self, hidden: int = 512, heads: int = 8, W: int = 12, alpha=1.0,
+                 base: Sequence[int] = FIB_BASE_987, rope_theta: float = 10000.0, mode: Optional[int] = None):
+        super().__init__()
+        if hidden % heads != 0 or hidden // heads != 64:
+            raise ValueError("head size hidden / heads must be 64")
+        self.heads, self.W, self.base, self.rope_theta = heads, int(W), tuple(base), float(rope_theta)
+        self.qkv = torch.nn.Linear(hidden, 3 * hidden, bias=False)
+        self.out = torch.nn.Linear(hidden, hidden, bias=False)
+        self.learned = isinstance(alpha, str) and alpha == "learned"
+        if self.learned:
+            self.dilation = LearnedDilation()
+            self.mode = INTERP if mode is None else int(mode)
+        else:
+            self.alpha = float(alpha)
+            self.mode = INT if mode is None else int(mode)
+
+    def forward(self, x):
+        B, N, C = x.shape
+        H = self.heads
+        qkv = self.qkv(x).view(B, N, 3, H, C // H).permute(2, 0, 3, 1, 4)
+        q, k, v = (t.contiguous() for t in qkv)
+        if self.learned:
+            a = self.dilation.alpha()
+            o = fib_sparse_attention(q, k, v, a, self.W, self.base, self.rope_theta, self.mode, alpha_range=(0.5, 1.5))
+        else:
+            o = fib_sparse_attention(q, k, v, self.alpha, self.W, self.base, self.rope_theta, self.mode)
+        return self.out(o.transpose(1, 2).reshape(B, N, C))

@@ -9,7 +9,7 @@ import fibonacci_offset_dilated_amd as F
 import oracle as O
 from fibonacci_offset_dilated_amd.autograd import LearnedDilation, fib_sparse_attention
 from fibonacci_offset_dilated_amd.workloads import BF16, F32, FIB_BASE, INT, INTERP
-from gpu_util import TOL, TOL_DALPHA, grad_excess, host, inputs, say
+from gpu_util import TOL, TOL_DALPHA, grad_excess, host, inputs, maxabs, say
 
 pytestmark = pytest.mark.gpu
 
@@ -60,3 +60,58 @@ def test_learned_dilation_theta_gradient():
     got = float(layer.theta.grad.item())
     say(f"dtheta {got:.6g} vs {want:.6g}")
     assert abs(got - want) <= TOL_DALPHA[F32] * rabs * 0.5 + 1e-9
+
+
+@pytest.mark.parametrize("learned", [False, True], ids=["static-int", "learned-interp"])
+def test_attention_layer_module(learned):
+    """FibSparseSelfAttention (fp32): output and gradients of x and of both projections against
+    an fp64 composition of the projections with the oracle's forward and backward. Bound:
+    the op's 1e-4 propagated through a projection row (|W| <= 1/sqrt(512), 512 terms: at most
+    512 * 0.0442 * 1e-4 = 2.3e-3), so 2.5e-3 on outputs and gradients."""
+    from fibonacci_offset_dilated_amd.autograd import FibSparseSelfAttention
+    torch.manual_seed(11)
+    B, N, C, H = 2, 300, 512, 8
+    layer = FibSparseSelfAttention(C, H, 12, "learned" if learned else 1.21).cuda()
+    if learned:
+        with torch.no_grad():
+            layer.dilation.theta.fill_(0.4)
+    rng = np.random.default_rng(12)
+    x64 = rng.standard_normal((B, N, C))
+    dy64 = rng.standard_normal((B, N, C))
+    x = torch.from_numpy(x64.astype(np.float32)).cuda().requires_grad_(True)
+    y = layer(x)
+    y.backward(torch.from_numpy(dy64.astype(np.float32)).cuda())
+    torch.cuda.synchronize()
+    # fp64 reference
+    x64 = x.detach().double().cpu().numpy()
+    wqkv = layer.qkv.weight.detach().double().cpu().numpy()
+    wo = layer.out.weight.detach().double().cpu().numpy()
+    if learned:
+        a = np.float32(layer.dilation.alpha().item())
+        mode = INTERP
+    else:
+        a = np.float32(1.21)
+        mode = INT
+    qkv = (x64 @ wqkv.T).reshape(B, N, 3, H, 64).transpose(2, 0, 3, 1, 4)
+    q, k, v = qkv[0], qkv[1], qkv[2]
+    o, _ = O.forward(q, k, v, 12, a, FIB_BASE, 10000.0, mode, workers=8)
+    o2 = o.transpose(0, 2, 1, 3).reshape(B, N, C)
+    y_ref = o2 @ wo.T
+    do2 = dy64 @ wo
+    dwo = np.einsum("bni,bnj->ij", dy64, o2)
+    do = do2.reshape(B, N, H, 64).transpose(0, 2, 1, 3)
+    dq, dk, dv, da, dabs = O.backward(q, k, v, do, 12, a, FIB_BASE, 10000.0, mode, workers=8, return_abs=True)
+    dqkv = np.stack([dq, dk, dv]).transpose(1, 3, 0, 2, 4).reshape(B, N, 3 * C)
+    dx = dqkv @ wqkv
+    dwqkv = np.einsum("bni,bnj->ij", dqkv, x64)
+    e = {"y": maxabs(host(y), y_ref), "dx": maxabs(host(x.grad), dx),
+         "dWqkv": maxabs(host(layer.qkv.weight.grad), dwqkv), "dWo": maxabs(host(layer.out.weight.grad), dwo)}
+    say(f"attention layer (learned={learned}): {e}")
+    assert max(e.values()) <= 2.5e-3
+    if learned:
+        th = float(layer.dilation.theta.item())
+        dmap = 0.5 * (1.0 - np.tanh(th) ** 2)
+        want = da * dmap
+        got = float(layer.dilation.theta.grad.item())
+        say(f"  dtheta {got:.6g} vs {want:.6g} (scale {dabs * dmap:.6g})")
+        assert abs(got - want) <= TOL_DALPHA[F32] * dabs * dmap
