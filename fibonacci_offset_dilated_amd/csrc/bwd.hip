@@ -423,9 +423,12 @@ hipError_t run(const BwdArgs& a) {
         (const T*)a.o, (const T*)a.dout, a.lse, (T*)a.dq, delta, part, a.N, a.W, a.tab, a.rope, scale, tiles,
         a.plan, a.heads_per_plan);
   }
+  // the query-side workgroups are head-major, so each layer's partials are one run
+  bool dalpha_done = false;
   if (bwdk_ring_supported(a) && (MODE == 0 || ps != nullptr)) {
-    const hipError_t e = launch_bwdk_ring(a, delta, ps);
+    const hipError_t e = launch_bwdk_ring(a, delta, ps, part, n_part / a.layers);
     if (e != hipSuccess) return e;
+    dalpha_done = true;  // the ring key side writes dalpha
   } else if (ps != nullptr) {
     bwd_key_ps_kernel<DEV><<<grid, block, 0, a.stream>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
         (const bf16_t*)a.v, (const bf16_t*)a.dout, a.lse, delta, ps, (bf16_t*)a.dk, (bf16_t*)a.dv, a.N, a.W, a.tab,
@@ -434,8 +437,7 @@ hipError_t run(const BwdArgs& a) {
     bwd_key_kernel<T, MODE, DEV><<<grid, block, 0, a.stream>>>((const T*)a.q, (const T*)a.k, (const T*)a.v,
         (const T*)a.dout, a.lse, delta, (T*)a.dk, (T*)a.dv, a.N, a.W, a.tab, a.rope, scale, tiles, a.plan, a.heads_per_plan);
   }
-  if (a.dalpha != nullptr) {
-    // the query-side workgroups are head-major, so each layer's partials are one run
+  if (a.dalpha != nullptr && !dalpha_done) {
     if (MODE == 1)
       dalpha_reduce_kernel<<<a.layers, 256, 0, a.stream>>>(part, n_part / a.layers, a.dalpha);
     else

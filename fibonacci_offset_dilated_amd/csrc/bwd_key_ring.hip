@@ -60,6 +60,13 @@ struct BkArgs {
   const DevPlan* plan;  // alpha in device memory: the split above comes from here (DEV instances)
   int n_far;            // far entries in use (DEV instances: NF is an upper bound)
   int heads_per_plan;   // DEV instances: head h reads plan[h / heads_per_plan]
+  // d(alpha) per layer, formed here because this kernel runs after the query side: block b <
+  // dal_layers writes dal_out[b] = the ordered sum of the dal_n partials of layer b
+  // (interpolated mode) or 0 (integer mode); dal_out may be null
+  const float* dal_part;
+  int64_t dal_n;
+  float* dal_out;
+  int dal_layers;
 };
 
 struct __align__(16) BkSmem {
@@ -364,16 +371,34 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
   load_step(s0);
   load_ps(s0);
   __syncthreads();
-  for (int j = 0; j < n_warm; ++j) {
-    const int qb = s0 + j * kT + 16 * wave;
-    uint4 q2[2], d2[2];
-    load2(Qh, row_elems(qb), q2);
-    load2(Dh, row_elems(qb), d2);
-    const int r = qb + n < N ? qb + n : N - 1;
-    float2 cs[8];
+  {
+    // kWB steps of warm rows in flight at once, then rotated and stored
+    constexpr int kWB = 3;
+    for (int j0 = 0; j0 < n_warm; j0 += kWB) {
+      uint4 wq[kWB][2], wd[kWB][2];
+      float wl[kWB], wt[kWB];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) cs[t] = compose(sm.warm_cs[j][8 * g + t], cs_t[t]);
-    put_query(qb, cs, q2, d2, Lh[r], Th[r]);
+      for (int jj = 0; jj < kWB; ++jj) {
+        if (j0 + jj < n_warm) {
+          const int qb = s0 + (j0 + jj) * kT + 16 * wave;
+          load2(Qh, row_elems(qb), wq[jj]);
+          load2(Dh, row_elems(qb), wd[jj]);
+          const int r = qb + n < N ? qb + n : N - 1;
+          wl[jj] = Lh[r];
+          wt[jj] = Th[r];
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < kWB; ++jj) {
+        if (j0 + jj < n_warm) {
+          const int qb = s0 + (j0 + jj) * kT + 16 * wave;
+          float2 cs[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) cs[t] = compose(sm.warm_cs[j0 + jj][8 * g + t], cs_t[t]);
+          put_query(qb, cs, wq[jj], wd[jj], wl[jj], wt[jj]);
+        }
+      }
+    }
   }
   FarQ<MODE == 0 ? NF : 0> fq;
   FarQI<MODE == 1 ? NF : 0> fi;
@@ -672,6 +697,17 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
     if constexpr (MODE == 1) load_far_qi<NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fi, a, Qh, Dh, Sh, S_n_cov, j0 + kT, l, n, g);
     __syncthreads();
   }
+  if (a.dal_out != nullptr && (int)blockIdx.x < a.dal_layers && wave == 0) {
+    // per-lane strided fp64 sums, then a fixed xor butterfly: the same order on every call
+    double sd = 0.0;
+    if constexpr (MODE == 1) {
+      const float* pp = a.dal_part + (int64_t)blockIdx.x * a.dal_n;
+      for (int64_t x = l; x < a.dal_n; x += 64) sd += (double)pp[x];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) sd += __shfl_xor(sd, off);
+    }
+    if (l == 0) a.dal_out[blockIdx.x] = (float)sd;
+  }
 }
 
 template <int MODE, int NC, int NF, bool DEV>
@@ -721,9 +757,14 @@ int bwdk_instance_key(const BwdArgs& f) {
   return (cov <= 8 ? 8 : 16) * 10 + far;
 }
 
-hipError_t launch_bwdk_ring(const BwdArgs& f, const float* delta, const uint32_t* ps) {
+hipError_t launch_bwdk_ring(const BwdArgs& f, const float* delta, const uint32_t* ps, const float* dal_part,
+                            int64_t dal_n) {
   if (f.mode == 1 && ps == nullptr) return hipErrorInvalidValue;
   BkArgs a;
+  a.dal_part = dal_part;
+  a.dal_n = dal_n;
+  a.dal_out = f.dalpha;
+  a.dal_layers = f.layers;
   a.q = (const bf16_t*)f.q;
   a.k = (const bf16_t*)f.k;
   a.v = (const bf16_t*)f.v;

@@ -180,6 +180,8 @@ hipError_t launch_bwdq_ring(const BwdArgs& a, float* delta, float* part, uint32_
 // key side on the LDS ring (bf16, W <= 16): dK, dV from Delta; in interpolated mode also
 // from the (P, dS) pairs ps that the ring query side stored (required there)
 bool bwdk_ring_supported(const BwdArgs& a);
-hipError_t launch_bwdk_ring(const BwdArgs& a, const float* delta, const uint32_t* ps);
+// Also writes dalpha (one value per layer) from the query side's dal_n partials per layer
+hipError_t launch_bwdk_ring(const BwdArgs& a, const float* delta, const uint32_t* ps, const float* dal_part,
+                            int64_t dal_n);
 
 }  // namespace fib
