@@ -132,9 +132,20 @@ def _check(status: int, where: str):
         raise FibError(status, where)
 
 
+_BASE_ARRAYS: dict = {}
+
+
 def _base_array(base: Sequence[int]):
-    arr = (ctypes.c_int32 * max(1, len(base)))(*[int(b) for b in base])
-    return arr, len(base)
+    """ctypes int32 copy of the base offsets (cached per distinct base: the library only
+    reads it during a call)."""
+    key = tuple(base)
+    hit = _BASE_ARRAYS.get(key)
+    if hit is None:
+        arr = (ctypes.c_int32 * max(1, len(key)))(*[int(b) for b in key])
+        if len(_BASE_ARRAYS) >= 64:
+            _BASE_ARRAYS.clear()
+        hit = _BASE_ARRAYS[key] = (arr, len(key))
+    return hit
 
 
 def schedule_alpha(kind: int, layer: int, n_layers: int) -> np.float32:
@@ -159,9 +170,15 @@ def offset_table(alpha, base: Sequence[int], W: int, mode: int):
 
 # ---- torch-facing wrappers ---------------------------------------------------------------
 
+_TORCH = None
+
+
 def _torch():
-    import torch
-    return torch
+    global _TORCH
+    if _TORCH is None:
+        import torch
+        _TORCH = torch
+    return _TORCH
 
 
 def _dtype_code(t) -> int:
@@ -174,19 +191,29 @@ def _dtype_code(t) -> int:
 
 
 def _stream(stream):
+    """hipStream_t of `stream`, or of the current device's current stream when None (read
+    through torch's raw-stream query, which skips building a Stream object)."""
     torch = _torch()
     if stream is None:
+        C = torch._C
+        if hasattr(C, "_cuda_getCurrentRawStream"):
+            return ctypes.c_void_p(C._cuda_getCurrentRawStream(C._cuda_getDevice()))
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
 
 
 def _check_qkv(*ts):
-    torch = _torch()
+    Tensor = _torch().Tensor
     ref = ts[0]
+    if not isinstance(ref, Tensor) or ref.get_device() < 0:
+        raise TypeError("tensors must be CUDA (HIP) tensors")
+    shape, dtype, dev = ref.shape, ref.dtype, ref.get_device()
+    if len(shape) != 4:
+        raise ValueError("q, k, v (and o, dout, grads) must share shape [B, H, N, D], dtype and device")
     for t in ts:
-        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        if not isinstance(t, Tensor) or t.get_device() < 0:
             raise TypeError("tensors must be CUDA (HIP) tensors")
-        if t.dim() != 4 or t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
+        if t.shape != shape or t.dtype != dtype or t.get_device() != dev:
             raise ValueError("q, k, v (and o, dout, grads) must share shape [B, H, N, D], dtype and device")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")

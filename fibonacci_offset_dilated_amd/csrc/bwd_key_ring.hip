@@ -713,8 +713,8 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
 template <int MODE, int NC, int NF, bool DEV>
 hipError_t launch(const BkArgs& a, unsigned blocks, hipStream_t s) {
   const size_t smem = sizeof(BkSmem);
-  hipError_t e = hipFuncSetAttribute((const void*)bwdk_ring_kernel<MODE, NC, NF, DEV>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  static std::atomic<uint32_t> lds_set{0};
+  hipError_t e = ensure_lds_limit(bwdk_ring_kernel<MODE, NC, NF, DEV>, lds_set, (int)smem);
   if (e != hipSuccess) return e;
   bwdk_ring_kernel<MODE, NC, NF, DEV><<<blocks, 512, smem, s>>>(a);
   return hipGetLastError();

@@ -612,8 +612,8 @@ hipError_t launch(const RingArgs& a, unsigned blocks, hipStream_t s) {
     return hipErrorInvalidValue;
   } else {
   const size_t smem = sizeof(Smem);
-  hipError_t e = hipFuncSetAttribute((const void*)fwd_ring_kernel<MODE, NC, NF, WAVES, DEV>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  static std::atomic<uint32_t> lds_set{0};
+  hipError_t e = ensure_lds_limit(fwd_ring_kernel<MODE, NC, NF, WAVES, DEV>, lds_set, (int)smem);
   if (e != hipSuccess) return e;
   fwd_ring_kernel<MODE, NC, NF, WAVES, DEV><<<blocks, 64 * WAVES, smem, s>>>(a);
   return hipGetLastError();

@@ -9,8 +9,25 @@
 #include "fib_common.h"
 #include "fib_launch.h"
 
+#include <atomic>
+
 namespace fib {
 namespace ring {
+
+// Raises a ring kernel's dynamic LDS limit to `bytes` on the current device, once per
+// device and kernel instance (`done` holds one bit per device): the setting is idempotent,
+// and repeating it on every launch costs host time that short calls notice.
+template <typename K>
+inline hipError_t ensure_lds_limit(K* kernel, std::atomic<uint32_t>& done, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint32_t bit = dev >= 0 && dev < 32 ? (1u << dev) : 0u;
+  if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+  e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f4;

@@ -34,7 +34,8 @@
  * Ownership: the caller allocates and owns all device buffers (outputs and backward
  * workspace included); the library never allocates or frees device memory. Host arrays
  * (base, out_* of the table helper) are read or written during the call only. The library
- * keeps no state between calls and is reentrant. Device work is enqueued on `stream`
+ * keeps no state between calls that affects results (it only records, per device, that a
+ * kernel's LDS limit has been raised, so the setting is made once) and is reentrant. Device work is enqueued on `stream`
  * (a hipStream_t; NULL = the null stream) and the call returns without synchronizing.
  *
  * Errors: every call returns FIB_OK (0) or a negative FIB_ERR_* status. On an argument
