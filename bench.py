@@ -243,10 +243,17 @@ def dropped_mass_diag(dev, stream, args):
                      device=dev)
     reps = max(5, args.steps // 5)
     ms = time_calls(lambda: F.dense_lse(q, k, 10000.0, lse=lse, workspace=ws), reps, 2, stream)
-    flops = w.B * w.H * (w.N * (w.N + 1) / 2) * D * 2
+    logits = w.B * w.H * (w.N * (w.N + 1) / 2)
+    flops = logits * D * 2
+    # VALU floor of the online log-sum-exp: per logit a max, an FMA and an add at full rate and
+    # one exp2 at quarter rate = 7 full-rate lane operations; 256 CUs x 4 SIMDs x 16 lanes x
+    # 2.4 GHz = 39.3e12 lane operations/s (no packed fp32 math)
+    valu_floor_s = logits * 7 / (256 * 4 * 16 * 2.4e9)
     out = {"dense_lse_b4h8n4096_us": round(ms * 1e3, 2),
            "dense_lse_b4h8n4096_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
-           "dense_lse_b4h8n4096_mfma_frac": round(flops / (ms * 1e-3) / 1e12 / 2500.0, 4)}
+           "dense_lse_b4h8n4096_mfma_frac": round(flops / (ms * 1e-3) / 1e12 / 2500.0, 4),
+           "dense_lse_b4h8n4096_valu_floor_us": round(valu_floor_s * 1e6, 1),
+           "dense_lse_b4h8n4096_valu_frac": round(valu_floor_s / (ms * 1e-3), 4)}
     for name, base in (("fib", FIB_BASE), ("pow2", POW2_BASE)):
         dm = F.dropped_mass(q, k, v, 12, 1.0, base)
         out[f"dropped_mass_b4h8n4096_{name}_mean"] = round(float(dm.mean().item()), 4)

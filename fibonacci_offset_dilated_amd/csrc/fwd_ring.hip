@@ -345,6 +345,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
   FarRows<NF> fr;
   load_far_k<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fr, a, Kh, s0 + 16 * wave, n, g,
                        lane_off);
+  if constexpr (MODE == 0)
+    load_far_v<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fr, a, Vh, s0 + 16 * wave, n, g,
+                         lane_off);
 
   int buf = 0;
   for (int p0 = s0; p0 < s1; p0 += kT, buf ^= 1) {
@@ -434,8 +437,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
         s_far[f] = fmaf(s, sl2, bias_diag);
         if (DEV && f >= S_n_far) s_far[f] = -INFINITY;  // slot beyond the table
       }
-      // their V rows, for the end of this step (K and V rows are never held together)
-      load_far_v<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fr, a, Vh, i0w, n, g, lane_off);
+      // interpolated: their V rows, for the end of this step (row pairs of K and V are never
+      // held together: the registers do not allow it); integer: requested with the K rows
+      if constexpr (MODE == 1)
+        load_far_v<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fr, a, Vh, i0w, n, g, lane_off);
 
 
       // ---- softmax over the window band and the entries (base-2 logits)
@@ -572,9 +577,13 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
         *reinterpret_cast<uint4*>(op + kHalf) = x1;
         if (g == 0 && a.lse != nullptr) (a.lse + (size_t)head * N + i0w)[n] = (m + log2f(lsum)) * 0.69314718055994530942f;
       }
-      // far K rows of the next step (the last step loads rows that are never used)
+      // far K rows of the next step, and in integer mode its far V rows (the last step loads
+      // rows that are never used)
       load_far_k<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fr, a, Kh, i0w + kT, n, g,
                            lane_off);
+      if constexpr (MODE == 0)
+        load_far_v<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fr, a, Vh, i0w + kT, n, g,
+                             lane_off);
     }
     __syncthreads();
   }
