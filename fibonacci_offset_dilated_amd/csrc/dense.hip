@@ -27,11 +27,15 @@ constexpr int kDT = 64;      // keys per LDS tile
 constexpr int kDQ = 128;     // queries per workgroup: 4 waves x 2 groups of 16
 constexpr int kDRow = 144;   // LDS row stride (128 bytes + 16 padding: 16 rows on distinct banks)
 
-// out[r] = R_pos(r) x[r] in bf16 (pos = r mod N); lane c of a row's 4 owns the RoPE pairs
+// out[r] = R_pos(r) x[r] in bf16 (pos = r mod N) for the rows of two tensors in one launch
+// (blockIdx.y selects x0 -> out0 or x1 -> out1); lane c of a row's 4 owns the RoPE pairs
 // (8c + t, 32 + 8c + t), t < 8.
 template <typename T>
-__global__ __launch_bounds__(256) void rotate_rows_kernel(const T* __restrict__ x, bf16_t* __restrict__ out,
+__global__ __launch_bounds__(256) void rotate_rows_kernel(const T* __restrict__ x0, bf16_t* __restrict__ out0,
+                                                          const T* __restrict__ x1, bf16_t* __restrict__ out1,
                                                           int64_t rows, int64_t N, Rope rope) {
+  const T* __restrict__ x = blockIdx.y == 0 ? x0 : x1;
+  bf16_t* __restrict__ out = blockIdx.y == 0 ? out0 : out1;
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t r = t >> 2;
   if (r >= rows) return;
@@ -179,13 +183,11 @@ hipError_t launch_dense_lse(const void* q, const void* k, float* lse, int64_t BH
   bf16_t* kr = qr + (size_t)BH * N * kD;
   const int64_t rows = BH * N;
   const unsigned rb = (unsigned)((rows * 4 + 255) / 256);
-  if (dtype == 0) {
-    rotate_rows_kernel<float><<<rb, 256, 0, s>>>((const float*)q, qr, rows, N, rope);
-    rotate_rows_kernel<float><<<rb, 256, 0, s>>>((const float*)k, kr, rows, N, rope);
-  } else {
-    rotate_rows_kernel<bf16_t><<<rb, 256, 0, s>>>((const bf16_t*)q, qr, rows, N, rope);
-    rotate_rows_kernel<bf16_t><<<rb, 256, 0, s>>>((const bf16_t*)k, kr, rows, N, rope);
-  }
+  const dim3 rgrid(rb, 2);  // y = 0: Q, y = 1: K
+  if (dtype == 0)
+    rotate_rows_kernel<float><<<rgrid, 256, 0, s>>>((const float*)q, qr, (const float*)k, kr, rows, N, rope);
+  else
+    rotate_rows_kernel<bf16_t><<<rgrid, 256, 0, s>>>((const bf16_t*)q, qr, (const bf16_t*)k, kr, rows, N, rope);
   const int qtiles = (int)((N + kDQ - 1) / kDQ);
   const float sl2 = (float)(1.4426950408889634 / sqrt((double)kD));
   dense_lse_kernel<<<(unsigned)(qtiles * BH), 256, 0, s>>>(qr, kr, lse, N, BH, qtiles, sl2);
