@@ -27,31 +27,44 @@ constexpr int kDT = 64;      // keys per LDS tile
 constexpr int kDQ = 128;     // queries per workgroup: 4 waves x 2 groups of 16
 constexpr int kDRow = 144;   // LDS row stride (128 bytes + 16 padding: 16 rows on distinct banks)
 
-// out[r] = R_pos(r) x[r] in bf16 (pos = r mod N) for the rows of two tensors in one launch
-// (blockIdx.y selects x0 -> out0 or x1 -> out1); lane c of a row's 4 owns the RoPE pairs
-// (8c + t, 32 + 8c + t), t < 8.
+// out[h][p] = R_p x[h][p] in bf16 for two tensors (x0 -> out0, x1 -> out1) of BH heads x N
+// rows. The cos/sin of a position do not depend on the head or the tensor, so a block takes
+// 64 positions (four lanes each; lane c owns the RoPE pairs (8c + t, 32 + 8c + t), t < 8)
+// and hpb heads (blockIdx.y), computes each position's angles once and applies them to both
+// tensors of all its heads.
+constexpr int64_t kRotHeads = 2;      // heads per block, unless the grid's y limit needs more
+constexpr int64_t kMaxGridY = 65535;
 template <typename T>
 __global__ __launch_bounds__(256) void rotate_rows_kernel(const T* __restrict__ x0, bf16_t* __restrict__ out0,
                                                           const T* __restrict__ x1, bf16_t* __restrict__ out1,
-                                                          int64_t rows, int64_t N, Rope rope) {
-  const T* __restrict__ x = blockIdx.y == 0 ? x0 : x1;
-  bf16_t* __restrict__ out = blockIdx.y == 0 ? out0 : out1;
+                                                          int64_t BH, int64_t N, int64_t hpb, Rope rope) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t r = t >> 2;
-  if (r >= rows) return;
+  const int64_t pos = t >> 2;
+  if (pos >= N) return;
   const int c = (int)(t & 3);
-  const int64_t pos = r % N;
-  float lo[8], hi[8], rl[8], rh[8];
-  Vec8<T>::load(x + r * kD + 8 * c, lo);
-  Vec8<T>::load(x + r * kD + kHalf + 8 * c, hi);
+  float2 cs[8];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const float2 cs = rope_cs(pos, rope.rev[8 * c + u]);
-    rl[u] = lo[u] * cs.x - hi[u] * cs.y;
-    rh[u] = hi[u] * cs.x + lo[u] * cs.y;
+  for (int u = 0; u < 8; ++u) cs[u] = rope_cs(pos, rope.rev[8 * c + u]);
+  const int64_t h0 = (int64_t)blockIdx.y * hpb;
+  const int64_t h1 = h0 + hpb < BH ? h0 + hpb : BH;
+  for (int64_t h = h0; h < h1; ++h) {
+    const int64_t r = h * N + pos;
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      const T* x = which == 0 ? x0 : x1;
+      bf16_t* out = which == 0 ? out0 : out1;
+      float lo[8], hi[8], rl[8], rh[8];
+      Vec8<T>::load(x + r * kD + 8 * c, lo);
+      Vec8<T>::load(x + r * kD + kHalf + 8 * c, hi);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        rl[u] = lo[u] * cs[u].x - hi[u] * cs[u].y;
+        rh[u] = hi[u] * cs[u].x + lo[u] * cs[u].y;
+      }
+      Vec8<bf16_t>::store(out + r * kD + 8 * c, rl);
+      Vec8<bf16_t>::store(out + r * kD + kHalf + 8 * c, rh);
+    }
   }
-  Vec8<bf16_t>::store(out + r * kD + 8 * c, rl);
-  Vec8<bf16_t>::store(out + r * kD + kHalf + 8 * c, rh);
 }
 
 __global__ __launch_bounds__(256) void dense_lse_kernel(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ kr,
@@ -181,13 +194,15 @@ hipError_t launch_dense_lse(const void* q, const void* k, float* lse, int64_t BH
                             const Rope& rope, void* workspace, hipStream_t s) {
   bf16_t* qr = static_cast<bf16_t*>(workspace);
   bf16_t* kr = qr + (size_t)BH * N * kD;
-  const int64_t rows = BH * N;
-  const unsigned rb = (unsigned)((rows * 4 + 255) / 256);
-  const dim3 rgrid(rb, 2);  // y = 0: Q, y = 1: K
+  // x: 64 positions per block; y: groups of hpb heads
+  int64_t hpb = kRotHeads;
+  if ((BH + hpb - 1) / hpb > kMaxGridY) hpb = (BH + kMaxGridY - 1) / kMaxGridY;
+  const dim3 rgrid((unsigned)((N * 4 + 255) / 256), (unsigned)((BH + hpb - 1) / hpb));
   if (dtype == 0)
-    rotate_rows_kernel<float><<<rgrid, 256, 0, s>>>((const float*)q, qr, (const float*)k, kr, rows, N, rope);
+    rotate_rows_kernel<float><<<rgrid, 256, 0, s>>>((const float*)q, qr, (const float*)k, kr, BH, N, hpb, rope);
   else
-    rotate_rows_kernel<bf16_t><<<rgrid, 256, 0, s>>>((const bf16_t*)q, qr, (const bf16_t*)k, kr, rows, N, rope);
+    rotate_rows_kernel<bf16_t><<<rgrid, 256, 0, s>>>((const bf16_t*)q, qr, (const bf16_t*)k, kr, BH, N, hpb,
+                                                     rope);
   const int qtiles = (int)((N + kDQ - 1) / kDQ);
   const float sl2 = (float)(1.4426950408889634 / sqrt((double)kD));
   dense_lse_kernel<<<(unsigned)(qtiles * BH), 256, 0, s>>>(qr, kr, lse, N, BH, qtiles, sl2);
