@@ -126,3 +126,31 @@ def dense_augmented(q, k, v, W, alpha_t, base, theta=10000.0):
         outs.append((p[..., None] * vals).sum(dim=-2))
         lses.append(torch.logsumexp(lg, dim=-1))
     return torch.stack(outs, dim=-2), torch.stack(lses, dim=-1)
+
+
+def moment_probe_v(N: int, D: int = 64, vrow=None) -> np.ndarray:
+    """V rows (x_j, x_j^2, 1, 0, ...) with x_j = vrow[j] (default j / N), [N, D] fp64."""
+    x = np.arange(N, dtype=np.float64) / N if vrow is None else np.asarray(vrow, dtype=np.float64)
+    v = np.zeros((N, D))
+    v[:, 0], v[:, 1], v[:, 2] = x, x ** 2, 1.0
+    return v
+
+
+def moment_probe_expected(N: int, W: int, alpha, base, interp: bool, vals=None) -> np.ndarray:
+    """Closed form of the moment probe, [N, 3]: with Q = 0 every attended (virtual) key of
+    query i gets the same weight, so O_i[:3] is the plain average over its attended set of
+    the first three V columns: vals [N, 3] (default (j/N, (j/N)^2, 1), moment_probe_v's rows).
+    Integer mode: the window and the distances that int_member accepts (<= i). Interpolated
+    mode: the window plus, for each entry of interp_virtuals with c <= i,
+    (1 - w) V[i - c] + w V[i - c + 1]."""
+    vals = moment_probe_v(N)[:, :3] if vals is None else np.asarray(vals, dtype=np.float64)
+    row = lambda j: vals[j]
+    offs = [] if interp else [d for d in range(W, N) if int_member(d, alpha, base, W)]
+    virt = interp_virtuals(alpha, base, W) if interp else []
+    out = np.zeros((N, 3))
+    for i in range(N):
+        terms = [row(i - s) for s in range(min(W, i + 1))]
+        terms += [row(i - d) for d in offs if d <= i]
+        terms += [(1 - w) * row(i - c) + w * row(i - c + 1) for _, c, _, w in virt if c <= i]
+        out[i] = np.mean(terms, axis=0)
+    return out

@@ -280,3 +280,27 @@ def test_long_many_heads(case, mode):
     say("  max err O", eo, "LSE", el)
     assert eo <= TOL[BF16] and el <= TOL[BF16]
     assert torch.isfinite(o.float()).all().item()
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("mode", [INT, INTERP], ids=["int", "interp"])
+def test_probe_moments(mode, dtype):
+    """Q = 0 and V[j] = (j/N, (j/N)^2, 1, 0, ...): O_i[:3] is the mean of the attended
+    positions, their second moment and 1 (closed form over an independently built attended
+    set; interpolated keys at their fractional positions). bf16: the closed form uses the
+    stored bf16 V values; the bound is the output's rounding (half an ulp below 1 is 2^-9)
+    plus the rounding of the interpolation weights in the MFMA path."""
+    from dense_reference import moment_probe_expected, moment_probe_v
+
+    N, W, a = 1500, 12, np.float32(1.37)
+    say("moment probe", mode, dtype)
+    (_, _), (k, _), (_, _) = inputs(78, (1, 2, N, 64), dtype)
+    vd = torch.from_numpy(np.broadcast_to(moment_probe_v(N), (1, 2, N, 64)).astype(np.float32).copy())
+    vd = vd.cuda().to(k.dtype)
+    o, _ = F.fwd(torch.zeros_like(k), k, vd, W, a, FIB_BASE, 10000.0, mode)
+    oh = host(o)
+    want = moment_probe_expected(N, W, a, FIB_BASE, mode == INTERP, vals=host(vd)[0, 0, :, :3])
+    tol = 1e-5 if dtype == F32 else 2.0 ** -8
+    for h in range(2):
+        assert maxabs(oh[0, h, :, :3], want) <= tol
+        assert np.abs(oh[0, h, :, 3:]).max() == 0.0

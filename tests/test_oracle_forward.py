@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle as O
-from dense_reference import dense_augmented, dense_int_forward, rope_complex
+from dense_reference import dense_augmented, dense_int_forward, moment_probe_expected, moment_probe_v, rope_complex
 from fibonacci_offset_dilated_amd.workloads import FIB_BASE, POW2_BASE
 
 SMALL_FIB = FIB_BASE[:10]  # up to 55, so that offsets bite at tiny N
@@ -118,3 +118,19 @@ def test_forward_rows_and_workers_agree():
     orow, lrow = O.forward_rows(q[0, 1], k[0, 1], v[0, 1], rows, 12, a, FIB_BASE, 10000.0, O.INTERP)
     np.testing.assert_allclose(orow, o[0, 1][rows], rtol=0, atol=1e-14)
     np.testing.assert_allclose(lrow, lse[0, 1][rows], rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("mode", [O.INT, O.INTERP], ids=["int", "interp"])
+def test_moment_probe_closed_form(mode):
+    """Q = 0, V[j] = (j/N, (j/N)^2, 1): O_i is the mean and second moment of the attended
+    positions (interpolated keys at their fractional position i - d)."""
+    N, W, a = 700, 12, np.float32(1.37)
+    rng = np.random.default_rng(31)
+    k = rng.standard_normal((1, 2, N, 64))
+    q = np.zeros_like(k)
+    v = np.broadcast_to(moment_probe_v(N), (1, 2, N, 64)).copy()
+    o, _ = O.forward(q, k, v, W, a, FIB_BASE, 10000.0, mode)
+    want = moment_probe_expected(N, W, a, FIB_BASE, mode == O.INTERP)
+    for h in range(2):
+        np.testing.assert_allclose(o[0, h, :, :3], want, rtol=0, atol=1e-13)
+        assert np.abs(o[0, h, :, 3:]).max() == 0.0
