@@ -77,54 +77,58 @@ struct __align__(16) Smem {
 
 // Rows of the far table entries for one step, held in registers and loaded one step ahead:
 // lane (n, g) holds, per far entry, K and V row i0w - d + n, dims 8g..8g+7 and 32+8g..32+8g+7
-// (K: the A operand of the logit MFMA; V: the lane's slice of O), and in interpolated mode
-// the same for the upper row (+1).
+// (K: the A operand of the logit MFMA; V: the lane's slice of O). In interpolated mode that
+// is the lower row; the upper row of query n is the lower row of query n + 1 (upper_rows), and
+// the one that no lane holds, row i0w - d + 16, is kept spread over the wave (kex, vex: lane l
+// holds its dword l % 32).
 template <int NF>
 struct FarRows {
   uint4 k[NF > 0 ? NF : 1][2];
-  uint4 kh[NF > 0 ? NF : 1][2];
   uint4 v[NF > 0 ? NF : 1][2];
-  uint4 vh[NF > 0 ? NF : 1][2];
+  uint32_t kex[NF > 0 ? NF : 1];
+  uint32_t vex[NF > 0 ? NF : 1];
 };
 
 // n_use: far slots in use (NF, or fewer in DEV instances: the unused slots are zero-filled
 // without a load; n_use is wave-uniform, so the test is a scalar branch)
 template <int MODE, int NF>
 __device__ __forceinline__ void load_far_k(const int* fdist, int n_use, FarRows<NF>& fr, const RingArgs& a,
-                                           const bf16_t* Kh, int i0w, int n, int g, int lane_off) {
+                                           const bf16_t* Kh, int i0w, int l, int n, int g, int lane_off) {
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     if (f >= n_use) {
-      fr.k[f][0] = fr.k[f][1] = fr.kh[f][0] = fr.kh[f][1] = make_uint4(0, 0, 0, 0);
+      fr.k[f][0] = fr.k[f][1] = make_uint4(0, 0, 0, 0);
+      fr.kex[f] = 0u;
       continue;
     }
     const bf16_t* kp = Kh + far_off(fdist[f], i0w, n, g, lane_off);
     fr.k[f][0] = *reinterpret_cast<const uint4*>(kp);
     fr.k[f][1] = *reinterpret_cast<const uint4*>(kp + kHalf);
     if (MODE == 1) {
-      const bf16_t* kq = Kh + far_off(fdist[f] - 1, i0w, n, g, lane_off);
-      fr.kh[f][0] = *reinterpret_cast<const uint4*>(kq);
-      fr.kh[f][1] = *reinterpret_cast<const uint4*>(kq + kHalf);
+      // row i0w - d + 16 (< N: far distances exceed the ring reach); rows before 0 only meet
+      // masked queries
+      const int r = i0w - fdist[f] + 16;
+      fr.kex[f] = reinterpret_cast<const uint32_t*>(Kh + (int64_t)(r > 0 ? r : 0) * kD)[l & 31];
     }
   }
 }
 
 template <int MODE, int NF>
 __device__ __forceinline__ void load_far_v(const int* fdist, int n_use, FarRows<NF>& fr, const RingArgs& a,
-                                           const bf16_t* Vh, int i0w, int n, int g, int lane_off) {
+                                           const bf16_t* Vh, int i0w, int l, int n, int g, int lane_off) {
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     if (f >= n_use) {
-      fr.v[f][0] = fr.v[f][1] = fr.vh[f][0] = fr.vh[f][1] = make_uint4(0, 0, 0, 0);
+      fr.v[f][0] = fr.v[f][1] = make_uint4(0, 0, 0, 0);
+      fr.vex[f] = 0u;
       continue;
     }
     const bf16_t* vp = Vh + far_off(fdist[f], i0w, n, g, lane_off);
     fr.v[f][0] = *reinterpret_cast<const uint4*>(vp);
     fr.v[f][1] = *reinterpret_cast<const uint4*>(vp + kHalf);
     if (MODE == 1) {
-      const bf16_t* vq = Vh + far_off(fdist[f] - 1, i0w, n, g, lane_off);
-      fr.vh[f][0] = *reinterpret_cast<const uint4*>(vq);
-      fr.vh[f][1] = *reinterpret_cast<const uint4*>(vq + kHalf);
+      const int r = i0w - fdist[f] + 16;
+      fr.vex[f] = reinterpret_cast<const uint32_t*>(Vh + (int64_t)(r > 0 ? r : 0) * kD)[l & 31];
     }
   }
 }
@@ -343,10 +347,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
   // (the first step's barrier orders these stores before any read of them)
   // far K rows of the first step (requested after the warm-up rows, whose registers they reuse)
   FarRows<NF> fr;
-  load_far_k<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fr, a, Kh, s0 + 16 * wave, n, g,
+  load_far_k<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fr, a, Kh, s0 + 16 * wave, l, n, g,
                        lane_off);
   if constexpr (MODE == 0)
-    load_far_v<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fr, a, Vh, s0 + 16 * wave, n, g,
+    load_far_v<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fr, a, Vh, s0 + 16 * wave, l, n, g,
                          lane_off);
 
   int buf = 0;
@@ -430,8 +434,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
         if (MODE == 1) {
           rotate_pack_f(qf, &sm.unc_cs[u + 1][8 * g], &r0, &r1);
           f4 H = {0, 0, 0, 0};
-          H = mfma32(as_bf8(fr.kh[f][0]), as_bf8(r0), H);
-          H = mfma32(as_bf8(fr.kh[f][1]), as_bf8(r1), H);
+          uint4 kh[2];
+          upper_rows(fr.k[f], fr.kex[f], g, kh);
+          H = mfma32(as_bf8(kh[0]), as_bf8(r0), H);
+          H = mfma32(as_bf8(kh[1]), as_bf8(r1), H);
           s = fmaf(S_far_w(f), sel4(H, l) - s, s);
         }
         s_far[f] = fmaf(s, sl2, bias_diag);
@@ -440,7 +446,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
       // interpolated: their V rows, for the end of this step (row pairs of K and V are never
       // held together: the registers do not allow it); integer: requested with the K rows
       if constexpr (MODE == 1)
-        load_far_v<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fr, a, Vh, i0w, n, g, lane_off);
+        load_far_v<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fr, a, Vh, i0w, l, n, g, lane_off);
 
 
       // ---- softmax over the window band and the entries (base-2 logits)
@@ -555,7 +561,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
           const uint32_t x = pack_bf2(p * (1.f - S_far_w(f)), p * S_far_w(f));
           const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute(diag_addr, (int)x);
           lnorm_far = dot2(y, kOnes, lnorm_far);
-          far_pv_interp(acc, fr.v[f][0], fr.v[f][1], fr.vh[f][0], fr.vh[f][1], y);
+          uint4 vh[2];
+          upper_rows(fr.v[f], fr.vex[f], g, vh);
+          far_pv_interp(acc, fr.v[f][0], fr.v[f][1], vh[0], vh[1], y);
         }
       }
 
@@ -579,10 +587,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
       }
       // far K rows of the next step, and in integer mode its far V rows (the last step loads
       // rows that are never used)
-      load_far_k<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fr, a, Kh, i0w + kT, n, g,
+      load_far_k<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fr, a, Kh, i0w + kT, l, n, g,
                            lane_off);
       if constexpr (MODE == 0)
-        load_far_v<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fr, a, Vh, i0w + kT, n, g,
+        load_far_v<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fr, a, Vh, i0w + kT, l, n, g,
                              lane_off);
     }
     __syncthreads();

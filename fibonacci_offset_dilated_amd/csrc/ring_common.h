@@ -185,5 +185,28 @@ inline int64_t ring_segments(int64_t BH, int64_t tiles) {
   return (tiles + per - 1) / per;
 }
 
+// Interpolated far entry: the upper rows (i0w - d + 1 + n) from the lower rows (lane (n, g)
+// holding row i0w - d + n, dims 8g.. and 32 + 8g..; ex: dword l % 32 of row i0w - d + 16). Lane n takes
+// lane n + 1's row (DPP row shift within the 16 lanes of a dim group); lane 15 takes row
+// i0w - d + 16 from the dwords spread over the wave.
+__device__ __forceinline__ void upper_rows(const uint4* lo, uint32_t ex, int g, uint4* hi) {
+  uint32_t w[8] = {lo[0].x, lo[0].y, lo[0].z, lo[0].w, lo[1].x, lo[1].y, lo[1].z, lo[1].w};
+  // (empty asm: the moves happen here, not hoisted to where their results would hold
+  // registers through other work)
+#pragma unroll
+  for (int x = 0; x < 8; ++x) asm volatile("" : "+v"(w[x]));
+  asm volatile("" : "+v"(ex));
+  uint32_t h[8];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    // dword x of the lane's slice: 16-byte half x / 4 (dims 8g.. or 32 + 8g..), word x % 4
+    const int src = 16 * (x >> 2) + 4 * g + (x & 3);
+    const int e = __builtin_amdgcn_ds_bpermute(4 * src, (int)ex);
+    h[x] = (uint32_t)__builtin_amdgcn_update_dpp(e, (int)w[x], 0x101, 0xf, 0xf, false);
+  }
+  hi[0] = make_uint4(h[0], h[1], h[2], h[3]);
+  hi[1] = make_uint4(h[4], h[5], h[6], h[7]);
+}
+
 }  // namespace ring
 }  // namespace fib
