@@ -346,6 +346,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="run one 1 GiB device-to-device copy first (reference for HBM byte counters)")
+    ap.add_argument("--bwd-only", action="store_true",
+                    help="profiling aid: one integer forward, then only integer backward calls "
+                         "(--warmup untimed, --steps timed); prints their time, not the bench line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (the op shards over "
@@ -378,6 +381,18 @@ def main():
 
     def fwd_int():
         F.fwd(q, k, v, W, alpha, FIB_BASE, 10000.0, INT, out=o, lse=lse)
+
+    if args.bwd_only:
+        fwd_int()
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        dal = torch.empty(1, dtype=torch.float32, device=dev)
+        ws = torch.empty(F.bwd_workspace_size(B, H, N, D, F.BF16, INT), dtype=torch.uint8, device=dev)
+        log("timing integer backward only")
+        ms_b = time_calls(lambda: F.bwd(q, k, v, o, lse, do, W, alpha, FIB_BASE, 10000.0, INT, dq=dq, dk=dk, dv=dv,
+                                        dalpha=dal, workspace=ws), args.steps, args.warmup, stream)
+        print(json.dumps({"profiling_aid": "bwd_int", "workload": "long_context_b1h32_n131072_bf16_w12_fib987_alpha1.5",
+                          "ms_per_call": ms_b, "steps": args.steps, "warmup": args.warmup}), flush=True)
+        return
 
     log("timing integer forward")
     ms = time_calls(fwd_int, args.steps, args.warmup, stream)
