@@ -140,13 +140,13 @@ __global__ __launch_bounds__(256) void dense_lse_kernel(const bf16_t* __restrict
 #pragma unroll
     for (int qg = 0; qg < 2; ++qg) {
       if (diag) {
+        // key t kDT + c comes after the query when its tile offset c exceeds lim
+        const int lim = (int)(qi[qg] - (int64_t)t * kDT);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int64_t j = (int64_t)t * kDT + 16 * kb + 4 * g + v;
-            acc[qg][kb][v] = j > qi[qg] ? -INFINITY : acc[qg][kb][v];
-          }
+          for (int v = 0; v < 4; ++v)
+            acc[qg][kb][v] = 16 * kb + 4 * g + v > lim ? -INFINITY : acc[qg][kb][v];
       }
       // raw logits: the scale (> 0) is applied in the exponent, exp2(s * scale_log2 - m)
       float tmax = acc[qg][0][0];
