@@ -461,6 +461,9 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "bytes_per_launch": bytes_per_launch},
         "cpu_baseline": cpu,
+        # each (b, h, i) is one query vector: B*H*N per call (= value); B*N sequence positions
+        "queries_per_s": rows / (ms * 1e-3),
+        "positions_per_s": B * N / (ms * 1e-3),
         "components": components,
     }
     print(json.dumps(out), flush=True)
