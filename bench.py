@@ -336,6 +336,105 @@ def layer_stacks(dev, stream, args, al4, al2, al3):
     return out
 
 
+def sweep(path, dev, stream, reps):
+    """One JSONL record per (workload, base, W, mode, pass, layer): GPU time per call from HIP
+    events around each call, tokens/s (B*H*N per layer), algorithmic GB/s and % of the 8 TB/s
+    peak, and the table size. Each layer has its own N(0, 1) inputs drawn on the device (seeded
+    by the workload recipe), so a 16-layer stack exceeds the 256 MB Infinity Cache and every
+    call reads cold data; the layers are called in turn, `reps` times."""
+    import torch
+
+    import fibonacci_offset_dilated_amd as F
+    from fibonacci_offset_dilated_amd.synthetic import seed_for, uniform_alphas
+    from fibonacci_offset_dilated_amd.workloads import (INT, INTERP, UNIFORM_ALPHA_RANGE, UNIFORM_ALPHA_SEED,
+                                                        WORKLOADS)
+
+    def alpha_for(w, l):
+        if w.schedule == "fixed1":
+            return F.schedule_alpha(F.SCHED_FIXED, l, 16)
+        if w.schedule == "linear":
+            return F.schedule_alpha(F.SCHED_LINEAR, l, 16)
+        if w.schedule == "coprime":
+            return F.schedule_alpha(F.SCHED_COPRIME, l, 16)
+        if w.schedule == "layer15_linear":
+            return F.schedule_alpha(F.SCHED_LINEAR, 15, 16)
+        return uniform_alphas(UNIFORM_ALPHA_SEED, 16, *UNIFORM_ALPHA_RANGE)[l]
+
+    out = open(path, "w")
+    summary = []
+    for w in WORKLOADS:
+        dt = torch.float32 if w.dtype == F.F32 else torch.bfloat16
+        esize = 4 if w.dtype == F.F32 else 2
+        for base_id, base in w.bases:
+            inputs = {}
+            for l in w.layers:
+                g = torch.Generator(device=dev)
+                g.manual_seed(seed_for(w.config, base_id, 0, l))
+                inputs[l] = [torch.randn((w.B, w.H, w.N, D), generator=g, device=dev).to(dt)
+                             for _ in range(4 if w.backward else 3)]
+            for W in w.windows:
+                for mode in (w.mode,) + tuple(w.extra_modes):
+                    passes = ("fwd", "bwd") if w.backward else ("fwd",)
+                    fw = {}
+                    for l in w.layers:
+                        q, k, v = inputs[l][:3]
+                        fw[l] = F.fwd(q, k, v, W, alpha_for(w, l), base, w.theta, mode)
+                    for ps in passes:
+                        ws = None
+                        if ps == "bwd":
+                            ws = torch.empty(F.bwd_workspace_size(w.B, w.H, w.N, D, w.dtype, mode), dtype=torch.uint8,
+                                             device=dev)
+                            grads = [torch.empty_like(inputs[w.layers[0]][0]) for _ in range(3)]
+                            dal = torch.empty(1, dtype=torch.float32, device=dev)
+
+                        def call(l):
+                            q, k, v = inputs[l][:3]
+                            o, lse = fw[l]
+                            if ps == "fwd":
+                                F.fwd(q, k, v, W, alpha_for(w, l), base, w.theta, mode, out=o, lse=lse)
+                            else:
+                                F.bwd(q, k, v, o, lse, inputs[l][3], W, alpha_for(w, l), base, w.theta, mode,
+                                      dq=grads[0], dk=grads[1], dv=grads[2], dalpha=dal, workspace=ws)
+
+                        for _ in range(max(3, -(-20 // len(w.layers)))):  # >= 20 warm-up calls (clocks)
+                            for l in w.layers:
+                                call(l)
+                        ev = {l: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                                  for _ in range(reps)] for l in w.layers}
+                        torch.cuda.synchronize()
+                        for r in range(reps):
+                            for l in w.layers:
+                                ev[l][r][0].record(stream)
+                                call(l)
+                                ev[l][r][1].record(stream)
+                        torch.cuda.synchronize()
+                        per = []
+                        for l in w.layers:
+                            us = 1e3 * sum(a.elapsed_time(b) for a, b in ev[l]) / reps
+                            rows = w.B * w.H * w.N
+                            nbytes = rows * ((4 if ps == "fwd" else 8) * D * esize + 4)
+                            gbs = nbytes / (us * 1e-6) / 1e9
+                            n_tab = len(F.offset_table(alpha_for(w, l), base, W, mode)[0])
+                            rec = {"workload": w.name, "config": w.config, "base": "fibonacci" if base_id == 0 else
+                                   "power_of_two", "W": W, "mode": "integer" if mode == INT else "interpolated",
+                                   "pass": ps, "layer": l, "alpha": float(alpha_for(w, l)), "table_entries": n_tab,
+                                   "us_per_call": round(us, 3), "tokens_per_s": rows / (us * 1e-6),
+                                   "algorithmic_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                                   "dtype": "f32" if w.dtype == F.F32 else "bf16",
+                                   "seed": seed_for(w.config, base_id, 0, l), "reps": reps}
+                            out.write(json.dumps(rec) + "\n")
+                            per.append(us)
+                        line = (f"{w.name} base={base_id} W={W} mode={mode} {ps}: us/call mean {sum(per) / len(per):.1f} "
+                                f"min {min(per):.1f} max {max(per):.1f}; hbm frac mean "
+                                f"{nbytes / (sum(per) / len(per) * 1e-6) / 1e9 / HBM_PEAK_GBS:.3f}")
+                        summary.append(line)
+                        log(line)
+            del inputs, fw
+            torch.cuda.empty_cache()
+    out.close()
+    return summary
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -346,6 +445,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="run one 1 GiB device-to-device copy first (reference for HBM byte counters)")
+    ap.add_argument("--sweep", metavar="JSONL",
+                    help="measurement aid: time every workload's layers, windows, bases, modes and passes "
+                         "(one JSONL record each) instead of the bench line")
     ap.add_argument("--bwd-only", action="store_true",
                     help="profiling aid: one integer forward, then only integer backward calls "
                          "(--warmup untimed, --steps timed); prints their time, not the bench line")
@@ -367,6 +469,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     F.lib()
+    if args.sweep:
+        sweep(args.sweep, dev, torch.cuda.current_stream(), max(3, args.steps // 10))
+        return
     log(f"inputs B={B} H={H} N={N} D={D} bf16 (seeded)")
     (q, k, v, do), arrs = make_inputs(B, H, N, seed_for(5, 0, 12, 15), True, dev)
     o = torch.empty_like(q)
