@@ -453,8 +453,9 @@ def main():
                          "(--warmup untimed, --steps timed); prints their time, not the bench line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (the op shards over "
-              "B*H with no communication; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path. Heads (B*H) are "
+              "independent, so the op would shard over them with no communication, plus one "
+              "d(alpha) all-reduce per layer in the backward. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

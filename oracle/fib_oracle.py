@@ -23,7 +23,7 @@ The dropped-attention-mass diagnostic follows "SSA: Sparse Sparse Attention" (ar
 attention weight that full attention gives to keys the sparse mechanism does not select.
 
 Readings taken where the pages leave a step open (each is the plainest one consistent with
-the rest; the same list is kept with the design notes):
+the rest):
   R1 window = distances 0..W-1 (the query itself included); causal (keys j <= i).
   R2 the elided base list is the 15 distinct Fibonacci numbers 1..987.
   R3 integer mode rounds alpha*f half to even; the product is exact (alpha is the exact value
