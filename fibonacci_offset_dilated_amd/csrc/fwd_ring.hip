@@ -8,8 +8,8 @@
 // a fused path; here both modes run fused in this kernel.
 //
 // Design (gfx950):
-//  * One workgroup per CU (8 waves, two per SIMD to cover latencies; 4 when four interpolated
-//    far entries need registers for eight far rows) sweeps a contiguous segment of one head
+//  * One workgroup per CU (8 waves, two per SIMD to cover latencies) sweeps a contiguous
+//    segment of one head
 //    in steps of 16 queries per wave; wave w owns queries p0 + 16w .. + 15.
 //  * LDS ring of the last kP rows: K rotated by RoPE (bf16) and raw V (bf16). Each row is
 //    loaded from HBM and rotated once, when it enters the ring; the window band and every
@@ -597,44 +597,26 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
   }
 }
 
-// Waves per workgroup and the table split: 8 waves (two per SIMD) where the registers fit
-// 256 per lane, else 4 (interpolated mode with many far entries: their row pairs need twice
-// the registers).
+// Waves per workgroup and the table split: 8 waves (two per SIMD). Every instance fits 256
+// registers per lane at 8 waves (the interpolated far entries hold only their lower rows).
 // With alpha in device memory the counts are upper bounds over the alpha range.
 int plan(const FwdArgs& f, int* n_cov, int* n_far) {
-  auto split = [&](int waves) {
-    if (f.plan != nullptr) {
-      range_counts(f.alpha_lo, f.alpha_hi, f.base, f.n_base, f.W, f.mode, f.N, waves, n_cov, n_far);
-    } else {
-      split_table(f.tab, f.N, waves, n_cov, n_far);
-    }
-  };
-  split(8);
-  if (f.mode == 1 && (*n_far > 3 || (*n_far == 3 && *n_cov > 8))) {
-    split(4);
-    return 4;
+  if (f.plan != nullptr) {
+    range_counts(f.alpha_lo, f.alpha_hi, f.base, f.n_base, f.W, f.mode, f.N, 8, n_cov, n_far);
+  } else {
+    split_table(f.tab, f.N, 8, n_cov, n_far);
   }
   return 8;
 }
 
-// instances that plan() never picks (they would not fit 256 registers at 8 waves)
-template <int MODE, int NC, int NF, int WAVES>
-constexpr bool unused_instance() {
-  return MODE == 1 && WAVES == 8 && (NF > 3 || (NF == 3 && NC > 8));
-}
-
 template <int MODE, int NC, int NF, int WAVES, bool DEV>
 hipError_t launch(const RingArgs& a, unsigned blocks, hipStream_t s) {
-  if constexpr (unused_instance<MODE, NC, NF, WAVES>()) {
-    return hipErrorInvalidValue;
-  } else {
   const size_t smem = sizeof(Smem);
   static std::atomic<uint32_t> lds_set{0};
   hipError_t e = ensure_lds_limit(fwd_ring_kernel<MODE, NC, NF, WAVES, DEV>, lds_set, (int)smem);
   if (e != hipSuccess) return e;
   fwd_ring_kernel<MODE, NC, NF, WAVES, DEV><<<blocks, 64 * WAVES, smem, s>>>(a);
   return hipGetLastError();
-  }
 }
 
 // kernel instance by (covered entries rounded up to 8 or 16, far entries, waves); with alpha
@@ -686,7 +668,7 @@ hipError_t launch_fwd_ring(const FwdArgs& f) {
   a.N = (int)f.N;
   a.W = f.W;
   int n_far;
-  const int waves = plan(f, &a.n_cov, &n_far);
+  const int waves = plan(f, &a.n_cov, &n_far);  // 8
   for (int e = 0; e < kMaxCov; ++e) {
     // slots past the covered prefix get a harmless in-ring distance and weight 0
     a.dist[e] = e < a.n_cov ? f.tab.dist[e] : kMaxBand;
@@ -722,12 +704,10 @@ hipError_t launch_fwd_ring(const FwdArgs& f) {
   a.heads_per_plan = f.heads_per_plan;
   if (f.plan != nullptr) {
     if (f.mode == 0) return launch_mode<0, 8, true>(a, n_far, blocks, f.stream);
-    if (waves == 8) return launch_mode<1, 8, true>(a, n_far, blocks, f.stream);
-    return launch_mode<1, 4, true>(a, n_far, blocks, f.stream);
+    return launch_mode<1, 8, true>(a, n_far, blocks, f.stream);
   }
   if (f.mode == 0) return launch_mode<0, 8>(a, n_far, blocks, f.stream);
-  if (waves == 8) return launch_mode<1, 8>(a, n_far, blocks, f.stream);
-  return launch_mode<1, 4>(a, n_far, blocks, f.stream);
+  return launch_mode<1, 8>(a, n_far, blocks, f.stream);
 }
 
 }  // namespace fib
