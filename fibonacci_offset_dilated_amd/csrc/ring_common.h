@@ -186,9 +186,10 @@ inline int64_t ring_segments(int64_t BH, int64_t tiles) {
 }
 
 // Interpolated far entry: the upper rows (i0w - d + 1 + n) from the lower rows (lane (n, g)
-// holding row i0w - d + n, dims 8g.. and 32 + 8g..; ex: dword l % 32 of row i0w - d + 16). Lane n takes
-// lane n + 1's row (DPP row shift within the 16 lanes of a dim group); lane 15 takes row
-// i0w - d + 16 from the dwords spread over the wave.
+// holding row i0w - d + n, dims 8g.. and 32 + 8g..; ex: dword l % 32 of row i0w - d + 16).
+// Lane n takes lane n + 1's row (DPP row shift within the 16 lanes of a dim group); lane 15
+// takes row i0w - d + 16 from the dwords spread over the wave. Call with every lane of the
+// wave active: both moves read other lanes' registers.
 __device__ __forceinline__ void upper_rows(const uint4* lo, uint32_t ex, int g, uint4* hi) {
   uint32_t w[8] = {lo[0].x, lo[0].y, lo[0].z, lo[0].w, lo[1].x, lo[1].y, lo[1].z, lo[1].w};
   // (empty asm: the moves happen here, not hoisted to where their results would hold
