@@ -268,6 +268,9 @@ def layer_stacks(dev, stream, args, al4, al2, al3):
     from fibonacci_offset_dilated_amd.workloads import BY_CONFIG, FIB_BASE, INT, INTERP
 
     reps = max(5, args.steps // 5)
+    # each timing warms up for 10 calls of its own (a 16-layer call is 0.2-1 ms of work: fewer
+    # leave the clocks ramping and favour whichever variant is timed later)
+    warm = 10
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed_for(4, 0, 12, 16))
     L = 16
@@ -283,9 +286,9 @@ def layer_stacks(dev, stream, args, al4, al2, al3):
     lse = torch.empty((L, w4.B, w4.H, w4.N), dtype=torch.float32, device=dev)
     a4 = np.array(al4, dtype=np.float32)
     us_f = time_calls(lambda: F.fwd_layers(q, k, v, 12, a4, FIB_BASE, 10000.0, INT, out=o, lse=lse, plan=plan),
-                      reps, 2, stream) * 1e3 / L
+                      reps, warm, stream) * 1e3 / L
     us_s = time_calls(lambda: [F.fwd(q[l], k[l], v[l], 12, a4[l], FIB_BASE, 10000.0, INT, out=o[l], lse=lse[l])
-                               for l in range(L)], reps, 2, stream) * 1e3 / L
+                               for l in range(L)], reps, warm, stream) * 1e3 / L
     rows4 = w4.B * w4.H * w4.N
     out["c4_stack16_fwd_int_us_per_layer"] = round(us_f, 2)
     out["c4_stack16_fwd_int_hbm_frac"] = round(rows4 * (4 * D * 2 + 4) / (us_f * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
@@ -299,21 +302,21 @@ def layer_stacks(dev, stream, args, al4, al2, al3):
     a2 = np.array(al2, dtype=np.float32)
     a3 = np.asarray(al3, dtype=np.float32)
     us_fi = time_calls(lambda: F.fwd_layers(q, k, v, 12, a2, FIB_BASE, 10000.0, INT, out=o, lse=lse, plan=plan),
-                       reps, 2, stream) * 1e3 / L
+                       reps, warm, stream) * 1e3 / L
     us_si = time_calls(lambda: [F.fwd(q[l], k[l], v[l], 12, a2[l], FIB_BASE, 10000.0, INT, out=o[l], lse=lse[l])
-                                for l in range(L)], reps, 2, stream) * 1e3 / L
+                                for l in range(L)], reps, warm, stream) * 1e3 / L
     us_fp = time_calls(lambda: F.fwd_layers(q, k, v, 12, a3, FIB_BASE, 10000.0, INTERP, out=o, lse=lse, plan=plan),
-                       reps, 2, stream) * 1e3 / L
+                       reps, warm, stream) * 1e3 / L
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     dal = torch.empty(L, dtype=torch.float32, device=dev)
     ws = torch.empty(F.bwd_workspace_size(L * w2.B, w2.H, w2.N, D, F.BF16, INTERP), dtype=torch.uint8, device=dev)
     us_fb = time_calls(lambda: F.bwd_layers(q, k, v, o, lse, do, 12, a3, FIB_BASE, 10000.0, INTERP, dq=dq, dk=dk,
-                                            dv=dv, dalpha=dal, workspace=ws, plan=plan), reps, 2, stream) * 1e3 / L
+                                            dv=dv, dalpha=dal, workspace=ws, plan=plan), reps, warm, stream) * 1e3 / L
     ws1 = torch.empty(F.bwd_workspace_size(w2.B, w2.H, w2.N, D, F.BF16, INTERP), dtype=torch.uint8, device=dev)
     dal1 = torch.empty(1, dtype=torch.float32, device=dev)
     us_sb = time_calls(lambda: [F.bwd(q[l], k[l], v[l], o[l], lse[l], do[l], 12, a3[l], FIB_BASE, 10000.0, INTERP,
                                       dq=dq[l], dk=dk[l], dv=dv[l], dalpha=dal1, workspace=ws1) for l in range(L)],
-                       reps, 2, stream) * 1e3 / L
+                       reps, warm, stream) * 1e3 / L
     rows2 = w2.B * w2.H * w2.N
     out["b8h8n1024_stack16_fwd_int_us_per_layer"] = round(us_fi, 2)
     out["b8h8n1024_stack16_fwd_int_hbm_frac"] = round(rows2 * (4 * D * 2 + 4) / (us_fi * 1e-6) / 1e9 / HBM_PEAK_GBS,
@@ -331,7 +334,7 @@ def layer_stacks(dev, stream, args, al4, al2, al3):
     ld = torch.empty((L, 8, 8), dtype=torch.float32, device=dev)
     for mode, a, name in ((INT, a2, "int"), (INTERP, a3, "interp")):
         us_d = time_calls(lambda: F.decode_layers(qd, kc, vc, 12, a, FIB_BASE, 10000.0, mode, out=od, lse=ld,
-                                                  plan=plan), reps, 2, stream) * 1e3 / L
+                                                  plan=plan), reps, warm, stream) * 1e3 / L
         out[f"decode_b8h8n4096_stack16_{name}_us_per_layer"] = round(us_d, 2)
     return out
 
