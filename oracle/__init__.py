@@ -5,8 +5,9 @@ bench.py may import or run anything in this package. The HIP library and its Pyt
 never import it, and the two share no code.
 
 Parity status: every function in fib_oracle is pinned by tests/test_oracle_*.py against
-values fixed independently of it (brute-force membership, closed forms, library special
-cases, hand-derived constants, finite differences and torch autograd); none is unpinned.
+values fixed independently of it: brute-force membership and brute-force masks (index_sets
+cell by cell in both modes), closed forms, library special cases, hand-derived constants,
+finite differences and torch autograd.
 """
 from .fib_oracle import *  # noqa: F401,F403
 from .fib_oracle import __all__  # noqa: F401

@@ -55,7 +55,7 @@ __all__ = [
     "INT", "INTERP",
     "exact_alpha", "f32_nearest", "schedule_linear", "schedule_coprime",
     "int_offsets", "interp_entries", "rope_omega", "rope", "rope_inverse",
-    "attended", "index_sets", "forward", "backward", "forward_rows",
+    "index_sets", "forward", "backward", "forward_rows",
     "dense_causal_lse", "dropped_mass",
 ]
 
@@ -195,29 +195,8 @@ def rope_inverse(x: np.ndarray, theta: float, positions=None) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------------------
-# attended set of one query
+# attended rows of every query
 # ---------------------------------------------------------------------------------------
-
-def attended(i: int, W: int, alpha, base, mode: int):
-    """The attended set of query i, as a list of (lo, hi, w) virtual keys.
-
-    Window keys and integer offsets are (j, j, 0): key row j with weight 1.
-    Interpolated offsets are (lo, lo+1, w): (1-w)*row lo + w*row hi.
-    Window first (distances 0..W-1 that are >= 0), then the offsets in table order.
-    """
-    keys = [(i - s, i - s, Fraction(0)) for s in range(min(W, i + 1))]
-    if mode == INT:
-        for r in int_offsets(alpha, base, W):
-            if r <= i:
-                keys.append((i - r, i - r, Fraction(0)))
-    elif mode == INTERP:
-        for f, c, w in interp_entries(alpha, base, W):
-            if c <= i:
-                keys.append((i - c, i - c + 1, w))
-    else:
-        raise ValueError("mode must be INT or INTERP")
-    return keys
-
 
 def index_sets(N: int, W: int, alpha, base, mode: int) -> np.ndarray:
     """Per-query attended rows as an int32 [N, W + n_entries] array, -1 where absent.

@@ -143,3 +143,84 @@ def test_index_set_cardinality_closed_form():
                 n = int((ids[i] >= 0).sum())
                 assert n == min(W, i + 1) + sum(1 for r in R if r <= i)
                 assert len(set(ids[i][ids[i] >= 0].tolist())) == n
+
+
+# ---- index_sets, cell by cell, against sets built without the oracle ----------------------
+
+def _int_offsets_brute(alpha, base, W):
+    """Every integer distance that int_member accepts, ascending (searched up to beyond the
+    largest product alpha * f, where no rounding can reach)."""
+    top = int(float(np.float32(alpha)) * max(base)) + 2
+    return [d for d in range(W, top + 1) if int_member(d, alpha, base, W)]
+
+
+def _expected_int_rows(N, W, alpha, base):
+    """[N, W + |R|]: window key i - s in column s (s <= i), then the keys at the brute-force
+    distances in ascending distance order (each present when the distance is <= i)."""
+    offs = _int_offsets_brute(alpha, base, W)
+    out = -np.ones((N, W + len(offs)), dtype=np.int64)
+    for i in range(N):
+        win = list(range(i, max(-1, i - W), -1))  # keys i, i - 1, ... down to i - W + 1 and >= 0
+        out[i, :len(win)] = win
+        for e, d in enumerate(offs):
+            if d <= i:
+                out[i, W + e] = i - d
+    return out
+
+
+def _expected_interp_rows(N, W, alpha, base):
+    """[N, W + n]: window keys as above, then per kept base entry (base order) the lower row
+    of its interpolated pair, i - c with c the smallest integer >= alpha f (interp_virtuals'
+    lo distance), present when c <= i."""
+    virt = interp_virtuals(alpha, base, W)
+    out = -np.ones((N, W + len(virt)), dtype=np.int64)
+    for i in range(N):
+        win = list(range(i, max(-1, i - W), -1))  # keys i, i - 1, ... down to i - W + 1 and >= 0
+        out[i, :len(win)] = win
+        for e, (_, c, c_hi, _) in enumerate(virt):
+            assert c_hi == c - 1  # the upper row is the next row, i - c + 1
+            if c <= i:
+                out[i, W + e] = i - c
+    return out
+
+
+INDEX_CASES = [
+    # (N, W, alpha, base): ties at 1.5 (55 -> 82.5, 987 -> 1480.5), W = 1, a window wider
+    # than the sequence start, the power-of-two base, alpha at both ends of the range
+    (1600, 12, np.float32(1.5), FIB_BASE),
+    (400, 1, np.float32(1.0), FIB_BASE),
+    (300, 12, O.schedule_linear(16)[5], FIB_BASE),
+    (700, 6, np.float32(0.5), FIB_BASE),
+    (2100, 12, np.float32(0.93), POW2_BASE),
+    (40, 16, np.float32(1.37), FIB_BASE),
+    (1, 12, np.float32(1.0), FIB_BASE),
+]
+
+
+@pytest.mark.parametrize("case", INDEX_CASES, ids=[f"N{c[0]}W{c[1]}a{float(c[2]):.4g}n{len(c[3])}" for c in INDEX_CASES])
+def test_index_sets_int_cell_by_cell(case):
+    N, W, a, base = case
+    got = O.index_sets(N, W, a, base, O.INT)
+    exp = _expected_int_rows(N, W, a, base)
+    assert got.shape == exp.shape
+    assert np.array_equal(got, exp)
+
+
+@pytest.mark.parametrize("case", INDEX_CASES, ids=[f"N{c[0]}W{c[1]}a{float(c[2]):.4g}n{len(c[3])}" for c in INDEX_CASES])
+def test_index_sets_interp_cell_by_cell(case):
+    N, W, a, base = case
+    got = O.index_sets(N, W, a, base, O.INTERP)
+    exp = _expected_interp_rows(N, W, a, base)
+    assert got.shape == exp.shape
+    assert np.array_equal(got, exp)
+
+
+def test_index_sets_int_rows_are_the_brute_force_mask():
+    """Integer mode: the set of rows in each query's row of index_sets equals the row of the
+    brute-force mask M[i, j] = 0 <= j <= i and (i - j < W or i - j attended)."""
+    from dense_reference import int_mask
+    for N, W, a in ((260, 12, np.float32(1.3)), (150, 6, np.float32(0.5)), (90, 1, np.float32(1.0))):
+        ids = O.index_sets(N, W, a, FIB_BASE, O.INT)
+        M = int_mask(N, W, a, FIB_BASE)
+        for i in range(N):
+            assert set(ids[i][ids[i] >= 0].tolist()) == set(np.nonzero(M[i])[0].tolist())
