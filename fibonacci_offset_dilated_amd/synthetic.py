@@ -14,6 +14,14 @@ so seeded Gaussian activations of the pages' shapes stand in for them):
 * seed = config * 10**6 + base_id * 10**5 + window * 10**3 + layer.
 * Per-layer alphas of the learned-dilation workload are drawn
   ``default_rng(seed).uniform(lo, hi, n_layers)`` and rounded to fp32.
+
+Two structured input sets serve as probes (values exact in bf16):
+
+* ``staircase_inputs``: Q, K ~ N(0, 1); V ~ N(0, 1) except column 0, which holds
+  (j mod 64) / 8 at position j; dO = the unit vector of column 0 at every position. The
+  per-query contributions to d(alpha) then share one sign instead of cancelling.
+* ``position_code_v``: V[j] holds binary codes of the position j (its bits and the bits of
+  two odd multiples of j, modulo 2^bits), and a constant 1.
 """
 from __future__ import annotations
 
@@ -26,6 +34,8 @@ __all__ = [
     "bf16_bits_to_f32",
     "uniform_alphas",
     "random_alpha_grid",
+    "staircase_inputs",
+    "position_code_v",
 ]
 
 
@@ -76,3 +86,36 @@ def uniform_alphas(seed: int, n: int, lo: float, hi: float) -> np.ndarray:
 def random_alpha_grid(seed: int, n: int, lo: float = 0.5, hi: float = 1.5) -> np.ndarray:
     """n random fp32 alphas in [lo, hi) for table sweeps."""
     return np.random.default_rng(seed).uniform(lo, hi, n).astype(np.float32)
+
+
+def staircase_inputs(seed: int, shape):
+    """Q, K, V, dO as fp32 arrays of ``shape`` [.., N, D]: Q, K and V drawn N(0, 1) from one
+    generator (in that order); V[..., j, 0] = (j mod 64) / 8; dO = 1 in column 0, else 0."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    N = shape[-2]
+    v[..., :, 0] = (np.arange(N) % 64).astype(np.float32) / 8.0
+    do = np.zeros(shape, dtype=np.float32)
+    do[..., :, 0] = 1.0
+    return q, k, v, do
+
+
+# odd multipliers of the position codes (any odd number permutes the residues mod 2^bits)
+CODE_MULT = (1, 40503, 51749)
+
+
+def position_code_v(N: int, D: int = 64, bits: int = 17) -> np.ndarray:
+    """[N, D] fp32 (0/1 values): column c * bits + b (c < 3, b < bits) holds bit b of
+    (j * CODE_MULT[c]) mod 2^bits for position j; the last column is 1; other columns 0."""
+    if 3 * bits + 1 > D:
+        raise ValueError("D too small for the codes")
+    j = np.arange(N, dtype=np.int64)
+    v = np.zeros((N, D), dtype=np.float32)
+    for c, m in enumerate(CODE_MULT):
+        code = (j * m) & ((1 << bits) - 1)
+        for b in range(bits):
+            v[:, c * bits + b] = (code >> b) & 1
+    v[:, D - 1] = 1.0
+    return v

@@ -56,7 +56,7 @@ __all__ = [
     "exact_alpha", "f32_nearest", "schedule_linear", "schedule_coprime",
     "int_offsets", "interp_entries", "rope_omega", "rope", "rope_inverse",
     "index_sets", "forward", "backward", "forward_rows",
-    "dense_causal_lse", "dropped_mass",
+    "dense_causal_lse", "dropped_mass", "DalphaScale",
 ]
 
 
@@ -299,6 +299,13 @@ def _head_backward(qh, kh, vh, doh, W, alpha, base, theta, mode, rows=None):
       dalpha = sum_ik -f_k [dS_ik <q^_i, k^_hi - k^_lo>/sqrt(D) + P_ik <dO_i, v_hi - v_lo>].
     Rotations are undone at the end: dQ_i = R_i^T dq^_i, dK_j = R_j^T dk^_j.
     ``rows`` restricts the queries whose contributions are summed (default: all).
+
+    Besides dalpha, four sums over queries i describe its size and conditioning (they enter
+    no result): with t_i = sum_k -f_k g_ik the query's contribution,
+      sum |t_i|, sum t_i^2, sum a_i^2 with a_i = sum_k f_k (|dS_ik ds_ik| + P_ik |ddp_ik|)
+      (ds = s_hi - s_lo, ddp = dp_hi - dp_lo), and sum b_i^2 with
+      b_i = sum_k f_k P_ik ((|dP_ik| + |Delta_i|)(|s_hi| + |s_lo|) + |dp_hi| + |dp_lo|),
+    the magnitudes of the parts whose rounding errors make up the error of t_i.
     """
     N, D = qh.shape
     qr = rope(qh, theta)
@@ -312,7 +319,7 @@ def _head_backward(qh, kh, vh, doh, W, alpha, base, theta, mode, rows=None):
     dkr = np.zeros((N, D))
     dv = np.zeros((N, D))
     dalpha = 0.0
-    dalpha_abs = 0.0  # sum over queries of |query's contribution to dalpha|
+    sums = np.zeros(4)  # sum |t_i|, sum t_i^2, sum a_i^2, sum b_i^2 (see above)
     S = W + len(dist)
     fk = np.concatenate([np.zeros(W), fs])
     step = _chunk(S, D)
@@ -351,10 +358,18 @@ def _head_backward(qh, kh, vh, doh, W, alpha, base, theta, mode, rows=None):
             g = ds * dk_diff + p * dv_diff
             per_query = np.sum(np.where(valid, -fk[None, :] * g, 0.0), axis=1)
             dalpha += float(np.sum(per_query))
-            dalpha_abs += float(np.sum(np.abs(per_query)))
+            a_i = np.sum(np.where(valid, fk[None, :] * (np.abs(ds * dk_diff) + p * np.abs(dv_diff)), 0.0), axis=1)
+            s_lo = np.einsum("nd,nsd->ns", q, kr[lo]) * scale
+            s_hi = np.einsum("nd,nsd->ns", q, kr[hi]) * scale
+            dp_lo = np.einsum("nd,nsd->ns", do, vh[lo])
+            dp_hi = np.einsum("nd,nsd->ns", do, vh[hi])
+            b_terms = p * ((np.abs(dp) + np.abs(delta)[:, None]) * (np.abs(s_hi) + np.abs(s_lo))
+                           + np.abs(dp_hi) + np.abs(dp_lo))
+            b_i = np.sum(np.where(valid, fk[None, :] * b_terms, 0.0), axis=1)
+            sums += [np.sum(np.abs(per_query)), np.sum(per_query ** 2), np.sum(a_i ** 2), np.sum(b_i ** 2)]
     dq = rope_inverse(dqr, theta)
     dk = rope_inverse(dkr, theta)
-    return dq, dk, dv, dalpha, dalpha_abs
+    return dq, dk, dv, dalpha, sums
 
 
 def _bh_iter(x):
@@ -410,12 +425,27 @@ def forward_rows(qh, kh, vh, rows, W, alpha, base, theta=10000.0, mode=INT):
     return _head_forward(qh, kh, vh, W, alpha, base, theta, mode, rows=rows)
 
 
-def backward(q, k, v, dout, W, alpha, base, theta=10000.0, mode=INT, workers=1, rows=None, return_abs=False):
+class DalphaScale(tuple):
+    """Size of dalpha's summands over all queries (see _head_backward): sum_abs = sum |t_i|,
+    rss_query = sqrt(sum t_i^2), rss_entry = sqrt(sum a_i^2), rss_wide = sqrt(sum b_i^2)."""
+
+    __slots__ = ()
+
+    def __new__(cls, sums):
+        return tuple.__new__(cls, (float(sums[0]), math.sqrt(sums[1]), math.sqrt(sums[2]), math.sqrt(sums[3])))
+
+    sum_abs = property(lambda self: self[0])
+    rss_query = property(lambda self: self[1])
+    rss_entry = property(lambda self: self[2])
+    rss_wide = property(lambda self: self[3])
+
+
+def backward(q, k, v, dout, W, alpha, base, theta=10000.0, mode=INT, workers=1, rows=None, return_scale=False):
     """dQ, dK, dV [B,H,N,D] (fp64, w.r.t. the un-rotated inputs) and dalpha (float).
 
-    With ``return_abs`` a fifth value is returned: the sum over queries of the absolute value
-    of each query's contribution to dalpha (the scale against which the summed dalpha can be
-    compared when the contributions cancel).
+    With ``return_scale`` a fifth value is returned, a DalphaScale: the sizes of the per-query
+    contributions to dalpha and of their parts (all zero in integer mode), against which an
+    approximate dalpha's error can be judged when the contributions cancel.
     """
     q, k, v, dout = (np.asarray(t, dtype=np.float64) for t in (q, k, v, dout))
     B, H, N, D = q.shape
@@ -423,7 +453,7 @@ def backward(q, k, v, dout, W, alpha, base, theta=10000.0, mode=INT, workers=1, 
     dk = np.zeros_like(q)
     dv = np.zeros_like(q)
     dalpha = 0.0
-    dalpha_abs = 0.0
+    sums = np.zeros(4)
     jobs = [(q[b, h], k[b, h], v[b, h], dout[b, h], W, alpha, base, theta, mode, rows)
             for b, h in _bh_iter(q)]
     nw = _workers(workers)
@@ -432,14 +462,14 @@ def backward(q, k, v, dout, W, alpha, base, theta=10000.0, mode=INT, workers=1, 
             res = list(ex.map(_bwd_task, jobs))
     else:
         res = [_bwd_task(j) for j in jobs]
-    for (b, h), (a, bb, c, da, dabs) in zip(_bh_iter(q), res):
+    for (b, h), (a, bb, c, da, hs) in zip(_bh_iter(q), res):
         dq[b, h] = a
         dk[b, h] = bb
         dv[b, h] = c
         dalpha += da
-        dalpha_abs += dabs
-    if return_abs:
-        return dq, dk, dv, dalpha, dalpha_abs
+        sums += hs
+    if return_scale:
+        return dq, dk, dv, dalpha, DalphaScale(sums)
     return dq, dk, dv, dalpha
 
 

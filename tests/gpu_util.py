@@ -15,10 +15,35 @@ TOL = {F32: 1e-4, BF16: 2e-2}
 # bound on dQ, dK, dV is the flat bound plus one ulp of the reference value:
 #   |got - ref| <= TOL + REL_ULP * |ref|   (REL_ULP = 2^-7 for bf16, 2^-23 for fp32)
 REL_ULP = {F32: 2.0 ** -23, BF16: 2.0 ** -7}
-# bound on dalpha, relative to the sum over queries of |query's contribution| (the oracle's
-# dalpha_abs): dalpha is a sum of per-query terms that can cancel, and each term carries the
-# relative error of the forward's logits; without cancellation this is a plain relative bound
-TOL_DALPHA = {F32: 1e-4, BF16: 1e-2}
+# bound on dalpha. dalpha = sum_i t_i over queries, and t_i = sum over the query's table
+# entries of parts f dS (s_hi - s_lo) and f P (dp_hi - dp_lo). The computed parts carry a few
+# rounding errors of the arithmetic's unit relative to their own size (bf16 operands: 2^-8;
+# fp32 arithmetic: 2^-24 per operation, a few dozen per 64-term dot product, 2^-20), so the
+# error of t_i is a few units times a_i = sum_k |parts| (oracle DalphaScale, rss_entry =
+# sqrt(sum a_i^2)). Roundings to nearest even are unbiased and those of different queries
+# independent, so the error of the sum grows like sqrt(sum a_i^2), not like sum a_i:
+#   |got - ref| <= C[dtype] * rss_entry + 2^-18 * sum_i |t_i|
+# The second term bounds the fp32 accumulation of the per-query terms (at most 64 terms per
+# running sum before a fixed-order tree in the kernels: 64 * 2^-24 = 2^-18 relative to the
+# sum of the magnitudes).
+DALPHA_C = {F32: 2.5 * 2.0 ** -20, BF16: 2.5 * 2.0 ** -8}
+DALPHA_ACC = 2.0 ** -18
+
+
+def dalpha_bound(scale, dtype: int, factor: float = 1.0) -> float:
+    """Bound on |dalpha_gpu - dalpha_ref| for the oracle's DalphaScale ``scale``; ``factor``
+    scales every summand (a chain-rule factor applied to dalpha, e.g. d alpha / d theta)."""
+    return factor * (DALPHA_C[dtype] * scale.rss_entry + DALPHA_ACC * scale.sum_abs)
+
+
+def dalpha_check(got: float, ref: float, scale, dtype: int, factor: float = 1.0, label: str = "dalpha") -> None:
+    """Asserts the dalpha bound; prints the error relative to |ref| and to the bound."""
+    err = abs(float(got) - float(ref))
+    bound = dalpha_bound(scale, dtype, factor)
+    say(f"  {label} {float(got):.7g} vs {float(ref):.7g}: |err|/|ref| {err / max(abs(ref), 1e-30):.2e}, "
+        f"|err|/bound {err / max(bound, 1e-30):.3f}, bound/|ref| {bound / max(abs(ref), 1e-30):.2e}, "
+        f"|err|/(2^-8 rss_entry) {err / max(2.0 ** -8 * factor * scale.rss_entry, 1e-30):.3f}")
+    assert err <= bound, (got, ref, bound)
 
 
 def say(*a):

@@ -1,9 +1,11 @@
 """GPU parity of the backward pass (dQ, dK, dV, dalpha) against the CPU oracle, via the C ABI.
 
 Bounds: |error| on dQ, dK, dV within 1e-4 (fp32) / 2e-2 (bf16) plus one ulp of the input
-dtype at the reference value (see gpu_util.grad_excess); |error| on dalpha within 1e-4 (fp32)
-/ 1e-2 (bf16) times the sum over queries of |each query's contribution| (gpu_util.TOL_DALPHA). The GPU uses its own bf16 O (for Delta) and fp32 LSE
-from the forward, as a training step would; the oracle computes exact gradients.
+dtype at the reference value (see gpu_util.grad_excess); |error| on dalpha within the bound
+derived from the rounding of its per-query parts (gpu_util.dalpha_bound), and, where the
+per-query contributions do not cancel, within 2e-2 of |dalpha|. The GPU uses its own bf16 O
+(for Delta) and fp32 LSE from the forward, as a training step would; the oracle computes exact
+gradients.
 """
 import os
 
@@ -16,7 +18,7 @@ import oracle as O
 from fibonacci_offset_dilated_amd.synthetic import seed_for, uniform_alphas
 from fibonacci_offset_dilated_amd.workloads import (BF16, BY_CONFIG, F32, FIB_BASE, INT, INTERP, POW2_BASE,
                                                     UNIFORM_ALPHA_RANGE, UNIFORM_ALPHA_SEED)
-from gpu_util import TOL, TOL_DALPHA, grad_excess, host, inputs, maxabs, say
+from gpu_util import TOL, dalpha_check, grad_excess, host, inputs, maxabs, say
 
 pytestmark = pytest.mark.gpu
 WORKERS = min(16, len(os.sched_getaffinity(0)))
@@ -33,18 +35,17 @@ def gpu_grads(qkvd, W, alpha, base, mode):
 def check(qkvd, W, alpha, base, mode, dtype):
     (_, q64), (_, k64), (_, v64), (_, d64) = qkvd
     dq, dk, dv, da = gpu_grads(qkvd, W, alpha, base, mode)
-    rq, rk, rv, ra, rabs = O.backward(q64, k64, v64, d64, W, alpha, base, 10000.0, mode, workers=WORKERS,
-                                      return_abs=True)
+    rq, rk, rv, ra, rsc = O.backward(q64, k64, v64, d64, W, alpha, base, 10000.0, mode, workers=WORKERS,
+                                     return_scale=True)
     eq, ek, ev = grad_excess(host(dq), rq, dtype), grad_excess(host(dk), rk, dtype), grad_excess(host(dv), rv, dtype)
     got_a = float(da.item())
+    say(f"  dQ {eq:.2e} dK {ek:.2e} dV {ev:.2e}")
+    assert max(eq, ek, ev) <= TOL[dtype], (eq, ek, ev)
     if mode == INT:
         assert got_a == 0.0
-        ea = 0.0
     else:
-        ea = abs(got_a - ra) / max(rabs, 1e-30)
-    say(f"  dQ {eq:.2e} dK {ek:.2e} dV {ev:.2e} dalpha {got_a:.6g} vs {ra:.6g} (scale {rabs:.6g}) err {ea:.2e}")
-    assert max(eq, ek, ev) <= TOL[dtype], (eq, ek, ev)
-    assert ea <= TOL_DALPHA[dtype]
+        dalpha_check(got_a, ra, rsc, dtype)
+    return got_a, ra
 
 
 @pytest.mark.parametrize("layer", range(16))
@@ -142,11 +143,11 @@ def test_long_context_backward_sampled(long_inputs, mode):
         sub = [t[:, hs].contiguous() for t, _ in long_inputs]
         o4, l4 = F.fwd(sub[0], sub[1], sub[2], 12, a, FIB_BASE, 10000.0, mode)
         _, _, _, da4 = F.bwd(sub[0], sub[1], sub[2], o4, l4, sub[3], 12, a, FIB_BASE, 10000.0, mode)
-        _, _, _, ra, rabs = O.backward(q64[:, hs], k64[:, hs], v64[:, hs], d64[:, hs], 12, a, FIB_BASE, 10000.0,
-                                       mode, workers=WORKERS, return_abs=True)
-        rel = abs(float(da4.item()) - ra) / rabs
-        say(f"  dalpha(4 heads) {float(da4.item()):.6g} vs {ra:.6g} (scale {rabs:.6g}) err {rel:.2e}")
-        assert rel <= TOL_DALPHA[BF16]
+        _, _, _, ra, rsc = O.backward(q64[:, hs], k64[:, hs], v64[:, hs], d64[:, hs], 12, a, FIB_BASE, 10000.0,
+                                      mode, workers=WORKERS, return_scale=True)
+        dalpha_check(float(da4.item()), ra, rsc, BF16, label="dalpha(4 heads)")
+        # the sum does not cancel here: also within 2e-2 of |dalpha|
+        assert abs(float(da4.item()) - ra) <= 2e-2 * abs(ra)
 
 
 def test_backward_deterministic():
@@ -195,3 +196,20 @@ def test_dalpha_output_is_overwritten(mode):
         assert np.all(np.isfinite(got_l))
         # the stack may split a layer's table differently from the single call (fp32 order)
         assert np.allclose(got_l, ref_l, rtol=1e-2, atol=1e-2 * np.abs(ref_l).max()), (got_l, ref_l)
+
+
+STAIR = [(2, 4, 2048, 1.0417), (1, 2, 3000, 1.37), (1, 1, 20000, 1.5)]
+
+
+@pytest.mark.parametrize("case", STAIR, ids=[f"B{c[0]}H{c[1]}N{c[2]}a{c[3]}" for c in STAIR])
+def test_dalpha_without_cancellation(case):
+    """Staircase probe (synthetic.staircase_inputs): the per-query contributions to dalpha
+    share one sign, so the bound is far below |dalpha|; dalpha must also be within 2e-2 of
+    |dalpha| (bf16, W 12, interpolated offsets, ring kernels)."""
+    from fibonacci_offset_dilated_amd.synthetic import staircase_inputs
+    from gpu_util import to_device
+    B, H, N, a = case
+    say("dalpha staircase", case)
+    qkvd = [to_device(x, BF16) for x in staircase_inputs(77, (B, H, N, 64))]
+    got, ref = check(qkvd, 12, np.float32(a), FIB_BASE, INTERP, BF16)
+    assert abs(got - ref) <= 2e-2 * abs(ref)

@@ -136,3 +136,38 @@ def test_graph_capture_device_alpha_updates():
         g.replay()
         torch.cuda.synchronize()
         assert _same(gb[:6], refs[s][:6]), f"replay {rep} (alpha {alphas[s]})"
+
+
+@pytest.mark.parametrize("mode", [INT, INTERP], ids=["int", "interp"])
+def test_explicit_stream_binding_allocations(mode):
+    """Explicit `stream` argument with every buffer left to the binding (outputs, backward
+    workspace, device-alpha plan): while the side stream's kernels may still run, the default
+    stream allocates and overwrites memory of the same sizes. The binding allocates on the
+    side stream, so those blocks are not handed out again before the side stream's work
+    ends, and the results equal a default-stream call bit for bit."""
+    say("explicit stream, binding-allocated buffers", mode)
+    (q, _), (k, _), (v, _), (do, _) = inputs(4601, (B, H, N, 64), BF16, with_dout=True)
+    ref_o, ref_lse = F.fwd(q, k, v, W, ALPHA, FIB_BASE, 10000.0, mode)
+    ref_g = F.bwd(q, k, v, ref_o, ref_lse, do, W, ALPHA, FIB_BASE, 10000.0, mode)
+    a_dev = torch.tensor([ALPHA], dtype=torch.float32, device=q.device)
+    ref_dev = F.fwd_dev(q, k, v, W, a_dev, (0.5, 1.5), FIB_BASE, 10000.0, mode)
+    ref_gdev = F.bwd_dev(q, k, v, ref_dev[0], ref_dev[1], do, W, a_dev, (0.5, 1.5), FIB_BASE, 10000.0, mode)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    ws_bytes = F.bwd_workspace_size(B, H, N, 64, F.BF16, mode)
+    for rep in range(3):
+        side.wait_stream(torch.cuda.current_stream())
+        o, lse = F.fwd(q, k, v, W, ALPHA, FIB_BASE, 10000.0, mode, stream=side)
+        g = F.bwd(q, k, v, o, lse, do, W, ALPHA, FIB_BASE, 10000.0, mode, stream=side)
+        od, ld = F.fwd_dev(q, k, v, W, a_dev, (0.5, 1.5), FIB_BASE, 10000.0, mode, stream=side)
+        gd = F.bwd_dev(q, k, v, od, ld, do, W, a_dev, (0.5, 1.5), FIB_BASE, 10000.0, mode, stream=side)
+        # the default stream grabs and scribbles over memory of the sizes just released
+        junk = [torch.full((max(ws_bytes, 16),), 0xAB, dtype=torch.uint8, device=q.device),
+                torch.full((F.plan_bytes(),), 0xCD, dtype=torch.uint8, device=q.device),
+                torch.full_like(q, float("nan")), torch.full_like(ref_lse, float("nan"))]
+        side.synchronize()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(lse, ref_lse), rep
+        assert _same(g[:3], ref_g[:3]) and (mode == INT or torch.equal(g[3], ref_g[3])), rep
+        assert torch.equal(od, ref_dev[0]) and _same(gd[:3], ref_gdev[:3]), rep
+        del junk
