@@ -202,6 +202,23 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on_stream(fn):
+    """Runs a binding call with `stream` (when given) as torch's current stream, so that every
+    tensor the binding allocates (outputs, workspace, plan, temporaries) belongs to that
+    stream in torch's caching allocator: a temporary dropped on return is then reused only by
+    later work on the same stream, never while the call's kernels may still use it."""
+    import functools
+
+    @functools.wraps(fn)
+    def call(*args, stream=None, **kw):
+        if stream is None:
+            return fn(*args, stream=None, **kw)
+        with _torch().cuda.stream(stream):
+            return fn(*args, stream=stream, **kw)
+
+    return call
+
+
 def _check_qkv(*ts):
     Tensor = _torch().Tensor
     ref = ts[0]
@@ -223,6 +240,7 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
+@_on_stream
 def fwd(q, k, v, W: int, alpha, base: Sequence[int], theta: float = 10000.0, mode: int = INT,
         out=None, lse=None, with_lse: bool = True, stream=None):
     """Sparse attention forward on the current stream; returns (O, LSE or None)."""
@@ -243,6 +261,7 @@ def fwd(q, k, v, W: int, alpha, base: Sequence[int], theta: float = 10000.0, mod
     return out, lse
 
 
+@_on_stream
 def decode(q, k_cache, v_cache, W: int, alpha, base: Sequence[int], theta: float = 10000.0, mode: int = INT,
            out=None, lse=None, with_lse: bool = True, stream=None):
     """One decode step: q [B, H, D] at position N - 1 of the caches [B, H, N, D]; returns
@@ -291,6 +310,7 @@ def _plan_buffer(plan, device):
     return plan
 
 
+@_on_stream
 def fwd_dev(q, k, v, W: int, alpha, alpha_range, base: Sequence[int], theta: float = 10000.0, mode: int = INT,
             out=None, lse=None, with_lse: bool = True, plan=None, stream=None):
     """Forward with alpha a one-element float32 device tensor (no host copy of alpha);
@@ -316,6 +336,7 @@ def fwd_dev(q, k, v, W: int, alpha, alpha_range, base: Sequence[int], theta: flo
     return out, lse
 
 
+@_on_stream
 def bwd_dev(q, k, v, o, lse, dout, W: int, alpha, alpha_range, base: Sequence[int], theta: float = 10000.0,
             mode: int = INT, dq=None, dk=None, dv=None, dalpha=None, workspace=None, want_dalpha: bool = True,
             plan=None, stream=None):
@@ -346,6 +367,7 @@ def bwd_dev(q, k, v, o, lse, dout, W: int, alpha, alpha_range, base: Sequence[in
     return dq, dk, dv, dalpha
 
 
+@_on_stream
 def decode_dev(q, k_cache, v_cache, W: int, alpha, alpha_range, base: Sequence[int], theta: float = 10000.0,
                mode: int = INT, out=None, lse=None, with_lse: bool = True, plan=None, stream=None):
     """Decode step with alpha in device memory (see fwd_dev and decode)."""
@@ -417,6 +439,7 @@ def _layers_plan(plan, L, device):
     return plan
 
 
+@_on_stream
 def fwd_layers(q, k, v, W: int, alpha, base: Sequence[int], theta: float = 10000.0, mode: int = INT,
                alpha_range=None, out=None, lse=None, with_lse: bool = True, plan=None, stream=None):
     """Forward of L layers in one call: q, k, v [L, B, H, N, D]; alpha: L host values, or
@@ -450,6 +473,7 @@ def fwd_layers(q, k, v, W: int, alpha, base: Sequence[int], theta: float = 10000
     return out, lse
 
 
+@_on_stream
 def decode_layers(q, k_cache, v_cache, W: int, alpha, base: Sequence[int], theta: float = 10000.0, mode: int = INT,
                   alpha_range=None, out=None, lse=None, with_lse: bool = True, plan=None, stream=None):
     """One decode step of L layers in one launch: q [L, B, H, D] at position N - 1 of the caches
@@ -486,6 +510,7 @@ def decode_layers(q, k_cache, v_cache, W: int, alpha, base: Sequence[int], theta
     return out, lse
 
 
+@_on_stream
 def bwd_layers(q, k, v, o, lse, dout, W: int, alpha, base: Sequence[int], theta: float = 10000.0, mode: int = INT,
                alpha_range=None, dq=None, dk=None, dv=None, dalpha=None, workspace=None, want_dalpha: bool = True,
                plan=None, stream=None):
@@ -522,6 +547,7 @@ def bwd_layers(q, k, v, o, lse, dout, W: int, alpha, base: Sequence[int], theta:
     return dq, dk, dv, dalpha
 
 
+@_on_stream
 def dense_lse(q, k, theta: float = 10000.0, lse=None, workspace=None, stream=None):
     """LSE [B, H, N] of dense causal attention over q, k [B, H, N, D] (bf16 MFMA; see
     fib_dense_causal_lse)."""
@@ -540,6 +566,7 @@ def dense_lse(q, k, theta: float = 10000.0, lse=None, workspace=None, stream=Non
     return lse
 
 
+@_on_stream
 def dropped_mass(q, k, v, W: int, alpha, base: Sequence[int], theta: float = 10000.0, stream=None):
     """Per query, the dense causal softmax mass outside the integer-mode attended set:
     1 - exp(LSE_sparse - LSE_dense) [B, H, N] (three kernels: sparse forward, dense LSE, map)."""
@@ -556,6 +583,7 @@ def bwd_workspace_size(B, H, N, D, dtype_code: int, mode: int) -> int:
     return int(lib().fib_sparse_attn_bwd_workspace_size(B, H, N, D, int(dtype_code), int(mode)))
 
 
+@_on_stream
 def bwd(q, k, v, o, lse, dout, W: int, alpha, base: Sequence[int], theta: float = 10000.0, mode: int = INT,
         dq=None, dk=None, dv=None, dalpha=None, workspace=None, want_dalpha: bool = True, stream=None):
     """Sparse attention backward; returns (dQ, dK, dV, dalpha tensor [1] or None)."""
@@ -581,6 +609,7 @@ def bwd(q, k, v, o, lse, dout, W: int, alpha, base: Sequence[int], theta: float 
     return dq, dk, dv, dalpha
 
 
+@_on_stream
 def index_set(N: int, W: int, alpha, base: Sequence[int], mode: int, device="cuda", stream=None):
     """Device export of the attended rows, int32 [N, W + n_entries] (-1 where absent)."""
     torch = _torch()

@@ -238,19 +238,19 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
 #pragma unroll
   for (int t = 0; t < 8; ++t) cs_t[t] = rope_cs(16 * wave + n, a.rope.rev[8 * g + t]);
   const float sl2 = a.scale_log2;
-  const float bias_diag = diag_lane ? 0.f : -INFINITY;
   // Lane constants formed anew in every step (a few VALU operations) rather than held in
   // registers through the loop: the window masks (query row 4g + v of slab 0, 16 + 4g + v of
   // slab 1, reads key n when 0 <= row - n < W) and the selectors of diag_block. (The empty asm
-  // makes W opaque, so the compiler does not hoist them out of the loop.)
-  auto window_bias = [&](float* bias0, float* bias1) {
+  // makes W opaque, so the compiler does not hoist them out of the loop.) Masks select -inf
+  // instead of adding it, so a NaN logit outside the attended set stays masked.
+  auto window_in = [&](bool* in0, bool* in1) {
     int Wp = a.W;
     asm volatile("" : "+s"(Wp));
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int d0 = 4 * g + v - n, d1 = 16 + 4 * g + v - n;
-      bias0[v] = (d0 >= 0 && d0 < Wp) ? 0.f : -INFINITY;
-      bias1[v] = d1 < Wp ? 0.f : -INFINITY;
+      in0[v] = d0 >= 0 && d0 < Wp;
+      in1[v] = d1 < Wp;
     }
   };
   auto diag_sel = [&](uint32_t* sel) {
@@ -457,14 +457,15 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
       D0 = mfma32(as_bf8(lds_read16(sm.ringD, sa + 64)), bv1, D0);
       D1 = mfma32(as_bf8(lds_read16(sm.ringD, sa + 16 * kRow)), bv0, D1);
       D1 = mfma32(as_bf8(lds_read16(sm.ringD, sa + 16 * kRow + 64)), bv1, D1);
-      float p[8], ds[8], bias0[4], bias1[4];
-      window_bias(bias0, bias1);
+      float p[8], ds[8];
+      bool in0[4], in1[4];
+      window_in(in0, in1);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const float2 l0 = *reinterpret_cast<const float2*>(sm.ringQ + band + lane_lv + v * kRow);
         const float2 l1 = *reinterpret_cast<const float2*>(sm.ringQ + band + lane_lv + (16 + v) * kRow);
-        p[v] = ex2(fmaf(S0[v], sl2, bias0[v]) - l0.x);
-        p[4 + v] = ex2(fmaf(S1[v], sl2, bias1[v]) - l1.x);
+        p[v] = ex2((in0[v] ? S0[v] * sl2 : -INFINITY) - l0.x);
+        p[4 + v] = ex2((in1[v] ? S1[v] * sl2 : -INFINITY) - l1.x);
         ds[v] = p[v] * (D0[v] - l0.y);
         ds[4 + v] = p[4 + v] * (D1[v] - l1.y);
       }
@@ -505,7 +506,7 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
         P = mfma32(as_bf8(lds_read16(sm.ringD, sl + lane_k + 64)), bv1, P);
         // (LSE, Delta) of query row j0 + r + n
         const float2 ld = *reinterpret_cast<const float2*>(sm.ringQ + sl + n * kRow + 128);
-        float x = fmaf(sel4(S, l), sl2, bias_diag);
+        float x = diag_lane ? sel4(S, l) * sl2 : -INFINITY;
         if (e + h >= S_n_cov) x = -INFINITY;
         p2[h] = ex2(x - ld.x);
         ds2[h] = p2[h] * (sel4(P, l) - ld.y);
@@ -571,7 +572,7 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
       f4 S = {0, 0, 0, 0};
       S = mfma32(as_bf8(r0), as_bf8(kraw0), S);
       S = mfma32(as_bf8(r1), as_bf8(kraw1), S);
-      float x = fmaf(sel4(S, l), sl2, bias_diag) - fq.lse2[f];
+      float x = (diag_lane ? sel4(S, l) * sl2 : -INFINITY) - fq.lse2[f];
       if (DEV && f >= S_n_far) x = -INFINITY;  // slot beyond the table
       const float p = __uint_as_float((uint32_t)__builtin_amdgcn_ds_bpermute(diag_addr, (int)__float_as_uint(ex2(x))));
       const float dp = quad_add(dot16_bf(fq.d[f][0], fq.d[f][1], v0, v1));

@@ -179,19 +179,19 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
 #pragma unroll
   for (int t = 0; t < 8; ++t) cs_t[t] = rope_cs(16 * wave + n, a.rope.rev[8 * g + t]);
   const float sl2 = a.scale_log2;
-  const float bias_diag = diag_lane ? 0.f : -INFINITY;
   // Lane constants formed anew in every step (a few VALU operations) rather than held in
   // registers through the loop: the window masks (band key kappa of the lane at distance
   // n + 16 - 4g - v in block 0 and n - 4g - v in block 1) and the selectors of diag_block.
-  // (The empty asm makes W and the lane opaque, so the compiler does not hoist them.)
-  auto window_bias = [&](float* bias0, float* bias1) {
+  // (The empty asm makes W and the lane opaque, so the compiler does not hoist them.) Masks
+  // select -inf instead of adding it, so a NaN logit of an unattended key stays masked.
+  auto window_in = [&](bool* in0, bool* in1) {
     int Wp = a.W;
     asm volatile("" : "+s"(Wp));
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int d0 = n + 16 - 4 * g - v, d1 = n - 4 * g - v;
-      bias0[v] = d0 < Wp ? 0.f : -INFINITY;
-      bias1[v] = (d1 >= 0 && d1 < Wp) ? 0.f : -INFINITY;
+      in0[v] = d0 < Wp;
+      in1[v] = d1 >= 0 && d1 < Wp;
     }
   };
   auto diag_sel = [&](uint32_t* sel) {
@@ -427,11 +427,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
     // ---- P, Delta, dS
     const float dlt = quad_add(dot16_bf(do0, do1, oo[0], oo[1]));
     float bds[8];  // band dS: sw0 (slab 0) then sw1 (slab 1), per the lane's 4 keys each
-    float bias0[4], bias1[4];
-    window_bias(bias0, bias1);
+    bool in0[4], in1[4];
+    window_in(in0, in1);
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      float x0 = fmaf(S0[v], sl2, bias0[v]), x1 = fmaf(S1[v], sl2, bias1[v]);
+      float x0 = in0[v] ? S0[v] * sl2 : -INFINITY, x1 = in1[v] ? S1[v] * sl2 : -INFINITY;
       if (early && n + 16 - 4 * g - v > iq) x0 = -INFINITY;
       const float p0v = ex2(x0 - lse2), p1v = ex2(x1 - lse2);
       bds[v] = p0v * (D0[v] - dlt);
@@ -447,7 +447,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
         s = fmaf(S_w(e), sd_e[e], s);
         dp = fmaf(S_w(e), dd_e[e], dp);
       }
-      float x = fmaf(s, sl2, bias_diag);
+      float x = diag_lane ? s * sl2 : -INFINITY;
       if (e >= S_n_cov || (early && S_dist(e) > iq)) x = -INFINITY;
       const float p = ex2(x - lse2);
       ds_e[e] = p * (dp - dlt);
@@ -515,7 +515,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
       const int u = MODE == 1 ? 2 * f : f;
       float s = s_f[f];
       if (MODE == 1) s = fmaf(S_far_w(f), sd_f[f], s);
-      float x = fmaf(s, sl2, bias_diag);
+      float x = diag_lane ? s * sl2 : -INFINITY;
       if (early && S_far_dist(f) > iq) x = -INFINITY;
       if (DEV && f >= S_n_far) x = -INFINITY;  // slot beyond the table
       // P of the query, from its diagonal lane to all four

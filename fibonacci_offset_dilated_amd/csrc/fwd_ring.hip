@@ -22,7 +22,9 @@
 //    step ahead into registers, and use relative RoPE <R_i q, R_(i-d) k> = <R_d q, k> with
 //    cos/sin of R_d computed once per workgroup; their P V runs on VALU (v_dot2_f32_bf16).
 //  * Softmax over all logits of a query at once (they fit in registers), fp32, base 2; the
-//    four lanes of a query combine through v_permlane16/32_swap.
+//    four lanes of a query combine through v_permlane16/32_swap. Logits outside a query's
+//    attended set are replaced (selected) by -inf, never offset, so a non-finite K row
+//    reaches exactly the queries that attend it.
 //  * P V on MFMA as O^T = V^T P^T: V^T operands come from the ring through the LDS transpose
 //    read (ds_read_b64_tr_b16); table entries use a diagonal P^T block, two slabs per MFMA
 //    (integer mode: two entries; interpolated mode: the lower and upper slab of one entry,
@@ -212,17 +214,17 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
   for (int t = 0; t < 8; ++t) cs_t[t] = rope_cs(16 * wave + n, a.rope.rev[8 * g + t]);
 
   const float sl2 = a.scale_log2;
-  // additive masks: window keys by distance (band key kappa of the lane at distance
-  // n + 16 - 4g - v in block 0 and n - 4g - v in block 1), table entries outside the
-  // diagonal lanes
-  float bias0[4], bias1[4];
+  // masks (selects, not additive biases, so that a NaN logit of a key that a query does not
+  // attend stays out of its softmax): window keys by distance (band key kappa of the lane at
+  // distance n + 16 - 4g - v in block 0 and n - 4g - v in block 1); table entries are kept in
+  // the diagonal lanes only
+  bool in0[4], in1[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int d0 = n + 16 - 4 * g - v, d1 = n - 4 * g - v;
-    bias0[v] = d0 < a.W ? 0.f : -INFINITY;
-    bias1[v] = (d1 >= 0 && d1 < a.W) ? 0.f : -INFINITY;
+    in0[v] = d0 < a.W;
+    in1[v] = d1 >= 0 && d1 < a.W;
   }
-  const float bias_diag = diag_lane ? 0.f : -INFINITY;
   // byte selectors of diag_block: slot s = l & 3 of slab A (lo half of x) and slab B (hi half)
   uint32_t sel[4];
   {
@@ -383,7 +385,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
       const int iq = i0w + n;  // this lane's query
       const bf16x8 bq0 = as_bf8(qh0), bq1 = as_bf8(qh1);
       // keys before position 0 (and table distances longer than the query position) occur
-      // only in the first steps of a sequence; afterwards the masks are the fixed biases
+      // only in the first steps of a sequence; afterwards the masks are the fixed ones above
       const bool early = i0w < S_early_rows;
 
       // ---- window band: keys i0w - 16 + kappa, kappa < 32
@@ -412,7 +414,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
           H = mfma32(as_bf8(lds_read16(sm.ringK, sl + kRow + 64)), bq1, H);
           s = fmaf(S_w(e), sel4(H, l) - s, s);
         }
-        s_ent[e] = fmaf(s, sl2, bias_diag);
+        s_ent[e] = diag_lane ? s * sl2 : -INFINITY;
       }
       if (S_n_cov < NC) {
 #pragma unroll
@@ -440,7 +442,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
           H = mfma32(as_bf8(kh[1]), as_bf8(r1), H);
           s = fmaf(S_far_w(f), sel4(H, l) - s, s);
         }
-        s_far[f] = fmaf(s, sl2, bias_diag);
+        s_far[f] = diag_lane ? s * sl2 : -INFINITY;
         if (DEV && f >= S_n_far) s_far[f] = -INFINITY;  // slot beyond the table
       }
       // interpolated: their V rows, for the end of this step (row pairs of K and V are never
@@ -453,8 +455,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
       float sw0[4], sw1[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        sw0[v] = fmaf(S0[v], sl2, bias0[v]);
-        sw1[v] = fmaf(S1[v], sl2, bias1[v]);
+        sw0[v] = in0[v] ? S0[v] * sl2 : -INFINITY;
+        sw1[v] = in1[v] ? S1[v] * sl2 : -INFINITY;
       }
       if (early) {
 #pragma unroll
