@@ -57,6 +57,9 @@ _SIGS = {
                                            _c.c_void_p]),
     "fib_sparse_attn_bwd_workspace_size": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64,
                                                          _c.c_int, _c.c_int]),
+    "fib_sparse_attn_bwd_workspace_size_for": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64,
+                                                             _c.c_int, _c.c_int, _c.c_int, _c.c_float, _c.c_void_p,
+                                                             _c.c_int]),
     "fib_sparse_attn_layers_plan_bytes": (_c.c_size_t, [_c.c_int64]),
     "fib_dense_lse_workspace_size": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int]),
     "fib_dense_causal_lse": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64,
@@ -352,11 +355,11 @@ def bwd_dev(q, k, v, o, lse, dout, W: int, alpha, alpha_range, base: Sequence[in
     _check_qkv(q, dq, dk, dv)
     if dalpha is None and want_dalpha:
         dalpha = torch.empty(1, dtype=torch.float32, device=q.device)
-    need = bwd_workspace_size(B, H, N, D, _dtype_code(q), mode)
+    lo, hi = alpha_range
+    need = bwd_workspace_size(B, H, N, D, _dtype_code(q), mode, W, hi, base)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     b, n = _base_array(base)
-    lo, hi = alpha_range
     st = lib().fib_sparse_attn_bwd_dev(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dalpha), B, H, N, D, _dtype_code(q),
                                        int(W), _ptr(alpha), ctypes.c_float(float(lo)), ctypes.c_float(float(hi)),
@@ -526,7 +529,8 @@ def bwd_layers(q, k, v, o, lse, dout, W: int, alpha, base: Sequence[int], theta:
     _check_layers(q, dq, dk, dv)
     if dalpha is None and want_dalpha:
         dalpha = torch.empty(L, dtype=torch.float32, device=q.device)
-    need = bwd_workspace_size(L * B, H, N, D, _dtype_code(q), mode)
+    need = bwd_workspace_size(L * B, H, N, D, _dtype_code(q), mode, W, hi if ad is not None else float(np.max(ah)),
+                              base)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     b, n = _base_array(base)
@@ -579,8 +583,14 @@ def dropped_mass(q, k, v, W: int, alpha, base: Sequence[int], theta: float = 100
     return out
 
 
-def bwd_workspace_size(B, H, N, D, dtype_code: int, mode: int) -> int:
-    return int(lib().fib_sparse_attn_bwd_workspace_size(B, H, N, D, int(dtype_code), int(mode)))
+def bwd_workspace_size(B, H, N, D, dtype_code: int, mode: int, W: int = None, alpha_max=None, base=None) -> int:
+    """Backward workspace bytes: for any base and alpha, or (W, alpha_max and base given) for
+    calls with that W and base and alphas <= alpha_max."""
+    if W is None:
+        return int(lib().fib_sparse_attn_bwd_workspace_size(B, H, N, D, int(dtype_code), int(mode)))
+    b, n = _base_array(base)
+    return int(lib().fib_sparse_attn_bwd_workspace_size_for(B, H, N, D, int(dtype_code), int(mode), int(W),
+                                                            ctypes.c_float(float(np.float32(alpha_max))), b, n))
 
 
 @_on_stream
@@ -596,7 +606,7 @@ def bwd(q, k, v, o, lse, dout, W: int, alpha, base: Sequence[int], theta: float 
     _check_qkv(q, dq, dk, dv)
     if dalpha is None and want_dalpha:
         dalpha = torch.empty(1, dtype=torch.float32, device=q.device)
-    need = bwd_workspace_size(B, H, N, D, _dtype_code(q), mode)
+    need = bwd_workspace_size(B, H, N, D, _dtype_code(q), mode, W, alpha, base)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     b, n = _base_array(base)

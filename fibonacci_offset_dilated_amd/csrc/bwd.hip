@@ -275,7 +275,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(
 }
 
 // Key side in interpolated mode when the query side stored each (query, entry)'s P and dS
-// (ps_pack words in ps[(head * kMaxEnt + e) * N + i]): the window queries are recomputed as in
+// (ps_pack words in ps[(head * ps_slots + e) * N + i]): the window queries are recomputed as in
 // bwd_key_kernel; for table entry e (c, w) row j is the lower row of query j + c (weight
 // 1 - w) and the upper row of query j + c - 1 (weight w), so
 //   dK_j += weight * dS * R_dist q_i / sqrt(D), dV_j += weight * P * dO_i
@@ -286,7 +286,7 @@ __global__ __launch_bounds__(256) void bwd_key_ps_kernel(
     const bf16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     const uint32_t* __restrict__ ps, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int64_t N, int W,
     Table tab_arg, Rope rope, float scale, int tiles, const DevPlan* __restrict__ plan,
-    int heads_per_plan) {
+    int heads_per_plan, int ps_slots) {
   const Table& tab = call_table<DEV>(tab_arg, plan, (int)(blockIdx.x / tiles) / heads_per_plan);
   __shared__ float2 cs[kCsSlots][kHalf];
   const bool cached = fill_cs(cs, W, tab, 1, rope);
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(256) void bwd_key_ps_kernel(
   for (int e = 0; e < tab.n; ++e) {
     const int64_t d = tab.dist[e];
     const float w = tab.w[e];
-    const uint32_t* pse = ps + ((size_t)head * kMaxEnt + e) * N;
+    const uint32_t* pse = ps + ((size_t)head * ps_slots + e) * N;
     const int64_t i_lo = jj + d;      // row j is its lower row
     const int64_t i_hi = jj + d - 1;  // row j is its upper row (its lower row j - 1 must exist)
     if (i_lo < N) {
@@ -397,7 +397,7 @@ int64_t tiles_of(int64_t N) { return (N + kRPB - 1) / kRPB; }
 
 // Workspace: Delta [BH * N] fp32 (padded to 64 floats), one d(alpha) partial per query-side
 // workgroup (at most BH * tiles_of(N)), 64 spare floats, then, for bf16 inputs in
-// interpolated mode, the (P, dS) words (ps_pack) [BH][kMaxEnt][N] (16-byte aligned).
+// interpolated mode, the (P, dS) words (ps_pack) [BH][ps_slots][N] (16-byte aligned).
 size_t ps_offset_bytes(int64_t BH, int64_t N) {
   const size_t floats = (size_t)(((BH * N + 63) / 64) * 64 + BH * tiles_of(N) + 64);
   return ((floats * sizeof(float) + 15) / 16) * 16;
@@ -432,7 +432,7 @@ hipError_t run(const BwdArgs& a) {
   } else if (ps != nullptr) {
     bwd_key_ps_kernel<DEV><<<grid, block, 0, a.stream>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
         (const bf16_t*)a.v, (const bf16_t*)a.dout, a.lse, delta, ps, (bf16_t*)a.dk, (bf16_t*)a.dv, a.N, a.W, a.tab,
-        a.rope, scale, tiles, a.plan, a.heads_per_plan);
+        a.rope, scale, tiles, a.plan, a.heads_per_plan, a.ps_slots);
   } else {
     bwd_key_kernel<T, MODE, DEV><<<grid, block, 0, a.stream>>>((const T*)a.q, (const T*)a.k, (const T*)a.v,
         (const T*)a.dout, a.lse, delta, (T*)a.dk, (T*)a.dv, a.N, a.W, a.tab, a.rope, scale, tiles, a.plan, a.heads_per_plan);
@@ -448,9 +448,18 @@ hipError_t run(const BwdArgs& a) {
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int64_t BH, int64_t N, int dtype, int mode) {
+size_t bwd_workspace_bytes(int64_t BH, int64_t N, int dtype, int mode, int ps_slots) {
   const size_t base = ps_offset_bytes(BH, N);
-  return dtype == 1 && mode == 1 ? base + (size_t)BH * kMaxEnt * (size_t)N * sizeof(uint32_t) : base;
+  return dtype == 1 && mode == 1 ? base + (size_t)BH * (size_t)ps_slots * (size_t)N * sizeof(uint32_t) : base;
+}
+
+int ps_entry_slots(float alpha_hi, const int32_t* base, int n_base, int W) {
+  // at least one slot: the ring key side reads (and discards) entry 0's words even when
+  // the table is empty
+  int n = 0;
+  for (int e = 0; e < n_base; ++e)
+    if ((double)alpha_hi * (double)base[e] >= (double)W) ++n;
+  return n > 0 ? n : 1;
 }
 
 hipError_t launch_bwd(const BwdArgs& a) {

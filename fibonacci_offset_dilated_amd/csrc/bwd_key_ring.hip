@@ -41,7 +41,8 @@ struct BkArgs {
   const bf16_t* dout;
   const float* lse;
   const float* delta;
-  const uint32_t* ps;  // interpolated: (P, dS) per (query, entry), [head][kMaxEnt][N]
+  const uint32_t* ps;  // interpolated: (P, dS) per (query, entry), [head][ps_slots][N]
+  int ps_slots;
   bf16_t* dk;
   bf16_t* dv;
   int N;
@@ -285,7 +286,7 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
   const bf16_t* Dh = a.dout + hoff;
   const float* Lh = a.lse + (size_t)head * N;
   const float* Th = a.delta + (size_t)head * N;
-  const uint32_t* Sh = MODE == 1 ? a.ps + (size_t)head * kMaxEnt * N : nullptr;
+  const uint32_t* Sh = MODE == 1 ? a.ps + (size_t)head * a.ps_slots * N : nullptr;
 
   auto row_elems = [&](int rb) -> int64_t {
     if (rb + 15 < N) return (int64_t)rb * kD + lane_off;
@@ -346,7 +347,9 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
       for (int e = 0; e < NC; ++e) {
         const int b = jb + S_dist(e) - 1 < N ? jb + S_dist(e) - 1 : N - 1;  // >= 0
         const int ilo = jb + S_dist(e) + n;
-        const uint32_t* se = Sh + (size_t)e * N + b;
+        // slots past the covered entries read entry 0's words (in bounds: the head has
+        // a.ps_slots >= 1 entry rows; the values are selected away below)
+        const uint32_t* se = Sh + (size_t)(e < S_n_cov ? e : 0) * N + b;
         uint32_t x = ld4(se, (uint32_t)((ilo < N ? ilo : N - 1) - b) * 4u);
         uint32_t y = ld4(se, (uint32_t)((ilo - 1 < N ? ilo - 1 : N - 1) - b) * 4u);
         asm volatile("" : "+v"(x), "+v"(y));  // keeps the loads unconditional (no branches)
@@ -773,6 +776,7 @@ hipError_t launch_bwdk_ring(const BwdArgs& f, const float* delta, const uint32_t
   a.lse = f.lse;
   a.delta = delta;
   a.ps = ps;
+  a.ps_slots = f.ps_slots;
   a.dk = (bf16_t*)f.dk;
   a.dv = (bf16_t*)f.dv;
   a.N = (int)f.N;

@@ -37,6 +37,7 @@ struct BqArgs {
   float* delta;
   float* dalpha_part;  // one per workgroup (interpolated mode)
   uint32_t* ps;        // interpolated mode: (P, dS) (ps_pack) per [head][entry][query], or null
+  int ps_slots;        // entries per head in ps
   int N;
   int W;
   int n_cov;
@@ -563,12 +564,13 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
       dal += dal_step;  // rows past the segment's end belong to another workgroup
       if (MODE == 1 && a.ps != nullptr && diag_lane) {
         // (P, dS) per entry, entry-major: the 16 queries of a wave are 64 contiguous bytes
-        uint32_t* pq = a.ps + (size_t)head * kMaxEnt * N + iq;
+        uint32_t* pq = a.ps + (size_t)head * a.ps_slots * N + iq;
 #pragma unroll
         for (int e = 0; e < NC; ++e)
           if (e < S_n_cov) pq[(size_t)e * N] = ps_e[e];
 #pragma unroll
-        for (int f = 0; f < NF; ++f) pq[(size_t)(S_n_cov + f) * N] = ps_f[f];
+        for (int f = 0; f < NF; ++f)
+          if (!DEV || f < S_n_far) pq[(size_t)(S_n_cov + f) * N] = ps_f[f];  // (DEV: NF bounds the far count)
       }
     }
     load_far<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, NF, fk, a, Kh, i0w + kT, l, n, g, lane_off);
@@ -689,6 +691,7 @@ hipError_t launch_bwdq_ring(const BwdArgs& f, float* delta, float* part, uint32_
   a.delta = delta;
   a.dalpha_part = part;
   a.ps = ps;
+  a.ps_slots = f.ps_slots;
   a.plan = f.plan;
   a.N = (int)f.N;
   a.W = f.W;

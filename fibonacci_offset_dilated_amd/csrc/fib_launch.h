@@ -145,6 +145,9 @@ struct BwdArgs {
   int n_base = 0;
   int heads_per_plan = 0x7fffffff;
   int layers = 1;  // dalpha holds one value per layer
+  // interpolated bf16 calls: table entries the (P, dS) words of the workspace have room for
+  // per query (an upper bound on the entry count of every layer of the call)
+  int ps_slots = 0;
 };
 
 hipError_t launch_fwd_generic(const FwdArgs& a);
@@ -168,12 +171,16 @@ hipError_t launch_dense_lse(const void* q, const void* k, float* lse, int64_t BH
 hipError_t launch_dropped_mass(const float* lse_sparse, const float* lse_dense, float* out, int64_t n,
                                hipStream_t s);
 
-size_t bwd_workspace_bytes(int64_t BH, int64_t N, int dtype, int mode);
+// ps_slots: (P, dS) words per query (interpolated bf16 calls; ps_entry_slots)
+size_t bwd_workspace_bytes(int64_t BH, int64_t N, int dtype, int mode, int ps_slots);
+// table entries of an interpolated call whose alphas are at most alpha_hi: the base entries
+// with alpha_hi * f >= W (the kept set only grows with alpha)
+int ps_entry_slots(float alpha_hi, const int32_t* base, int n_base, int W);
 hipError_t launch_bwd(const BwdArgs& a);
 // query side of the backward on the LDS ring (bf16, W <= 16): dQ, Delta [BH * N], one
 // d(alpha) partial per workgroup (bwdq_ring_blocks of them) and, in interpolated mode when ps
 // is not null, each (query, table entry)'s softmax weight P and dS (one ps_pack word) in
-// ps[(head * kMaxEnt + entry) * N + query]
+// ps[(head * a.ps_slots + entry) * N + query]
 bool bwdq_ring_supported(const BwdArgs& a);
 int64_t bwdq_ring_blocks(const BwdArgs& a);
 hipError_t launch_bwdq_ring(const BwdArgs& a, float* delta, float* part, uint32_t* ps);

@@ -200,6 +200,16 @@ int check_alpha(const AlphaArg& al) {
   return FIB_OK;
 }
 
+// The largest alpha a (checked) call can use: the host value, the top of the declared range
+// (device alphas are clamped into it) or the largest of the host list.
+float alpha_max(const AlphaArg& al) {
+  if (!al.uses_plan()) return al.host;
+  if (al.dev) return al.hi;
+  float m = al.host_list[0];
+  for (int64_t l = 1; l < al.layers; ++l) m = fmaxf(m, al.host_list[l]);
+  return m;
+}
+
 // The call's table: built on the host, or by a kernel (one thread per layer) enqueued on the
 // stream ahead of the attention kernels, which then read it from the plan.
 template <typename Args>
@@ -352,7 +362,8 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 3u) || ((uintptr_t)dalpha & 3u))
     return FIB_ERR_ALIGN;
-  const size_t need = bwd_workspace_bytes(B * H, N, dtype, mode);
+  const int ps_slots = ps_entry_slots(alpha_max(al), base, n_base, W);
+  const size_t need = bwd_workspace_bytes(B * H, N, dtype, mode, ps_slots);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FIB_ERR_WORKSPACE;
   if (workspace != nullptr && !aligned16(workspace)) return FIB_ERR_ALIGN;
   BwdArgs a;
@@ -361,6 +372,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   a.BH = B * H; a.N = N; a.dtype = dtype; a.mode = mode; a.W = W;
   a.rope = make_rope(rope_theta);
   a.workspace = workspace;
+  a.ps_slots = ps_slots;
   a.stream = (hipStream_t)stream;
   st = set_table(a, al, base, n_base);
   if (st) return st;
@@ -412,7 +424,15 @@ int fib_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cac
 size_t fib_sparse_attn_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, int mode) {
   if (check_shape(B, H, N, D, dtype) != FIB_OK) return 0;
   if (mode != FIB_INT && mode != FIB_INTERP) return 0;
-  return bwd_workspace_bytes(B * H, N, dtype, mode);
+  return bwd_workspace_bytes(B * H, N, dtype, mode, kMaxEnt);
+}
+
+size_t fib_sparse_attn_bwd_workspace_size_for(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, int mode,
+                                              int W, float alpha_max, const int32_t* base, int n_base) {
+  if (check_shape(B, H, N, D, dtype) != FIB_OK) return 0;
+  if (mode != FIB_INT && mode != FIB_INTERP) return 0;
+  if (check_base(base, n_base) != FIB_OK || W < 1 || !isfinite(alpha_max) || alpha_max <= 0.f) return 0;
+  return bwd_workspace_bytes(B * H, N, dtype, mode, ps_entry_slots(alpha_max, base, n_base, W));
 }
 
 int fib_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,

@@ -123,12 +123,21 @@ int fib_sparse_attn_bwd(const void* q, const void* k, const void* v, const void*
                         float rope_theta, int mode,
                         void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace fib_sparse_attn_bwd needs for these sizes (0 on bad sizes):
- * about 4 bytes per (b, h, n) row for Delta = <dO, O> and the d(alpha) partials, plus, for
- * bf16 inputs in FIB_INTERP mode, 128 bytes per row in which the query side hands each
- * (query, table entry) pair's softmax weight and dS (32 bits per pair) to the key side. */
+/* Bytes of device workspace fib_sparse_attn_bwd needs for these sizes (0 on bad sizes),
+ * enough for any base and alpha: about 4 bytes per (b, h, n) row for Delta = <dO, O> and the
+ * d(alpha) partials, plus, for bf16 inputs in FIB_INTERP mode, 4 bytes per row and possible
+ * table entry (FIB_MAX_BASE of them) in which the query side hands each (query, entry)
+ * pair's softmax weight and dS to the key side. */
 size_t fib_sparse_attn_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D,
                                           int dtype, int mode);
+
+/* The same for calls with this W and base and every alpha <= alpha_max (a host alpha, the
+ * top of a device alpha's declared range, or the largest alpha of a layer stack): the
+ * (query, entry) words then cover only the base entries with alpha_max * f >= W, the entries
+ * such a call can keep (interpolated mode keeps d = alpha f >= W). 0 on bad arguments. A
+ * backward call checks its workspace against this size for its own alphas. */
+size_t fib_sparse_attn_bwd_workspace_size_for(int64_t B, int64_t H, int64_t N, int64_t D, int dtype, int mode,
+                                              int W, float alpha_max, const int32_t* base, int n_base);
 
 /*
  * Decode step: the newest position of a key/value cache attends its window and offset keys
@@ -292,11 +301,16 @@ int fib_sparse_attn_offset_table(float alpha, const int32_t* base, int n_base, i
                                  int32_t* out_dist, float* out_w, int32_t* out_f, int* out_n);
 
 /*
- * Device debug export of the attended rows, computed by the same device table and
- * validity code as the attention kernels. out: device int32 [N, out_cols], out_cols must
- * equal W + (entry count of fib_sparse_attn_offset_table); column s < W holds the window
- * key i - s, column W + e the row i - dist[e] (interpolated: the lower row i - c_e), and
- * -1 where the key does not exist (before position 0).
+ * Device debug export of the attended rows ([FIB] Method > Architecture and attention
+ * mechanism: window of W keys plus one row, or one interpolated row pair, per kept offset).
+ * It is built from the device offset table and the per-query validity rule of the general
+ * (non-ring) kernels; the LDS-ring kernels apply the same table with their own masking and
+ * ring addressing, so this export pins the table and the general kernels, not the ring
+ * kernels (their attended sets are checked through their outputs). out: device int32
+ * [N, out_cols], out_cols must equal W + (entry count of fib_sparse_attn_offset_table), i.e.
+ * W plus the kept entries (at most n_base); column s < W holds the window key i - s, column
+ * W + e the row i - dist[e] (interpolated: the lower row i - c_e), and -1 where the key does
+ * not exist (before position 0).
  */
 int fib_sparse_attn_index_set(int64_t N, int W, float alpha, const int32_t* base, int n_base,
                               int mode, int32_t* out, int64_t out_cols, void* stream);

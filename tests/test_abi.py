@@ -177,8 +177,9 @@ def test_layers_argument_errors():
         return L.fib_sparse_attn_bwd_layers(p, p, p, p, p, p, p, p, p, p, 4, 1, 1, 8, 64, 1, 12, alpha, b, 15,
                                             ctypes.c_float(10000.0), 1, ws, ws_bytes, p, nbytes, None)
     assert bwd(alpha=None) == -1 and bwd(ws=None) == -11 and bwd(nbytes=need - 1) == -11
-    # the workspace of L layers is the single-layer size at L * B batches
-    ws_need = F.bwd_workspace_size(4, 1, 8, 64, F.BF16, F.INTERP)
+    # the workspace of L layers is the single-layer size at L * B batches, for the largest alpha
+    ws_need = F.bwd_workspace_size(4, 1, 8, 64, F.BF16, F.INTERP, 12, 1.5, FIB_BASE)
+    assert 0 < ws_need < F.bwd_workspace_size(4, 1, 8, 64, F.BF16, F.INTERP)
     assert bwd(ws_bytes=ws_need - 1) == -11
     assert L.fib_sparse_attn_bwd_layers_dev(p, p, p, p, p, p, p, p, p, p, 4, 1, 1, 8, 64, 1, 12, None,
                                             ctypes.c_float(0.5), ctypes.c_float(1.5), b, 15, ctypes.c_float(10000.0),
@@ -217,14 +218,27 @@ def test_bwd_argument_errors():
     assert call(ws=None) == -11
     assert call(ws_bytes=3) == -11
     assert call(dalpha=0x1002) == -10
-    need = F.bwd_workspace_size(1, 1, 8, 64, F.BF16, F.INTERP)
+    need = F.bwd_workspace_size(1, 1, 8, 64, F.BF16, F.INTERP, 12, 1.0, FIB_BASE)
     assert need > 0 and call(ws_bytes=need - 1) == -11
 
 
 def test_workspace_size():
-    assert F.bwd_workspace_size(1, 32, 131072, 64, F.BF16, F.INTERP) >= 32 * 131072 * 4
+    big = F.bwd_workspace_size(1, 32, 131072, 64, F.BF16, F.INTERP)
+    assert big >= 32 * 131072 * 4 * 32  # one 32-bit word per row and possible entry (32)
     assert F.bwd_workspace_size(0, 1, 8, 64, F.BF16, F.INT) == 0
     assert F.bwd_workspace_size(1, 1, 8, 32, F.BF16, F.INT) == 0
+    # for a known base and alpha: the entries alpha * f >= W only (11 at alpha 1.5, W 12)
+    exact = F.bwd_workspace_size(1, 32, 131072, 64, F.BF16, F.INTERP, 12, 1.5, FIB_BASE)
+    int_ws = F.bwd_workspace_size(1, 32, 131072, 64, F.BF16, F.INT)
+    assert exact - int_ws == 32 * 131072 * 4 * 11
+    assert F.bwd_workspace_size(1, 32, 131072, 64, F.BF16, F.INT, 12, 1.5, FIB_BASE) == int_ws
+    assert big - int_ws == 32 * 131072 * 4 * 32
+    # fp32 inputs use no (P, dS) words; bad arguments give 0
+    assert F.bwd_workspace_size(1, 2, 100, 64, F.F32, F.INTERP, 12, 1.5, FIB_BASE) == \
+        F.bwd_workspace_size(1, 2, 100, 64, F.F32, F.INT)
+    assert F.bwd_workspace_size(1, 2, 100, 64, F.BF16, F.INTERP, 0, 1.5, FIB_BASE) == 0
+    assert F.bwd_workspace_size(1, 2, 100, 64, F.BF16, F.INTERP, 12, float("nan"), FIB_BASE) == 0
+    assert F.bwd_workspace_size(1, 2, 100, 64, F.BF16, F.INTERP, 12, 1.0, (3, 2)) == 0
 
 
 def test_index_set_argument_errors():
