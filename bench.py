@@ -308,24 +308,32 @@ def layer_stacks(dev, stream, args, al4, al2, al3):
     us_fp = time_calls(lambda: F.fwd_layers(q, k, v, 12, a3, FIB_BASE, 10000.0, INTERP, out=o, lse=lse, plan=plan),
                        reps, warm, stream) * 1e3 / L
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    dal = torch.empty(L, dtype=torch.float32, device=dev)
-    ws = torch.empty(F.bwd_workspace_size(L * w2.B, w2.H, w2.N, D, F.BF16, INTERP), dtype=torch.uint8, device=dev)
-    us_fb = time_calls(lambda: F.bwd_layers(q, k, v, o, lse, do, 12, a3, FIB_BASE, 10000.0, INTERP, dq=dq, dk=dk,
-                                            dv=dv, dalpha=dal, workspace=ws, plan=plan), reps, warm, stream) * 1e3 / L
-    ws1 = torch.empty(F.bwd_workspace_size(w2.B, w2.H, w2.N, D, F.BF16, INTERP), dtype=torch.uint8, device=dev)
-    dal1 = torch.empty(1, dtype=torch.float32, device=dev)
-    us_sb = time_calls(lambda: [F.bwd(q[l], k[l], v[l], o[l], lse[l], do[l], 12, a3[l], FIB_BASE, 10000.0, INTERP,
-                                      dq=dq[l], dk=dk[l], dv=dv[l], dalpha=dal1, workspace=ws1) for l in range(L)],
-                       reps, warm, stream) * 1e3 / L
+    us_fb = us_sb = None
+    if args.bwd_stacks:
+        # (off by default: a GPU memory fault was first seen at a layer-stack backward test
+        # case, and its cause is not yet shown)
+        dal = torch.empty(L, dtype=torch.float32, device=dev)
+        ws = torch.empty(F.bwd_workspace_size(L * w2.B, w2.H, w2.N, D, F.BF16, INTERP), dtype=torch.uint8,
+                         device=dev)
+        us_fb = time_calls(lambda: F.bwd_layers(q, k, v, o, lse, do, 12, a3, FIB_BASE, 10000.0, INTERP, dq=dq, dk=dk,
+                                                dv=dv, dalpha=dal, workspace=ws, plan=plan), reps, warm,
+                           stream) * 1e3 / L
+        ws1 = torch.empty(F.bwd_workspace_size(w2.B, w2.H, w2.N, D, F.BF16, INTERP), dtype=torch.uint8, device=dev)
+        dal1 = torch.empty(1, dtype=torch.float32, device=dev)
+        us_sb = time_calls(lambda: [F.bwd(q[l], k[l], v[l], o[l], lse[l], do[l], 12, a3[l], FIB_BASE, 10000.0,
+                                          INTERP, dq=dq[l], dk=dk[l], dv=dv[l], dalpha=dal1, workspace=ws1)
+                                    for l in range(L)], reps, warm, stream) * 1e3 / L
+        del ws
     rows2 = w2.B * w2.H * w2.N
     out["b8h8n1024_stack16_fwd_int_us_per_layer"] = round(us_fi, 2)
     out["b8h8n1024_stack16_fwd_int_hbm_frac"] = round(rows2 * (4 * D * 2 + 4) / (us_fi * 1e-6) / 1e9 / HBM_PEAK_GBS,
                                                       4)
     out["b8h8n1024_stack16_separate_calls_fwd_int_us_per_layer"] = round(us_si, 2)
     out["b8h8n1024_stack16_fwd_interp_us_per_layer"] = round(us_fp, 2)
-    out["b8h8n1024_stack16_bwd_interp_us_per_layer"] = round(us_fb, 2)
-    out["b8h8n1024_stack16_separate_calls_bwd_interp_us_per_layer"] = round(us_sb, 2)
-    del q, k, v, do, o, lse, dq, dk, dv, ws
+    if us_fb is not None:
+        out["b8h8n1024_stack16_bwd_interp_us_per_layer"] = round(us_fb, 2)
+        out["b8h8n1024_stack16_separate_calls_bwd_interp_us_per_layer"] = round(us_sb, 2)
+    del q, k, v, do, o, lse, dq, dk, dv
 
     # decode over a 16-layer cache stack at B8 H8 N4096 in one launch
     kc, vc = [torch.randn((L, 8, 8, 4096, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(2)]
@@ -445,6 +453,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20, help="untimed steps first (the GPU clocks ramp up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-components", action="store_true")
+    ap.add_argument("--bwd-stacks", action="store_true",
+                    help="also time the 16-layer backward stack (held off by default: a GPU memory fault was "
+                         "first seen at a layer-stack backward test case)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="run one 1 GiB device-to-device copy first (reference for HBM byte counters)")
