@@ -167,6 +167,20 @@ def small_configs(dev, stream, args):
         return ms * 1e3 / len(calls)
 
     out = {}
+    # the single-head fp32 workload (B1 H1 N1024, W 12, alpha 1, integer offsets): 16 calls
+    # back to back, per-call time
+    w1 = BY_CONFIG[1]
+    q1, k1, v1 = (torch.randn((w1.B, w1.H, w1.N, D), generator=torch.Generator(device=dev).manual_seed(seed_for(1)),
+                              device=dev, dtype=torch.float32) for _ in range(3))
+    o1 = torch.empty_like(q1)
+    l1 = torch.empty((w1.B, w1.H, w1.N), dtype=torch.float32, device=dev)
+    us1 = per_layer_us(lambda l: (lambda: F.fwd(q1, k1, v1, 12, np.float32(1.0), FIB_BASE, 10000.0, INT, out=o1,
+                                                lse=l1)), range(16))
+    rows1 = w1.B * w1.H * w1.N
+    out["c1_fp32_fwd_int_us"] = round(us1, 2)
+    out["c1_fp32_fwd_int_hbm_frac"] = round(rows1 * (4 * D * 4 + 4) / (us1 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    del q1, k1, v1, o1, l1
+
     w4 = BY_CONFIG[4]
     (q, k, v), _ = make_inputs(w4.B, w4.H, w4.N, seed_for(4, 0, 12, 0), False, dev)
     o = torch.empty_like(q)
@@ -463,8 +477,10 @@ def main():
                     help="measurement aid: time every workload's layers, windows, bases, modes and passes "
                          "(one JSONL record each) instead of the bench line")
     ap.add_argument("--bwd-only", action="store_true",
-                    help="profiling aid: one integer forward, then only integer backward calls "
-                         "(--warmup untimed, --steps timed); prints their time, not the bench line")
+                    help="profiling aid: one forward, then only backward calls (--warmup untimed, --steps "
+                         "timed); prints their time, not the bench line")
+    ap.add_argument("--bwd-mode", choices=("int", "interp"), default="int",
+                    help="offset mode of the --bwd-only calls")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path. Heads (B*H) are "
@@ -503,14 +519,17 @@ def main():
         F.fwd(q, k, v, W, alpha, FIB_BASE, 10000.0, INT, out=o, lse=lse)
 
     if args.bwd_only:
-        fwd_int()
+        bmode = INT if args.bwd_mode == "int" else INTERP
+        F.fwd(q, k, v, W, alpha, FIB_BASE, 10000.0, bmode, out=o, lse=lse)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
         dal = torch.empty(1, dtype=torch.float32, device=dev)
-        ws = torch.empty(F.bwd_workspace_size(B, H, N, D, F.BF16, INT), dtype=torch.uint8, device=dev)
-        log("timing integer backward only")
-        ms_b = time_calls(lambda: F.bwd(q, k, v, o, lse, do, W, alpha, FIB_BASE, 10000.0, INT, dq=dq, dk=dk, dv=dv,
+        ws = torch.empty(F.bwd_workspace_size(B, H, N, D, F.BF16, bmode, W, alpha, FIB_BASE), dtype=torch.uint8,
+                         device=dev)
+        log(f"timing {args.bwd_mode} backward only")
+        ms_b = time_calls(lambda: F.bwd(q, k, v, o, lse, do, W, alpha, FIB_BASE, 10000.0, bmode, dq=dq, dk=dk, dv=dv,
                                         dalpha=dal, workspace=ws), args.steps, args.warmup, stream)
-        print(json.dumps({"profiling_aid": "bwd_int", "workload": "long_context_b1h32_n131072_bf16_w12_fib987_alpha1.5",
+        print(json.dumps({"profiling_aid": f"bwd_{args.bwd_mode}",
+                          "workload": "long_context_b1h32_n131072_bf16_w12_fib987_alpha1.5",
                           "ms_per_call": ms_b, "steps": args.steps, "warmup": args.warmup}), flush=True)
         return
 
