@@ -376,8 +376,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
     float s_e[NC], dp_e[NC], sd_e[MODE == 1 ? NC : 1], dd_e[MODE == 1 ? NC : 1];
 #pragma unroll
     for (int e = 0; e < NC; ++e) {
-      int sl = row_off(bw - S_dist(e)) + lane_k;
-      if (MODE == 1 && (e & 1) == 0) asm volatile("" : "+v"(sl));
+      const int sl = row_off(bw - S_dist(e)) + lane_k;
       f4 S = {0, 0, 0, 0}, P = {0, 0, 0, 0};
       S = mfma32(as_bf8(lds_read16(sm.ringK, sl)), bq0, S);
       S = mfma32(as_bf8(lds_read16(sm.ringK, sl + 64)), bq1, S);
@@ -393,12 +392,6 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
         Q = mfma32(as_bf8(lds_read16(sm.ringV, sl + kRow + 64)), bd1, Q);
         sd_e[e] = sel4(H, l) - s_e[e];  // s_hi - s_lo
         dd_e[e] = sel4(Q, l) - dp_e[e];  // dp_hi - dp_lo
-        // at most two entries' accumulators (16 registers each) in flight at a time: left to
-        // itself the compiler issues every entry's MFMAs back to back and runs out of
-        // registers. (Empty asm: the results of entries e - 1 and e are taken before the
-        // slab address of entry e + 1 is formed.)
-        if (e & 1) asm volatile("" : "+v"(s_e[e]), "+v"(dp_e[e]), "+v"(sd_e[e]), "+v"(dd_e[e]),
-                                "+v"(s_e[e - 1]), "+v"(dp_e[e - 1]), "+v"(sd_e[e - 1]), "+v"(dd_e[e - 1]));
       }
     }
     // ---- far entries: logits (relative RoPE); their V rows for dP are requested now

@@ -162,6 +162,11 @@ hipError_t launch_index_set(int32_t* out, int64_t N, int W, const Table& tab, in
 // one query per (batch, head) at position N - 1 of a K/V cache of N rows: q and o are
 // [BH, D], k and v [BH, N, D], lse [BH]
 hipError_t launch_decode(const FwdArgs& a);
+// forward of small problems (at most kGatherMaxRows query rows) that the ring kernel does not
+// take: the decode kernel's structure with 1-4 queries per block, all keys requested at once
+constexpr int64_t kGatherMaxRows = 1 << 16;
+bool fwd_gather_preferred(const FwdArgs& a);
+hipError_t launch_fwd_gather(const FwdArgs& a);
 
 // dense causal LSE (bf16 MFMA on rotated bf16 copies of q and k in the workspace) and the
 // dropped mass 1 - exp(lse_sparse - lse_dense)

@@ -331,7 +331,9 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   st = set_table(a, al, base, n_base);
   if (st) return st;
   auto launch = [&](const FwdArgs& b) {
-    return decode ? launch_decode(b) : fwd_ring_supported(b) ? launch_fwd_ring(b) : launch_fwd_generic(b);
+    if (decode) return launch_decode(b);
+    if (fwd_ring_supported(b)) return launch_fwd_ring(b);
+    return fwd_gather_preferred(b) ? launch_fwd_gather(b) : launch_fwd_generic(b);
   };
   // (the decode kernel is one instance for every table: one launch serves any stack)
   if (decode || al.dev || al.host_list == nullptr || al.layers == 1)

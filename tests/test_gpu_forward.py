@@ -306,3 +306,27 @@ def test_probe_moments(mode, dtype):
     for h in range(2):
         assert maxabs(oh[0, h, :, :3], want) <= tol
         assert np.abs(oh[0, h, :, 3:]).max() == 0.0
+
+
+# the forward of small problems that the ring kernel does not take (fp32, or W > 16) runs on
+# the gather kernel (every key of a query requested at once, 1-4 queries per block) up to 2^16
+# query rows, on the general kernel above; both sides of the switch, both modes, 1, 2 and 4
+# queries per block (the block size follows the window plus table size)
+GATHER_SWITCH = [
+    # (B, H, N, W, alpha, base, dtype)
+    (1, 2, 32768, 12, 1.0, FIB_BASE, F32),     # 65536 rows: gather, 2 queries per block
+    (1, 2, 32769, 12, 1.0, FIB_BASE, F32),     # 65538 rows: general kernel
+    (2, 3, 700, 4, 0.77, (1, 2, 3, 5, 8, 13), F32),   # 4 queries per block
+    (1, 1, 900, 40, 1.1, FIB_BASE, F32),       # 1 query per block, more keys than quads
+    (2, 2, 600, 24, 0.93, POW2_BASE, BF16),    # bf16 with W > 16
+]
+
+
+@pytest.mark.parametrize("mode", [INT, INTERP], ids=["int", "interp"])
+@pytest.mark.parametrize("case", GATHER_SWITCH,
+                         ids=[f"B{c[0]}H{c[1]}N{c[2]}W{c[3]}a{c[4]}n{len(c[5])}d{c[6]}" for c in GATHER_SWITCH])
+def test_gather_and_general_forward(case, mode):
+    B, H, N, W, alpha, base, dtype = case
+    say("gather / general forward", case, "mode", mode)
+    qkv = inputs(6100 + N + W, (B, H, N, 64), dtype)
+    check_full(qkv, W, np.float32(alpha), base, mode, dtype)
