@@ -8,7 +8,7 @@ hand-written HIP kernels of libfibattn.so; this package is its thin Python bindi
 """
 from ._lib import (  # noqa: F401
     BF16, F32, INT, INTERP, SCHED_COPRIME, SCHED_FIXED, SCHED_LINEAR,
-    FibError, bwd, bwd_dev, bwd_layers, bwd_workspace_size, decode, decode_dev, decode_layers, dense_lse,
+    NOALLOC_SCRATCH_BYTES, FibError, bwd, bwd_dev, bwd_layers, bwd_noalloc, bwd_workspace_size, decode, decode_dev, decode_layers, dense_lse,
     dropped_mass, fwd, fwd_dev, fwd_layers, index_set, layers_plan_bytes, lib, offset_table, plan_bytes,
     schedule_alpha, status_string,
 )

@@ -55,6 +55,11 @@ _SIGS = {
                                            _c.c_int, _c.c_void_p, _c.c_float, _c.c_float, _c.c_void_p, _c.c_int,
                                            _c.c_float, _c.c_int, _c.c_void_p, _c.c_size_t, _c.c_void_p, _c.c_size_t,
                                            _c.c_void_p]),
+    "fib_sparse_attn_bwd_noalloc": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                               _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                               _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int,
+                                               _c.c_int, _c.c_float, _c.c_void_p, _c.c_int, _c.c_float, _c.c_int,
+                                               _c.c_void_p]),
     "fib_sparse_attn_bwd_workspace_size": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64,
                                                          _c.c_int, _c.c_int]),
     "fib_sparse_attn_bwd_workspace_size_for": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64,
@@ -616,6 +621,33 @@ def bwd(q, k, v, o, lse, dout, W: int, alpha, base: Sequence[int], theta: float 
                                    ctypes.c_float(float(theta)), int(mode), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "fib_sparse_attn_bwd")
+    return dq, dk, dv, dalpha
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+@_on_stream
+def bwd_noalloc(q, k, v, o, lse, dout, W: int, alpha, base: Sequence[int], theta: float = 10000.0, mode: int = INT,
+                dq=None, dk=None, dv=None, dalpha=None, want_dalpha: bool = True, stream=None):
+    """Backward through fib_sparse_attn_bwd_noalloc: no workspace (the library's fixed scratch,
+    NOALLOC_SCRATCH_BYTES per GPU); returns (dQ, dK, dV, dalpha tensor [1] or None). Pass
+    preallocated dq, dk, dv, dalpha to allocate nothing at all."""
+    torch = _torch()
+    _check_qkv(q, k, v, o, dout)
+    B, H, N, D = q.shape
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    _check_qkv(q, dq, dk, dv)
+    if dalpha is None and want_dalpha:
+        dalpha = torch.empty(1, dtype=torch.float32, device=q.device)
+    b, n = _base_array(base)
+    st = lib().fib_sparse_attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dalpha), B, H, N, D, _dtype_code(q),
+                                           int(W), ctypes.c_float(float(np.float32(alpha))), b, n,
+                                           ctypes.c_float(float(theta)), int(mode), _stream(stream))
+    _check(st, "fib_sparse_attn_bwd_noalloc")
     return dq, dk, dv, dalpha
 
 

@@ -8,6 +8,7 @@
 //   Method > Experimental variables: Fixed (alpha = 1), Staggered-linear (0.5 at layer 0 to
 //   1.5 at the last layer) and Staggered-coprime (the linear values reassigned by
 //   l -> 7l mod L) schedules.
+#include <mutex>
 #include <math.h>
 #include <string.h>
 
@@ -82,6 +83,32 @@ float f32_nearest_ratio(int64_t p, int64_t q) {
   return best;
 }
 
+// ---- fixed scratch of the no-alloc backward -------------------------------------------------
+// The workspace of fib_sparse_attn_bwd_noalloc: a device array in this code object, loaded
+// (and held until the process ends) on each GPU the library runs on. Host code never passes
+// the array's name to a kernel or a copy (on the host it is only a stand-in for the symbol):
+// it uses the device address that hipGetSymbolAddress returns, once per device, with that
+// device current.
+constexpr size_t kScratchBytes = FIB_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FIB_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return FIB_ERR_LAUNCH;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return FIB_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -103,6 +130,7 @@ const char* fib_status_string(int status) {
     case FIB_ERR_LAUNCH: return "kernel launch failed";
     case FIB_ERR_SCHEDULE: return "bad schedule kind, layer or layer count";
     case FIB_ERR_CAPACITY: return "output array too small";
+    case FIB_ERR_SCRATCH: return "backward workspace need exceeds the no-alloc scratch (64 MiB)";
     default: return "unknown status";
   }
 }
@@ -346,10 +374,10 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   return FIB_OK;
 }
 
-int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-             void* dq, void* dk, void* dv, float* dalpha, int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
-             int W, const AlphaArg& al, const int32_t* base, int n_base, float rope_theta, int mode,
-             void* workspace, size_t workspace_bytes, void* stream) {
+// Every argument check of a backward call except the workspace's.
+int bwd_check(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+              void* dq, void* dk, void* dv, float* dalpha, int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+              int W, const AlphaArg& al, const int32_t* base, int n_base, float rope_theta, int mode) {
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || dout == nullptr || lse == nullptr ||
       dq == nullptr || dk == nullptr || dv == nullptr)
     return FIB_ERR_NULL;
@@ -364,6 +392,17 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 3u) || ((uintptr_t)dalpha & 3u))
     return FIB_ERR_ALIGN;
+  return FIB_OK;
+}
+
+int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             void* dq, void* dk, void* dv, float* dalpha, int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+             int W, const AlphaArg& al, const int32_t* base, int n_base, float rope_theta, int mode,
+             void* workspace, size_t workspace_bytes, void* stream) {
+  const int st0 = bwd_check(q, k, v, o, dout, lse, dq, dk, dv, dalpha, B, H, N, D, dtype, W, al, base, n_base,
+                            rope_theta, mode);
+  if (st0) return st0;
+  int st;
   const int ps_slots = ps_entry_slots(alpha_max(al), base, n_base, W);
   const size_t need = bwd_workspace_bytes(B * H, N, dtype, mode, ps_slots);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FIB_ERR_WORKSPACE;
@@ -446,6 +485,24 @@ int fib_sparse_attn_bwd(const void* q, const void* k, const void* v, const void*
                         void* workspace, size_t workspace_bytes, void* stream) {
   return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, dalpha, B, H, N, D, dtype, W, host_alpha(alpha), base, n_base,
                   rope_theta, mode, workspace, workspace_bytes, stream);
+}
+
+int fib_sparse_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                const void* dout, const float* lse,
+                                void* dq, void* dk, void* dv, float* dalpha,
+                                int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                                int W, float alpha, const int32_t* base, int n_base,
+                                float rope_theta, int mode, void* stream) {
+  const int st0 = bwd_check(q, k, v, o, dout, lse, dq, dk, dv, dalpha, B, H, N, D, dtype, W, host_alpha(alpha), base,
+                            n_base, rope_theta, mode);
+  if (st0) return st0;
+  const size_t need = fib_sparse_attn_bwd_workspace_size_for(B, H, N, D, dtype, mode, W, alpha, base, n_base);
+  if (need == 0 || need > kScratchBytes) return FIB_ERR_SCRATCH;
+  void* ws = nullptr;
+  const int st = scratch_address(&ws);
+  if (st != FIB_OK) return st;
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, dalpha, B, H, N, D, dtype, W, host_alpha(alpha), base, n_base,
+                  rope_theta, mode, ws, kScratchBytes, stream);
 }
 
 size_t fib_dense_lse_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D, int dtype) {

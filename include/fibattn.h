@@ -68,6 +68,8 @@ extern "C" {
 #define FIB_ERR_LAUNCH (-12)     /* the HIP runtime reported an error at launch */
 #define FIB_ERR_SCHEDULE (-13)   /* bad schedule kind, layer or layer count */
 #define FIB_ERR_CAPACITY (-14)   /* an output array is too small */
+#define FIB_ERR_SCRATCH (-15)    /* fib_sparse_attn_bwd_noalloc: the call needs more workspace than the
+                                    library's fixed scratch (FIB_NOALLOC_SCRATCH_BYTES) */
 
 /* element types of Q, K, V, O, dO, dQ, dK, dV */
 #define FIB_F32 0
@@ -122,6 +124,27 @@ int fib_sparse_attn_bwd(const void* q, const void* k, const void* v, const void*
                         int W, float alpha, const int32_t* base, int n_base,
                         float rope_theta, int mode,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fib_sparse_attn_bwd without a workspace argument, for callers that cannot allocate device
+ * memory around the call (code under HIP graph capture, tight training loops, harnesses that
+ * forbid allocation). The workspace lives in a fixed device array inside the library,
+ * FIB_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, held from the first call on that GPU until the
+ * process ends; the call allocates and frees nothing. Arguments, results and errors are those
+ * of fib_sparse_attn_bwd, plus FIB_ERR_SCRATCH (nothing launched) when
+ * fib_sparse_attn_bwd_workspace_size_for(B, H, N, D, dtype, mode, W, alpha, base, n_base)
+ * exceeds the scratch: e.g. every FIB_INT call up to about 16M (b, h, n) rows, and FIB_INTERP
+ * bf16 calls up to 64 MiB / (8 + 4 x entries) bytes per row (about 1.1M rows with 11 entries).
+ * All calls on one GPU share the array: calls that overlap in time on that GPU (different
+ * streams, or host threads) race and must be serialized by the caller.
+ */
+#define FIB_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int fib_sparse_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                const void* dout, const float* lse,
+                                void* dq, void* dk, void* dv, float* dalpha,
+                                int64_t B, int64_t H, int64_t N, int64_t D, int dtype,
+                                int W, float alpha, const int32_t* base, int n_base,
+                                float rope_theta, int mode, void* stream);
 
 /* Bytes of device workspace fib_sparse_attn_bwd needs for these sizes (0 on bad sizes),
  * enough for any base and alpha: about 4 bytes per (b, h, n) row for Delta = <dO, O> and the

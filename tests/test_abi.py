@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for st in range(0, -15, -1):
+    for st in range(0, -16, -1):
         assert F.status_string(st) and F.status_string(st) != "unknown status"
     assert F.status_string(-99) == "unknown status"
 
@@ -254,3 +254,25 @@ def test_no_fallback_when_library_missing(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libfibattn.so"))
     with pytest.raises(RuntimeError, match="missing"):
         _lib.lib()
+
+
+def test_bwd_noalloc_argument_errors():
+    """The no-alloc backward reports argument errors like fib_sparse_attn_bwd and rejects a
+    call whose workspace would exceed the fixed scratch, before anything is launched."""
+    L = F.lib()
+    b = (ctypes.c_int32 * 15)(*FIB_BASE)
+    p = 16
+
+    def call(B=1, H=1, N=8, mode=1, lse=p, dq=p, alpha=1.0, W=12, dtype=1, nb=15):
+        return L.fib_sparse_attn_bwd_noalloc(p, p, p, p, p, lse, dq, p, p, p, B, H, N, 64, dtype, W,
+                                             ctypes.c_float(alpha), b, nb, ctypes.c_float(10000.0), mode, None)
+    assert call(lse=None) == -1 and call(dq=None) == -1
+    assert call(mode=5) == -9 and call(W=0) == -5 and call(alpha=float("nan")) == -6
+    assert call(B=0) == -2 and call(dtype=3) == -4 and call(nb=0) == -7
+    # the long-context interpolated backward needs ~201 MB of (P, dS) words: more than 64 MiB
+    need = F.bwd_workspace_size(1, 32, 131072, 64, F.BF16, F.INTERP, 12, 1.5, FIB_BASE)
+    assert need > F.NOALLOC_SCRATCH_BYTES
+    assert call(B=1, H=32, N=131072, alpha=1.5) == -15
+    # its integer-mode backward fits
+    assert F.bwd_workspace_size(1, 32, 131072, 64, F.BF16, F.INT, 12, 1.5, FIB_BASE) <= F.NOALLOC_SCRATCH_BYTES
+    assert "scratch" in F.status_string(-15)
