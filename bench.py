@@ -481,12 +481,24 @@ def main():
                          "timed); prints their time, not the bench line")
     ap.add_argument("--bwd-mode", choices=("int", "interp"), default="int",
                     help="offset mode of the --bwd-only calls")
+    ap.add_argument("--memprobe", action="store_true",
+                    help="measurement aid: run the memory-delivery probe (the long-context forward's loads and "
+                         "stores without its arithmetic, in several lane layouts and far distances); prints "
+                         "one JSON line per variant instead of the bench line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path. Heads (B*H) are "
               "independent, so the op would shard over them with no communication, plus one "
               "d(alpha) all-reduce per layer in the backward. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.memprobe:
+        # a child process of its own (built by fibonacci_offset_dilated_amd.build)
+        import subprocess
+        exe = os.path.join(ROOT, "fibonacci_offset_dilated_amd", "probe", "memprobe")
+        if not os.path.exists(exe):
+            raise SystemExit(f"{exe} is missing: build first (python -m fibonacci_offset_dilated_amd.build)")
+        sys.exit(subprocess.run([exe]).returncode)
 
     import torch
 

@@ -58,7 +58,23 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, OUT)
+    build_probe()
     return OUT
+
+
+PROBE_SRC = os.path.join(PKG, "probe", "memprobe.hip")
+PROBE_OUT = os.path.join(PKG, "probe", "memprobe")
+
+
+def build_probe() -> str:
+    """The memory-delivery probe (a measurement aid that bench.py --memprobe runs; not part
+    of the library)."""
+    cmd = [hipcc(), *[f for f in flags() if f not in ("-fPIC",)], PROBE_SRC, "-o", PROBE_OUT + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on memprobe.hip:\n{r.stdout}\n{r.stderr}")
+    os.replace(PROBE_OUT + ".tmp", PROBE_OUT)
+    return PROBE_OUT
 
 
 def main():
