@@ -79,7 +79,8 @@ struct __align__(16) BkSmem {
 };
 
 // raw q and dO rows of the far queries j0 + r + n (row N - 1 past the end; masked), and their
-// LSE * log2 e (+inf past the end) and Delta
+// LSE and Delta as loaded (the use masks the rows past the end: a select here, next to the
+// load, would make the wave wait for the load at once)
 template <int NF>
 struct FarQ {
   uint4 q[NF > 0 ? NF : 1][2];
@@ -94,7 +95,6 @@ template <int NF>
 __device__ __forceinline__ void load_far_q(const int* fdist, int n_use, FarQ<NF>& fq, const BkArgs& a,
                                            const bf16_t* Qh, const bf16_t* Dh, const float* Lh, const float* Th, int j0,
                                            int n, int g, int lane_off) {
-  const float log2e = 1.4426950408889634f;
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     if (f >= n_use) {
@@ -116,7 +116,7 @@ __device__ __forceinline__ void load_far_q(const int* fdist, int n_use, FarQ<NF>
     fq.d[f][0] = *reinterpret_cast<const uint4*>(Dh + off);
     fq.d[f][1] = *reinterpret_cast<const uint4*>(Dh + off + kHalf);
     const int rc = r < a.N ? r : a.N - 1;
-    fq.lse2[f] = r < a.N ? Lh[rc] * log2e : INFINITY;
+    fq.lse2[f] = Lh[rc];
     fq.dlt[f] = Th[rc];
   }
 }
@@ -129,7 +129,7 @@ struct FarQI {
   uint4 q[NF > 0 ? NF : 1][2];
   uint4 d[NF > 0 ? NF : 1][2];
   uint32_t ex[NF > 0 ? NF : 1];
-  uint32_t pl[NF > 0 ? NF : 1];
+  uint32_t pl[NF > 0 ? NF : 1];  // as loaded: rows past the end are masked at the use
   uint32_t ph[NF > 0 ? NF : 1];
 };
 
@@ -164,17 +164,13 @@ __device__ __forceinline__ void load_far_qi(const int* fdist, int n_use, FarQI<N
     fq.q[f][1] = ld16(qb, off + 2 * kHalf);
     fq.d[f][0] = ld16(db, off);
     fq.d[f][1] = ld16(db, off + 2 * kHalf);
-    // (no branches here: every load is in bounds, the unused values are selected away)
+    // (every load is in bounds; the words of rows past the end are masked where they are
+    // used, so no select waits on a load here)
     const int re = r0 - 1 < a.N ? r0 - 1 : a.N - 1;
-    const uint32_t eq = ld4(Qh + (int64_t)re * kD, 4u * (uint32_t)(l & 31));
-    const uint32_t ed = ld4(Dh + (int64_t)re * kD, 4u * (uint32_t)(l & 31));
-    fq.ex[f] = l < 32 ? eq : ed;
+    fq.ex[f] = ld4((l < 32 ? Qh : Dh) + (int64_t)re * kD, 4u * (uint32_t)(l & 31));
     const uint32_t* se = Sh + (size_t)(n_cov + f) * a.N + rb;
-    uint32_t x = ld4(se, (uint32_t)((r < a.N ? r : a.N - 1) - rb) * 4u);
-    uint32_t y = ld4(se - 1, (uint32_t)((r - 1 < a.N ? r - 1 : a.N - 1) - rb + 1) * 4u);
-    asm volatile("" : "+v"(x), "+v"(y));  // keeps the loads unconditional (no branches)
-    fq.pl[f] = r < a.N ? x : 0u;
-    fq.ph[f] = r - 1 < a.N ? y : 0u;
+    fq.pl[f] = ld4(se, (uint32_t)((r < a.N ? r : a.N - 1) - rb) * 4u);
+    fq.ph[f] = ld4(se - 1, (uint32_t)((r - 1 < a.N ? r - 1 : a.N - 1) - rb + 1) * 4u);
   }
 }
 
@@ -238,6 +234,10 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
   float2 cs_t[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) cs_t[t] = rope_cs(16 * wave + n, a.rope.rev[8 * g + t]);
+  // the lane's inverse frequency for the per-step base rotation (wave 0, lanes < 32), read once:
+  // indexed per lane, it is a memory load, and inside the step loop its wait would also wait
+  // for the next step's rows requested just before it
+  const double rev_l = a.rope.rev[l & (kHalf - 1)];
   const float sl2 = a.scale_log2;
   // Lane constants formed anew in every step (a few VALU operations) rather than held in
   // registers through the loop: the window masks (query row 4g + v of slab 0, 16 + 4g + v of
@@ -337,11 +337,13 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
   uint4 pk[2], pv[2], pq[2], pd[2];
   float plse, pdlt;
   // interpolated: the stored (P, dS) of the covered entries' lower and upper query of the
-  // lane's key (in its diagonal lane; zero elsewhere and past the end)
+  // lane's key, as loaded (only the diagonal lane's words of entries in use and of rows
+  // before the end count: the use masks the others)
   uint32_t psl[MODE == 1 ? NC : 1], psh[MODE == 1 ? NC : 1];
   auto load_ps = [&](int pb) {
     if constexpr (MODE == 1) {
-      // (no branches: loads at clamped rows, unused values selected away)
+      // (loads at clamped rows; the words that must not count are masked where they are
+      // used, so no select waits on a load here)
       const int jb = pb + 16 * wave;
 #pragma unroll
       for (int e = 0; e < NC; ++e) {
@@ -350,12 +352,8 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
         // slots past the covered entries read entry 0's words (in bounds: the head has
         // a.ps_slots >= 1 entry rows; the values are selected away below)
         const uint32_t* se = Sh + (size_t)(e < S_n_cov ? e : 0) * N + b;
-        uint32_t x = ld4(se, (uint32_t)((ilo < N ? ilo : N - 1) - b) * 4u);
-        uint32_t y = ld4(se, (uint32_t)((ilo - 1 < N ? ilo - 1 : N - 1) - b) * 4u);
-        asm volatile("" : "+v"(x), "+v"(y));  // keeps the loads unconditional (no branches)
-        const bool use = diag_lane && e < S_n_cov;
-        psl[e] = use && ilo < N ? x : 0u;
-        psh[e] = use && ilo - 1 < N ? y : 0u;
+        psl[e] = ld4(se, (uint32_t)((ilo < N ? ilo : N - 1) - b) * 4u);
+        psh[e] = ld4(se, (uint32_t)((ilo - 1 < N ? ilo - 1 : N - 1) - b) * 4u);
       }
     }
   };
@@ -433,8 +431,8 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
     const int pn = p0 + kT;
     load_step(pn < s1 ? pn : p0);
     if (wave == 0 && l < kHalf) {
-      sm.base_cs[buf ^ 1][0][l] = rope_cs(pn, a.rope.rev[l]);
-      sm.base_cs[buf ^ 1][1][l] = rope_cs(pn + S_lead, a.rope.rev[l]);
+      sm.base_cs[buf ^ 1][0][l] = rope_cs(pn, rev_l);
+      sm.base_cs[buf ^ 1][1][l] = rope_cs(pn + S_lead, rev_l);
     }
 
     const int j0 = p0 + 16 * wave;
@@ -532,11 +530,14 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
 #pragma unroll
       for (int e = 0; e < NC; ++e) {
         const float w = S_w(e);
-        const float xs = ps_ds(psl[e]) * (1.f - w), ys = ps_ds(psh[e]) * w;
+        const int ilo = jk + S_dist(e);  // the key's lower query
+        const bool use = diag_lane && e < S_n_cov;
+        const uint32_t wl = use && ilo < N ? psl[e] : 0u, wh = use && ilo - 1 < N ? psh[e] : 0u;
+        const float xs = ps_ds(wl) * (1.f - w), ys = ps_ds(wh) * w;
         const uint32_t hs = pack_bf2(xs, ys);
         const bf16x8 bs = diag_block(hs, sel);
         const bf16x8 bs2 = diag_block(pack_bf2(xs - bf_lo(hs), ys - bf_hi(hs)), sel);
-        const bf16x8 bp = diag_block(pack_bf2(ps_p(psl[e]) * (1.f - w), ps_p(psh[e]) * w), sel);
+        const bf16x8 bp = diag_block(pack_bf2(ps_p(wl) * (1.f - w), ps_p(wh) * w), sel);
         const int ra = row_off(j0 + S_dist(e)) + lane_t, rb = row_off(j0 + S_dist(e) - 1) + lane_t;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
@@ -575,7 +576,9 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
       f4 S = {0, 0, 0, 0};
       S = mfma32(as_bf8(r0), as_bf8(kraw0), S);
       S = mfma32(as_bf8(r1), as_bf8(kraw1), S);
-      float x = (diag_lane ? sel4(S, l) * sl2 : -INFINITY) - fq.lse2[f];
+      const int rq = jk + S_far_dist(f);  // the key's far query
+      const float lse2 = rq < N ? fq.lse2[f] * log2e : INFINITY;
+      float x = (diag_lane ? sel4(S, l) * sl2 : -INFINITY) - lse2;
       if (DEV && f >= S_n_far) x = -INFINITY;  // slot beyond the table
       const float p = __uint_as_float((uint32_t)__builtin_amdgcn_ds_bpermute(diag_addr, (int)__float_as_uint(ex2(x))));
       const float dp = quad_add(dot16_bf(fq.d[f][0], fq.d[f][1], v0, v1));
@@ -608,8 +611,10 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
         const float w = S_far_w(f);
         // (a slot beyond the table weighs nothing)
         const float keep = DEV && f >= S_n_far ? 0.f : 1.f;
-        const float al = keep * ps_ds(fi.pl[f]) * (1.f - w), ah = keep * ps_ds(fi.ph[f]) * w;
-        const float pl = keep * ps_p(fi.pl[f]) * (1.f - w), ph = keep * ps_p(fi.ph[f]) * w;
+        const int rq = jk + S_far_dist(f);  // the key's lower far query (rows past the end count 0)
+        const uint32_t wl = rq < N ? fi.pl[f] : 0u, wh = rq - 1 < N ? fi.ph[f] : 0u;
+        const float al = keep * ps_ds(wl) * (1.f - w), ah = keep * ps_ds(wh) * w;
+        const float pl = keep * ps_p(wl) * (1.f - w), ph = keep * ps_p(wh) * w;
 #pragma unroll
         for (int tsr = 0; tsr < 2; ++tsr) {
 #pragma unroll

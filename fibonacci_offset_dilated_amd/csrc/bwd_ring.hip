@@ -179,6 +179,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
   float2 cs_t[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) cs_t[t] = rope_cs(16 * wave + n, a.rope.rev[8 * g + t]);
+  // the lane's inverse frequency for the per-step base rotation (wave 0, lanes < 32), read once:
+  // indexed per lane, it is a memory load, and inside the step loop its wait would also wait
+  // for the next step's rows requested just before it
+  const double rev_l = a.rope.rev[l & (kHalf - 1)];
   const float sl2 = a.scale_log2;
   // Lane constants formed anew in every step (a few VALU operations) rather than held in
   // registers through the loop: the window masks (band key kappa of the lane at distance
@@ -346,7 +350,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
       const int r = pr + 16 * wave + n;
       plse = Lh[r < N ? r : N - 1];
     }
-    if (wave == 0 && l < kHalf) sm.base_cs[buf ^ 1][l] = rope_cs(pn, a.rope.rev[l]);
+    if (wave == 0 && l < kHalf) sm.base_cs[buf ^ 1][l] = rope_cs(pn, rev_l);
 
     const int bw = p0 + 16 * wave;
     const int i0w = bw;

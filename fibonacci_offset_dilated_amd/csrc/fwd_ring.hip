@@ -212,6 +212,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
   float2 cs_t[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) cs_t[t] = rope_cs(16 * wave + n, a.rope.rev[8 * g + t]);
+  // the lane's inverse frequency for the per-step base rotation (wave 0, lanes < 32), read once:
+  // indexed per lane, it is a memory load, and inside the step loop its wait would also wait
+  // for the next step's rows requested just before it
+  const double rev_l = a.rope.rev[l & (kHalf - 1)];
 
   const float sl2 = a.scale_log2;
   // masks (selects, not additive biases, so that a NaN logit of a key that a query does not
@@ -378,7 +382,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
     // next step's rows (the last step loads harmless repeats) and base rotation
     const int pn = p0 + kT;
     load_rows(pn < s1 ? pn : p0, pq, pk, pv);
-    if (wave == 0 && l < kHalf) sm.base_cs[buf ^ 1][l] = rope_cs(pn, a.rope.rev[l]);
+    if (wave == 0 && l < kHalf) sm.base_cs[buf ^ 1][l] = rope_cs(pn, rev_l);
 
     {
       const int i0w = p0 + 16 * wave;
