@@ -429,7 +429,11 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
     }
     __syncthreads();
     const int pn = p0 + kT;
-    load_step(pn < s1 ? pn : p0);
+    // the next step's keys and query rows: integer mode requests them here, a whole step
+    // ahead; interpolated mode after the covered entries, so that their registers are not
+    // held through the step's register peak (held, they cost spills whose reloads wait for
+    // every load in flight)
+    if constexpr (MODE == 0) load_step(pn < s1 ? pn : p0);
     if (wave == 0 && l < kHalf) {
       sm.base_cs[buf ^ 1][0][l] = rope_cs(pn, rev_l);
       sm.base_cs[buf ^ 1][1][l] = rope_cs(pn + S_lead, rev_l);
@@ -549,6 +553,7 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
         }
       }
     }
+    if constexpr (MODE == 1) load_step(pn < s1 ? pn : p0);
     // undo R_j on dK^: dims 8g+t (acck[0], acck[1]) pair with 32+8g+t (acck[2], acck[3])
     float kl[8], khv[8], vl[8], vhv[8];
 #pragma unroll

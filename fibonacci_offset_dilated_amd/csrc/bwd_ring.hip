@@ -340,7 +340,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
     const float lse2 = plse * log2e;
     __syncthreads();
     const int pn = p0 + kT;
-    {
+    // the next step's rows (this step's were consumed by the insert above). Integer mode
+    // requests them here, a whole step ahead; interpolated mode, whose steps are twice as
+    // long, after the covered entries, so that their 33 registers are not held through the
+    // step's register peak (held, they cost spills whose reloads wait for every load in
+    // flight)
+    auto prefetch = [&]() {
       const int pr = pn < s1 ? pn : p0;
       const int64_t off = row_elems(pr + 16 * wave);
       load2(Qh, off, pq);
@@ -349,7 +354,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
       load2(Dh, off, pd);
       const int r = pr + 16 * wave + n;
       plse = Lh[r < N ? r : N - 1];
-    }
+    };
+    if constexpr (MODE == 0) prefetch();
     if (wave == 0 && l < kHalf) sm.base_cs[buf ^ 1][l] = rope_cs(pn, rev_l);
 
     const int bw = p0 + 16 * wave;
@@ -496,6 +502,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
         }
       }
     }
+    if constexpr (MODE == 1) prefetch();
     // undo R_i: dims 8g+t (acc[0], acc[1]) pair with 32+8g+t (acc[2], acc[3])
     float ql[8], qhv[8];
 #pragma unroll
