@@ -429,11 +429,9 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
     }
     __syncthreads();
     const int pn = p0 + kT;
-    // the next step's keys and query rows: integer mode requests them here, a whole step
-    // ahead; interpolated mode after the covered entries, so that their registers are not
-    // held through the step's register peak (held, they cost spills whose reloads wait for
-    // every load in flight)
-    if constexpr (MODE == 0) load_step(pn < s1 ? pn : p0);
+    // (the next step's keys and query rows are requested after the covered entries, so that
+    // their registers are not held through the step's register peak: held, they cost spills
+    // whose reloads wait for every load in flight)
     if (wave == 0 && l < kHalf) {
       sm.base_cs[buf ^ 1][0][l] = rope_cs(pn, rev_l);
       sm.base_cs[buf ^ 1][1][l] = rope_cs(pn + S_lead, rev_l);
@@ -553,7 +551,7 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
         }
       }
     }
-    if constexpr (MODE == 1) load_step(pn < s1 ? pn : p0);
+    load_step(pn < s1 ? pn : p0);
     // undo R_j on dK^: dims 8g+t (acck[0], acck[1]) pair with 32+8g+t (acck[2], acck[3])
     float kl[8], khv[8], vl[8], vhv[8];
 #pragma unroll
@@ -604,7 +602,6 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
         vhv[2 * u + 1] = dot2(de[4 + u], p_hi, vhv[2 * u + 1]);
       }
     }
-    load_far_q<NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fq, a, Qh, Dh, Lh, Th, j0 + kT, n, g, lane_off);
     } else {
       // interpolated far entries: the lower query row (the lane's, rotated by R_c) and the
       // upper row (rotated by R_(c-1)) in fp32, weighted by the stored (P, dS) in fp32.
@@ -706,8 +703,11 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
       *reinterpret_cast<uint4*>(vp) = y0;
       *reinterpret_cast<uint4*>(vp + kHalf) = y1;
     }
-    // interpolated: the next step's far rows, requested after the stores (the far terms above
-    // feed only the stores; requested earlier, the new rows would be held alongside them)
+    // the next step's far rows, requested after the stores: the far terms above feed only the
+    // stores, so requested earlier the new rows would be held alongside them (and, before the
+    // conditional store, they need copies at the end of the step that wait for every load)
+    if constexpr (MODE == 0)
+      load_far_q<NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fq, a, Qh, Dh, Lh, Th, j0 + kT, n, g, lane_off);
     if constexpr (MODE == 1) load_far_qi<NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fi, a, Qh, Dh, Sh, S_n_cov, j0 + kT, l, n, g);
     __syncthreads();
   }
