@@ -565,8 +565,11 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
       vhv[t] = accv[2 + (t >> 2)][t & 3];
     }
     // ---- far offsets: raw q (rotated by R_r, bf16) and dO rows from global memory; dK and dV
-    // terms on VALU with the bf16 weights (dS, P) of the query's diagonal lane
+    // terms on VALU with the bf16 weights (dS, P) of the query's diagonal lane. (Scheduling
+    // barrier: the far rows, requested at the end of the previous step, are first waited for
+    // here, not in the window band, where work hoisted from this section would wait for them)
     if constexpr (MODE == 0) {
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       uint4 r0, r1;
