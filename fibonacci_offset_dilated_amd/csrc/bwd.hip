@@ -396,12 +396,15 @@ __global__ void store_zero_kernel(float* out, int n) {
 int64_t tiles_of(int64_t N) { return (N + kRPB - 1) / kRPB; }
 
 // Workspace: Delta [BH * N] fp32 (padded to 64 floats), one d(alpha) partial per query-side
-// workgroup (at most BH * tiles_of(N)), 64 spare floats, then, for bf16 inputs in
-// interpolated mode, the (P, dS) words (ps_pack) [BH][ps_slots][N] (16-byte aligned).
-size_t ps_offset_bytes(int64_t BH, int64_t N) {
+// workgroup (at most BH * tiles_of(N)), 64 spare floats; then, for bf16 inputs in
+// interpolated mode, the rotated rows R_i q_i and R_j k_j [BH][N][D] (bf16, 16-byte aligned)
+// that the ring query side writes and the (P, dS) words (ps_pack) [BH][ps_slots][N].
+size_t rot_offset_bytes(int64_t BH, int64_t N) {
   const size_t floats = (size_t)(((BH * N + 63) / 64) * 64 + BH * tiles_of(N) + 64);
   return ((floats * sizeof(float) + 15) / 16) * 16;
 }
+size_t rot_bytes(int64_t BH, int64_t N) { return (size_t)BH * (size_t)N * kD * sizeof(bf16_t); }
+size_t ps_offset_bytes(int64_t BH, int64_t N) { return rot_offset_bytes(BH, N) + 2 * rot_bytes(BH, N); }
 
 template <typename T, int MODE, bool DEV>
 hipError_t run(const BwdArgs& a) {
@@ -413,9 +416,14 @@ hipError_t run(const BwdArgs& a) {
   dim3 grid((unsigned)blocks), block(256);
   int64_t n_part = blocks;
   uint32_t* ps = nullptr;  // per-(query, entry) P and dS, stored by the ring query side
-  if (bwdq_ring_supported(a)) {
+  // interpolated: rotated query and key rows, written by the ring query side for the ring key
+  // side
+  bf16_t* qr = MODE == 1 ? (bf16_t*)((char*)a.workspace + rot_offset_bytes(a.BH, a.N)) : nullptr;
+  bf16_t* kr = MODE == 1 ? qr + (size_t)a.BH * (size_t)a.N * kD : nullptr;
+  const bool q_ring = bwdq_ring_supported(a);
+  if (q_ring) {
     if (MODE == 1) ps = (uint32_t*)((char*)a.workspace + ps_offset_bytes(a.BH, a.N));
-    const hipError_t e = launch_bwdq_ring(a, delta, part, ps);
+    const hipError_t e = launch_bwdq_ring(a, delta, part, ps, qr, kr);
     if (e != hipSuccess) return e;
     n_part = bwdq_ring_blocks(a);
   } else {
@@ -426,7 +434,7 @@ hipError_t run(const BwdArgs& a) {
   // the query-side workgroups are head-major, so each layer's partials are one run
   bool dalpha_done = false;
   if (bwdk_ring_supported(a) && (MODE == 0 || ps != nullptr)) {
-    const hipError_t e = launch_bwdk_ring(a, delta, ps, part, n_part / a.layers);
+    const hipError_t e = launch_bwdk_ring(a, delta, ps, part, n_part / a.layers, qr, kr);
     if (e != hipSuccess) return e;
     dalpha_done = true;  // the ring key side writes dalpha
   } else if (ps != nullptr) {
@@ -449,8 +457,8 @@ hipError_t run(const BwdArgs& a) {
 }  // namespace
 
 size_t bwd_workspace_bytes(int64_t BH, int64_t N, int dtype, int mode, int ps_slots) {
-  const size_t base = ps_offset_bytes(BH, N);
-  return dtype == 1 && mode == 1 ? base + (size_t)BH * (size_t)ps_slots * (size_t)N * sizeof(uint32_t) : base;
+  if (dtype != 1 || mode != 1) return rot_offset_bytes(BH, N);
+  return ps_offset_bytes(BH, N) + (size_t)BH * (size_t)ps_slots * (size_t)N * sizeof(uint32_t);
 }
 
 int ps_entry_slots(float alpha_hi, const int32_t* base, int n_base, int W) {

@@ -16,8 +16,12 @@
 // 16-row query slab whose diagonal is used); dK^T = Q^T dS^T and dV^T = dO^T P^T on MFMA
 // through transpose reads (addressed so that lane (n, g) accumulates dims 8g..8g+7 and
 // 32+8g..32+8g+7 of key n). The ring leads the keys by the largest covered offset: at step
-// p0 it receives the query rows p0 + kLead ... Offsets beyond the ring read raw q and dO rows
-// from global memory and use relative RoPE <R_r q_i, k_j>.
+// p0 it receives the query rows p0 + kLead ... Offsets beyond the ring read q and dO rows
+// from global memory. Integer offsets: raw q rows, rotated here (relative RoPE <R_r q_i, k_j>,
+// their dK terms added after R_j is undone). Interpolated offsets, where this kernel's VALU
+// work bounds it: the rotated rows K^ and Q^ come from the workspace, where the query side
+// (the kernel before this one) wrote every row, and a far entry's dK terms dS q^ join the
+// rotated frame before R_j is undone.
 //
 // Interpolated offsets: key j is the lower row (weight 1 - w) of query j + c and the upper
 // row (weight w) of query j + c - 1, for each entry (c = ceil(d), w = c - d). The query side
@@ -43,6 +47,8 @@ struct BkArgs {
   const float* delta;
   const uint32_t* ps;  // interpolated: (P, dS) per (query, entry), [head][ps_slots][N]
   int ps_slots;
+  const bf16_t* qr;    // interpolated: rotated rows R_i q_i, [head][N][D] (from the query side)
+  const bf16_t* kr;    // interpolated: rotated rows R_j k_j, [head][N][D] (from the query side)
   bf16_t* dk;
   bf16_t* dv;
   int N;
@@ -73,12 +79,12 @@ struct BkArgs {
 struct __align__(16) BkSmem {
   uint8_t ringQ[(kP + kMirror) * kRow];  // Q^ rows; bytes 128..135: (LSE * log2 e, Delta)
   uint8_t ringD[(kP + kMirror) * kRow];  // dO rows
-  float2 unc_cs[kMaxUnc][kHalf];  // far distances (interpolated: c and c - 1)
-  float2 base_cs[2][2][kHalf];  // [buffer][keys, queries]
-  float2 warm_cs[8][kHalf];
+  float2 unc_cs[kMaxUnc][kHalf];  // integer mode: the far offsets' rotations
+  float2 base_cs[2][2][kHalf];    // [buffer][keys, queries (integer mode)]
+  float2 warm_cs[8][kHalf];       // integer mode: the warm-up query rows' rotations
 };
 
-// raw q and dO rows of the far queries j0 + r + n (row N - 1 past the end; masked), and their
+// Q^ (rotated) and dO rows of the far queries j0 + r + n (row N - 1 past the end; masked), and their
 // LSE and Delta as loaded (the use masks the rows past the end: a select here, next to the
 // load, would make the wave wait for the load at once)
 template <int NF>
@@ -121,9 +127,9 @@ __device__ __forceinline__ void load_far_q(const int* fdist, int n_use, FarQ<NF>
   }
 }
 
-// Interpolated far entries, per entry: the lower query row j0 + c + n of the lane's key (raw
-// q and dO, the lane's dims), the row j0 + c - 1 spread over the wave (lane l: dword l & 31
-// of q if l < 32, else of dO) and the stored (P, dS) of the key's lower and upper query.
+// Interpolated far entries, per entry: the lower query row j0 + c + n of the lane's key (Q^
+// and dO, the lane's dims), the row j0 + c - 1 spread over the wave (lane l: dword l & 31
+// of Q^ if l < 32, else of dO) and the stored (P, dS) of the key's lower and upper query.
 template <int NF>
 struct FarQI {
   uint4 q[NF > 0 ? NF : 1][2];
@@ -222,14 +228,14 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
   auto S_far_w = [&](int x) -> float { if constexpr (DEV) return lcl.far_w[x]; else return a.far_w[x]; };
 
 
-  constexpr int n_unc = MODE == 1 ? 2 * NF : NF;
-  for (int x = tid; x < n_unc * kHalf; x += kThreads) {
-    const int u = x / kHalf, j = x % kHalf;
-    int fd;
-    if constexpr (DEV) fd = pl->s8.far_dist[MODE == 1 ? u >> 1 : u];
-    else fd = S_far_dist(MODE == 1 ? u >> 1 : u);  // (a's arrays: constant indices in DEV instances)
-    const int d = MODE == 1 ? fd - (u & 1) : fd;
-    sm.unc_cs[u][j] = rope_cs(d, a.rope.rev[j]);
+  if constexpr (MODE == 0) {
+    for (int x = tid; x < NF * kHalf; x += kThreads) {
+      const int u = x / kHalf, j = x % kHalf;
+      int d;
+      if constexpr (DEV) d = pl->s8.far_dist[u];
+      else d = S_far_dist(u);  // (a's arrays: constant indices in DEV instances)
+      sm.unc_cs[u][j] = rope_cs(d, a.rope.rev[j]);
+    }
   }
   float2 cs_t[8];
 #pragma unroll
@@ -280,13 +286,14 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
   const int s0 = seg * a.seg_len;
   const int s1 = s0 + a.seg_len < N ? s0 + a.seg_len : N;
   const size_t hoff = (size_t)head * (size_t)N * kD;
-  const bf16_t* Qh = a.q + hoff;
-  const bf16_t* Kh = a.k + hoff;
   const bf16_t* Vh = a.v + hoff;
   const bf16_t* Dh = a.dout + hoff;
   const float* Lh = a.lse + (size_t)head * N;
   const float* Th = a.delta + (size_t)head * N;
   const uint32_t* Sh = MODE == 1 ? a.ps + (size_t)head * a.ps_slots * N : nullptr;
+  // integer mode: raw q and k rows, rotated here; interpolated: the rotated rows
+  const bf16_t* Qs = MODE == 1 ? a.qr + hoff : a.q + hoff;
+  const bf16_t* Ks = MODE == 1 ? a.kr + hoff : a.k + hoff;
 
   auto row_elems = [&](int rb) -> int64_t {
     if (rb + 15 < N) return (int64_t)rb * kD + lane_off;
@@ -297,18 +304,21 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
     x[0] = *reinterpret_cast<const uint4*>(base + off);
     x[1] = *reinterpret_cast<const uint4*>(base + off + kHalf);
   };
-  // query row qb + n into the ring: Q^ (rotated by cs), dO, (LSE log2e, Delta); rows past
-  // the end hold zeros and LSE = +inf (P = 0)
+  // query row qb + n into the ring: Q^ (integer mode: rotated here by cs; interpolated: as
+  // the query side wrote it), dO, (LSE log2e, Delta); rows past the end hold zeros and
+  // LSE = +inf (P = 0)
   auto put_query = [&](int qb, const float2* cs, const uint4* q2, const uint4* d2, float lse, float dlt) {
     const bool live = qb + n < N;
-    float qf[16];
-    unpack8(q2[0], qf);
-    unpack8(q2[1], qf + 8);
-    uint4 r0, r1;
-    rotate_pack_f(qf, cs, &r0, &r1);
     const uint4 z = make_uint4(0, 0, 0, 0);
-    const uint4 d0 = live ? d2[0] : z, d1 = live ? d2[1] : z;
+    uint4 r0 = q2[0], r1 = q2[1];
+    if constexpr (MODE == 0) {
+      float qf[16];
+      unpack8(q2[0], qf);
+      unpack8(q2[1], qf + 8);
+      rotate_pack_f(qf, cs, &r0, &r1);
+    }
     if (!live) r0 = r1 = z;
+    const uint4 d0 = live ? d2[0] : z, d1 = live ? d2[1] : z;
     const float2 ld = live ? make_float2(lse * log2e, dlt) : make_float2(INFINITY, 0.f);
     const int slot = qb & (kP - 1);
     auto put = [&](int ro) {
@@ -327,10 +337,10 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
 
   // ---- warm-up: query rows [s0, s0 + lead) (lead is a step multiple)
   const int n_warm = S_lead / kT;
-  if (tid < kHalf * (n_warm + 2)) {
+  if (tid < kHalf * (MODE == 0 ? n_warm + 2 : 1)) {
     const int j = tid / kHalf, t = tid % kHalf;
-    if (j < n_warm) sm.warm_cs[j][t] = rope_cs(s0 + j * kT, a.rope.rev[t]);
-    else if (j == n_warm) sm.base_cs[0][0][t] = rope_cs(s0, a.rope.rev[t]);
+    if (MODE == 1 || j == n_warm) sm.base_cs[0][0][t] = rope_cs(s0, a.rope.rev[t]);
+    else if (j < n_warm) sm.warm_cs[j][t] = rope_cs(s0 + j * kT, a.rope.rev[t]);
     else sm.base_cs[0][1][t] = rope_cs(s0 + S_lead, a.rope.rev[t]);
   }
   // this step's keys and inserted query rows, prefetched one step ahead
@@ -359,11 +369,11 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
   };
   auto load_step = [&](int pb) {
     const int64_t ko = row_elems(pb + 16 * wave);
-    load2(Kh, ko, pk);
+    load2(Ks, ko, pk);
     load2(Vh, ko, pv);
     const int qb = pb + S_lead + 16 * wave;
     const int64_t qo = row_elems(qb);
-    load2(Qh, qo, pq);
+    load2(Qs, qo, pq);
     load2(Dh, qo, pd);
     const int r = qb + n < N ? qb + n : N - 1;
     plse = Lh[r];
@@ -373,7 +383,7 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
   load_ps(s0);
   __syncthreads();
   {
-    // kWB steps of warm rows in flight at once, then rotated and stored
+    // kWB steps of warm rows in flight at once, then (integer mode: rotated and) stored
     constexpr int kWB = 3;
     for (int j0 = 0; j0 < n_warm; j0 += kWB) {
       uint4 wq[kWB][2], wd[kWB][2];
@@ -382,7 +392,7 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
       for (int jj = 0; jj < kWB; ++jj) {
         if (j0 + jj < n_warm) {
           const int qb = s0 + (j0 + jj) * kT + 16 * wave;
-          load2(Qh, row_elems(qb), wq[jj]);
+          load2(Qs, row_elems(qb), wq[jj]);
           load2(Dh, row_elems(qb), wd[jj]);
           const int r = qb + n < N ? qb + n : N - 1;
           wl[jj] = Lh[r];
@@ -394,8 +404,10 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
         if (j0 + jj < n_warm) {
           const int qb = s0 + (j0 + jj) * kT + 16 * wave;
           float2 cs[8];
+          if constexpr (MODE == 0) {
 #pragma unroll
-          for (int t = 0; t < 8; ++t) cs[t] = compose(sm.warm_cs[j0 + jj][8 * g + t], cs_t[t]);
+            for (int t = 0; t < 8; ++t) cs[t] = compose(sm.warm_cs[j0 + jj][8 * g + t], cs_t[t]);
+          }
           put_query(qb, cs, wq[jj], wd[jj], wl[jj], wt[jj]);
         }
       }
@@ -404,17 +416,17 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
   FarQ<MODE == 0 ? NF : 0> fq;
   FarQI<MODE == 1 ? NF : 0> fi;
   if constexpr (MODE == 0)
-    load_far_q<NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fq, a, Qh, Dh, Lh, Th, s0 + 16 * wave, n, g, lane_off);
+    load_far_q<NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fq, a, Qs, Dh, Lh, Th, s0 + 16 * wave, n, g, lane_off);
   else
-    load_far_qi<NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fi, a, Qh, Dh, Sh, S_n_cov, s0 + 16 * wave, l, n, g);
+    load_far_qi<NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fi, a, Qs, Dh, Sh, S_n_cov, s0 + 16 * wave, l, n, g);
 
   int buf = 0;
   for (int p0 = s0; p0 < s1; p0 += kT, buf ^= 1) {
-    // ---- this step's keys (rotated K^ and raw V; raw K for the far offsets) and the query
-    // rows entering the ring
-    uint4 kh0, kh1;
+    // ---- this step's keys (rotated K^ and raw V; integer mode: raw K for the far offsets)
+    // and the query rows entering the ring
+    uint4 kh0 = pk[0], kh1 = pk[1];
     const uint4 kraw0 = pk[0], kraw1 = pk[1], v0 = pv[0], v1 = pv[1];
-    {
+    if constexpr (MODE == 0) {
       float2 csk[8], csq[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
@@ -426,6 +438,8 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
       unpack8(pk[1], kf + 8);
       rotate_pack_f(kf, csk, &kh0, &kh1);
       put_query(p0 + S_lead + 16 * wave, csq, pq, pd, plse, pdlt);
+    } else {
+      put_query(p0 + S_lead + 16 * wave, nullptr, pq, pd, plse, pdlt);
     }
     __syncthreads();
     const int pn = p0 + kT;
@@ -434,7 +448,7 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
     // whose reloads wait for every load in flight)
     if (wave == 0 && l < kHalf) {
       sm.base_cs[buf ^ 1][0][l] = rope_cs(pn, rev_l);
-      sm.base_cs[buf ^ 1][1][l] = rope_cs(pn + S_lead, rev_l);
+      if constexpr (MODE == 0) sm.base_cs[buf ^ 1][1][l] = rope_cs(pn + S_lead, rev_l);
     }
 
     const int j0 = p0 + 16 * wave;
@@ -552,6 +566,75 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
       }
     }
     load_step(pn < s1 ? pn : p0);
+    // ---- interpolated far offsets: Q^ and dO rows from global memory; dK^ and dV terms on
+    // VALU with the stored weights of the query, added in the rotated frame before R_j is
+    // undone below
+    if constexpr (MODE == 1) {
+      // the lower query row (the lane's) and the upper row, both Q^, weighted by the stored dS
+      // in fp32; the dO rows weighted by the stored P in bf16, as on the ring path.
+      // (Scheduling barriers keep each entry's cross-lane moves and unpacked values from
+      // spreading over the other entries and the MFMA part, where they would hold registers;
+      // the first one also keeps work of this section out of the window band, where it would
+      // wait for the far rows.)
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const float w = S_far_w(f);
+        // (a slot beyond the table weighs nothing)
+        const float keep = DEV && f >= S_n_far ? 0.f : 1.f;
+        const int rq = jk + S_far_dist(f);  // the key's lower far query (rows past the end count 0)
+        const uint32_t wl = rq < N ? fi.pl[f] : 0u, wh = rq - 1 < N ? fi.ph[f] : 0u;
+        const float al = keep * ps_ds(wl) * (1.f - w), ah = keep * ps_ds(wh) * w;
+        const uint32_t pw = pack_bf2(keep * ps_p(wl) * (1.f - w), keep * ps_p(wh) * w);
+#pragma unroll
+        for (int tsr = 0; tsr < 2; ++tsr) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          // words 2hh, 2hh + 1 of each 16-byte half of the lane's slice: dims 8g + 4hh..+3 and
+          // 32 + 8g + 4hh..+3
+          const uint4 a0 = tsr == 0 ? fi.q[f][0] : fi.d[f][0], a1 = tsr == 0 ? fi.q[f][1] : fi.d[f][1];
+          uint32_t lo[4] = {hh == 0 ? a0.x : a0.z, hh == 0 ? a0.y : a0.w, hh == 0 ? a1.x : a1.z, hh == 0 ? a1.y : a1.w};
+          uint32_t ex = fi.ex[f];
+          // (empty asm: pins the uses of these registers below this point)
+#pragma unroll
+          for (int x = 0; x < 4; ++x) asm volatile("" : "+v"(lo[x]));
+          asm volatile("" : "+v"(ex));
+          uint32_t hi[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            // the same word of row j0 + c - 1 (tensor tsr, 16-byte half x / 2, word 2hh + x % 2),
+            // for the lanes of key 0; every other lane takes lane n - 1's row
+            const int src = 32 * tsr + 16 * (x >> 1) + 4 * g + 2 * hh + (x & 1);
+            const int e = __builtin_amdgcn_ds_bpermute(4 * src, (int)ex);
+            hi[x] = (uint32_t)__builtin_amdgcn_update_dpp(e, (int)lo[x], 0x111, 0xf, 0xf, false);
+          }
+          // lo[x], hi[x]: word x of the lower and the upper row; dim 8g + 4hh + t is half t % 2 of
+          // word t / 2 (accumulator element acc[hh][t]), dim 32 + 8g + 4hh + t the same half of
+          // word 2 + t / 2 (element acc[2 + hh][t])
+          if (tsr == 0) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const uint32_t xa = lo[t >> 1], xb = lo[2 + (t >> 1)], ya = hi[t >> 1], yb = hi[2 + (t >> 1)];
+              const float la = (t & 1) ? bf_hi(xa) : bf_lo(xa), lb = (t & 1) ? bf_hi(xb) : bf_lo(xb);
+              const float ua = (t & 1) ? bf_hi(ya) : bf_lo(ya), ub = (t & 1) ? bf_hi(yb) : bf_lo(yb);
+              acck[hh][t] = fmaf(al, la, fmaf(ah, ua, acck[hh][t]));
+              acck[2 + hh][t] = fmaf(al, lb, fmaf(ah, ub, acck[2 + hh][t]));
+            }
+          } else {
+            // dO: (lower, upper) pairs of each dim against the bf16 weights (P_lo, P_hi)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+              accv[hh][t] = dot2(__builtin_amdgcn_perm(hi[t >> 1], lo[t >> 1], sel), pw, accv[hh][t]);
+              accv[2 + hh][t] = dot2(__builtin_amdgcn_perm(hi[2 + (t >> 1)], lo[2 + (t >> 1)], sel), pw,
+                                     accv[2 + hh][t]);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        }
+      }
+    }
     // undo R_j on dK^: dims 8g+t (acck[0], acck[1]) pair with 32+8g+t (acck[2], acck[3])
     float kl[8], khv[8], vl[8], vhv[8];
 #pragma unroll
@@ -564,10 +647,12 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
       vl[t] = accv[t >> 2][t & 3];
       vhv[t] = accv[2 + (t >> 2)][t & 3];
     }
-    // ---- far offsets: raw q (rotated by R_r, bf16) and dO rows from global memory; dK and dV
-    // terms on VALU with the bf16 weights (dS, P) of the query's diagonal lane. (Scheduling
-    // barrier: the far rows, requested at the end of the previous step, are first waited for
-    // here, not in the window band, where work hoisted from this section would wait for them)
+
+    // ---- integer far offsets: raw q (rotated by R_r, bf16) and dO rows from global memory;
+    // dK and dV terms on VALU with the bf16 weights (dS, P) of the query's diagonal lane, in
+    // the un-rotated frame. (Scheduling barrier: the far rows, requested at the end of the
+    // previous step, are first waited for here, not in the window band, where work hoisted
+    // from this section would wait for them)
     if constexpr (MODE == 0) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -605,76 +690,6 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
         vhv[2 * u + 1] = dot2(de[4 + u], p_hi, vhv[2 * u + 1]);
       }
     }
-    } else {
-      // interpolated far entries: the lower query row (the lane's, rotated by R_c) and the
-      // upper row (rotated by R_(c-1)) in fp32, weighted by the stored (P, dS) in fp32.
-      // (Scheduling barriers keep each entry's cross-lane moves and unpacked values from
-      // spreading over the other entries and the MFMA part, where they would hold registers.)
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const float w = S_far_w(f);
-        // (a slot beyond the table weighs nothing)
-        const float keep = DEV && f >= S_n_far ? 0.f : 1.f;
-        const int rq = jk + S_far_dist(f);  // the key's lower far query (rows past the end count 0)
-        const uint32_t wl = rq < N ? fi.pl[f] : 0u, wh = rq - 1 < N ? fi.ph[f] : 0u;
-        const float al = keep * ps_ds(wl) * (1.f - w), ah = keep * ps_ds(wh) * w;
-        const float pl = keep * ps_p(wl) * (1.f - w), ph = keep * ps_p(wh) * w;
-#pragma unroll
-        for (int tsr = 0; tsr < 2; ++tsr) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          // words 2hh, 2hh + 1 of each 16-byte half of the lane's slice: dims 8g + 4hh..+3 and
-          // 32 + 8g + 4hh..+3 (rotation partners)
-          const uint4 a0 = tsr == 0 ? fi.q[f][0] : fi.d[f][0], a1 = tsr == 0 ? fi.q[f][1] : fi.d[f][1];
-          uint32_t lo[4] = {hh == 0 ? a0.x : a0.z, hh == 0 ? a0.y : a0.w, hh == 0 ? a1.x : a1.z, hh == 0 ? a1.y : a1.w};
-          uint32_t ex = fi.ex[f];
-          // (empty asm: pins the uses of these registers below this point)
-#pragma unroll
-          for (int x = 0; x < 4; ++x) asm volatile("" : "+v"(lo[x]));
-          asm volatile("" : "+v"(ex));
-          uint32_t hi[4];
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            // the same word of row j0 + c - 1 (tensor tsr, 16-byte half x / 2, word 2hh + x % 2),
-            // for the lanes of key 0; every other lane takes lane n - 1's row
-            const int src = 32 * tsr + 16 * (x >> 1) + 4 * g + 2 * hh + (x & 1);
-            const int e = __builtin_amdgcn_ds_bpermute(4 * src, (int)ex);
-            hi[x] = (uint32_t)__builtin_amdgcn_update_dpp(e, (int)lo[x], 0x111, 0xf, 0xf, false);
-          }
-          // xl[0..3]: dims 8g + 4hh + t, xl[4..7]: dims 32 + 8g + 4hh + t (t < 4)
-          float xl[8], xh[8];
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            xl[(x >> 1) * 4 + 2 * (x & 1)] = bf_lo(lo[x]);
-            xl[(x >> 1) * 4 + 2 * (x & 1) + 1] = bf_hi(lo[x]);
-            xh[(x >> 1) * 4 + 2 * (x & 1)] = bf_lo(hi[x]);
-            xh[(x >> 1) * 4 + 2 * (x & 1) + 1] = bf_hi(hi[x]);
-          }
-          if (tsr == 0) {
-            const float2* cl = &sm.unc_cs[2 * f][8 * g + 4 * hh];
-            const float2* ch = &sm.unc_cs[2 * f + 1][8 * g + 4 * hh];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const float2 c0 = cl[t], c1 = ch[t];
-              const int u = 4 * hh + t;
-              kl[u] = fmaf(al, xl[t] * c0.x - xl[4 + t] * c0.y, kl[u]);
-              khv[u] = fmaf(al, xl[4 + t] * c0.x + xl[t] * c0.y, khv[u]);
-              kl[u] = fmaf(ah, xh[t] * c1.x - xh[4 + t] * c1.y, kl[u]);
-              khv[u] = fmaf(ah, xh[4 + t] * c1.x + xh[t] * c1.y, khv[u]);
-            }
-          } else {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const int u = 4 * hh + t;
-              vl[u] = fmaf(pl, xl[t], fmaf(ph, xh[t], vl[u]));
-              vhv[u] = fmaf(pl, xl[4 + t], fmaf(ph, xh[4 + t], vhv[u]));
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        }
-      }
     }
 
     // ---- epilogue: dK = scale * (the lane's dims), dV
@@ -688,8 +703,13 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
       for (int t = 0; t < 8; ++t) asm volatile("" : "+v"(kl[t]), "+v"(khv[t]), "+v"(vl[t]), "+v"(vhv[t]));
     }
     if (jk < s1) {
-      bf16_t* kp = a.dk + hoff + (int64_t)j0 * kD + lane_off;
-      bf16_t* vp = a.dv + hoff + (int64_t)j0 * kD + lane_off;
+      // (wave-uniform row bases plus the lane's 32-bit byte offset, made opaque here so that
+      // the compiler does not form per-lane 64-bit addresses before the loop and hold them
+      // through it)
+      char* kp = reinterpret_cast<char*>(a.dk + hoff + (int64_t)j0 * kD);
+      char* vp = reinterpret_cast<char*>(a.dv + hoff + (int64_t)j0 * kD);
+      uint32_t lb = 2u * (uint32_t)lane_off;
+      asm volatile("" : "+v"(lb));
       uint4 x0, x1, y0, y1;
       x0.x = pack_bf2(kl[0] * a.scale, kl[1] * a.scale);
       x0.y = pack_bf2(kl[2] * a.scale, kl[3] * a.scale);
@@ -701,17 +721,17 @@ __global__ __launch_bounds__(512, 1) void bwdk_ring_kernel(BkArgs a) {
       x1.w = pack_bf2(khv[6] * a.scale, khv[7] * a.scale);
       y0 = pack8(vl);
       y1 = pack8(vhv);
-      *reinterpret_cast<uint4*>(kp) = x0;
-      *reinterpret_cast<uint4*>(kp + kHalf) = x1;
-      *reinterpret_cast<uint4*>(vp) = y0;
-      *reinterpret_cast<uint4*>(vp + kHalf) = y1;
+      *reinterpret_cast<uint4*>(kp + lb) = x0;
+      *reinterpret_cast<uint4*>(kp + lb + 2 * kHalf) = x1;
+      *reinterpret_cast<uint4*>(vp + lb) = y0;
+      *reinterpret_cast<uint4*>(vp + lb + 2 * kHalf) = y1;
     }
     // the next step's far rows, requested after the stores: the far terms above feed only the
     // stores, so requested earlier the new rows would be held alongside them (and, before the
     // conditional store, they need copies at the end of the step that wait for every load)
     if constexpr (MODE == 0)
-      load_far_q<NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fq, a, Qh, Dh, Lh, Th, j0 + kT, n, g, lane_off);
-    if constexpr (MODE == 1) load_far_qi<NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fi, a, Qh, Dh, Sh, S_n_cov, j0 + kT, l, n, g);
+      load_far_q<NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fq, a, Qs, Dh, Lh, Th, j0 + kT, n, g, lane_off);
+    if constexpr (MODE == 1) load_far_qi<NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fi, a, Qs, Dh, Sh, S_n_cov, j0 + kT, l, n, g);
     __syncthreads();
   }
   if (a.dal_out != nullptr && (int)blockIdx.x < a.dal_layers && wave == 0) {
@@ -775,7 +795,7 @@ int bwdk_instance_key(const BwdArgs& f) {
 }
 
 hipError_t launch_bwdk_ring(const BwdArgs& f, const float* delta, const uint32_t* ps, const float* dal_part,
-                            int64_t dal_n) {
+                            int64_t dal_n, const bf16_t* qr, const bf16_t* kr) {
   if (f.mode == 1 && ps == nullptr) return hipErrorInvalidValue;
   BkArgs a;
   a.dal_part = dal_part;
@@ -790,6 +810,8 @@ hipError_t launch_bwdk_ring(const BwdArgs& f, const float* delta, const uint32_t
   a.delta = delta;
   a.ps = ps;
   a.ps_slots = f.ps_slots;
+  a.qr = qr;
+  a.kr = kr;
   a.dk = (bf16_t*)f.dk;
   a.dv = (bf16_t*)f.dv;
   a.N = (int)f.N;

@@ -16,10 +16,18 @@
 // dQ^T = K^T dS^T on MFMA, K^T read from the ring through the transpose read with addresses
 // chosen so that lane (n, g) accumulates dims 8g..8g+7 and 32+8g..32+8g+7 of query n: the
 // same dims whose RoPE angles it computed for the insert, so it undoes R_i in registers. Far
-// entries (beyond the ring) read raw K and V rows from global memory; their logits use the
-// relative rotation <R_d q, k>, their dP a VALU dot, and their dQ contribution
-// dS R_(-d) k is added in the un-rotated frame.
+// entries (beyond the ring) read K and V rows from global memory, their dP a VALU dot. In
+// interpolated mode the kernel writes every rotated row R_i q_i and R_j k_j of its segment to
+// the workspace (the key side, bound there by its VALU work, reads them instead of rotating
+// its own; the integer mode, bound by its memory traffic, does without the writes). Far K
+// rows: either those rotated rows (ROT instances, interpolated mode; the workgroup first
+// writes the rotated rows before its segment that its far entries read), whose logits are
+// then an MFMA with the rotated queries and whose dQ contribution dS k^ joins the rotated
+// frame before R_i is undone; or raw K rows, with the relative rotation <R_d q, k> for the
+// logits and dS R_(-d) k added in the un-rotated frame.
 #include "ring_common.h"
+
+#include <algorithm>
 
 namespace fib {
 namespace {
@@ -38,6 +46,9 @@ struct BqArgs {
   float* dalpha_part;  // one per workgroup (interpolated mode)
   uint32_t* ps;        // interpolated mode: (P, dS) (ps_pack) per [head][entry][query], or null
   int ps_slots;        // entries per head in ps
+  bf16_t* qr;          // interpolated: rotated rows R_i q_i, [head][N][D] (written)
+  bf16_t* kr;          // interpolated: rotated rows R_j k_j, [head][N][D] (written; ROT instances also read them)
+  int far_reach;       // the largest far distance in use (ROT instances; DEV: from the plan)
   int N;
   int W;
   int n_cov;
@@ -129,7 +140,38 @@ __device__ __forceinline__ void add_unrot(float* lo, float* hi, float c, uint4 x
   }
 }
 
-template <int MODE, int NC, int NF, int WAVES, bool DEV>
+// acc (the rotated frame: dims 8g+t in acc[t / 4][t % 4], 32+8g+t in acc[2 + t / 4][t % 4])
+// += c * x for a packed rotated row x
+__device__ __forceinline__ void add_rot(f4* acc, float c, uint4 x0, uint4 x1) {
+  float xf[16];
+  unpack8(x0, xf);
+  unpack8(x1, xf + 8);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    acc[t >> 2][t & 3] = fmaf(c, xf[t], acc[t >> 2][t & 3]);
+    acc[2 + (t >> 2)][t & 3] = fmaf(c, xf[8 + t], acc[2 + (t >> 2)][t & 3]);
+  }
+}
+
+// (cos, sin) of the angle sum of two (cos, sin) pairs, with the operations spelled out: the
+// warm-up and the step loop rotate the same rows and must round them identically
+__device__ __forceinline__ float2 compose_cs(float2 b, float2 t) {
+  return make_float2(fmaf(b.x, t.x, -(b.y * t.y)), fmaf(b.y, t.x, b.x * t.y));
+}
+// R x of 16 unpacked values (pairs (x[t], x[8 + t])), packed bf16 halves; spelled out as
+// compose_cs
+__device__ __forceinline__ void rotate_pack_x(const float* x, const float2* cs, uint4* out_lo, uint4* out_hi) {
+  float ra[8], rb[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    ra[t] = fmaf(x[t], cs[t].x, -(x[8 + t] * cs[t].y));
+    rb[t] = fmaf(x[8 + t], cs[t].x, x[t] * cs[t].y);
+  }
+  *out_lo = pack8(ra);
+  *out_hi = pack8(rb);
+}
+
+template <int MODE, int NC, int NF, int WAVES, bool DEV, bool ROT>
 __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
   constexpr int kThreads = 64 * WAVES;
   constexpr int kT = step_rows(WAVES);
@@ -164,6 +206,13 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
   auto S_far_dist = [&](int x) -> int { if constexpr (DEV) return lcl.far_dist[x]; else return a.far_dist[x]; };
   auto S_far_w = [&](int x) -> float { if constexpr (DEV) return lcl.far_w[x]; else return a.far_w[x]; };
   auto S_far_f = [&](int x) -> float { if constexpr (DEV) return lcl.far_f[x]; else return a.far_f[x]; };
+  // (DEV: over every far slot the kernel loads, the unused ones included)
+  int S_far_reach = a.far_reach;
+  if constexpr (DEV) {
+    S_far_reach = 0;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) S_far_reach = lcl.far_dist[f] > S_far_reach ? lcl.far_dist[f] : S_far_reach;
+  }
 
 
   {
@@ -230,6 +279,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
   const bf16_t* Oh = a.o + hoff;
   const bf16_t* Dh = a.dout + hoff;
   const float* Lh = a.lse + (size_t)head * N;
+  bf16_t* QRh = MODE == 1 ? a.qr + hoff : nullptr;
+  bf16_t* KRh = MODE == 1 ? a.kr + hoff : nullptr;
+  // the far entries' K rows: rotated (ROT) or raw
+  const bf16_t* Fh = ROT ? KRh : Kh;
 
   // stores row rb + n of the lane: K^ and V, both in natural dim order
   auto put_row = [&](int rb, uint4 k0, uint4 k1, uint4 v0, uint4 v1) {
@@ -252,6 +305,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
   auto load2 = [&](const bf16_t* base, int64_t off, uint4* x) {
     x[0] = *reinterpret_cast<const uint4*>(base + off);
     x[1] = *reinterpret_cast<const uint4*>(base + off + kHalf);
+  };
+  // the lane's part of row rb + n of a rotated-row buffer (a wave-uniform row base plus the
+  // lane's 32-bit byte offset, made opaque so that no per-lane 64-bit address is held)
+  auto put_rot = [&](bf16_t* base, int rb, uint4 x0, uint4 x1) {
+    char* b = reinterpret_cast<char*>(base + (int64_t)rb * kD);
+    uint32_t lb = 2u * (uint32_t)lane_off;
+    asm volatile("" : "+v"(lb));
+    *reinterpret_cast<uint4*>(b + lb) = x0;
+    *reinterpret_cast<uint4*>(b + lb + 2 * kHalf) = x1;
   };
 
   // ---- warm-up (as in the forward): ring rows [ws, s0)
@@ -296,22 +358,69 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
         if (j0 + jj < n_warm) {
           float2 cs[8];
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const float2 b = sm.warm_cs[j0 + jj][8 * g + t];
-            cs[t] = make_float2(b.x * cs_t[t].x - b.y * cs_t[t].y, b.y * cs_t[t].x + b.x * cs_t[t].y);
-          }
+          for (int t = 0; t < 8; ++t) cs[t] = compose_cs(sm.warm_cs[j0 + jj][8 * g + t], cs_t[t]);
           float kf[16];
           unpack8(wk[jj][0], kf);
           unpack8(wk[jj][1], kf + 8);
           uint4 kr0, kr1;
-          rotate_pack_f(kf, cs, &kr0, &kr1);
+          rotate_pack_x(kf, cs, &kr0, &kr1);
           put_row(ws + (j0 + jj) * kT + 16 * wave, kr0, kr1, wv[jj][0], wv[jj][1]);
+          // (the far entries of the first steps read these rows, which precede the segment)
+          if constexpr (ROT) put_rot(KRh, ws + (j0 + jj) * kT + 16 * wave, kr0, kr1);
         }
       }
     }
   }
+  if constexpr (ROT) {
+    // the rotated rows [s0 - far_reach, ws) that the far entries read before the step loop
+    // has written them (rows of the previous segment; its workgroup writes the same values)
+    const int xs = s0 - S_far_reach > 0 ? s0 - S_far_reach : 0;
+    const int n_ext = ws > xs ? (ws - xs + kT - 1) / kT : 0;  // 128-row blocks below ws
+    for (int j0 = 0; j0 < n_ext; j0 += 8) {
+      __syncthreads();  // (warm_cs is reused)
+      if (tid < kHalf * 8) {
+        const int j = tid / kHalf, t = tid % kHalf;
+        if (j0 + j < n_ext) sm.warm_cs[j][t] = rope_cs(ws - (j0 + j + 1) * kT, a.rope.rev[t]);
+      }
+      __syncthreads();
+      for (int jj = 0; jj < 8 && j0 + jj < n_ext; ++jj) {
+        const int rb = ws - (j0 + jj + 1) * kT + 16 * wave;
+        if (rb + 15 >= xs) {
+          const int r = rb + n >= 0 ? rb + n : 0;
+          uint4 xk[2];
+          load2(Kh, (int64_t)r * kD + 8 * g, xk);
+          float2 cs[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) cs[t] = compose_cs(sm.warm_cs[jj][8 * g + t], cs_t[t]);
+          float kf[16];
+          unpack8(xk[0], kf);
+          unpack8(xk[1], kf + 8);
+          uint4 kr0, kr1;
+          rotate_pack_x(kf, cs, &kr0, &kr1);
+          if (rb + n >= 0) put_rot(KRh, rb, kr0, kr1);
+        }
+      }
+    }
+    // the first segment's far rows before the step loop are all row 0 (clamped): its rotation,
+    // as the first step's insert forms it
+    if (s0 == 0 && wave == 0) {
+      uint4 xk[2];
+      load2(Kh, (int64_t)(n < N ? n : N - 1) * kD + 8 * g, xk);
+      float2 cs[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) cs[t] = compose_cs(sm.base_cs[0][8 * g + t], cs_t[t]);
+      float kf[16];
+      unpack8(xk[0], kf);
+      unpack8(xk[1], kf + 8);
+      uint4 kr0, kr1;
+      rotate_pack_x(kf, cs, &kr0, &kr1);
+      if (n < N) put_rot(KRh, 0, kr0, kr1);
+    }
+    // the rows written above and in the warm-up are read by other waves after this
+    __syncthreads();
+  }
   FarK<MODE, NF> fk;
-  load_far<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, NF, fk, a, Kh, s0 + 16 * wave, l, n, g, lane_off);
+  load_far<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, NF, fk, a, Fh, s0 + 16 * wave, l, n, g, lane_off);
   float dal = 0.f;  // d(alpha) contributions of this lane's queries
 
   int buf = 0;
@@ -319,10 +428,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
     // ---- insert: K^ and V of rows p0 + 16w + n; rotated Q of the step's queries
     float2 cs[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const float2 b = sm.base_cs[buf][8 * g + t];
-      cs[t] = make_float2(b.x * cs_t[t].x - b.y * cs_t[t].y, b.y * cs_t[t].x + b.x * cs_t[t].y);
-    }
+    for (int t = 0; t < 8; ++t) cs[t] = compose_cs(sm.base_cs[buf][8 * g + t], cs_t[t]);
     float qf[16];
     uint4 qh0, qh1;
     {
@@ -332,9 +438,14 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
       unpack8(pk[0], kf);
       unpack8(pk[1], kf + 8);
       uint4 kr0, kr1;
-      rotate_pack_f(kf, cs, &kr0, &kr1);
-      rotate_pack_f(qf, cs, &qh0, &qh1);
+      rotate_pack_x(kf, cs, &kr0, &kr1);
+      rotate_pack_x(qf, cs, &qh0, &qh1);
       put_row(p0 + 16 * wave, kr0, kr1, pv[0], pv[1]);
+      // the segment's rotated rows, for the key side (and the far entries of later steps)
+      if (MODE == 1 && p0 + 16 * wave + n < s1) {
+        put_rot(KRh, p0 + 16 * wave, kr0, kr1);
+        put_rot(QRh, p0 + 16 * wave, qh0, qh1);
+      }
     }
     const uint4 do0 = pd[0], do1 = pd[1];
     const float lse2 = plse * log2e;
@@ -409,14 +520,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const int u = MODE == 1 ? 2 * f : f;
-      uint4 r0, r1;
-      rotate_pack_f(qf, &sm.unc_cs[u][8 * g], &r0, &r1);
+      // the query operand: the rotated query against rotated rows (ROT), else R_d q
+      uint4 r0 = qh0, r1 = qh1;
+      if constexpr (!ROT) rotate_pack_f(qf, &sm.unc_cs[u][8 * g], &r0, &r1);
       f4 S = {0, 0, 0, 0};
       S = mfma32(as_bf8(fk.k[f][0]), as_bf8(r0), S);
       S = mfma32(as_bf8(fk.k[f][1]), as_bf8(r1), S);
       s_f[f] = sel4(S, l);
       if (MODE == 1) {
-        rotate_pack_f(qf, &sm.unc_cs[u + 1][8 * g], &r0, &r1);
+        if constexpr (!ROT) rotate_pack_f(qf, &sm.unc_cs[u + 1][8 * g], &r0, &r1);
         uint4 kh[2];
         upper_rows(fk.k[f], fk.ex[f], g, kh);
         f4 H = {0, 0, 0, 0};
@@ -503,47 +615,54 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
       }
     }
     if constexpr (MODE == 1) prefetch();
-    // undo R_i: dims 8g+t (acc[0], acc[1]) pair with 32+8g+t (acc[2], acc[3])
     float ql[8], qhv[8];
+    // ---- far entries: dP on VALU, P from the diagonal lane, dS; dQ in the rotated frame
+    // (ROT: before R_i is undone) or in the un-rotated frame (after)
+    uint32_t ps_f[MODE == 1 && NF > 0 ? NF : 1];
+    auto far_terms = [&]() {
+      if constexpr (MODE == 1) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int u = MODE == 1 ? 2 * f : f;
+        float s = s_f[f];
+        if (MODE == 1) s = fmaf(S_far_w(f), sd_f[f], s);
+        float x = diag_lane ? s * sl2 : -INFINITY;
+        if (early && S_far_dist(f) > iq) x = -INFINITY;
+        if (DEV && f >= S_n_far) x = -INFINITY;  // slot beyond the table
+        // P of the query, from its diagonal lane to all four
+        const float p = __uint_as_float(
+            (uint32_t)__builtin_amdgcn_ds_bpermute(diag_addr, (int)__float_as_uint(ex2(x - lse2))));
+        const float dp_lo = quad_add(dot16_bf(do0, do1, fv.k[f][0], fv.k[f][1]));
+        if (MODE == 0) {
+          const float ds = p * (dp_lo - dlt);
+          if constexpr (ROT) add_rot(acc, ds, fk.k[f][0], fk.k[f][1]);
+          else add_unrot(ql, qhv, ds, fk.k[f][0], fk.k[f][1], &sm.unc_cs[u][8 * g]);
+        } else {
+          uint4 vh[2], kh[2];
+          upper_rows(fv.k[f], fv.ex[f], g, vh);
+          const float dp_hi = quad_add(dot16_bf(do0, do1, vh[0], vh[1]));
+          const float w = S_far_w(f);
+          const float ds = p * (fmaf(w, dp_hi - dp_lo, dp_lo) - dlt);
+          if constexpr (ROT) add_rot(acc, ds * (1.f - w), fk.k[f][0], fk.k[f][1]);
+          else add_unrot(ql, qhv, ds * (1.f - w), fk.k[f][0], fk.k[f][1], &sm.unc_cs[u][8 * g]);
+          upper_rows(fk.k[f], fk.ex[f], g, kh);
+          if constexpr (ROT) add_rot(acc, ds * w, kh[0], kh[1]);
+          else add_unrot(ql, qhv, ds * w, kh[0], kh[1], &sm.unc_cs[u + 1][8 * g]);
+          // the diagonal lane holds s_hi - s_lo of its query
+          if (diag_lane) dal_step = fmaf(-S_far_f(f), ds * a.scale * sd_f[f] + p * (dp_hi - dp_lo), dal_step);
+          ps_f[f] = ps_pack(p, ds);
+        }
+      }
+    };
+    if constexpr (ROT) far_terms();
+    // undo R_i: dims 8g+t (acc[0], acc[1]) pair with 32+8g+t (acc[2], acc[3])
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const float x = acc[t >> 2][t & 3], y = acc[2 + (t >> 2)][t & 3];
       ql[t] = x * cs[t].x + y * cs[t].y;
       qhv[t] = y * cs[t].x - x * cs[t].y;
     }
-
-    // ---- far entries: dP on VALU, P from the diagonal lane, dS, dQ in the un-rotated frame
-    uint32_t ps_f[MODE == 1 && NF > 0 ? NF : 1];
-    if constexpr (MODE == 1) __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int u = MODE == 1 ? 2 * f : f;
-      float s = s_f[f];
-      if (MODE == 1) s = fmaf(S_far_w(f), sd_f[f], s);
-      float x = diag_lane ? s * sl2 : -INFINITY;
-      if (early && S_far_dist(f) > iq) x = -INFINITY;
-      if (DEV && f >= S_n_far) x = -INFINITY;  // slot beyond the table
-      // P of the query, from its diagonal lane to all four
-      const float p = __uint_as_float(
-          (uint32_t)__builtin_amdgcn_ds_bpermute(diag_addr, (int)__float_as_uint(ex2(x - lse2))));
-      const float dp_lo = quad_add(dot16_bf(do0, do1, fv.k[f][0], fv.k[f][1]));
-      if (MODE == 0) {
-        const float ds = p * (dp_lo - dlt);
-        add_unrot(ql, qhv, ds, fk.k[f][0], fk.k[f][1], &sm.unc_cs[u][8 * g]);
-      } else {
-        uint4 vh[2], kh[2];
-        upper_rows(fv.k[f], fv.ex[f], g, vh);
-        const float dp_hi = quad_add(dot16_bf(do0, do1, vh[0], vh[1]));
-        const float w = S_far_w(f);
-        const float ds = p * (fmaf(w, dp_hi - dp_lo, dp_lo) - dlt);
-        add_unrot(ql, qhv, ds * (1.f - w), fk.k[f][0], fk.k[f][1], &sm.unc_cs[u][8 * g]);
-        upper_rows(fk.k[f], fk.ex[f], g, kh);
-        add_unrot(ql, qhv, ds * w, kh[0], kh[1], &sm.unc_cs[u + 1][8 * g]);
-        // the diagonal lane holds s_hi - s_lo of its query
-        if (diag_lane) dal_step = fmaf(-S_far_f(f), ds * a.scale * sd_f[f] + p * (dp_hi - dp_lo), dal_step);
-        ps_f[f] = ps_pack(p, ds);
-      }
-    }
+    if constexpr (!ROT) far_terms();
 
     // ---- epilogue: dQ = scale * (the lane's 16 dims), Delta
     if constexpr (MODE == 1) {
@@ -552,7 +671,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
       for (int t = 0; t < 8; ++t) asm volatile("" : "+v"(ql[t]), "+v"(qhv[t]));
     }
     if (iq < s1) {
-      bf16_t* dp = a.dq + hoff + (int64_t)i0w * kD + lane_off;
+      // (a wave-uniform row base plus the lane's 32-bit byte offset, made opaque here so that
+      // the compiler does not form a per-lane 64-bit address before the loop and hold it)
+      char* dp = reinterpret_cast<char*>(a.dq + hoff + (int64_t)i0w * kD);
+      uint32_t lb = 2u * (uint32_t)lane_off;
+      asm volatile("" : "+v"(lb));
       uint4 x0, x1;
       x0.x = pack_bf2(ql[0] * a.scale, ql[1] * a.scale);
       x0.y = pack_bf2(ql[2] * a.scale, ql[3] * a.scale);
@@ -562,8 +685,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
       x1.y = pack_bf2(qhv[2] * a.scale, qhv[3] * a.scale);
       x1.z = pack_bf2(qhv[4] * a.scale, qhv[5] * a.scale);
       x1.w = pack_bf2(qhv[6] * a.scale, qhv[7] * a.scale);
-      *reinterpret_cast<uint4*>(dp) = x0;
-      *reinterpret_cast<uint4*>(dp + kHalf) = x1;
+      *reinterpret_cast<uint4*>(dp + lb) = x0;
+      *reinterpret_cast<uint4*>(dp + lb + 2 * kHalf) = x1;
       if (g == 0) (a.delta + (size_t)head * N + i0w)[n] = dlt;
       dal += dal_step;  // rows past the segment's end belong to another workgroup
       if (MODE == 1 && a.ps != nullptr && diag_lane) {
@@ -577,7 +700,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
           if (!DEV || f < S_n_far) pq[(size_t)(S_n_cov + f) * N] = ps_f[f];  // (DEV: NF bounds the far count)
       }
     }
-    load_far<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, NF, fk, a, Kh, i0w + kT, l, n, g, lane_off);
+    load_far<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, NF, fk, a, Fh, i0w + kT, l, n, g, lane_off);
     __syncthreads();
   }
   if (MODE == 1) {
@@ -600,46 +723,48 @@ __global__ __launch_bounds__(64 * WAVES, 1) void bwdq_ring_kernel(BqArgs a) {
 constexpr bool fits8(int nc, int nf) { return !(nc > 8 && nf > 3); }
 
 // instances that plan() never picks (not compiled); at 4 waves the table is split again
-// with the longer ring reach, so any 4-wave instance can occur
-template <int MODE, int NC, int NF, int WAVES>
+// with the longer ring reach, so any 4-wave instance can occur. Far rows from the rotated
+// rows (ROT) are picked for interpolated mode, 8 waves and at least one far entry only.
+template <int MODE, int NC, int NF, int WAVES, bool ROT>
 constexpr bool unused_instance() {
-  return WAVES == 8 && !fits8(NC, NF);
+  return (WAVES == 8 && !fits8(NC, NF)) || (ROT && (MODE != 1 || WAVES != 8 || NF == 0));
 }
 
-template <int MODE, int NC, int NF, int WAVES, bool DEV>
+template <int MODE, int NC, int NF, int WAVES, bool DEV, bool ROT>
 hipError_t launch(const BqArgs& a, unsigned blocks, hipStream_t s) {
-  if constexpr (unused_instance<MODE, NC, NF, WAVES>()) {
+  if constexpr (unused_instance<MODE, NC, NF, WAVES, ROT>()) {
     return hipErrorInvalidValue;
   } else {
     const size_t smem = sizeof(BqSmem);
     static std::atomic<uint32_t> lds_set{0};
-    hipError_t e = ensure_lds_limit(bwdq_ring_kernel<MODE, NC, NF, WAVES, DEV>, lds_set, (int)smem);
+    hipError_t e = ensure_lds_limit(bwdq_ring_kernel<MODE, NC, NF, WAVES, DEV, ROT>, lds_set, (int)smem);
     if (e != hipSuccess) return e;
-    bwdq_ring_kernel<MODE, NC, NF, WAVES, DEV><<<blocks, 64 * WAVES, smem, s>>>(a);
+    bwdq_ring_kernel<MODE, NC, NF, WAVES, DEV, ROT><<<blocks, 64 * WAVES, smem, s>>>(a);
     return hipGetLastError();
   }
 }
 
-// kernel instance by (covered entries rounded up to 8 or 16, far entries); with alpha in
-// device memory (DEV) the counts are bounds over the alpha range
-template <int MODE, int WAVES, bool DEV = false>
-hipError_t launch_far(const BqArgs& a, int n_far, unsigned blocks, hipStream_t s) {
-  if (a.n_cov > 8) {
-    switch (n_far) {
-      case 0: return launch<MODE, 16, 0, WAVES, DEV>(a, blocks, s);
-      case 1: return launch<MODE, 16, 1, WAVES, DEV>(a, blocks, s);
-      case 2: return launch<MODE, 16, 2, WAVES, DEV>(a, blocks, s);
-      case 3: return launch<MODE, 16, 3, WAVES, DEV>(a, blocks, s);
-      default: return launch<MODE, 16, 4, WAVES, DEV>(a, blocks, s);
-    }
-  }
+template <int MODE, int NC, int WAVES, bool DEV, bool ROT>
+hipError_t launch_nf(const BqArgs& a, int n_far, unsigned blocks, hipStream_t s) {
   switch (n_far) {
-    case 0: return launch<MODE, 8, 0, WAVES, DEV>(a, blocks, s);
-    case 1: return launch<MODE, 8, 1, WAVES, DEV>(a, blocks, s);
-    case 2: return launch<MODE, 8, 2, WAVES, DEV>(a, blocks, s);
-    case 3: return launch<MODE, 8, 3, WAVES, DEV>(a, blocks, s);
-    default: return launch<MODE, 8, 4, WAVES, DEV>(a, blocks, s);
+    case 0: return launch<MODE, NC, 0, WAVES, DEV, false>(a, blocks, s);
+    case 1: return launch<MODE, NC, 1, WAVES, DEV, ROT>(a, blocks, s);
+    case 2: return launch<MODE, NC, 2, WAVES, DEV, ROT>(a, blocks, s);
+    case 3: return launch<MODE, NC, 3, WAVES, DEV, ROT>(a, blocks, s);
+    default: return launch<MODE, NC, 4, WAVES, DEV, ROT>(a, blocks, s);
   }
+}
+
+// kernel instance by (covered entries rounded up to 8 or 16, far entries, far rows rotated);
+// with alpha in device memory (DEV) the counts are bounds over the alpha range
+template <int MODE, int WAVES, bool DEV = false>
+hipError_t launch_far(const BqArgs& a, int n_far, bool rot, unsigned blocks, hipStream_t s) {
+  if (WAVES == 8 && rot) {
+    return a.n_cov > 8 ? launch_nf<MODE, 16, WAVES, DEV, true>(a, n_far, blocks, s)
+                       : launch_nf<MODE, 8, WAVES, DEV, true>(a, n_far, blocks, s);
+  }
+  return a.n_cov > 8 ? launch_nf<MODE, 16, WAVES, DEV, false>(a, n_far, blocks, s)
+                     : launch_nf<MODE, 8, WAVES, DEV, false>(a, n_far, blocks, s);
 }
 
 // With alpha in device memory the counts are upper bounds over the alpha range.
@@ -683,7 +808,7 @@ int64_t bwdq_ring_blocks(const BwdArgs& f) {
   return ring_segments(f.BH, tiles) * f.BH;
 }
 
-hipError_t launch_bwdq_ring(const BwdArgs& f, float* delta, float* part, uint32_t* ps) {
+hipError_t launch_bwdq_ring(const BwdArgs& f, float* delta, float* part, uint32_t* ps, bf16_t* qr, bf16_t* kr) {
   BqArgs a;
   a.q = (const bf16_t*)f.q;
   a.k = (const bf16_t*)f.k;
@@ -696,6 +821,8 @@ hipError_t launch_bwdq_ring(const BwdArgs& f, float* delta, float* part, uint32_
   a.dalpha_part = part;
   a.ps = ps;
   a.ps_slots = f.ps_slots;
+  a.qr = qr;
+  a.kr = kr;
   a.plan = f.plan;
   a.N = (int)f.N;
   a.W = f.W;
@@ -733,20 +860,37 @@ hipError_t launch_bwdq_ring(const BwdArgs& f, float* delta, float* part, uint32_
   a.rope = f.rope;
   a.n_far = n_far;
   a.heads_per_plan = f.heads_per_plan;
+  // Interpolated mode: far rows from the rotated rows when the rows before a segment that its
+  // workgroup must rotate first (far reach minus the ring warm-up) are at most a quarter of
+  // the segment.
+  // With alpha in device memory the reach is bounded over the range: the largest usable
+  // base entry's ceil(alpha_hi f) + 1 (the plan's far distances are alpha f rounded).
+  int reach = 0;
+  if (f.plan != nullptr) {
+    for (int e = 0; e < f.n_base; ++e) {
+      if ((double)f.alpha_lo * (double)f.base[e] >= (double)f.N) continue;
+      const double d = ceil((double)f.alpha_hi * (double)f.base[e]) + 1.0;
+      reach = (int)std::max<double>(reach, std::min<double>(d, (double)(f.N - 1)));
+    }
+  } else {
+    for (int x = 0; x < n_far; ++x) reach = std::max(reach, a.far_dist[x]);
+  }
+  a.far_reach = reach;
+  const bool rot = f.mode == 1 && waves == 8 && n_far > 0 && (int64_t)std::max(0, reach - a.warm) * 4 <= (int64_t)a.seg_len;
   if (f.plan != nullptr) {
     if (f.mode == 0) {
-      return waves == 8 ? launch_far<0, 8, true>(a, n_far, (unsigned)blocks, f.stream)
-                        : launch_far<0, 4, true>(a, n_far, (unsigned)blocks, f.stream);
+      return waves == 8 ? launch_far<0, 8, true>(a, n_far, rot, (unsigned)blocks, f.stream)
+                        : launch_far<0, 4, true>(a, n_far, rot, (unsigned)blocks, f.stream);
     }
-    return waves == 8 ? launch_far<1, 8, true>(a, n_far, (unsigned)blocks, f.stream)
-                      : launch_far<1, 4, true>(a, n_far, (unsigned)blocks, f.stream);
+    return waves == 8 ? launch_far<1, 8, true>(a, n_far, rot, (unsigned)blocks, f.stream)
+                      : launch_far<1, 4, true>(a, n_far, rot, (unsigned)blocks, f.stream);
   }
   if (f.mode == 0) {
-    return waves == 8 ? launch_far<0, 8>(a, n_far, (unsigned)blocks, f.stream)
-                      : launch_far<0, 4>(a, n_far, (unsigned)blocks, f.stream);
+    return waves == 8 ? launch_far<0, 8>(a, n_far, rot, (unsigned)blocks, f.stream)
+                      : launch_far<0, 4>(a, n_far, rot, (unsigned)blocks, f.stream);
   }
-  return waves == 8 ? launch_far<1, 8>(a, n_far, (unsigned)blocks, f.stream)
-                    : launch_far<1, 4>(a, n_far, (unsigned)blocks, f.stream);
+  return waves == 8 ? launch_far<1, 8>(a, n_far, rot, (unsigned)blocks, f.stream)
+                    : launch_far<1, 4>(a, n_far, rot, (unsigned)blocks, f.stream);
 }
 
 }  // namespace fib

@@ -183,17 +183,19 @@ size_t bwd_workspace_bytes(int64_t BH, int64_t N, int dtype, int mode, int ps_sl
 int ps_entry_slots(float alpha_hi, const int32_t* base, int n_base, int W);
 hipError_t launch_bwd(const BwdArgs& a);
 // query side of the backward on the LDS ring (bf16, W <= 16): dQ, Delta [BH * N], one
-// d(alpha) partial per workgroup (bwdq_ring_blocks of them) and, in interpolated mode when ps
-// is not null, each (query, table entry)'s softmax weight P and dS (one ps_pack word) in
-// ps[(head * a.ps_slots + entry) * N + query]
+// d(alpha) partial per workgroup (bwdq_ring_blocks of them) and, in interpolated mode, the
+// rotated rows R_i q_i in qr and R_j k_j in kr ([BH][N][D] bf16, every row) and, when ps is
+// not null, each (query, table entry)'s softmax weight P and dS (one ps_pack word) in
+// ps[(head * a.ps_slots + entry) * N + query] (qr and kr are not used in integer mode)
 bool bwdq_ring_supported(const BwdArgs& a);
 int64_t bwdq_ring_blocks(const BwdArgs& a);
-hipError_t launch_bwdq_ring(const BwdArgs& a, float* delta, float* part, uint32_t* ps);
+hipError_t launch_bwdq_ring(const BwdArgs& a, float* delta, float* part, uint32_t* ps, bf16_t* qr, bf16_t* kr);
 // key side on the LDS ring (bf16, W <= 16): dK, dV from Delta; in interpolated mode also
-// from the (P, dS) pairs ps that the ring query side stored (required there)
+// from the rotated rows qr, kr and the (P, dS) pairs ps that the ring query side stored
+// (required there)
 bool bwdk_ring_supported(const BwdArgs& a);
 // Also writes dalpha (one value per layer) from the query side's dal_n partials per layer
 hipError_t launch_bwdk_ring(const BwdArgs& a, const float* delta, const uint32_t* ps, const float* dal_part,
-                            int64_t dal_n);
+                            int64_t dal_n, const bf16_t* qr, const bf16_t* kr);
 
 }  // namespace fib

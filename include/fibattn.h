@@ -134,7 +134,8 @@ int fib_sparse_attn_bwd(const void* q, const void* k, const void* v, const void*
  * of fib_sparse_attn_bwd, plus FIB_ERR_SCRATCH (nothing launched) when
  * fib_sparse_attn_bwd_workspace_size_for(B, H, N, D, dtype, mode, W, alpha, base, n_base)
  * exceeds the scratch: e.g. every FIB_INT call up to about 16M (b, h, n) rows, and FIB_INTERP
- * bf16 calls up to 64 MiB / (8 + 4 x entries) bytes per row (about 1.1M rows with 11 entries).
+ * bf16 calls up to 64 MiB / (264 + 4 x entries) bytes per row (about 220K rows with 11
+ * entries).
  * All calls on one GPU share the array: calls that overlap in time on that GPU (different
  * streams, or host threads) race and must be serialized by the caller.
  */
@@ -148,8 +149,9 @@ int fib_sparse_attn_bwd_noalloc(const void* q, const void* k, const void* v, con
 
 /* Bytes of device workspace fib_sparse_attn_bwd needs for these sizes (0 on bad sizes),
  * enough for any base and alpha: about 4 bytes per (b, h, n) row for Delta = <dO, O> and the
- * d(alpha) partials, plus, for bf16 inputs in FIB_INTERP mode, 4 bytes per row and possible
- * table entry (FIB_MAX_BASE of them) in which the query side hands each (query, entry)
+ * d(alpha) partials; for bf16 inputs in FIB_INTERP mode also 4 * D bytes per row, where the
+ * query side leaves the RoPE-rotated q and k rows (bf16) for the key side, and 4 bytes per
+ * row and possible table entry (FIB_MAX_BASE of them) in which it hands each (query, entry)
  * pair's softmax weight and dS to the key side. */
 size_t fib_sparse_attn_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D,
                                           int dtype, int mode);

@@ -228,11 +228,13 @@ def test_workspace_size():
     assert F.bwd_workspace_size(0, 1, 8, 64, F.BF16, F.INT) == 0
     assert F.bwd_workspace_size(1, 1, 8, 32, F.BF16, F.INT) == 0
     # for a known base and alpha: the entries alpha * f >= W only (11 at alpha 1.5, W 12)
+    # (interpolated bf16 calls also hold the rotated q and k rows: 2 x 64 bf16 per row)
     exact = F.bwd_workspace_size(1, 32, 131072, 64, F.BF16, F.INTERP, 12, 1.5, FIB_BASE)
     int_ws = F.bwd_workspace_size(1, 32, 131072, 64, F.BF16, F.INT)
-    assert exact - int_ws == 32 * 131072 * 4 * 11
+    assert exact - int_ws == 32 * 131072 * (2 * 64 * 2 + 4 * 11)
     assert F.bwd_workspace_size(1, 32, 131072, 64, F.BF16, F.INT, 12, 1.5, FIB_BASE) == int_ws
-    assert big - int_ws == 32 * 131072 * 4 * 32
+    assert big - int_ws == 32 * 131072 * (2 * 64 * 2 + 4 * 32)
+    assert int_ws == F.bwd_workspace_size(1, 32, 131072, 64, F.F32, F.INT)
     # fp32 inputs use no (P, dS) words; bad arguments give 0
     assert F.bwd_workspace_size(1, 2, 100, 64, F.F32, F.INTERP, 12, 1.5, FIB_BASE) == \
         F.bwd_workspace_size(1, 2, 100, 64, F.F32, F.INT)
@@ -269,10 +271,12 @@ def test_bwd_noalloc_argument_errors():
     assert call(lse=None) == -1 and call(dq=None) == -1
     assert call(mode=5) == -9 and call(W=0) == -5 and call(alpha=float("nan")) == -6
     assert call(B=0) == -2 and call(dtype=3) == -4 and call(nb=0) == -7
-    # the long-context interpolated backward needs ~201 MB of (P, dS) words: more than 64 MiB
+    # the long-context interpolated backward needs ~1.1 GB for the rotated rows and ~201 MB of
+    # (P, dS) words: more than 64 MiB
     need = F.bwd_workspace_size(1, 32, 131072, 64, F.BF16, F.INTERP, 12, 1.5, FIB_BASE)
     assert need > F.NOALLOC_SCRATCH_BYTES
     assert call(B=1, H=32, N=131072, alpha=1.5) == -15
-    # its integer-mode backward fits
+    # its integer-mode backward fits, and so does the interpolated one at the training shape
     assert F.bwd_workspace_size(1, 32, 131072, 64, F.BF16, F.INT, 12, 1.5, FIB_BASE) <= F.NOALLOC_SCRATCH_BYTES
+    assert F.bwd_workspace_size(8, 8, 1024, 64, F.BF16, F.INTERP, 12, 1.05, FIB_BASE) <= F.NOALLOC_SCRATCH_BYTES
     assert "scratch" in F.status_string(-15)
