@@ -150,6 +150,63 @@ def test_long_context_backward_sampled(long_inputs, mode):
         assert abs(float(da4.item()) - ra) <= 2e-2 * abs(ra)
 
 
+def _sixteen_heads(N, seed):
+    """16-head inputs whose heads 0 and 15 hold seeded N(0, 1) draws and the rest zeros (their
+    gradients and d(alpha) parts are 0), with the fp64 copies of the two live heads."""
+    live = inputs(seed, (1, 2, N, 64), BF16, with_dout=True)
+    out = []
+    for t, t64 in live:
+        z = torch.zeros((1, 16, N, 64), dtype=t.dtype, device=t.device)
+        z[:, 0], z[:, 15] = t[:, 0], t[:, 1]
+        out.append((z, t64))
+    return out
+
+
+def test_interp_backward_far_rows_rotated():
+    """Interpolated backward where the query side reads its far K rows as rotated rows that it
+    wrote itself (16 heads of 65536 rows: segments of 2048 rows, far distances 549 and 889 at
+    alpha 0.9, so each workgroup first rotates the rows before its segment): every row of the
+    two live heads against the oracle, and dalpha."""
+    N, a = 65536, np.float32(0.9)
+    say(f"bwd rotated far rows B1H16N{N} alpha={a}")
+    qkvd = _sixteen_heads(N, 7700)
+    dq, dk, dv, da = gpu_grads(qkvd, 12, a, FIB_BASE, INTERP)
+    (_, q64), (_, k64), (_, v64), (_, d64) = qkvd
+    rq, rk, rv, ra, rsc = O.backward(q64, k64, v64, d64, 12, a, FIB_BASE, 10000.0, INTERP, workers=WORKERS,
+                                     return_scale=True)
+    for h, hr in ((0, 0), (15, 1)):
+        eq = grad_excess(host(dq[0, h]), rq[0, hr], BF16)
+        ek = grad_excess(host(dk[0, h]), rk[0, hr], BF16)
+        ev = grad_excess(host(dv[0, h]), rv[0, hr], BF16)
+        say(f"  head {h} dQ {eq:.2e} dK {ek:.2e} dV {ev:.2e}")
+        assert max(eq, ek, ev) <= TOL[BF16]
+    for h in range(1, 15):
+        assert not dq[0, h].any() and not dk[0, h].any() and not dv[0, h].any()
+    dalpha_check(float(da.item()), ra, rsc, BF16)
+
+
+def test_interp_backward_far_rows_rotated_device_alpha():
+    """The same path with alpha in device memory (16 heads of 131072 rows, alpha 0.9 in the
+    declared range [0.85, 0.95]): gradients and dalpha against the host-alpha call, whose
+    kernels read the same table."""
+    N, a = 131072, np.float32(0.9)
+    say(f"bwd rotated far rows, device alpha, B1H16N{N}")
+    qkvd = _sixteen_heads(N, 7800)
+    (q, _), (k, _), (v, _), (do, _) = qkvd
+    o, lse = F.fwd(q, k, v, 12, a, FIB_BASE, 10000.0, INTERP)
+    ref = F.bwd(q, k, v, o, lse, do, 12, a, FIB_BASE, 10000.0, INTERP)
+    ad = torch.tensor([float(a)], dtype=torch.float32, device="cuda")
+    got = F.bwd_dev(q, k, v, o, lse, do, 12, ad, (0.85, 0.95), FIB_BASE, 10000.0, INTERP)
+    torch.cuda.synchronize()
+    for name, x, y in zip(("dQ", "dK", "dV"), ref[:3], got[:3]):
+        e = maxabs(host(x), host(y))
+        say(f"  {name} device vs host alpha {e:.2e}")
+        assert e <= TOL[BF16], name
+    ea = abs(float(got[3].item()) - float(ref[3].item()))
+    say(f"  dalpha device {float(got[3].item()):.7g} host {float(ref[3].item()):.7g}")
+    assert ea <= 1e-3 * abs(float(ref[3].item()))
+
+
 def test_backward_deterministic():
     say("bwd determinism")
     qkvd = inputs(9, (1, 4, 2500, 64), BF16, with_dout=True)

@@ -9,9 +9,9 @@ as a difference between runs, including in dalpha, which sums many per-query par
 nearly cancel and so amplifies any such error.
 
 The cases cover the kernel families that the launch logic picks: the LDS-ring kernels at
-8 and 4 waves with 8 and 16 covered slots and up to 4 far slots, the general kernels (fp32,
-window wider than the band), the gather kernel of small forwards, alpha in device memory,
-and layer stacks.
+8 and 4 waves with 8 and 16 covered slots and up to 4 far slots, far rows read pre-rotated,
+the general kernels (fp32, window wider than the band), the gather kernel of small forwards,
+alpha in device memory, and layer stacks.
 """
 import numpy as np
 import pytest
@@ -37,6 +37,10 @@ CASES = [
     ("general-f32", (1, 2, 40000), 12, 1.5, FIB_BASE, F32),
     ("wide-window", (1, 2, 2048), 40, 1.0, FIB_BASE, BF16),
     ("wide-window-large", (1, 2, 40000), 40, 1.0, FIB_BASE, BF16),
+    # interpolated: far K rows read as the rotated rows the query side wrote (segments of 2048
+    # rows whose workgroups first rotate the rows before them, which the previous segment's
+    # workgroup also writes)
+    ("ring-rotated-far", (1, 16, 65536), 12, 0.9, FIB_BASE, BF16),
 ]
 
 
@@ -107,19 +111,22 @@ def test_repeated_calls_bitwise(case, mode):
     check_runs(case[0], runs)
 
 
+@pytest.mark.parametrize("shape", [(1, 4, 16384, 1.37, (1.0, 1.5)), (1, 16, 131072, 0.9, (0.85, 0.95))],
+                         ids=["h4", "rotated-far"])
 @pytest.mark.parametrize("mode", [INT, INTERP], ids=["int", "interp"])
-def test_repeated_calls_bitwise_device_alpha(mode):
-    B, H, N, W = 1, 4, 16384, 12
-    say("determinism device alpha", B, H, N, W, mode)
+def test_repeated_calls_bitwise_device_alpha(mode, shape):
+    B, H, N, a, rng = shape
+    W = 12
+    say("determinism device alpha", B, H, N, W, a, rng, mode)
     q, k, v, do = rand_inputs(5, (B, H, N, 64), BF16, 4)
-    alpha = torch.tensor([1.37], dtype=torch.float32, device="cuda")
+    alpha = torch.tensor([a], dtype=torch.float32, device="cuda")
     gen = torch.Generator(device="cuda")
     gen.manual_seed(12)
     runs = []
     for how in FILLS:
         churn(how, gen, 64 << 20)
-        o, lse = F.fwd_dev(q, k, v, W, alpha, (1.0, 1.5), FIB_BASE, 10000.0, mode)
-        dq, dk, dv, da = F.bwd_dev(q, k, v, o, lse, do, W, alpha, (1.0, 1.5), FIB_BASE, 10000.0, mode)
+        o, lse = F.fwd_dev(q, k, v, W, alpha, rng, FIB_BASE, 10000.0, mode)
+        dq, dk, dv, da = F.bwd_dev(q, k, v, o, lse, do, W, alpha, rng, FIB_BASE, 10000.0, mode)
         torch.cuda.synchronize()
         runs.append({"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv, "dalpha": da})
     check_runs("device alpha", runs)
