@@ -21,6 +21,12 @@
 //  * Table entries beyond the ring read raw K and V rows from global memory, prefetched one
 //    step ahead into registers, and use relative RoPE <R_i q, R_(i-d) k> = <R_d q, k> with
 //    cos/sin of R_d computed once per workgroup; their P V runs on VALU (v_dot2_f32_bf16).
+//  * Integer mode, long segments: up to two entries a few steps beyond the ring reach are
+//    "queued": each step copies the slab (rotated K, V) that the step `depth` steps ahead
+//    needs from the ring into registers while its rows are still there, so those rows are
+//    read from memory once instead of again per entry. The registers of 8 waves hold two
+//    steps of one entry's K and V and five of a second entry's K (its V rows come from global
+//    memory). A segment's first `depth` steps load their slabs from global memory.
 //  * Softmax over all logits of a query at once (they fit in registers), fp32, base 2; the
 //    four lanes of a query combine through v_permlane16/32_swap. Logits outside a query's
 //    attended set are replaced (selected) by -inf, never offset, so a non-finite K row
@@ -37,6 +43,8 @@
 //    transpose reads (4 rows x 32 bytes per 16 lanes) are conflict-free, and every read of a
 //    row is one base address plus immediate offsets.
 #include "ring_common.h"
+
+#include <algorithm>
 
 namespace fib {
 namespace {
@@ -67,6 +75,7 @@ struct RingArgs {
   const DevPlan* plan;  // alpha in device memory: the split above comes from here (DEV instances)
   int n_far;            // far entries in use (DEV instances: NF is an upper bound)
   int heads_per_plan;   // DEV instances: head h reads plan[h / heads_per_plan]
+  int q_dist[kMaxQ];    // queued entries (integer mode): distances in the two queue slots
 };
 
 struct __align__(16) Smem {
@@ -75,6 +84,7 @@ struct __align__(16) Smem {
   float2 unc_cs[kMaxUnc][kHalf];
   float2 base_cs[2][kHalf];
   float2 warm_cs[8][kHalf];  // step bases of the warm-up rows
+  float2 q_cs[kQDepth0 + kQDepth1][kHalf];  // bases of the queued slabs loaded from global memory
 };
 
 // Rows of the far table entries for one step, held in registers and loaded one step ahead:
@@ -162,8 +172,11 @@ __device__ __forceinline__ void far_pv_interp(f4* acc, uint4 x0, uint4 x1, uint4
   }
 }
 
-template <int MODE, int NC, int NF, int WAVES, bool DEV>
+// NQ: queued entries (integer mode; 0, 1 or 2): the table entries after the covered ones,
+// within queue_fits of depth kQDepth0 (slot 0) and kQDepth1 (slot 1)
+template <int MODE, int NC, int NF, int WAVES, bool DEV, int NQ>
 __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
+  static_assert(NQ == 0 || (MODE == 0 && !DEV), "queued entries: integer mode, alpha on the host");
   constexpr int kThreads = 64 * WAVES;
   constexpr int kT = step_rows(WAVES);
   constexpr uint32_t kOnes = 0x3f803f80u;  // bf16 pair (1, 1)
@@ -249,6 +262,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
   const int lane_v = (4 * g + jr) * kRow + 8 * jc;
   // element offset of the lane's part of a 16-row slab: row n, dims 8g.. (and 32+8g..)
   const int lane_off = n * kD + 8 * g;
+  // queued V reads: row n, ring positions 4g, 16 + 4g, 32 + 4g, 48 + 4g (dims 8g..8g+7 and
+  // 32+8g..32+8g+7 in the order of a far V row)
+  const int lane_vq = n * kRow + 8 * g;
 
   // stores row rb + n of the lane (rb wave-uniform): K^ as given; V in output order, dims
   // 8g..8g+3 | 8g+4.. | 32+8g.. | 36+8g.. at ring positions 4g, 16+4g, 32+4g, 48+4g
@@ -313,6 +329,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
     if (j < n_warm) sm.warm_cs[j][t] = rope_cs(ws + j * kT, a.rope.rev[t]);
     else sm.base_cs[0][t] = rope_cs(s0, a.rope.rev[t]);
   }
+  if constexpr (NQ > 0) {
+    // slab x of slot 0 (x < kQDepth0), then of slot 1: rows s0 + x T - d + 16w + n
+    constexpr int n_qs = NQ > 1 ? kQDepth0 + kQDepth1 : kQDepth0;
+    for (int x = tid; x < n_qs * kHalf; x += kThreads) {
+      const int u = x / kHalf, t = x % kHalf;
+      const int base = u < kQDepth0 ? s0 + kT * u - a.q_dist[0] : s0 + kT * (u - kQDepth0) - a.q_dist[1];
+      sm.q_cs[u][t] = rope_cs(base, a.rope.rev[t]);
+    }
+  }
   uint4 pq[2], pk[2], pv[2];
   load_rows(s0, pq, pk, pv);
   __syncthreads();
@@ -358,6 +383,70 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
   if constexpr (MODE == 0)
     load_far_v<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fr, a, Vh, s0 + 16 * wave, l, n, g,
                          lane_off);
+
+  // ---- queued entries: slab x of a slot serves the step x steps ahead (x = 0: this step).
+  // Those of the segment's first steps come from global memory (raw rows, K rotated here by
+  // its row's position); each later one is read from the ring, `depth` steps before its use.
+  // Lane (n, g) holds row n: K^ as a logit A operand, V as a far V row (dims 8g.. and 32+8g..).
+  // Slot 1 queues only K (the registers of 8 waves hold no more); its V rows are loaded from
+  // global memory one step ahead, as a far entry's.
+  uint4 qk0[kQDepth0][2], qv0[kQDepth0][2], qk1[kQDepth1][2], qv1[2];
+  // rows pb + 16w - d + n (pb: a step's first row)
+  auto q_global = [&](int d, int pb, uint4* k2, uint4* v2) {
+    const int64_t off = far_off(d, pb + 16 * wave, n, g, lane_off);
+    k2[0] = *reinterpret_cast<const uint4*>(Kh + off);
+    k2[1] = *reinterpret_cast<const uint4*>(Kh + off + kHalf);
+    if (v2 != nullptr) {
+      v2[0] = *reinterpret_cast<const uint4*>(Vh + off);
+      v2[1] = *reinterpret_cast<const uint4*>(Vh + off + kHalf);
+    }
+  };
+  auto q_global_v = [&](int d, int pb, uint4* v2) {
+    const int64_t off = far_off(d, pb + 16 * wave, n, g, lane_off);
+    v2[0] = *reinterpret_cast<const uint4*>(Vh + off);
+    v2[1] = *reinterpret_cast<const uint4*>(Vh + off + kHalf);
+  };
+  // rotation by R_(base + 16w + n), base cos/sin from q_cs[u] (rows before 0 only meet masked
+  // queries; far_off loaded row 0 for them)
+  auto q_rotate = [&](int u, uint4* k2) {
+    float2 cs[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float2 b = sm.q_cs[u][8 * g + t];
+      cs[t] = make_float2(b.x * cs_t[t].x - b.y * cs_t[t].y, b.y * cs_t[t].x + b.x * cs_t[t].y);
+    }
+    float kf[16];
+    unpack8(k2[0], kf);
+    unpack8(k2[1], kf + 8);
+    rotate_pack_f(kf, cs, &k2[0], &k2[1]);
+  };
+  // rows rb - d + n (rb: this wave's first row of a step) from the ring
+  auto q_ring = [&](int d, int rb, uint4* k2, uint4* v2) {
+    const int ro = row_off(rb - d);
+    k2[0] = lds_read16(sm.ringK, ro + lane_k);
+    k2[1] = lds_read16(sm.ringK, ro + lane_k + 64);
+    if (v2 == nullptr) return;
+    const int vo = ro + lane_vq;
+    const uint2 x0 = lds_read8(sm.ringV, vo), x1 = lds_read8(sm.ringV, vo + 32);
+    const uint2 x2 = lds_read8(sm.ringV, vo + 64), x3 = lds_read8(sm.ringV, vo + 96);
+    v2[0] = make_uint4(x0.x, x0.y, x1.x, x1.y);
+    v2[1] = make_uint4(x2.x, x2.y, x3.x, x3.y);
+  };
+  if constexpr (NQ > 0) {
+#pragma unroll
+    for (int x = 0; x < kQDepth0; ++x) q_global(a.q_dist[0], s0 + kT * x, qk0[x], qv0[x]);
+    if constexpr (NQ > 1) {
+#pragma unroll
+      for (int x = 0; x < kQDepth1; ++x) q_global(a.q_dist[1], s0 + kT * x, qk1[x], nullptr);
+      q_global_v(a.q_dist[1], s0, qv1);
+    }
+#pragma unroll
+    for (int x = 0; x < kQDepth0; ++x) q_rotate(x, qk0[x]);
+    if constexpr (NQ > 1) {
+#pragma unroll
+      for (int x = 0; x < kQDepth1; ++x) q_rotate(kQDepth0 + x, qk1[x]);
+    }
+  }
 
   int buf = 0;
   for (int p0 = s0; p0 < s1; p0 += kT, buf ^= 1) {
@@ -449,6 +538,18 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
         s_far[f] = diag_lane ? s * sl2 : -INFINITY;
         if (DEV && f >= S_n_far) s_far[f] = -INFINITY;  // slot beyond the table
       }
+      // queued entries: slab 0 of each slot
+      float s_q[kMaxQ];
+      if constexpr (NQ > 0) {
+        auto q_logit = [&](const uint4* k2) {
+          f4 S = {0, 0, 0, 0};
+          S = mfma32(as_bf8(k2[0]), bq0, S);
+          S = mfma32(as_bf8(k2[1]), bq1, S);
+          return diag_lane ? sel4(S, l) * sl2 : -INFINITY;
+        };
+        s_q[0] = q_logit(qk0[0]);
+        if constexpr (NQ > 1) s_q[1] = q_logit(qk1[0]);
+      }
       // interpolated: their V rows, for the end of this step (row pairs of K and V are never
       // held together: the registers do not allow it); integer: requested with the K rows
       if constexpr (MODE == 1)
@@ -472,6 +573,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
 #pragma unroll
         for (int f = 0; f < NF; ++f)
           if (S_far_dist(f) > iq) s_far[f] = -INFINITY;
+#pragma unroll
+        for (int x = 0; x < NQ; ++x)
+          if (a.q_dist[x] > iq) s_q[x] = -INFINITY;
       }
       float m = fmaxf(fmaxf(sw0[0], sw0[1]), fmaxf(sw0[2], sw0[3]));
 #pragma unroll
@@ -480,6 +584,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
       for (int e = 0; e < NC; ++e) m = fmaxf(m, s_ent[e]);
 #pragma unroll
       for (int f = 0; f < NF; ++f) m = fmaxf(m, s_far[f]);
+#pragma unroll
+      for (int x = 0; x < NQ; ++x) m = fmaxf(m, s_q[x]);
       m = quad_max(m);  // every query has its own key (distance 0), so m is finite
       // lsum: the fp32 sum of the weights, for LSE (each query's weights are spread over its
       // four lanes: window keys in all four, table entries in its diagonal lane)
@@ -499,6 +605,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
       for (int f = 0; f < NF; ++f) {
         s_far[f] = ex2(s_far[f] - m);
         lsum += s_far[f];
+      }
+#pragma unroll
+      for (int x = 0; x < NQ; ++x) {
+        s_q[x] = ex2(s_q[x] - m);
+        lsum += s_q[x];
       }
       lsum = quad_add(lsum);
 
@@ -573,6 +684,32 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
         }
       }
 
+      // queued entries on VALU as the far ones; then each slot's slabs move one step down and
+      // its last one is read from the ring (rows of the step `depth` steps ahead)
+      if constexpr (NQ > 0) {
+        const uint32_t x = pack_bf2(s_q[0], NQ > 1 ? s_q[1] : 0.f);
+        const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute(diag_addr, (int)x);
+        lnorm_far = dot2(y, kOnes, lnorm_far);
+        far_pv_int(acc, qv0[0][0], qv0[0][1], y & 0xffffu, y << 16);
+        if constexpr (NQ > 1) far_pv_int(acc, qv1[0], qv1[1], y >> 16, y & 0xffff0000u);
+#pragma unroll
+        for (int x2 = 0; x2 + 1 < kQDepth0; ++x2)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            qk0[x2][h] = qk0[x2 + 1][h];
+            qv0[x2][h] = qv0[x2 + 1][h];
+          }
+        q_ring(a.q_dist[0], bw + kT * kQDepth0, qk0[kQDepth0 - 1], qv0[kQDepth0 - 1]);
+        if constexpr (NQ > 1) {
+#pragma unroll
+          for (int x2 = 0; x2 + 1 < kQDepth1; ++x2)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) qk1[x2][h] = qk1[x2 + 1][h];
+          q_ring(a.q_dist[1], bw + kT * kQDepth1, qk1[kQDepth1 - 1], nullptr);
+          q_global_v(a.q_dist[1], p0 + kT, qv1);  // (the last step loads rows never used)
+        }
+      }
+
       // ---- epilogue: the lane's dims 8g..8g+7 (acc[0], acc[1]) and 32+8g.. (acc[2], acc[3])
       if (iq < s1) {
         const float lnorm = accn[0] + lnorm_far;
@@ -603,25 +740,52 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
   }
 }
 
+// Steps per segment of a launch of BH heads of N rows (ring_segments).
+int64_t segment_steps(int64_t BH, int64_t N, int waves) {
+  const int kT = step_rows(waves);
+  const int64_t tiles = (N + kT - 1) / kT;
+  const int64_t segs = ring_segments(BH, tiles);
+  return (tiles + segs - 1) / segs;
+}
+
 // Waves per workgroup and the table split: 8 waves (two per SIMD). Every instance fits 256
 // registers per lane at 8 waves (the interpolated far entries hold only their lower rows).
-// With alpha in device memory the counts are upper bounds over the alpha range.
-int plan(const FwdArgs& f, int* n_cov, int* n_far) {
+// With alpha in device memory the counts are upper bounds over the alpha range. Queued
+// entries (integer mode, alpha on the host): the first entries past the covered ones that
+// fit the queue slots, when segments are long enough (8 steps) for the ring to serve most of
+// their slabs, in the instances that fit the registers: one queued entry with up to two far
+// ones, two with up to two (up to 8 covered entries) or one (up to 16).
+int plan(const FwdArgs& f, int* n_cov, int* n_q, int* n_far) {
+  *n_q = 0;
   if (f.plan != nullptr) {
     range_counts(f.alpha_lo, f.alpha_hi, f.base, f.n_base, f.W, f.mode, f.N, 8, n_cov, n_far);
-  } else {
-    split_table(f.tab, f.N, 8, n_cov, n_far);
+    return 8;
+  }
+  split_table(f.tab, f.N, 8, n_cov, n_far);
+  if (f.mode == 0 && segment_steps(f.BH, f.N, 8) >= 8 && *n_cov <= kMaxCov) {
+    const int c = *n_cov;
+    int q = 0;
+    if (*n_far >= 1 && queue_fits(f.tab.dist[c], kQDepth0, 8)) {
+      q = 1;
+      if (*n_far >= 2 && queue_fits(f.tab.dist[c + 1], kQDepth1, 8)) q = 2;
+    }
+    for (; q > 0; --q) {
+      const int rest = *n_far - q;
+      if (rest <= (q == 2 && c > 8 ? 1 : 2)) break;
+    }
+    *n_q = q;
+    *n_far -= q;
   }
   return 8;
 }
 
-template <int MODE, int NC, int NF, int WAVES, bool DEV>
+template <int MODE, int NC, int NF, int WAVES, bool DEV, int NQ>
 hipError_t launch(const RingArgs& a, unsigned blocks, hipStream_t s) {
   const size_t smem = sizeof(Smem);
   static std::atomic<uint32_t> lds_set{0};
-  hipError_t e = ensure_lds_limit(fwd_ring_kernel<MODE, NC, NF, WAVES, DEV>, lds_set, (int)smem);
+  hipError_t e = ensure_lds_limit(fwd_ring_kernel<MODE, NC, NF, WAVES, DEV, NQ>, lds_set, (int)smem);
   if (e != hipSuccess) return e;
-  fwd_ring_kernel<MODE, NC, NF, WAVES, DEV><<<blocks, 64 * WAVES, smem, s>>>(a);
+  fwd_ring_kernel<MODE, NC, NF, WAVES, DEV, NQ><<<blocks, 64 * WAVES, smem, s>>>(a);
   return hipGetLastError();
 }
 
@@ -631,36 +795,61 @@ template <int MODE, int WAVES, bool DEV = false>
 hipError_t launch_mode(const RingArgs& a, int n_far, unsigned blocks, hipStream_t s) {
   if (a.n_cov <= 8) {
     switch (n_far) {
-      case 0: return launch<MODE, 8, 0, WAVES, DEV>(a, blocks, s);
-      case 1: return launch<MODE, 8, 1, WAVES, DEV>(a, blocks, s);
-      case 2: return launch<MODE, 8, 2, WAVES, DEV>(a, blocks, s);
-      case 3: return launch<MODE, 8, 3, WAVES, DEV>(a, blocks, s);
-      default: return launch<MODE, 8, 4, WAVES, DEV>(a, blocks, s);
+      case 0: return launch<MODE, 8, 0, WAVES, DEV, 0>(a, blocks, s);
+      case 1: return launch<MODE, 8, 1, WAVES, DEV, 0>(a, blocks, s);
+      case 2: return launch<MODE, 8, 2, WAVES, DEV, 0>(a, blocks, s);
+      case 3: return launch<MODE, 8, 3, WAVES, DEV, 0>(a, blocks, s);
+      default: return launch<MODE, 8, 4, WAVES, DEV, 0>(a, blocks, s);
     }
   }
   switch (n_far) {
-    case 0: return launch<MODE, 16, 0, WAVES, DEV>(a, blocks, s);
-    case 1: return launch<MODE, 16, 1, WAVES, DEV>(a, blocks, s);
-    case 2: return launch<MODE, 16, 2, WAVES, DEV>(a, blocks, s);
-    case 3: return launch<MODE, 16, 3, WAVES, DEV>(a, blocks, s);
-    default: return launch<MODE, 16, 4, WAVES, DEV>(a, blocks, s);
+    case 0: return launch<MODE, 16, 0, WAVES, DEV, 0>(a, blocks, s);
+    case 1: return launch<MODE, 16, 1, WAVES, DEV, 0>(a, blocks, s);
+    case 2: return launch<MODE, 16, 2, WAVES, DEV, 0>(a, blocks, s);
+    case 3: return launch<MODE, 16, 3, WAVES, DEV, 0>(a, blocks, s);
+    default: return launch<MODE, 16, 4, WAVES, DEV, 0>(a, blocks, s);
   }
+}
+
+// integer mode with queued entries (the combinations plan() picks)
+template <int NC>
+hipError_t launch_queued_nc(const RingArgs& a, int n_q, int n_far, unsigned blocks, hipStream_t s) {
+  if (n_q == 1) {
+    switch (n_far) {
+      case 0: return launch<0, NC, 0, 8, false, 1>(a, blocks, s);
+      case 1: return launch<0, NC, 1, 8, false, 1>(a, blocks, s);
+      default: return launch<0, NC, 2, 8, false, 1>(a, blocks, s);
+    }
+  }
+  switch (n_far) {
+    case 0: return launch<0, NC, 0, 8, false, 2>(a, blocks, s);
+    case 1: return launch<0, NC, 1, 8, false, 2>(a, blocks, s);
+    default:
+      if constexpr (NC == 8) return launch<0, NC, 2, 8, false, 2>(a, blocks, s);
+      return hipErrorInvalidValue;  // (not picked)
+  }
+}
+hipError_t launch_queued(const RingArgs& a, int n_q, int n_far, unsigned blocks, hipStream_t s) {
+  return a.n_cov <= 8 ? launch_queued_nc<8>(a, n_q, n_far, blocks, s)
+                      : launch_queued_nc<16>(a, n_q, n_far, blocks, s);
 }
 
 }  // namespace
 
 bool fwd_ring_supported(const FwdArgs& f) {
   if (f.dtype != 1 || f.W > kMaxBand || f.N > (1LL << 30)) return false;
-  int cov, far;
-  plan(f, &cov, &far);
-  return far <= kMaxFar && cov <= kMaxCov;
+  int cov, q, far;
+  plan(f, &cov, &q, &far);
+  return q + far <= kMaxFar && cov <= kMaxCov;
 }
 
+// (layer stacks group consecutive layers by this key and launch each group with the split
+// from the alpha range, which queues no entries: queued and far entries count alike here)
 int fwd_instance_key(const FwdArgs& f) {
   if (!fwd_ring_supported(f)) return -1;
-  int cov, far;
-  const int waves = plan(f, &cov, &far);
-  return waves * 1000 + (cov <= 8 ? 8 : 16) * 10 + far;
+  int cov, q, far;
+  const int waves = plan(f, &cov, &q, &far);
+  return waves * 1000 + (cov <= 8 ? 8 : 16) * 10 + q + far;
 }
 
 hipError_t launch_fwd_ring(const FwdArgs& f) {
@@ -673,16 +862,19 @@ hipError_t launch_fwd_ring(const FwdArgs& f) {
   a.lse = f.lse;
   a.N = (int)f.N;
   a.W = f.W;
-  int n_far;
-  const int waves = plan(f, &a.n_cov, &n_far);  // 8
+  int n_q, n_far;
+  const int waves = plan(f, &a.n_cov, &n_q, &n_far);  // 8
   for (int e = 0; e < kMaxCov; ++e) {
     // slots past the covered prefix get a harmless in-ring distance and weight 0
     a.dist[e] = e < a.n_cov ? f.tab.dist[e] : kMaxBand;
     a.w[e] = e < a.n_cov ? f.tab.w[e] : 0.f;
   }
+  // queued entries follow the covered ones in the table, far entries follow those
+  for (int x = 0; x < kMaxQ; ++x) a.q_dist[x] = x < n_q ? f.tab.dist[a.n_cov + x] : 0;
+  const int c = a.n_cov + n_q;
   for (int x = 0; x < kMaxFar; ++x) {
-    a.far_dist[x] = x < n_far ? f.tab.dist[a.n_cov + x] : 0;
-    a.far_w[x] = x < n_far ? f.tab.w[a.n_cov + x] : 0.f;
+    a.far_dist[x] = x < n_far ? f.tab.dist[c + x] : 0;
+    a.far_w[x] = x < n_far ? f.tab.w[c + x] : 0.f;
   }
   int u = 0;
   for (int x = 0; x < n_far; ++x) {
@@ -691,12 +883,15 @@ hipError_t launch_fwd_ring(const FwdArgs& f) {
   }
   for (; u < kMaxUnc; ++u) a.unc_dist[u] = 0;
   const int kT = step_rows(waves);
-  // rows before a segment start that the ring must hold: the band and the covered distances
+  // rows before a segment start that the ring must hold: the band, the covered distances and
+  // the rows of the queued slabs read at the first step (d - depth T back)
   int need = kMaxBand;
   for (int e = 0; e < a.n_cov; ++e) need = f.tab.dist[e] > need ? f.tab.dist[e] : need;
+  if (n_q > 0) need = std::max(need, a.q_dist[0] - kT * kQDepth0);
+  if (n_q > 1) need = std::max(need, a.q_dist[1] - kT * kQDepth1);
   a.warm = ((need + kT - 1) / kT) * kT;
   int early = kMaxBand;
-  for (int e = 0; e < a.n_cov + n_far; ++e) early = f.tab.dist[e] > early ? f.tab.dist[e] : early;
+  for (int e = 0; e < a.n_cov + n_q + n_far; ++e) early = f.tab.dist[e] > early ? f.tab.dist[e] : early;
   a.early_rows = early;
   // segments per head: see ring_segments
   const int64_t tiles = (f.N + kT - 1) / kT;
@@ -712,6 +907,7 @@ hipError_t launch_fwd_ring(const FwdArgs& f) {
     if (f.mode == 0) return launch_mode<0, 8, true>(a, n_far, blocks, f.stream);
     return launch_mode<1, 8, true>(a, n_far, blocks, f.stream);
   }
+  if (n_q > 0) return launch_queued(a, n_q, n_far, blocks, f.stream);
   if (f.mode == 0) return launch_mode<0, 8>(a, n_far, blocks, f.stream);
   return launch_mode<1, 8>(a, n_far, blocks, f.stream);
 }

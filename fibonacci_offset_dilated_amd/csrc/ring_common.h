@@ -48,12 +48,28 @@ constexpr int kMirror = 32;
 static_assert(kP == kRingRows && kMaxBand == kBandRows && kMaxCov == kSplitCov && kMaxFar == kSplitFar,
               "ring geometry and RingSplit must agree");
 
+// Queued table entries (integer forward): a distance a few steps beyond the ring reach whose
+// 16-row slab is read from the ring `depth` steps before its queries run, while its rows are
+// still there, and held in registers until then. The slab of the wave's queries p + 16w..
+// at distance d is rows p + 16w - d.. : read at step p - depth * T (T rows per step), they
+// lie inside the ring then (ring rows p - depth T - reach .. p - depth T + T - 1) exactly when
+// depth * T <= d <= reach + depth * T. Two queue slots, with these depths.
+constexpr int kMaxQ = 2;
+constexpr int kQDepth0 = 2;
+constexpr int kQDepth1 = 5;
+constexpr bool queue_fits(int d, int depth, int waves) {
+  return d > max_cov(waves) && depth * step_rows(waves) <= d && d <= max_cov(waves) + depth * step_rows(waves);
+}
+
 // byte offset of ring row `row` (any integer, negative rows included: slots are row mod kP);
 // wave-uniform arguments keep it on the scalar unit
 __device__ __forceinline__ int row_off(int row) { return (row & (kP - 1)) * kRow; }
 
 __device__ __forceinline__ uint4 lds_read16(const uint8_t* base, int off) {
   return *reinterpret_cast<const uint4*>(base + off);
+}
+__device__ __forceinline__ uint2 lds_read8(const uint8_t* base, int off) {
+  return *reinterpret_cast<const uint2*>(base + off);
 }
 __device__ __forceinline__ void lds_write16(uint8_t* base, int off, uint4 x) {
   *reinterpret_cast<uint4*>(base + off) = x;
