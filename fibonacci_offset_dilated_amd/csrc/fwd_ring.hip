@@ -706,7 +706,6 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) qk1[x2][h] = qk1[x2 + 1][h];
           q_ring(a.q_dist[1], bw + kT * kQDepth1, qk1[kQDepth1 - 1], nullptr);
-          q_global_v(a.q_dist[1], p0 + kT, qv1);  // (the last step loads rows never used)
         }
       }
 
@@ -735,6 +734,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
       if constexpr (MODE == 0)
         load_far_v<MODE, NF>(DEV ? lcl.far_dist : a.far_dist, DEV ? S_n_far : NF, fr, a, Vh, i0w + kT, l, n, g,
                              lane_off);
+      // (with them: requested before the stores, their registers would be copied at the step's
+      // end, which waits for the loads)
+      if constexpr (NQ > 1) q_global_v(a.q_dist[1], p0 + kT, qv1);
     }
     __syncthreads();
   }
