@@ -21,12 +21,14 @@
 //  * Table entries beyond the ring read raw K and V rows from global memory, prefetched one
 //    step ahead into registers, and use relative RoPE <R_i q, R_(i-d) k> = <R_d q, k> with
 //    cos/sin of R_d computed once per workgroup; their P V runs on VALU (v_dot2_f32_bf16).
-//  * Integer mode, long segments: up to two entries a few steps beyond the ring reach are
-//    "queued": each step copies the slab (rotated K, V) that the step `depth` steps ahead
-//    needs from the ring into registers while its rows are still there, so those rows are
-//    read from memory once instead of again per entry. The registers of 8 waves hold two
-//    steps of one entry's K and V and five of a second entry's K (its V rows come from global
-//    memory). A segment's first `depth` steps load their slabs from global memory.
+//  * Long segments: up to two entries (integer mode; one in interpolated mode) a few steps
+//    beyond the ring reach are "queued": each step copies the slab (rotated K, V) that the
+//    step `depth` steps ahead needs from the ring into registers while its rows are still
+//    there, so those rows are read from memory once instead of again per entry. The registers
+//    of 8 waves hold two steps of one entry's K and V and five of a second entry's K (its V
+//    rows come from global memory); an interpolated entry's slabs are its lower rows plus one
+//    dword per lane of the row after them, as a far entry's. A segment's first `depth` steps
+//    load their slabs from global memory.
 //  * Softmax over all logits of a query at once (they fit in registers), fp32, base 2; the
 //    four lanes of a query combine through v_permlane16/32_swap. Logits outside a query's
 //    attended set are replaced (selected) by -inf, never offset, so a non-finite K row
@@ -75,7 +77,8 @@ struct RingArgs {
   const DevPlan* plan;  // alpha in device memory: the split above comes from here (DEV instances)
   int n_far;            // far entries in use (DEV instances: NF is an upper bound)
   int heads_per_plan;   // DEV instances: head h reads plan[h / heads_per_plan]
-  int q_dist[kMaxQ];    // queued entries (integer mode): distances in the two queue slots
+  int q_dist[kMaxQ];    // queued entries: distances in the queue slots (interpolated: c, one slot)
+  float q_w[kMaxQ];     // their weights (interpolated mode)
 };
 
 struct __align__(16) Smem {
@@ -172,11 +175,11 @@ __device__ __forceinline__ void far_pv_interp(f4* acc, uint4 x0, uint4 x1, uint4
   }
 }
 
-// NQ: queued entries (integer mode; 0, 1 or 2): the table entries after the covered ones,
-// within queue_fits of depth kQDepth0 (slot 0) and kQDepth1 (slot 1)
+// NQ: queued entries (integer mode 0, 1 or 2; interpolated mode 0 or 1): the table entries
+// after the covered ones, within queue_fits of depth kQDepth0 (slot 0) and kQDepth1 (slot 1)
 template <int MODE, int NC, int NF, int WAVES, bool DEV, int NQ>
 __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
-  static_assert(NQ == 0 || (MODE == 0 && !DEV), "queued entries: integer mode, alpha on the host");
+  static_assert(NQ == 0 || (!DEV && (MODE == 0 || NQ == 1)), "queued entries: alpha on the host");
   constexpr int kThreads = 64 * WAVES;
   constexpr int kT = step_rows(WAVES);
   constexpr uint32_t kOnes = 0x3f803f80u;  // bf16 pair (1, 1)
@@ -391,6 +394,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
   // Slot 1 queues only K (the registers of 8 waves hold no more); its V rows are loaded from
   // global memory one step ahead, as a far entry's.
   uint4 qk0[kQDepth0][2], qv0[kQDepth0][2], qk1[kQDepth1][2], qv1[2];
+  // interpolated mode (slot 0): the slabs are the lower rows c back; the upper rows come from
+  // the neighbouring lane and the row after the slab, held one dword per lane (as a far
+  // entry's): dword l % 32 of K^ and of V (in the natural dim order)
+  uint32_t qkx0[kQDepth0], qvx0[kQDepth0];
+  // byte offset of V dword l % 32 (dims 2j, 2j + 1) in a ring row (output order)
+  const int vex_off = [&] {
+    const int j = l & 31, jj = j & 15, t = jj & 3;
+    return 64 * (j >> 4) + 8 * (jj >> 2) + (t < 2 ? 4 * t : 32 + 4 * (t - 2));
+  }();
   // rows pb + 16w - d + n (pb: a step's first row)
   auto q_global = [&](int d, int pb, uint4* k2, uint4* v2) {
     const int64_t off = far_off(d, pb + 16 * wave, n, g, lane_off);
@@ -420,6 +432,20 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
     unpack8(k2[1], kf + 8);
     rotate_pack_f(kf, cs, &k2[0], &k2[1]);
   };
+  // interpolated: the row after the slab (pb + 16w - c + 16), dword l % 32 of K (rotated by
+  // its position with its RoPE partner dword l % 32 ^ 16) and of V
+  auto q_global_ex = [&](int c, int pb, uint32_t* kx, uint32_t* vx) {
+    const int r = pb + 16 * wave - c + 16;
+    const int64_t ro = (int64_t)(r > 0 ? r : 0) * kD;  // (rows before 0 only meet masked queries)
+    const uint32_t* kr = reinterpret_cast<const uint32_t*>(Kh + ro);
+    const int j = l & 31;
+    const uint32_t x = kr[j], y = kr[j ^ 16];
+    *vx = reinterpret_cast<const uint32_t*>(Vh + ro)[j];
+    const int m = 2 * (j & 15);
+    const float2 c0 = rope_cs(r, a.rope.rev[m]), c1 = rope_cs(r, a.rope.rev[m + 1]);
+    const float sg = j < 16 ? -1.f : 1.f;  // x'_m = x_m c - x_(m+32) s; x'_(m+32) = x_(m+32) c + x_m s
+    *kx = pack_bf2(bf_lo(x) * c0.x + sg * bf_lo(y) * c0.y, bf_hi(x) * c1.x + sg * bf_hi(y) * c1.y);
+  };
   // rows rb - d + n (rb: this wave's first row of a step) from the ring
   auto q_ring = [&](int d, int rb, uint4* k2, uint4* v2) {
     const int ro = row_off(rb - d);
@@ -432,9 +458,18 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
     v2[0] = make_uint4(x0.x, x0.y, x1.x, x1.y);
     v2[1] = make_uint4(x2.x, x2.y, x3.x, x3.y);
   };
+  auto q_ring_ex = [&](int c, int rb, uint32_t* kx, uint32_t* vx) {
+    const int ro = row_off(rb - c + 16);
+    *kx = lds_read4(sm.ringK, ro + 4 * (l & 31));
+    *vx = lds_read4(sm.ringV, ro + vex_off);
+  };
   if constexpr (NQ > 0) {
 #pragma unroll
     for (int x = 0; x < kQDepth0; ++x) q_global(a.q_dist[0], s0 + kT * x, qk0[x], qv0[x]);
+    if constexpr (MODE == 1) {
+#pragma unroll
+      for (int x = 0; x < kQDepth0; ++x) q_global_ex(a.q_dist[0], s0 + kT * x, &qkx0[x], &qvx0[x]);
+    }
     if constexpr (NQ > 1) {
 #pragma unroll
       for (int x = 0; x < kQDepth1; ++x) q_global(a.q_dist[1], s0 + kT * x, qk1[x], nullptr);
@@ -547,8 +582,21 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
           S = mfma32(as_bf8(k2[1]), bq1, S);
           return diag_lane ? sel4(S, l) * sl2 : -INFINITY;
         };
-        s_q[0] = q_logit(qk0[0]);
-        if constexpr (NQ > 1) s_q[1] = q_logit(qk1[0]);
+        if constexpr (MODE == 0) {
+          s_q[0] = q_logit(qk0[0]);
+          if constexpr (NQ > 1) s_q[1] = q_logit(qk1[0]);
+        } else {
+          f4 S = {0, 0, 0, 0}, H = {0, 0, 0, 0};
+          S = mfma32(as_bf8(qk0[0][0]), bq0, S);
+          S = mfma32(as_bf8(qk0[0][1]), bq1, S);
+          uint4 kh[2];
+          upper_rows(qk0[0], qkx0[0], g, kh);
+          H = mfma32(as_bf8(kh[0]), bq0, H);
+          H = mfma32(as_bf8(kh[1]), bq1, H);
+          const float lo = sel4(S, l);
+          const float sv = fmaf(a.q_w[0], sel4(H, l) - lo, lo);
+          s_q[0] = diag_lane ? sv * sl2 : -INFINITY;
+        }
       }
       // interpolated: their V rows, for the end of this step (row pairs of K and V are never
       // held together: the registers do not allow it); integer: requested with the K rows
@@ -687,11 +735,21 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
       // queued entries on VALU as the far ones; then each slot's slabs move one step down and
       // its last one is read from the ring (rows of the step `depth` steps ahead)
       if constexpr (NQ > 0) {
-        const uint32_t x = pack_bf2(s_q[0], NQ > 1 ? s_q[1] : 0.f);
-        const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute(diag_addr, (int)x);
-        lnorm_far = dot2(y, kOnes, lnorm_far);
-        far_pv_int(acc, qv0[0][0], qv0[0][1], y & 0xffffu, y << 16);
-        if constexpr (NQ > 1) far_pv_int(acc, qv1[0], qv1[1], y >> 16, y & 0xffff0000u);
+        if constexpr (MODE == 0) {
+          const uint32_t x = pack_bf2(s_q[0], NQ > 1 ? s_q[1] : 0.f);
+          const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute(diag_addr, (int)x);
+          lnorm_far = dot2(y, kOnes, lnorm_far);
+          far_pv_int(acc, qv0[0][0], qv0[0][1], y & 0xffffu, y << 16);
+          if constexpr (NQ > 1) far_pv_int(acc, qv1[0], qv1[1], y >> 16, y & 0xffff0000u);
+        } else {
+          const float p = s_q[0];
+          const uint32_t x = pack_bf2(p * (1.f - a.q_w[0]), p * a.q_w[0]);
+          const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute(diag_addr, (int)x);
+          lnorm_far = dot2(y, kOnes, lnorm_far);
+          uint4 vh[2];
+          upper_rows(qv0[0], qvx0[0], g, vh);
+          far_pv_interp(acc, qv0[0][0], qv0[0][1], vh[0], vh[1], y);
+        }
 #pragma unroll
         for (int x2 = 0; x2 + 1 < kQDepth0; ++x2)
 #pragma unroll
@@ -700,6 +758,14 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
             qv0[x2][h] = qv0[x2 + 1][h];
           }
         q_ring(a.q_dist[0], bw + kT * kQDepth0, qk0[kQDepth0 - 1], qv0[kQDepth0 - 1]);
+        if constexpr (MODE == 1) {
+#pragma unroll
+          for (int x2 = 0; x2 + 1 < kQDepth0; ++x2) {
+            qkx0[x2] = qkx0[x2 + 1];
+            qvx0[x2] = qvx0[x2 + 1];
+          }
+          q_ring_ex(a.q_dist[0], bw + kT * kQDepth0, &qkx0[kQDepth0 - 1], &qvx0[kQDepth0 - 1]);
+        }
         if constexpr (NQ > 1) {
 #pragma unroll
           for (int x2 = 0; x2 + 1 < kQDepth1; ++x2)
@@ -764,6 +830,15 @@ int plan(const FwdArgs& f, int* n_cov, int* n_q, int* n_far) {
     return 8;
   }
   split_table(f.tab, f.N, 8, n_cov, n_far);
+  if (f.mode == 1 && segment_steps(f.BH, f.N, 8) >= 8 && *n_cov <= kMaxCov) {
+    // interpolated: slot 0 only (with its lower slab, the neighbouring row and up to two far
+    // entries the registers are full)
+    if (*n_far >= 1 && *n_far <= 3 && queue_fits_interp(f.tab.dist[*n_cov], kQDepth0, 8)) {
+      *n_q = 1;
+      *n_far -= 1;
+    }
+    return 8;
+  }
   if (f.mode == 0 && segment_steps(f.BH, f.N, 8) >= 8 && *n_cov <= kMaxCov) {
     const int c = *n_cov;
     int q = 0;
@@ -831,7 +906,18 @@ hipError_t launch_queued_nc(const RingArgs& a, int n_q, int n_far, unsigned bloc
       return hipErrorInvalidValue;  // (not picked)
   }
 }
-hipError_t launch_queued(const RingArgs& a, int n_q, int n_far, unsigned blocks, hipStream_t s) {
+template <int NC>
+hipError_t launch_queued_interp_nc(const RingArgs& a, int n_far, unsigned blocks, hipStream_t s) {
+  switch (n_far) {
+    case 0: return launch<1, NC, 0, 8, false, 1>(a, blocks, s);
+    case 1: return launch<1, NC, 1, 8, false, 1>(a, blocks, s);
+    default: return launch<1, NC, 2, 8, false, 1>(a, blocks, s);
+  }
+}
+hipError_t launch_queued(const RingArgs& a, int mode, int n_q, int n_far, unsigned blocks, hipStream_t s) {
+  if (mode == 1)
+    return a.n_cov <= 8 ? launch_queued_interp_nc<8>(a, n_far, blocks, s)
+                        : launch_queued_interp_nc<16>(a, n_far, blocks, s);
   return a.n_cov <= 8 ? launch_queued_nc<8>(a, n_q, n_far, blocks, s)
                       : launch_queued_nc<16>(a, n_q, n_far, blocks, s);
 }
@@ -872,7 +958,10 @@ hipError_t launch_fwd_ring(const FwdArgs& f) {
     a.w[e] = e < a.n_cov ? f.tab.w[e] : 0.f;
   }
   // queued entries follow the covered ones in the table, far entries follow those
-  for (int x = 0; x < kMaxQ; ++x) a.q_dist[x] = x < n_q ? f.tab.dist[a.n_cov + x] : 0;
+  for (int x = 0; x < kMaxQ; ++x) {
+    a.q_dist[x] = x < n_q ? f.tab.dist[a.n_cov + x] : 0;
+    a.q_w[x] = x < n_q ? f.tab.w[a.n_cov + x] : 0.f;
+  }
   const int c = a.n_cov + n_q;
   for (int x = 0; x < kMaxFar; ++x) {
     a.far_dist[x] = x < n_far ? f.tab.dist[c + x] : 0;
@@ -909,7 +998,7 @@ hipError_t launch_fwd_ring(const FwdArgs& f) {
     if (f.mode == 0) return launch_mode<0, 8, true>(a, n_far, blocks, f.stream);
     return launch_mode<1, 8, true>(a, n_far, blocks, f.stream);
   }
-  if (n_q > 0) return launch_queued(a, n_q, n_far, blocks, f.stream);
+  if (n_q > 0) return launch_queued(a, f.mode, n_q, n_far, blocks, f.stream);
   if (f.mode == 0) return launch_mode<0, 8>(a, n_far, blocks, f.stream);
   return launch_mode<1, 8>(a, n_far, blocks, f.stream);
 }

@@ -60,6 +60,10 @@ constexpr int kQDepth1 = 5;
 constexpr bool queue_fits(int d, int depth, int waves) {
   return d > max_cov(waves) && depth * step_rows(waves) <= d && d <= max_cov(waves) + depth * step_rows(waves);
 }
+// Interpolated entries (distance c = ceil(alpha f)) read the 17 rows c back .. c - 16 back.
+constexpr bool queue_fits_interp(int c, int depth, int waves) {
+  return c > max_cov(waves) && depth * step_rows(waves) + 1 <= c && c <= max_cov(waves) + depth * step_rows(waves);
+}
 
 // byte offset of ring row `row` (any integer, negative rows included: slots are row mod kP);
 // wave-uniform arguments keep it on the scalar unit
@@ -67,6 +71,9 @@ __device__ __forceinline__ int row_off(int row) { return (row & (kP - 1)) * kRow
 
 __device__ __forceinline__ uint4 lds_read16(const uint8_t* base, int off) {
   return *reinterpret_cast<const uint4*>(base + off);
+}
+__device__ __forceinline__ uint32_t lds_read4(const uint8_t* base, int off) {
+  return *reinterpret_cast<const uint32_t*>(base + off);
 }
 __device__ __forceinline__ uint2 lds_read8(const uint8_t* base, int off) {
   return *reinterpret_cast<const uint2*>(base + off);

@@ -284,10 +284,11 @@ def test_long_many_heads(case, mode):
     assert torch.isfinite(o.float()).all().item()
 
 
-# ---- queued entries (integer mode, long segments): table entries a few steps beyond the ring
-# reach whose slabs are read from the ring ahead of their use and held in registers (two slots:
-# distances in (384, 640] and (640, 1024]); in each segment's first steps they come from global
-# memory. Rows checked: the first six steps of several segments, random rows, the end.
+# ---- queued entries (long segments): table entries a few steps beyond the ring reach whose
+# slabs are read from the ring ahead of their use and held in registers (integer mode: two
+# slots, distances in (384, 640] and (640, 1024]; interpolated mode: the first slot); in each
+# segment's first steps they come from global memory. Rows checked: the first six steps of
+# several segments, random rows, the end.
 
 def ring_segment_len(BH, N, T=128):
     """Rows per segment of a ring-kernel launch (the library's ring_segments)."""
@@ -308,18 +309,20 @@ QUEUED = [
     (2, 4, 50000, 12, 1.0, FIB_BASE + (1597, 2584)),  # two queued, two far
     (1, 8, 60000, 12, 1.0, tuple(range(20, 380, 25)) + (600, 900, 1300)),  # 15 covered
     (1, 8, 60000, 12, 1.0, (1, 2, 500, 1100, 1300)),  # slot 0 only, two far
+    (1, 8, 60000, 12, 1.37, FIB_BASE),             # interpolated weights 0.51 (queued), ...
 ]
 
 
+@pytest.mark.parametrize("mode", [INT, INTERP], ids=["int", "interp"])
 @pytest.mark.parametrize("case", QUEUED, ids=[f"B{c[0]}H{c[1]}N{c[2]}W{c[3]}a{c[4]}n{len(c[5])}" for c in QUEUED])
-def test_queued_entries(case):
+def test_queued_entries(case, mode):
     B, H, N, W, alpha, base = case
     alpha = np.float32(alpha)
     seg = ring_segment_len(B * H, N)
     assert seg >= 8 * 128
-    say("queued entries", case, "segment rows", seg)
+    say("queued entries", case, "mode", mode, "segment rows", seg)
     qkv = inputs(5000 + N + W, (B, H, N, 64), BF16)
-    o, lse = run_fwd(qkv, W, alpha, base, INT)
+    o, lse = run_fwd(qkv, W, alpha, base, mode)
     n_seg = -(-N // seg)
     firsts = [seg * k for k in sorted({0, 1, 2, n_seg // 2, n_seg - 1})]
     rng = np.random.default_rng(N + W)
@@ -329,7 +332,7 @@ def test_queued_entries(case):
     (_, q64), (_, k64), (_, v64) = qkv[:3]
     eo = el = 0.0
     for b, h in [(0, 0), (B - 1, H - 1)]:
-        ro, rl = O.forward_rows(q64[b, h], k64[b, h], v64[b, h], rows, W, alpha, base, 10000.0, INT)
+        ro, rl = O.forward_rows(q64[b, h], k64[b, h], v64[b, h], rows, W, alpha, base, 10000.0, mode)
         eo = max(eo, maxabs(host(o[b, h])[rows], ro))
         el = max(el, maxabs(host(lse[b, h])[rows], rl))
     say("  max err O", eo, "LSE", el, "rows", len(rows))
