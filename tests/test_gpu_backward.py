@@ -150,6 +150,47 @@ def test_long_context_backward_sampled(long_inputs, mode):
         assert abs(float(da4.item()) - ra) <= 2e-2 * abs(ra)
 
 
+# Long segments (at least 8 steps) with the entries just past the ring reach (384, 640], at
+# the edges of that range, after none or 15 covered entries: the integer query side's dQ on
+# the first three steps of several segments (where the far rows precede the segment), random
+# rows and the end, against the oracle.
+FAR_EDGE_BWD = [
+    # (B, H, N, W, alpha, base)
+    (1, 16, 40000, 12, 1.5, FIB_BASE),           # far entries 566, 915 and 1480
+    (1, 8, 70000, 16, 1.0, (1, 2, 640, 1024)),
+    (1, 8, 70000, 16, 1.0, (1, 2, 385, 641)),
+    (1, 8, 60000, 12, 1.0, tuple(range(20, 380, 25)) + (600, 900)),  # 15 covered
+    (1, 8, 60000, 12, 1.0, (1, 2, 500)),
+]
+
+
+@pytest.mark.parametrize("case", FAR_EDGE_BWD, ids=[f"B{c[0]}H{c[1]}N{c[2]}W{c[3]}a{c[4]}n{len(c[5])}" for c in FAR_EDGE_BWD])
+def test_far_entries_long_segments_backward(case):
+    from test_gpu_forward import ring_segment_len
+
+    B, H, N, W, alpha, base = case
+    alpha = np.float32(alpha)
+    seg = ring_segment_len(B * H, N)
+    assert seg >= 8 * 128
+    say("far entries, long segments, backward", case, "segment rows", seg)
+    qkvd = inputs(6000 + N + W, (B, H, N, 64), BF16, with_dout=True)
+    dq, _, _, da = gpu_grads(qkvd, W, alpha, base, INT)
+    n_seg = -(-N // seg)
+    firsts = [seg * k for k in sorted({0, 1, 2, n_seg // 2, n_seg - 1})]
+    rng = np.random.default_rng(N + W + 1)
+    rows = np.unique(np.concatenate([np.arange(s, min(s + 3 * 128 + 8, N)) for s in firsts]
+                                    + [rng.integers(0, N, 100), np.arange(N - 24, N)]))
+    (_, q64), (_, k64), (_, v64), (_, d64) = qkvd
+    eq = 0.0
+    for b, h in [(0, 0), (B - 1, H - 1)]:
+        rq, _, _, _ = O.backward(q64[b:b + 1, h:h + 1], k64[b:b + 1, h:h + 1], v64[b:b + 1, h:h + 1],
+                                 d64[b:b + 1, h:h + 1], W, alpha, base, 10000.0, INT, rows=rows)
+        eq = max(eq, grad_excess(host(dq[b, h])[rows], rq[0, 0][rows], BF16))
+    say(f"  dQ {eq:.2e} over {len(rows)} rows")
+    assert eq <= TOL[BF16]
+    assert float(da.item()) == 0.0
+
+
 def _sixteen_heads(N, seed):
     """16-head inputs whose heads 0 and 15 hold seeded N(0, 1) draws and the rest zeros (their
     gradients and d(alpha) parts are 0), with the fp64 copies of the two live heads."""
