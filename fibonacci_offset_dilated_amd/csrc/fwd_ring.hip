@@ -481,6 +481,19 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_ring_kernel(RingArgs a) {
 #pragma unroll
       for (int x = 0; x < kQDepth1; ++x) q_rotate(kQDepth0 + x, qk1[x]);
     }
+    // Interpolated mode: the raw rows loaded here are made ready before the step loop (an
+    // empty asm that reads them). Left in flight into the loop, the moves of its queue at each
+    // step's start would wait for every load in flight. (The integer instances have no such
+    // moves, and there the asm costs them their register fit.)
+    if constexpr (MODE == 1) {
+      auto ready = [](uint4& v) { asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w)); };
+#pragma unroll
+      for (int x = 0; x < kQDepth0; ++x) {
+        ready(qv0[x][0]);
+        ready(qv0[x][1]);
+        asm volatile("" : "+v"(qkx0[x]), "+v"(qvx0[x]));
+      }
+    }
   }
 
   int buf = 0;
