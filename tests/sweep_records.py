@@ -11,7 +11,10 @@ configuration:
   row need every query that reads it); ``dalpha_err_over_bound`` where the oracle's dalpha is
   computed over all heads (N <= 4096);
 * ``index_set_match``: the device export of the attended rows (fib_sparse_attn_index_set)
-  equals the oracle's index_sets exactly.
+  equals the oracle's index_sets exactly;
+* ``oracle_tokens_per_s`` (N <= 4096): the fp64 oracle's rate on the same layer call (the
+  whole forward, or the whole backward), timed with time.perf_counter on the host cores of
+  the same box, one worker process per core (``oracle_cores``), median of 3 runs.
 
 The parity inputs follow the workload recipe (seeded N(0, 1) draws rounded to the workload
 dtype, one set per layer); the timing inputs are drawn on the device, as in the sweep.
@@ -23,7 +26,9 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
+import time
 
 import numpy as np
 
@@ -55,6 +60,17 @@ def parity(w, base_id, base, layer, alpha_of, modes, say):
     heads = [(0, 0), (w.B - 1, w.H - 1)]
     rows = sample_rows(w.N)
     alpha = alpha_of(w, layer)
+    workers = min(16, len(os.sched_getaffinity(0)))
+    tokens = w.B * w.H * w.N
+
+    def oracle_rate(fn):
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return {"oracle_tokens_per_s": tokens / statistics.median(ts), "oracle_cores": workers}
+
     out = {}
     for W in w.windows:
         for mode in modes:
@@ -70,6 +86,9 @@ def parity(w, base_id, base, layer, alpha_of, modes, say):
             match = bool(np.array_equal(ix, O.index_sets(w.N, W, alpha, base, mode)))
             rec = {"max_abs_err_o": eo, "max_abs_err_lse": el, "index_set_match": match,
                    "parity_sample": f"rows {len(rows)} of heads {heads}"}
+            if w.N <= 4096:
+                rec.update(oracle_rate(lambda: O.forward(q64, k64, v64, W, alpha, base, w.theta, mode,
+                                                         workers=workers)))
             out[(W, mode, "fwd")] = rec
             say(f"  {w.name} base {base_id} layer {layer} W {W} mode {mode} fwd: O {eo:.2e} LSE {el:.2e} "
                 f"index set {'match' if match else 'MISMATCH'}")
@@ -85,9 +104,10 @@ def parity(w, base_id, base, layer, alpha_of, modes, say):
                 brec = {"max_abs_err_dq": edq, "index_set_match": match,
                         "parity_sample": f"dQ rows {len(rows)} of heads {heads}"}
                 if w.N <= 4096:
-                    workers = min(16, len(os.sched_getaffinity(0)))
                     rq, rk, rv, ra, rsc = O.backward(q64, k64, v64, d64, W, alpha, base, w.theta, mode,
                                                      workers=workers, return_scale=True)
+                    brec.update(oracle_rate(lambda: O.backward(q64, k64, v64, d64, W, alpha, base, w.theta, mode,
+                                                               workers=workers)))
                     brec["max_abs_err_dq"] = float(np.abs(dqh - rq).max())
                     brec["max_abs_err_dk"] = float(np.abs(host(dk) - rk).max())
                     brec["max_abs_err_dv"] = float(np.abs(host(dv) - rv).max())
