@@ -832,10 +832,11 @@ int64_t segment_steps(int64_t BH, int64_t N, int waves) {
 // Waves per workgroup and the table split: 8 waves (two per SIMD). Every instance fits 256
 // registers per lane at 8 waves (the interpolated far entries hold only their lower rows).
 // With alpha in device memory the counts are upper bounds over the alpha range. Queued
-// entries (integer mode, alpha on the host): the first entries past the covered ones that
-// fit the queue slots, when segments are long enough (8 steps) for the ring to serve most of
-// their slabs, in the instances that fit the registers: one queued entry with up to two far
-// ones, two with up to two (up to 8 covered entries) or one (up to 16).
+// entries (alpha on the host): the first entries past the covered ones that fit the queue
+// slots, when segments are long enough (8 steps) for the ring to serve most of their slabs,
+// in the instances that fit the registers. Integer mode: one queued entry with up to two far
+// ones, two with up to two (up to 8 covered entries) or one (up to 16); interpolated mode:
+// one queued entry with up to two far ones.
 int plan(const FwdArgs& f, int* n_cov, int* n_q, int* n_far) {
   *n_q = 0;
   if (f.plan != nullptr) {

@@ -48,12 +48,13 @@ constexpr int kMirror = 32;
 static_assert(kP == kRingRows && kMaxBand == kBandRows && kMaxCov == kSplitCov && kMaxFar == kSplitFar,
               "ring geometry and RingSplit must agree");
 
-// Queued table entries (integer forward): a distance a few steps beyond the ring reach whose
-// 16-row slab is read from the ring `depth` steps before its queries run, while its rows are
-// still there, and held in registers until then. The slab of the wave's queries p + 16w..
-// at distance d is rows p + 16w - d.. : read at step p - depth * T (T rows per step), they
-// lie inside the ring then (ring rows p - depth T - reach .. p - depth T + T - 1) exactly when
-// depth * T <= d <= reach + depth * T. Two queue slots, with these depths.
+// Queued table entries (forward): a distance a few steps beyond the ring reach whose 16-row
+// slab is read from the ring `depth` steps before its queries run, while its rows are still
+// there, and held in registers until then. The slab of the wave's queries p + 16w.. at
+// distance d is rows p + 16w - d.. : read at step p - depth * T (T rows per step), they lie
+// inside the ring then (ring rows p - depth T - reach .. p - depth T + T - 1) exactly when
+// depth * T <= d <= reach + depth * T. Two queue slots, with these depths (interpolated
+// mode uses the first).
 constexpr int kMaxQ = 2;
 constexpr int kQDepth0 = 2;
 constexpr int kQDepth1 = 5;
