@@ -310,6 +310,9 @@ QUEUED = [
     (1, 8, 60000, 12, 1.0, tuple(range(20, 380, 25)) + (600, 900, 1300)),  # 15 covered
     (1, 8, 60000, 12, 1.0, (1, 2, 500, 1100, 1300)),  # slot 0 only, two far
     (1, 8, 60000, 12, 1.37, FIB_BASE),             # interpolated weights 0.51 (queued), ...
+    (1, 8, 60000, 12, 1.0, (1, 2, 500)),           # one queued entry, no far entry
+    (1, 8, 60000, 12, 1.0, (1, 2, 500, 1100)),     # one queued, one far
+    (1, 8, 70000, 1, 1.5, FIB_BASE),               # W 1: 12 covered entries, then 566, 915, 1480
 ]
 
 
